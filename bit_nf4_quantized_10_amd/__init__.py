@@ -1,0 +1,221 @@
+"""Python binding of the MI355X QLoRA NF4 library (libqlora_nf4.so).
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind the C ABI declared in include/qlora_nf4.h.  PyTorch provides device
+memory and the current stream.  There is no CPU fallback: if the library is
+not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqlora_nf4.so")
+
+NF4_OK, NF4_EINVAL, NF4_ENONFINITE, NF4_EPADDING, NF4_EHIP = 0, 1, 2, 4, 8
+NF4_OUT_F32, NF4_OUT_BF16 = 0, 1
+KERNEL_IDS = {
+    "quant_pass1": 0, "quant_mean": 1, "quant_pass2": 2, "dequant": 3, "lora_down": 4,
+    "fwd_gemm": 5, "fwd_gemv": 6, "bwd_dz": 7, "bwd_dx": 8, "bwd_da": 9, "bwd_db": 10,
+    "reduce": 11,
+}
+C_FUNCTIONS = [
+    "nf4_sizes", "nf4_quantize", "nf4_dequantize", "qlora_workspace_bytes",
+    "qlora_linear_fwd", "qlora_linear_bwd", "nf4_status_read", "qlora_timer_enable",
+    "qlora_timer_read", "nf4_error_string",
+]
+
+
+class NF4Error(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: error {code}")
+        self.code = code
+
+
+class _State(ctypes.Structure):
+    _fields_ = [("numel", ctypes.c_int64), ("codes", ctypes.c_void_p), ("qabsmax", ctypes.c_void_p),
+                ("absmax2", ctypes.c_void_p), ("offset", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m bit_nf4_quantized_10_amd.build_lib`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, i32p = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
+        sp = ctypes.POINTER(_State)
+        L.nf4_sizes.argtypes = [i64] + [ctypes.POINTER(i64)] * 4
+        L.nf4_quantize.argtypes = [vp, sp, vp, i64, i32p, vp]
+        L.nf4_dequantize.argtypes = [sp, vp, ctypes.c_int, i32p, vp]
+        L.qlora_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        L.qlora_linear_fwd.argtypes = [i64, i64, i64, i64, vp, sp, vp, vp, ctypes.c_float, vp, vp, vp, i64, vp]
+        L.qlora_linear_bwd.argtypes = [i64, i64, i64, i64, vp, vp, vp, sp, vp, vp, ctypes.c_float,
+                                       vp, vp, vp, vp, i64, vp]
+        L.nf4_status_read.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), vp]
+        L.qlora_timer_enable.argtypes = [ctypes.c_int, ctypes.c_int]
+        L.qlora_timer_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+        L.nf4_error_string.argtypes = [ctypes.c_int]
+        L.nf4_error_string.restype = ctypes.c_char_p
+        for name in C_FUNCTIONS[:-1]:
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != NF4_OK:
+        raise NF4Error(rc, f"{what} ({lib().nf4_error_string(rc).decode()})")
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _require_cuda(t, name: str, dtype=None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+@dataclass
+class NF4State:
+    """Frozen NF4 state of one weight tensor (device tensors)."""
+    numel: int
+    codes: "torch.Tensor"     # uint8[ceil(P/2)]
+    qabsmax: "torch.Tensor"   # int8[n1]
+    absmax2: "torch.Tensor"   # float32[n2]
+    offset: "torch.Tensor"    # float32[1]
+
+    def c_struct(self) -> _State:
+        return _State(self.numel, self.codes.data_ptr(), self.qabsmax.data_ptr(),
+                      self.absmax2.data_ptr(), self.offset.data_ptr())
+
+
+def nf4_sizes(numel: int) -> dict:
+    out = [ctypes.c_int64() for _ in range(4)]
+    _check(lib().nf4_sizes(numel, *[ctypes.byref(o) for o in out]), "nf4_sizes")
+    return dict(zip(("code_bytes", "n1", "n2", "quant_workspace_bytes"), (o.value for o in out)))
+
+
+def empty_state(numel: int, device="cuda") -> NF4State:
+    import torch
+    s = nf4_sizes(numel)
+    return NF4State(numel, torch.empty(s["code_bytes"], dtype=torch.uint8, device=device),
+                    torch.empty(s["n1"], dtype=torch.int8, device=device),
+                    torch.empty(s["n2"], dtype=torch.float32, device=device),
+                    torch.empty(1, dtype=torch.float32, device=device))
+
+
+def nf4_quantize(W, state: NF4State | None = None, workspace=None, status=None, stream=None):
+    """Encode fp32 weights (any shape, flattened row-major) into an NF4State.
+    Returns (state, status) where status is the device int32 status word."""
+    import torch
+    _require_cuda(W, "W", torch.float32)
+    P = W.numel()
+    if state is None:
+        state = empty_state(P, W.device)
+    sizes = nf4_sizes(P)
+    if workspace is None:
+        workspace = torch.empty(sizes["quant_workspace_bytes"], dtype=torch.uint8, device=W.device)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=W.device)
+    st = state.c_struct()
+    _check(lib().nf4_quantize(W.data_ptr(), ctypes.byref(st), workspace.data_ptr(), workspace.numel(),
+                              status.data_ptr(), _stream(stream)), "nf4_quantize")
+    return state, status
+
+
+def nf4_dequantize(state: NF4State, out_dtype: str = "bf16", out=None, status=None, stream=None):
+    import torch
+    dt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    if out is None:
+        out = torch.empty(state.numel, dtype=dt, device=state.codes.device)
+    st = state.c_struct()
+    _check(lib().nf4_dequantize(ctypes.byref(st), out.data_ptr(),
+                                NF4_OUT_BF16 if out_dtype == "bf16" else NF4_OUT_F32,
+                                _ptr(status), _stream(stream)), "nf4_dequantize")
+    return out
+
+
+def nf4_status_read(status, stream=None) -> int:
+    v = ctypes.c_int32()
+    _check(lib().nf4_status_read(status.data_ptr(), ctypes.byref(v), _stream(stream)), "nf4_status_read")
+    return v.value
+
+
+def qlora_workspace_bytes(M: int, K: int, N: int, r: int) -> tuple[int, int]:
+    f, b = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().qlora_workspace_bytes(M, K, N, r, ctypes.byref(f), ctypes.byref(b)), "qlora_workspace_bytes")
+    return f.value, b.value
+
+
+def qlora_linear_fwd(X, state: NF4State, A, B, c: float, K: int, N: int, Y=None, Z=None,
+                     workspace=None, stream=None):
+    """Y = X Ŵ + c (X A) B.  X: M x K bf16, A: K x r, B: r x N.  Returns (Y, Z)."""
+    import torch
+    M, r = X.shape[0], A.shape[1]
+    for t, n in ((X, "X"), (A, "A"), (B, "B")):
+        _require_cuda(t, n, torch.bfloat16)
+    if Y is None:
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device=X.device)
+    if Z is None:
+        Z = torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
+    if workspace is None:
+        workspace = torch.empty(max(qlora_workspace_bytes(M, K, N, r)[0], 256), dtype=torch.uint8,
+                                device=X.device)
+    st = state.c_struct()
+    _check(lib().qlora_linear_fwd(M, K, N, r, X.data_ptr(), ctypes.byref(st), A.data_ptr(), B.data_ptr(),
+                                  float(c), Y.data_ptr(), Z.data_ptr(), workspace.data_ptr(),
+                                  workspace.numel(), _stream(stream)), "qlora_linear_fwd")
+    return Y, Z
+
+
+def qlora_linear_bwd(G, X, Z, state: NF4State, A, B, c: float, K: int, N: int, need_dx: bool = True,
+                     dX=None, dA=None, dB=None, workspace=None, stream=None):
+    """dZ = c G Bᵀ, dA = Xᵀ dZ, dB = c Zᵀ G, dX = G Ŵᵀ + dZ Aᵀ.  Returns (dX, dA, dB)."""
+    import torch
+    M, r = X.shape[0], A.shape[1]
+    for t, n in ((G, "G"), (X, "X"), (Z, "Z"), (A, "A"), (B, "B")):
+        _require_cuda(t, n, torch.bfloat16)
+    if need_dx and dX is None:
+        dX = torch.empty(M, K, dtype=torch.bfloat16, device=X.device)
+    if dA is None:
+        dA = torch.empty(K, r, dtype=torch.float32, device=X.device)
+    if dB is None:
+        dB = torch.empty(r, N, dtype=torch.float32, device=X.device)
+    if workspace is None:
+        workspace = torch.empty(max(qlora_workspace_bytes(M, K, N, r)[1], 256), dtype=torch.uint8,
+                                device=X.device)
+    st = state.c_struct()
+    _check(lib().qlora_linear_bwd(M, K, N, r, G.data_ptr(), X.data_ptr(), Z.data_ptr(), ctypes.byref(st),
+                                  A.data_ptr(), B.data_ptr(), float(c), _ptr(dX if need_dx else None),
+                                  dA.data_ptr(), dB.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                  _stream(stream)), "qlora_linear_bwd")
+    return (dX if need_dx else None), dA, dB
+
+
+def qlora_timer_enable(kernel: str, enable: bool = True) -> None:
+    _check(lib().qlora_timer_enable(KERNEL_IDS[kernel], int(enable)), "qlora_timer_enable")
+
+
+def qlora_timer_read(kernel: str) -> tuple[float, int]:
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(lib().qlora_timer_read(KERNEL_IDS[kernel], ctypes.byref(ms), ctypes.byref(n)), "qlora_timer_read")
+    return ms.value, n.value

@@ -1,0 +1,198 @@
+// C ABI of the QLoRA NF4 library: argument validation, workspace carving and
+// dispatch onto the caller's stream.  No allocation, no synchronisation
+// (except nf4_status_read and qlora_timer_read, which exist to wait).
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/qlora_nf4.h"
+#include "kernels.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+void counts(int64_t P, int64_t* n1, int64_t* n2) {
+  *n1 = (P + NF4_BLOCK1 - 1) / NF4_BLOCK1;
+  *n2 = (*n1 + NF4_BLOCK2 - 1) / NF4_BLOCK2;
+}
+
+bool state_ok(const nf4_state_t* s) {
+  return s != nullptr && s->numel >= 1 && s->codes != nullptr && s->qabsmax != nullptr &&
+         s->absmax2 != nullptr && s->offset != nullptr;
+}
+
+bool layer_shape_ok(int64_t M, int64_t K, int64_t N, int64_t r) {
+  return M >= 1 && K >= 1 && N >= 1 && r >= 1 && N % NF4_BLOCK1 == 0 && K % 8 == 0 && r % 8 == 0 &&
+         r <= 256 && M <= (int64_t(1) << 20) && K <= (int64_t(1) << 24) && N <= (int64_t(1) << 24);
+}
+
+// ---------------------------------------------------------------- timers
+struct TimerSlot {
+  bool enabled = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
+  std::vector<hipEvent_t> pool;
+};
+std::mutex g_timer_mu;
+TimerSlot g_timers[QK_NUM_KERNELS];
+
+hipEvent_t take_event(TimerSlot& s) {
+  if (!s.pool.empty()) {
+    hipEvent_t e = s.pool.back();
+    s.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+namespace qn {
+
+Timer::Timer(int kernel_id, hipStream_t stream) : id_(kernel_id), stream_(stream), stop_event_(nullptr) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  TimerSlot& s = g_timers[id_];
+  if (!s.enabled) return;
+  hipEvent_t a = take_event(s), b = take_event(s);
+  if (a == nullptr || b == nullptr) return;
+  (void)hipEventRecord(a, stream_);
+  s.pending.emplace_back(a, b);
+  stop_event_ = b;
+}
+
+void Timer::stop() {
+  if (stop_event_ != nullptr) (void)hipEventRecord(static_cast<hipEvent_t>(stop_event_), stream_);
+  stop_event_ = nullptr;
+}
+
+}  // namespace qn
+
+extern "C" {
+
+int nf4_sizes(int64_t numel, int64_t* code_bytes, int64_t* n1, int64_t* n2, int64_t* quant_workspace_bytes) {
+  if (numel < 1) return NF4_EINVAL;
+  int64_t a, b;
+  counts(numel, &a, &b);
+  if (code_bytes) *code_bytes = (numel + 1) / 2;
+  if (n1) *n1 = a;
+  if (n2) *n2 = b;
+  if (quant_workspace_bytes) *quant_workspace_bytes = align256(4 * a) + align256(8 * b);
+  return NF4_OK;
+}
+
+int nf4_quantize(const float* W, const nf4_state_t* out, void* workspace, int64_t workspace_bytes,
+                 int32_t* status, void* stream) {
+  if (W == nullptr || !state_ok(out) || workspace == nullptr || status == nullptr) return NF4_EINVAL;
+  if (!aligned16(W) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return NF4_EINVAL;
+  int64_t n1, n2, need;
+  nf4_sizes(out->numel, nullptr, &n1, &n2, &need);
+  if (workspace_bytes < need) return NF4_EINVAL;
+  if (n2 > 0x7fffffff) return NF4_EINVAL;
+  char* ws = static_cast<char*>(workspace);
+  float* ws_absmax = reinterpret_cast<float*>(ws);
+  double* ws_gsum = reinterpret_cast<double*>(ws + align256(4 * n1));
+  hipError_t e = qn::launch_quantize(W, out->numel, out->codes, out->qabsmax, out->absmax2, out->offset,
+                                     ws_absmax, ws_gsum, status, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4_OK : NF4_EHIP;
+}
+
+int nf4_dequantize(const nf4_state_t* state, void* out, int out_dtype, int32_t* status, void* stream) {
+  if (!state_ok(state) || out == nullptr || !aligned16(out)) return NF4_EINVAL;
+  if (out_dtype != NF4_OUT_F32 && out_dtype != NF4_OUT_BF16) return NF4_EINVAL;
+  hipError_t e = qn::launch_dequantize(state->codes, state->qabsmax, state->absmax2, state->offset,
+                                       state->numel, out, out_dtype, status, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4_OK : NF4_EHIP;
+}
+
+int qlora_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r, int64_t* fwd_bytes, int64_t* bwd_bytes) {
+  if (!layer_shape_ok(M, K, N, r)) return NF4_EINVAL;
+  if (fwd_bytes) *fwd_bytes = qn::fwd_workspace_bytes(M, K, N, r);
+  if (bwd_bytes) *bwd_bytes = qn::bwd_workspace_bytes(M, K, N, r);
+  return NF4_OK;
+}
+
+int qlora_linear_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const nf4_state_t* W,
+                     const uint16_t* A, const uint16_t* B, float c, uint16_t* Y, uint16_t* Z, void* workspace,
+                     int64_t workspace_bytes, void* stream) {
+  if (!layer_shape_ok(M, K, N, r) || !state_ok(W) || W->numel != K * N) return NF4_EINVAL;
+  if (!X || !A || !B || !Y || !Z || !workspace) return NF4_EINVAL;
+  if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y) || !aligned16(Z) ||
+      !aligned16(W->codes) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return NF4_EINVAL;
+  if (workspace_bytes < qn::fwd_workspace_bytes(M, K, N, r)) return NF4_EINVAL;
+  qn::NF4View v{W->codes, W->qabsmax, W->absmax2, W->offset};
+  hipError_t e = qn::launch_fwd(M, K, N, r, X, v, A, B, c, Y, Z, workspace, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4_OK : NF4_EHIP;
+}
+
+int qlora_linear_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* X,
+                     const uint16_t* Z, const nf4_state_t* W, const uint16_t* A, const uint16_t* B, float c,
+                     uint16_t* dX, float* dA, float* dB, void* workspace, int64_t workspace_bytes,
+                     void* stream) {
+  if (!layer_shape_ok(M, K, N, r) || !state_ok(W) || W->numel != K * N) return NF4_EINVAL;
+  if (!G || !X || !Z || !A || !B || !dA || !dB || !workspace) return NF4_EINVAL;
+  if (!aligned16(G) || !aligned16(X) || !aligned16(Z) || !aligned16(A) || !aligned16(B) || !aligned16(dA) ||
+      !aligned16(dB) || (dX && !aligned16(dX)) || !aligned16(W->codes) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return NF4_EINVAL;
+  if (workspace_bytes < qn::bwd_workspace_bytes(M, K, N, r)) return NF4_EINVAL;
+  qn::NF4View v{W->codes, W->qabsmax, W->absmax2, W->offset};
+  hipError_t e = qn::launch_bwd(M, K, N, r, G, X, Z, v, A, B, c, dX, dA, dB, workspace,
+                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4_OK : NF4_EHIP;
+}
+
+int nf4_status_read(const int32_t* status, int32_t* host_value, void* stream) {
+  if (status == nullptr || host_value == nullptr) return NF4_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) return NF4_EHIP;
+  if (hipMemcpy(host_value, status, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess) return NF4_EHIP;
+  return NF4_OK;
+}
+
+int qlora_timer_enable(int kernel_id, int enable) {
+  if (kernel_id < 0 || kernel_id >= QK_NUM_KERNELS) return NF4_EINVAL;
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  g_timers[kernel_id].enabled = enable != 0;
+  return NF4_OK;
+}
+
+int qlora_timer_read(int kernel_id, double* total_ms, int64_t* launches) {
+  if (kernel_id < 0 || kernel_id >= QK_NUM_KERNELS || total_ms == nullptr || launches == nullptr)
+    return NF4_EINVAL;
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  TimerSlot& s = g_timers[kernel_id];
+  double total = 0.0;
+  int64_t n = 0;
+  int rc = NF4_OK;
+  for (auto& pr : s.pending) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(pr.second) != hipSuccess || hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess)
+      rc = NF4_EHIP;
+    total += ms;
+    ++n;
+    s.pool.push_back(pr.first);
+    s.pool.push_back(pr.second);
+  }
+  s.pending.clear();
+  *total_ms = total;
+  *launches = n;
+  return rc;
+}
+
+const char* nf4_error_string(int code) {
+  switch (code) {
+    case NF4_OK: return "ok";
+    case NF4_EINVAL: return "invalid argument";
+    case NF4_ENONFINITE: return "non-finite weight or reconstruction";
+    case NF4_EPADDING: return "pad nibble of an odd-length payload is not code 7";
+    case NF4_EHIP: return "HIP runtime error";
+    default: return "several status bits set";
+  }
+}
+
+}  // extern "C"

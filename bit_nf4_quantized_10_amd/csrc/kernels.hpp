@@ -1,0 +1,50 @@
+// Host-side declarations shared by the kernel translation units and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qn {
+
+// Optional per-kernel event timer (see qlora_timer_enable).  Construct right
+// before a launch, call stop() right after it; a no-op unless enabled.
+class Timer {
+ public:
+  Timer(int kernel_id, hipStream_t stream);
+  void stop();
+
+ private:
+  int id_;
+  hipStream_t stream_;
+  void* stop_event_;
+};
+
+hipError_t launch_quantize(const float* W, int64_t P, uint8_t* codes, int8_t* qabsmax,
+                           float* absmax2, float* offset, float* ws_absmax, double* ws_gsum,
+                           int32_t* status, hipStream_t stream);
+
+hipError_t launch_dequantize(const uint8_t* codes, const int8_t* qabsmax, const float* absmax2,
+                             const float* offset, int64_t P, void* out, int out_dtype,
+                             int32_t* status, hipStream_t stream);
+
+struct NF4View {
+  const uint8_t* codes;
+  const int8_t* qabsmax;
+  const float* absmax2;
+  const float* offset;
+};
+
+// Workspace needs (bytes) of the layer kernels; the C ABI adds them up.
+int64_t fwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r);
+int64_t bwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r);
+
+hipError_t launch_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W,
+                      const uint16_t* A, const uint16_t* B, float c, uint16_t* Y, uint16_t* Z,
+                      void* ws, hipStream_t stream);
+
+hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G,
+                      const uint16_t* X, const uint16_t* Z, NF4View W, const uint16_t* A,
+                      const uint16_t* B, float c, uint16_t* dX, float* dA, float* dB, void* ws,
+                      hipStream_t stream);
+
+}  // namespace qn

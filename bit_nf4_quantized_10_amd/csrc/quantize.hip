@@ -1,0 +1,316 @@
+// NF4 encoder and decoder kernels for gfx950.
+//
+// Encoding follows the page "QLoRA：冻结的 4-bit 权重怎样参与一次微调":
+// per 64-weight block the absmax a (scale 1 for an all-zero block), the NF4
+// code nearest to w / a with ties to the smaller index, two codes per byte
+// with the first in the high nibble and code 7 as odd-length padding
+// (sections "NF4 保存的是索引而不是均匀整数值", "从 NF4 索引打包成字节");
+// then the double quantization of the absmax values: global mean offset,
+// centred values coded in 8 bits per group of 256 with an fp32 scale
+// (section "Double Quantization 压缩的是 Scale").
+//
+// Exactness: the nearest code is decided without dividing.  With m_j the
+// midpoint of codes j and j+1 (exact in double) the code is the number of
+// midpoints strictly below w / a, and "w > m_j * a" is decided exactly in
+// double because m_j has at most 26 significant bits and a at most 24, so
+// the product is exact.  A 256-bin table indexed by an fp32 estimate of
+// w / a names the one midpoint that can lie near it (bins are 1/128 wide and
+// padded by 2^-12, far below the 0.08 gap between midpoints), so each weight
+// costs one double comparison.  The same argument, with the 255 midpoints of
+// the linear 8-bit code, decides the second-level codes.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qn {
+
+namespace {
+
+constexpr int kQuantThreads = 256;
+constexpr double kBinPad = 0x1p-12;
+
+__device__ __forceinline__ float dpp_max_row8(float x) {
+  // max over each aligned group of 8 lanes: xor 1, xor 2 (quad_perm), then
+  // the half-row mirror pairs quads {0..3} <-> {7..4}.
+  int v = __builtin_bit_cast(int, x);
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false)));
+  v = __builtin_bit_cast(int, x);
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false)));
+  v = __builtin_bit_cast(int, x);
+  x = fmaxf(x, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false)));
+  return x;
+}
+
+// Midpoint between NF4 codes j and j+1, exact in double; +4 for j = 15 so a
+// comparison against it is always false.
+__device__ __forceinline__ double nf4_midpoint(int j) {
+  return j < 15 ? 0.5 * (static_cast<double>(kNF4[j]) + static_cast<double>(kNF4[j + 1])) : 4.0;
+}
+
+}  // namespace
+
+// Pass 1: one workgroup per group of 256 blocks (16384 weights).  Each lane
+// owns 8 consecutive weights; 8 lanes form a block.  Writes the packed codes,
+// the exact fp32 absmax per block and the fp64 stride-halving sum of the
+// group's absmax values.
+__global__ __launch_bounds__(kQuantThreads) void nf4_quant_pass1_kernel(
+    const float* __restrict__ W, int64_t P, uint8_t* __restrict__ codes,
+    float* __restrict__ absmax, double* __restrict__ group_sum, int32_t* __restrict__ status) {
+  __shared__ uint8_t s_bin[256];
+  __shared__ double s_mid[16];
+  __shared__ float s_abs[kBlock2];
+
+  const int tid = threadIdx.x;
+  {
+    // bin b covers estimates in [b/128 - 1, (b+1)/128 - 1); its entry is the
+    // number of midpoints below the padded lower edge.
+    const double lo = static_cast<double>(tid) / 128.0 - 1.0 - kBinPad;
+    int cnt = 0;
+    for (int j = 0; j < 15; ++j) cnt += nf4_midpoint(j) < lo ? 1 : 0;
+    s_bin[tid] = static_cast<uint8_t>(cnt);
+    if (tid < 16) s_mid[tid] = nf4_midpoint(tid);
+  }
+  __syncthreads();
+
+  const int64_t n1 = (P + kBlock1 - 1) / kBlock1;
+  const int64_t code_bytes = (P + 1) / 2;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int sub = lane & 7;
+  bool bad = false;
+
+  for (int it = 0; it < 8; ++it) {
+    const int bl = wave * 64 + it * 8 + (lane >> 3);   // block within the group
+    const int64_t block = static_cast<int64_t>(blockIdx.x) * kBlock2 + bl;
+    const int64_t e0 = block * kBlock1 + sub * 8;
+    float w[8];
+    if (e0 + 8 <= P) {
+      const float4 v0 = *reinterpret_cast<const float4*>(W + e0);
+      const float4 v1 = *reinterpret_cast<const float4*>(W + e0 + 4);
+      w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
+      w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = (e0 + i < P) ? W[e0 + i] : 0.0f;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      bad |= !is_finite_bits(w[i]);
+      m = fmaxf(m, fabsf(w[i]));
+    }
+    m = dpp_max_row8(m);
+    const float a = (m == 0.0f) ? 1.0f : m;
+    // fp32 estimate of w / a; tiny scales are lifted by 2^64 first so that
+    // the reciprocal stays finite (exact power-of-two scaling).
+    const float lift = (a < 0x1p-100f) ? 0x1p64f : 1.0f;
+    const float inv = 1.0f / (a * lift);
+    const double ad = static_cast<double>(a);
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float est = (w[i] * lift) * inv;
+      int bin = static_cast<int>(floorf(fmaf(est, 128.0f, 128.0f)));
+      bin = min(max(bin, 0), 255);
+      const int L = s_bin[bin];
+      const int code = L + ((static_cast<double>(w[i]) > s_mid[L] * ad) ? 1 : 0);
+      // byte i/2 of the little-endian word: even i -> high nibble
+      word |= static_cast<uint32_t>(code) << (8 * (i >> 1) + ((i & 1) ? 0 : 4));
+    }
+    if (e0 + 8 <= P) {
+      *reinterpret_cast<uint32_t*>(codes + e0 / 2) = word;
+    } else if (e0 < P) {
+      for (int b = 0; b < 4; ++b) {
+        const int64_t byte_idx = e0 / 2 + b;
+        if (byte_idx < code_bytes) codes[byte_idx] = static_cast<uint8_t>(word >> (8 * b));
+      }
+    }
+    if (sub == 0) {
+      if (block < n1) absmax[block] = a;
+      s_abs[bl] = (block < n1) ? a : 0.0f;
+    }
+  }
+  if (bad) atomicOr(status, NF4_ENONFINITE);
+  __syncthreads();
+
+  if (wave == 0) {
+    // stride-halving fp64 sum of the 256 values (pairs i, i+128; i, i+64; ...)
+    const double s0 = static_cast<double>(s_abs[lane]) + static_cast<double>(s_abs[lane + 128]);
+    const double s1 = static_cast<double>(s_abs[lane + 64]) + static_cast<double>(s_abs[lane + 192]);
+    double t = s0 + s1;
+    for (int h = 32; h >= 1; h >>= 1) t = t + __shfl_down(t, h, 64);
+    if (lane == 0) group_sum[blockIdx.x] = t;
+  }
+}
+
+// Offset: stride-halving fp64 sum of the n2 group sums (zero-padded to a
+// power of two), divided by n1 in fp64 and rounded to fp32.  One workgroup.
+// Thread t first sums {x[t + s*T]} for s < L/T in stride-halving order,
+// computed as the adjacent-pairwise sum of the bit-reversed sequence.
+__global__ __launch_bounds__(kQuantThreads) void nf4_quant_mean_kernel(
+    const double* __restrict__ group_sum, int64_t n2, int64_t n1, float* __restrict__ offset) {
+  __shared__ double s_x[kQuantThreads];
+  const int tid = threadIdx.x;
+  int64_t L = 1;
+  while (L < n2) L <<= 1;
+  double v = 0.0;
+  if (L <= kQuantThreads) {
+    v = (tid < n2) ? group_sum[tid] : 0.0;
+  } else {
+    const int64_t S = L / kQuantThreads;
+    int lg = 0;
+    while ((int64_t(1) << lg) < S) ++lg;
+    double stack[40];
+    for (int64_t i = 0; i < S; ++i) {
+      int64_t s = 0;
+      for (int b = 0; b < lg; ++b) s |= ((i >> b) & 1) << (lg - 1 - b);
+      const int64_t idx = tid + s * kQuantThreads;
+      double x = (idx < n2) ? group_sum[idx] : 0.0;
+      int l = 0;
+      while ((i >> l) & 1) {
+        x = stack[l] + x;
+        ++l;
+      }
+      stack[l] = x;
+    }
+    v = stack[lg];
+  }
+  s_x[tid] = v;
+  __syncthreads();
+  for (int h = kQuantThreads / 2; h >= 1; h >>= 1) {
+    if (tid < h) s_x[tid] = s_x[tid] + s_x[tid + h];
+    __syncthreads();
+  }
+  if (tid == 0) offset[0] = __double2float_rn(__ddiv_rn(s_x[0], static_cast<double>(n1)));
+}
+
+// Pass 2: one workgroup per group of 256 first-level scales.  c = a - offset
+// (fp32), s2 = max |c| (1 if zero), q = nearest fl32(q/127) to c / s2 with
+// ties to the smaller q.  Also checks that the reconstructed scale is finite.
+__global__ __launch_bounds__(kQuantThreads) void nf4_quant_pass2_kernel(
+    const float* __restrict__ absmax, int64_t n1, const float* __restrict__ offset,
+    int8_t* __restrict__ qabsmax, float* __restrict__ absmax2, int32_t* __restrict__ status) {
+  __shared__ float s_red[kQuantThreads / 64];
+  const int tid = threadIdx.x;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kBlock2 + tid;
+  const bool valid = idx < n1;
+  const float off = offset[0];
+  const float c = valid ? __fsub_rn(absmax[idx], off) : 0.0f;
+  float m = fabsf(c);
+  for (int h = 32; h >= 1; h >>= 1) m = fmaxf(m, __shfl_xor(m, h, 64));
+  if ((tid & 63) == 0) s_red[tid >> 6] = m;
+  __syncthreads();
+  float s2 = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  if (s2 == 0.0f) s2 = 1.0f;
+  if (!valid) return;
+
+  const float est = __fdiv_rn(c, s2);
+  int q = static_cast<int>(rintf(est * static_cast<float>(kLevels2)));
+  q = min(max(q, -kLevels2), kLevels2);
+  const double cd = c, sd = s2;
+  auto mid = [](int k) {  // midpoint between codes k and k+1, exact in double
+    return 0.5 * (static_cast<double>(q2_value(k)) + static_cast<double>(q2_value(k + 1)));
+  };
+  for (int it = 0; it < 2; ++it)
+    if (q > -kLevels2 && cd <= mid(q - 1) * sd) --q;
+  for (int it = 0; it < 2; ++it)
+    if (q < kLevels2 && cd > mid(q) * sd) ++q;
+  qabsmax[idx] = static_cast<int8_t>(q);
+  if (tid == 0) absmax2[blockIdx.x] = s2;
+  if (!is_finite_bits(absmax_hat(q, s2, off))) atomicOr(status, NF4_ENONFINITE);
+}
+
+// Decoder: each thread turns one 32-bit code word (8 weights) into fp32 or
+// bf16 reconstructions; grid-stride over the words.
+__global__ __launch_bounds__(kQuantThreads) void nf4_dequant_kernel(
+    const uint8_t* __restrict__ codes, const int8_t* __restrict__ qabsmax,
+    const float* __restrict__ absmax2, const float* __restrict__ offset, int64_t P,
+    void* __restrict__ out, int out_dtype, int32_t* __restrict__ status) {
+  __shared__ float s_lut[16];
+  if (threadIdx.x < 16) s_lut[threadIdx.x] = kNF4[threadIdx.x];
+  __syncthreads();
+  const float off = offset[0];
+  const int64_t words = (P + 7) / 8;
+  const int64_t code_bytes = (P + 1) / 2;
+  for (int64_t wi = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; wi < words;
+       wi += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t e0 = wi * 8;
+    uint32_t word;
+    if (e0 + 8 <= P) {
+      word = *reinterpret_cast<const uint32_t*>(codes + wi * 4);
+    } else {
+      word = 0;
+      for (int b = 0; b < 4; ++b)
+        if (wi * 4 + b < code_bytes) word |= static_cast<uint32_t>(codes[wi * 4 + b]) << (8 * b);
+      if ((P & 1) && status) {
+        const uint32_t last = codes[code_bytes - 1];
+        if ((last & 15u) != 7u) atomicOr(status, NF4_EPADDING);
+      }
+    }
+    const int64_t block = e0 / kBlock1;
+    const float ahat = absmax_hat(qabsmax[block], absmax2[block / kBlock2], off);
+    float v[8];
+    decode8(word, ahat, s_lut, v);
+    if (out_dtype == NF4_OUT_BF16) {
+      uint16_t* o = static_cast<uint16_t*>(out) + e0;
+      if (e0 + 8 <= P) {
+        uint4 pk;
+        pk.x = pack_bf16x2(v[0], v[1]);
+        pk.y = pack_bf16x2(v[2], v[3]);
+        pk.z = pack_bf16x2(v[4], v[5]);
+        pk.w = pack_bf16x2(v[6], v[7]);
+        *reinterpret_cast<uint4*>(o) = pk;
+      } else {
+        for (int i = 0; i < 8; ++i)
+          if (e0 + i < P) o[i] = static_cast<uint16_t>(pack_bf16x2(v[i], 0.0f) & 0xffffu);
+      }
+    } else {
+      float* o = static_cast<float*>(out) + e0;
+      if (e0 + 8 <= P) {
+        *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      } else {
+        for (int i = 0; i < 8; ++i)
+          if (e0 + i < P) o[i] = v[i];
+      }
+    }
+  }
+}
+
+__global__ void nf4_status_clear_kernel(int32_t* status) { status[0] = 0; }
+
+// ----------------------------------------------------------------- launchers
+hipError_t launch_quantize(const float* W, int64_t P, uint8_t* codes, int8_t* qabsmax,
+                           float* absmax2, float* offset, float* ws_absmax, double* ws_gsum,
+                           int32_t* status, hipStream_t stream) {
+  const int64_t n1 = (P + kBlock1 - 1) / kBlock1;
+  const int64_t n2 = (n1 + kBlock2 - 1) / kBlock2;
+  hipLaunchKernelGGL(nf4_status_clear_kernel, dim3(1), dim3(1), 0, stream, status);
+  Timer t1(QK_QUANT_PASS1, stream);
+  hipLaunchKernelGGL(nf4_quant_pass1_kernel, dim3(static_cast<unsigned>(n2)), dim3(kQuantThreads), 0,
+                     stream, W, P, codes, ws_absmax, ws_gsum, status);
+  t1.stop();
+  Timer t2(QK_QUANT_MEAN, stream);
+  hipLaunchKernelGGL(nf4_quant_mean_kernel, dim3(1), dim3(kQuantThreads), 0, stream, ws_gsum, n2, n1,
+                     offset);
+  t2.stop();
+  Timer t3(QK_QUANT_PASS2, stream);
+  hipLaunchKernelGGL(nf4_quant_pass2_kernel, dim3(static_cast<unsigned>(n2)), dim3(kQuantThreads), 0,
+                     stream, ws_absmax, n1, offset, qabsmax, absmax2, status);
+  t3.stop();
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, const int8_t* qabsmax, const float* absmax2,
+                             const float* offset, int64_t P, void* out, int out_dtype,
+                             int32_t* status, hipStream_t stream) {
+  const int64_t words = (P + 7) / 8;
+  int64_t blocks = (words + kQuantThreads - 1) / kQuantThreads;
+  if (blocks > 65536) blocks = 65536;
+  Timer t(QK_DEQUANT, stream);
+  hipLaunchKernelGGL(nf4_dequant_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kQuantThreads), 0,
+                     stream, codes, qabsmax, absmax2, offset, P, out, out_dtype, status);
+  t.stop();
+  return hipGetLastError();
+}
+
+}  // namespace qn

@@ -1,0 +1,162 @@
+/*
+ * qlora_nf4.h - C ABI of the MI355X (gfx950) QLoRA NF4 linear-layer library.
+ *
+ * The library computes, on one GPU, the frozen-base encoding and the layer of
+ * the page "QLoRA：冻结的 4-bit 权重怎样参与一次微调" (charlestar.github.io):
+ *   - NF4 encoding of a weight in blocks of 64 with an fp32 absmax per block,
+ *     nearest code with ties to the smaller index, two codes per byte with the
+ *     first code in the high nibble and code 7 padding an odd length
+ *     (sections "NF4 保存的是索引而不是均匀整数值", "从 NF4 索引打包成字节");
+ *   - double quantization of those absmax values: mean offset, 8-bit codes in
+ *     blocks of 256 with one fp32 scale per block (section
+ *     "Double Quantization 压缩的是 Scale");
+ *   - the layer Y = X Ŵ + c (X A) B and its gradients dX, dA, dB, with the
+ *     packed weight frozen (sections "量化基座与可训练支路怎样相加",
+ *     "冻结权重为什么仍然需要输入梯度").
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device buffers are device pointers (HIP), owned by
+ *     the caller; the library never allocates, frees or keeps them.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it and the call returns without synchronising.
+ *   - bf16 tensors are passed as uint16_t bit patterns, row-major, dense.
+ *   - Argument errors are returned synchronously (NF4_EINVAL) before any
+ *     launch; nothing is enqueued then.  Errors found by the GPU (non-finite
+ *     weights, a bad pad nibble) are OR-ed into the caller's device status
+ *     word; read it with nf4_status_read().  Outputs are undefined when a
+ *     call returns non-zero or leaves a non-zero status.
+ *   - Weight layout: W is K x N row-major (index k*N + n).  Blocks of 64 run
+ *     over that flat index, so the layer entry points require N % 64 == 0 so
+ *     that a block never straddles two rows.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return / status codes. */
+#define NF4_OK          0
+#define NF4_EINVAL      1  /* bad argument (NULL, size, alignment, workspace) */
+#define NF4_ENONFINITE  2  /* status bit: a weight or a reconstruction is not finite */
+#define NF4_EPADDING    4  /* status bit: odd length whose pad nibble is not code 7 */
+#define NF4_EHIP        8  /* a HIP runtime call or kernel launch failed */
+
+/* Output dtypes of nf4_dequantize. */
+#define NF4_OUT_F32   0
+#define NF4_OUT_BF16  1
+
+/* Fixed format constants: 64 weights per first-level block, 256 first-level
+ * scales per second-level block, second-level codes q in [-127, 127] standing
+ * for fl32(q / 127) (a signed linear 8-bit code; the page names an 8-bit
+ * codebook without printing it). */
+#define NF4_BLOCK1  64
+#define NF4_BLOCK2  256
+#define NF4_LEVELS2 127
+
+/* The stored, frozen state of one weight tensor (all device pointers). */
+typedef struct nf4_state {
+  int64_t  numel;    /* P, the logical number of weights (>= 1)            */
+  uint8_t* codes;    /* ceil(P/2) bytes, packed NF4 codes                  */
+  int8_t*  qabsmax;  /* n1 = ceil(P/64) second-level codes                 */
+  float*   absmax2;  /* n2 = ceil(n1/256) fp32 second-level scales         */
+  float*   offset;   /* 1 fp32, the mean of the first-level absmax values  */
+} nf4_state_t;
+
+/* Host only.  Sizes of the state of a P-weight tensor (closed forms of the
+ * storage bill in "Double Quantization 压缩的是 Scale") and the workspace
+ * nf4_quantize needs.  Any output pointer may be NULL.  NF4_EINVAL if P < 1. */
+int nf4_sizes(int64_t numel, int64_t* code_bytes, int64_t* n1, int64_t* n2,
+              int64_t* quant_workspace_bytes);
+
+/* Encode P fp32 weights (device, 16-byte aligned) into `out` (all buffers
+ * sized per nf4_sizes; out->numel must equal P).  `workspace` is device
+ * memory of at least quant_workspace_bytes, 256-byte aligned.  `status` is a
+ * device int32 that the call first sets to 0; the GPU ORs NF4_ENONFINITE into
+ * it if a weight is NaN/Inf or a reconstructed scale overflows (the page
+ * rejects both).  Codes use the exact first-level absmax; the offset is the
+ * fp64 fixed-tree mean rounded to fp32. */
+int nf4_quantize(const float* W, const nf4_state_t* out, void* workspace,
+                 int64_t workspace_bytes, int32_t* status, void* stream);
+
+/* Decode a state to P weights: ŵ = fl32(C[j] * â) with
+ * â = fl32(fl32(fl32(q/127) * s2) + offset), written as fp32
+ * (NF4_OUT_F32) or round-to-nearest-even bf16 (NF4_OUT_BF16).  `out` is
+ * device memory of P elements, 16-byte aligned.  `status` (device int32,
+ * may be NULL) receives NF4_EPADDING if P is odd and the last pad nibble is
+ * not 7 (the page's unpack check); it is not cleared first. */
+int nf4_dequantize(const nf4_state_t* state, void* out, int out_dtype,
+                   int32_t* status, void* stream);
+
+/* Host only.  Workspace sizes (bytes) of qlora_linear_fwd and
+ * qlora_linear_bwd for the given shape; NF4_EINVAL for a shape the layer
+ * entry points reject. */
+int qlora_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r,
+                          int64_t* fwd_bytes, int64_t* bwd_bytes);
+
+/* Forward of one QLoRA linear (page section "量化基座与可训练支路怎样相加"):
+ *   Z = X A            (M x r, bf16 output, fp32 accumulation)
+ *   Y = X Ŵ + c Z B    (M x N, bf16 output, fp32 accumulation)
+ * X: M x K bf16, W: state of the K x N weight (W->numel == K*N), A: K x r
+ * bf16, B: r x N bf16, c = alpha / r.  Ŵ is exactly the bf16 weight that
+ * nf4_dequantize(W, NF4_OUT_BF16) returns.  Z is written for the backward
+ * pass.  Requirements: M, K, N, r >= 1, N % 64 == 0, K % 8 == 0, r % 8 == 0,
+ * r <= 256, all pointers 16-byte aligned, workspace >= fwd_bytes.  The
+ * state is only read.  M <= 16 runs the memory-bound dequant-GEMV kernels. */
+int qlora_linear_fwd(int64_t M, int64_t K, int64_t N, int64_t r,
+                     const uint16_t* X, const nf4_state_t* W,
+                     const uint16_t* A, const uint16_t* B, float c,
+                     uint16_t* Y, uint16_t* Z,
+                     void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Backward of the same linear given G = dL/dY (page section
+ * "冻结权重为什么仍然需要输入梯度"):
+ *   dZ = c G Bᵀ,  dA = Xᵀ dZ (K x r fp32),  dB = c Zᵀ G (r x N fp32),
+ *   dX = G Ŵᵀ + dZ Aᵀ (M x K bf16; skipped when dX is NULL).
+ * Z is the forward's Z.  The frozen state receives no gradient and is only
+ * read.  Same requirements as the forward; workspace >= bwd_bytes.  dA and
+ * dB are computed with deterministic (fixed-order) split reductions. */
+int qlora_linear_bwd(int64_t M, int64_t K, int64_t N, int64_t r,
+                     const uint16_t* G, const uint16_t* X, const uint16_t* Z,
+                     const nf4_state_t* W, const uint16_t* A, const uint16_t* B,
+                     float c, uint16_t* dX, float* dA, float* dB,
+                     void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Synchronise `stream`, then copy the device status word to *host_value.
+ * Returns NF4_EHIP if the copy fails, else NF4_OK. */
+int nf4_status_read(const int32_t* status, int32_t* host_value, void* stream);
+
+/* Instrumentation.  Kernel ids for the timer below. */
+#define QK_QUANT_PASS1  0
+#define QK_QUANT_MEAN   1
+#define QK_QUANT_PASS2  2
+#define QK_DEQUANT      3
+#define QK_LORA_DOWN    4   /* Z = X A (split-K partials)               */
+#define QK_FWD_GEMM     5   /* fused dequant-GEMM + LoRA epilogue       */
+#define QK_FWD_GEMV     6   /* small-M dequant-GEMV                     */
+#define QK_BWD_DZ       7   /* dZ = c G Bᵀ partials                     */
+#define QK_BWD_DX       8   /* dX = G Ŵᵀ + dZ Aᵀ                        */
+#define QK_BWD_DA       9   /* dA = Xᵀ dZ partials                      */
+#define QK_BWD_DB       10  /* dB = c Zᵀ G partials                     */
+#define QK_REDUCE       11  /* fixed-order split reductions             */
+#define QK_NUM_KERNELS  12
+
+/* When enabled, the library records a pair of hipEvents on the launch
+ * stream around every launch of kernel `kernel_id`.  qlora_timer_read
+ * waits for the recorded events, returns the summed elapsed milliseconds
+ * and the launch count since the last read, and resets them.  Host-side
+ * only; meant for benchmarks (it adds two event records per launch). */
+int qlora_timer_enable(int kernel_id, int enable);
+int qlora_timer_read(int kernel_id, double* total_ms, int64_t* launches);
+
+/* Short English text for a return code or status bit set. */
+const char* nf4_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H */

@@ -75,6 +75,7 @@ __all__ = [
     "first_level_absmax", "nf4_codes", "pack_nibbles", "unpack_nibbles",
     "tree_offset", "linear_absmax_table", "linear_absmax_codes",
     "double_quantize", "reconstruct_absmax", "quantize", "dequantize",
+    "reconstruct_weights",
     "bf16_round", "layer_forward", "layer_backward", "storage_bits",
     "counts",
 ]
@@ -279,8 +280,14 @@ def dequantize(state: dict, out: str = "fp32") -> np.ndarray:
     P = int(state["numel"])
     codes = unpack_nibbles(state["codes_packed"], P)
     ahat = reconstruct_absmax(state["qabsmax"], state["absmax2"], state["offset"])
-    scale = np.repeat(ahat, BLOCK1)[:P]
-    w = (NF4_CODEBOOK.astype(np.float32)[codes] * scale).astype(np.float32)
+    return reconstruct_weights(codes, np.repeat(ahat, BLOCK1)[:P], out)
+
+
+def reconstruct_weights(codes, ahat_per_weight, out: str = "fp32") -> np.ndarray:
+    """ŵ = fl32(C[j] * â) for each code with its block's reconstructed scale
+    (reading R5), optionally rounded to bf16."""
+    scale = np.asarray(ahat_per_weight, dtype=np.float32)
+    w = (NF4_CODEBOOK.astype(np.float32)[np.asarray(codes, dtype=np.int64)] * scale).astype(np.float32)
     if not np.all(np.isfinite(w)):
         raise ValueError("nonfinite reconstruction")
     if out == "fp32":

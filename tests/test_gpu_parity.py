@@ -1,0 +1,370 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bit-exact: packed codes, second-level codes and scales, offset, dequantized
+fp32/bf16 weights, and the layer outputs of the exact-integer special case.
+Floating point layer outputs: max|err| / max|ref| <= 1e-2 against the fp64
+oracle (the tolerance the method's target states).
+"""
+import hashlib
+
+import numpy as np
+import pytest
+
+import bit_nf4_quantized_10_amd as qn
+import synth_inputs as si
+from oracle import nf4_oracle as o
+from tests.gpu_util import OracleWeight, dev_bf16, dev_f32, host, rel_err, say, state_to_host
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qn.lib()  # fails loudly if the HIP library is missing
+
+
+def _quantize(w32):
+    W = dev_f32(w32)
+    state, status = qn.nf4_quantize(W)
+    return state, qn.nf4_status_read(status)
+
+
+def _assert_state_equal(got: dict, ref: dict):
+    assert got["numel"] == ref["numel"]
+    np.testing.assert_array_equal(got["codes_packed"], ref["codes_packed"])
+    np.testing.assert_array_equal(got["qabsmax"], ref["qabsmax"])
+    np.testing.assert_array_equal(got["absmax2"].view(np.uint32), np.asarray(ref["absmax2"]).view(np.uint32))
+    assert np.float32(got["offset"]).view(np.uint32) == np.float32(ref["offset"]).view(np.uint32)
+
+
+# ------------------------------------------------------------------ quantizer
+def test_quantize_page_examples():
+    cases = {
+        "worked block": ([0.0, 0.2, -0.4, 1.0], "793f"),
+        "zero block": ([0.0, 0.0], "77"),
+        "merge requant": ([0.53, -0.44], "f1"),
+        "layer example": ([0.5, -0.5], "f0"),
+    }
+    for name, (vals, hexbytes) in cases.items():
+        say(f"quantize page example: {name}")
+        state, status = _quantize(np.array(vals, np.float32))
+        assert status == 0
+        got = state_to_host(state)
+        assert got["codes_packed"].tobytes().hex() == hexbytes
+        _assert_state_equal(got, o.quantize(np.array(vals, np.float32)))
+        rec = host(qn.nf4_dequantize(state, "fp32"))
+        np.testing.assert_array_equal(rec, o.dequantize(o.quantize(np.array(vals, np.float32)), "fp32"))
+
+
+def _special_tensors():
+    rng = np.random.default_rng(123)
+    t = {}
+    t["P1"] = np.array([0.3], np.float32)
+    t["P3_odd"] = np.array([0.1, -0.2, 0.05], np.float32)
+    t["P65"] = (rng.standard_normal(65) * 0.02).astype(np.float32)
+    t["P1000"] = (rng.standard_normal(1000) * 0.02).astype(np.float32)
+    t["P16385"] = (rng.standard_normal(16385) * 0.02).astype(np.float32)
+    t["tiny_256x256"] = si.weight(256, 256, 101, False)
+    z = si.weight(256, 256, 101, False).copy()
+    z.ravel()[64 * 37:64 * 38] = 0.0
+    t["tiny_zero_block"] = z
+    t["all_zero_4096"] = np.zeros(4096, np.float32)
+    mags = np.exp(rng.uniform(np.log(1e-30), np.log(1e30), 64 * 300)).astype(np.float32)
+    t["mixed_magnitudes"] = (mags * np.sign(rng.standard_normal(mags.size))).astype(np.float32)
+    sub = (rng.standard_normal(64 * 40) * 1e-40).astype(np.float32)   # subnormal blocks
+    t["subnormal"] = sub
+    t["outliers_300k"] = si.weight(300, 1000, 7, True).ravel()
+    # weights exactly on NF4 midpoints for power-of-two scales: ties -> smaller code
+    C = o.NF4_CODEBOOK
+    mids = (C[:-1] + C[1:]) / 2
+    ties = []
+    for e in range(-4, 4):
+        for m in mids:
+            v = np.float32(m * 2.0 ** e)
+            if float(v) == m * 2.0 ** e:
+                blk = np.zeros(64, np.float32)
+                blk[0] = np.float32(2.0 ** e)
+                blk[1] = v
+                blk[2] = -v
+                blk[3] = np.nextafter(v, np.float32(0))
+                blk[4] = np.nextafter(v, np.float32(10))
+                ties.append(blk)
+    t["midpoint_ties"] = np.concatenate(ties)
+    # groups with a large absmax spread: reconstructed scales may go negative
+    spread = (rng.standard_normal(64 * 512) * 1e-3).astype(np.float32)
+    spread[::64 * 7] = 50.0
+    t["scale_spread"] = spread
+    return t
+
+
+@pytest.mark.parametrize("name", list(_special_tensors().keys()))
+def test_quantize_dequantize_bit_exact(name):
+    w = _special_tensors()[name].ravel()
+    say(f"quantize/dequantize bit-exact: {name} P={w.size}")
+    state, status = _quantize(w)
+    assert status == 0
+    ref = o.quantize(w)
+    _assert_state_equal(state_to_host(state), ref)
+    for dt in ("fp32", "bf16"):
+        got = host(qn.nf4_dequantize(state, dt))
+        exp = o.dequantize(ref, dt)
+        np.testing.assert_array_equal(got.view(np.uint32), exp.view(np.uint32))
+
+
+def test_quantize_flags_nonfinite():
+    for bad in (np.nan, np.inf, -np.inf):
+        w = np.zeros(300, np.float32)
+        w[123] = bad
+        say(f"quantize non-finite {bad}")
+        _, status = _quantize(w)
+        assert status & qn.NF4_ENONFINITE
+    _, status = _quantize(np.ones(300, np.float32))
+    assert status == 0
+
+
+def test_dequantize_checks_pad_nibble():
+    import torch
+    w = np.array([0.1, -0.2, 0.05], np.float32)
+    state, _ = _quantize(w)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    qn.nf4_dequantize(state, "fp32", status=status)
+    assert qn.nf4_status_read(status) == 0
+    state.codes[1] = (state.codes[1] & 0xF0) | 3
+    qn.nf4_dequantize(state, "fp32", status=status)
+    assert qn.nf4_status_read(status) & qn.NF4_EPADDING
+
+
+def test_quantize_attn7b_full_bit_exact():
+    W = si.weight(4096, 4096, 202, True)
+    say("quantize attn7b 4096x4096 full")
+    state, status = _quantize(W)
+    assert status == 0
+    ref = o.quantize(W)
+    _assert_state_equal(state_to_host(state), ref)
+    got = host(qn.nf4_dequantize(state, "bf16"))
+    np.testing.assert_array_equal(got.view(np.uint32), o.dequantize(ref, "bf16").view(np.uint32))
+
+
+def test_quantize_decode65b_sampled_bit_exact():
+    W = si.weight(8192, 22016, 404, True)
+    say("quantize decode65b 8192x22016, sampled blocks")
+    state, status = _quantize(W)
+    assert status == 0
+    ow = OracleWeight(W)
+    got = state_to_host(state)
+    np.testing.assert_array_equal(got["qabsmax"], ow.q)
+    np.testing.assert_array_equal(got["absmax2"].view(np.uint32), ow.s2.view(np.uint32))
+    assert np.float32(got["offset"]).view(np.uint32) == np.float32(ow.offset).view(np.uint32)
+    rng = np.random.default_rng(0)
+    blocks = np.sort(rng.choice(ow.a.size, 4000, replace=False))
+    blocks[-1] = ow.a.size - 1
+    codes = ow.block_codes(blocks)
+    packed = got["codes_packed"].reshape(-1, 32)[blocks]
+    exp = ((codes[:, 0::2] << 4) | codes[:, 1::2]).astype(np.uint8)
+    np.testing.assert_array_equal(packed, exp)
+
+
+# -------------------------------------------------------------------- layer
+def _layer_case(M, K, N, r, c, seed):
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((K, N)) * 0.02).astype(np.float32)
+    W.ravel()[rng.choice(W.size, max(1, W.size // 1000), replace=False)] *= 10
+    mk = lambda shape, std: si.bf16_normal(shape, std, int(rng.integers(1 << 30)))
+    Xb, X = mk((M, K), 1.0)
+    Ab, A = mk((K, r), 1.0 / r)
+    Bb, B = mk((r, N), 0.01 * 10)   # a larger B makes the LoRA term visible
+    Gb, G = mk((M, N), 1.0)
+    return dict(W=W, Xb=Xb, X=X, Ab=Ab, A=A, Bb=Bb, B=B, Gb=Gb, G=G, c=c)
+
+
+def _run_layer(case, M, K, N, r, need_dx=True):
+    state, status = _quantize(case["W"])
+    assert status == 0
+    X, A, B, G = (dev_bf16(case[k]) for k in ("Xb", "Ab", "Bb", "Gb"))
+    Y, Z = qn.qlora_linear_fwd(X, state, A, B, case["c"], K, N)
+    dX, dA, dB = qn.qlora_linear_bwd(G, X, Z, state, A, B, case["c"], K, N, need_dx=need_dx)
+    return state, Y, Z, dX, dA, dB
+
+
+LAYER_SHAPES = [
+    (16, 256, 256, 8, 2.0),      # tiny: small-M path
+    (1, 64, 64, 8, 0.5),         # single row
+    (8, 512, 192, 16, 1.0),
+    (17, 256, 256, 8, 2.0),      # large-M path, ragged M
+    (130, 264, 320, 24, 0.25),   # ragged M, K % 32 != 0, N % 128 != 0, r % 32 != 0
+    (256, 512, 512, 64, 0.25),
+]
+
+
+@pytest.mark.parametrize("M,K,N,r,c", LAYER_SHAPES)
+def test_layer_fwd_bwd_matches_oracle(M, K, N, r, c):
+    say(f"layer fwd/bwd M={M} K={K} N={N} r={r}")
+    case = _layer_case(M, K, N, r, c, seed=M * 7 + K)
+    state, Y, Z, dX, dA, dB = _run_layer(case, M, K, N, r)
+    W_hat = o.dequantize(o.quantize(case["W"]), "bf16").reshape(K, N)
+    Yr, Zr = o.layer_forward(case["X"], W_hat, case["A"], case["B"], c)
+    dXr, dAr, dBr, _ = o.layer_backward(case["G"], case["X"], W_hat, case["A"], case["B"], c)
+    errs = {"Y": rel_err(host(Y), Yr), "Z": rel_err(host(Z), Zr), "dX": rel_err(host(dX), dXr),
+            "dA": rel_err(host(dA), dAr), "dB": rel_err(host(dB), dBr)}
+    say(f"errors {errs}")
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
+    # LoRA-branch isolation: Y - X Ŵ is the adapter term
+    lora = host(Y).astype(np.float64) - case["X"].astype(np.float64) @ W_hat.astype(np.float64)
+    assert rel_err(lora, c * Zr @ case["B"]) <= 0.1
+
+
+def test_layer_bwd_without_dx():
+    M, K, N, r = 64, 256, 128, 16
+    case = _layer_case(M, K, N, r, 0.5, seed=5)
+    say("layer bwd with dX skipped")
+    _, _, _, dX, dA, dB = _run_layer(case, M, K, N, r, need_dx=False)
+    assert dX is None
+    W_hat = o.dequantize(o.quantize(case["W"]), "bf16").reshape(K, N)
+    _, dAr, dBr, _ = o.layer_backward(case["G"], case["X"], W_hat, case["A"], case["B"], 0.5)
+    assert rel_err(host(dA), dAr) <= TOL and rel_err(host(dB), dBr) <= TOL
+
+
+def _integer_case(M, K, N, r, seed):
+    """Every block holds +-2^e, so the double quantization is exact and every
+    accumulation is an exact small-integer sum in fp32 (and bf16)."""
+    rng = np.random.default_rng(seed)
+    e = -2
+    W = rng.choice([-1.0, 0.0, 1.0], size=(K, N), p=[0.3, 0.4, 0.3]).astype(np.float32)
+    W.reshape(-1, 64)[:, 0] = rng.choice([-1.0, 1.0], size=W.size // 64)
+    W *= np.float32(2.0 ** e)
+    sparse = lambda shape, p: rng.choice([-1.0, 0.0, 1.0], size=shape, p=[p / 2, 1 - p, p / 2]).astype(np.float32)
+    X = sparse((M, K), 0.1)
+    A = sparse((K, r), 0.05)
+    B = sparse((r, N), 0.2)
+    G = rng.integers(-2, 3, size=(M, N)).astype(np.float32) * sparse((M, N), 0.2)
+    bits = lambda a: si.to_bf16_bits(a)
+    return dict(W=W, X=X, A=A, B=B, G=G, Xb=bits(X), Ab=bits(A), Bb=bits(B), Gb=bits(G), c=0.5)
+
+
+@pytest.mark.parametrize("M,K,N,r", [(16, 256, 256, 8), (96, 320, 384, 16)])
+def test_layer_exact_integer_case_bit_exact(M, K, N, r):
+    say(f"exact-integer layer M={M} K={K} N={N} r={r}")
+    case = _integer_case(M, K, N, r, seed=M + N)
+    state, Y, Z, dX, dA, dB = _run_layer(case, M, K, N, r)
+    W_hat = o.dequantize(o.quantize(case["W"]), "bf16").reshape(K, N)
+    assert np.all(np.abs(W_hat) == 0.25) or np.all(np.isin(W_hat, [-0.25, 0.0, 0.25]))
+    Yr, Zr = o.layer_forward(case["X"], W_hat, case["A"], case["B"], case["c"])
+    dXr, dAr, dBr, _ = o.layer_backward(case["G"], case["X"], W_hat, case["A"], case["B"], case["c"])
+    for got, ref, name in ((Y, Yr, "Y"), (Z, Zr, "Z"), (dX, dXr, "dX")):
+        r32 = o.bf16_round(ref.astype(np.float32))
+        assert np.array_equal(r32, ref.astype(np.float32)), f"{name} not bf16-exact by construction"
+        np.testing.assert_array_equal(host(got), r32, err_msg=name)
+    np.testing.assert_array_equal(host(dA), dAr.astype(np.float32))
+    np.testing.assert_array_equal(host(dB), dBr.astype(np.float32))
+
+
+@pytest.mark.parametrize("variant", ["W_zero", "B_zero", "c_zero"])
+def test_layer_isolation_cases(variant):
+    M, K, N, r = 48, 256, 192, 16
+    case = _layer_case(M, K, N, r, 0.5, seed=11)
+    if variant == "W_zero":
+        case["W"] = np.zeros_like(case["W"])
+    if variant == "B_zero":
+        case["Bb"] = np.zeros_like(case["Bb"])
+        case["B"] = np.zeros_like(case["B"])
+    if variant == "c_zero":
+        case["c"] = 0.0
+    say(f"layer isolation {variant}")
+    state, Y, Z, dX, dA, dB = _run_layer(case, M, K, N, r)
+    W_hat = o.dequantize(o.quantize(case["W"]), "bf16").reshape(K, N)
+    Yr, Zr = o.layer_forward(case["X"], W_hat, case["A"], case["B"], case["c"])
+    dXr, dAr, dBr, _ = o.layer_backward(case["G"], case["X"], W_hat, case["A"], case["B"], case["c"])
+    assert rel_err(host(Y), Yr) <= TOL and rel_err(host(Z), Zr) <= TOL and rel_err(host(dX), dXr) <= TOL
+    if variant in ("B_zero", "c_zero"):
+        assert np.all(host(dA) == 0.0)
+        if variant == "c_zero":
+            assert np.all(host(dB) == 0.0)
+        else:
+            assert rel_err(host(dB), dBr) <= TOL
+    else:
+        assert rel_err(host(dA), dAr) <= TOL and rel_err(host(dB), dBr) <= TOL
+
+
+def test_frozen_state_unchanged_and_deterministic():
+    M, K, N, r = 64, 256, 256, 16
+    case = _layer_case(M, K, N, r, 1.0, seed=3)
+    say("frozen state hash and determinism")
+    state, status = _quantize(case["W"])
+    digest = lambda: hashlib.sha256(b"".join(host(t).tobytes() for t in
+                                             (state.codes, state.qabsmax, state.absmax2, state.offset))).hexdigest()
+    before = digest()
+    X, A, B, G = (dev_bf16(case[k]) for k in ("Xb", "Ab", "Bb", "Gb"))
+    outs = []
+    for _ in range(2):
+        Y, Z = qn.qlora_linear_fwd(X, state, A, B, 1.0, K, N)
+        dX, dA, dB = qn.qlora_linear_bwd(G, X, Z, state, A, B, 1.0, K, N)
+        outs.append([host(t).tobytes() for t in (Y, Z, dX, dA, dB)])
+    assert digest() == before
+    assert outs[0] == outs[1]
+
+
+# ------------------------------------------------------- full-size workloads
+def _full_size_check(name, matrix=0, M=None, row_samples=48, col_groups=3):
+    d = si.layer_inputs(name, matrix=matrix, M=M)
+    M, K, N, r, c = d["M"], d["K"], d["N"], d["r"], d["c"]
+    say(f"full-size {name}[{matrix}] M={M} K={K} N={N} r={r}")
+    state, status = _quantize(d["W"])
+    assert status == 0
+    X, A, B, G = (dev_bf16(d[k]) for k in ("X_bits", "A_bits", "B_bits", "G_bits"))
+    Y, Z = qn.qlora_linear_fwd(X, state, A, B, c, K, N)
+    dX, dA, dB = qn.qlora_linear_bwd(G, X, Z, state, A, B, c, K, N)
+    ow = OracleWeight(d["W"])
+    rng = np.random.default_rng(1)
+    Xf, Af, Bf, Gf = (d[k].astype(np.float64) for k in ("X", "A", "B", "G"))
+    Zr = Xf @ Af
+    # Y on sampled 64-column groups (all rows)
+    groups = rng.choice(N // 64, col_groups, replace=False)
+    groups[0] = N // 64 - 1
+    cols, Wc = ow.columns(groups)
+    Yr = Xf @ Wc.astype(np.float64) + c * (Zr @ Bf[:, cols])
+    e_y = rel_err(host(Y)[:, cols], Yr)
+    # dX on sampled columns k (all rows)
+    ks = rng.choice(K, row_samples, replace=False)
+    ks[0] = K - 1
+    dZr = c * (Gf @ Bf.T)
+    dXr = Gf @ ow.rows(ks).astype(np.float64).T + dZr @ Af[ks].T
+    e_dx = rel_err(host(dX)[:, ks], dXr)
+    e_da = rel_err(host(dA), Xf.T @ dZr)
+    e_db = rel_err(host(dB), c * (Zr.T @ Gf))
+    e_z = rel_err(host(Z), Zr)
+    say(f"errors Y={e_y:.2e} Z={e_z:.2e} dX={e_dx:.2e} dA={e_da:.2e} dB={e_db:.2e}")
+    for v in (e_y, e_z, e_dx, e_da, e_db):
+        assert v <= TOL
+
+
+def test_full_size_attn7b():
+    _full_size_check("attn7b_4096")
+
+
+def test_full_size_mlp7b_down():
+    _full_size_check("mlp7b_4096x11008", matrix=2)
+
+
+@pytest.mark.parametrize("M", [1, 8, 16])
+def test_full_size_decode65b_gemv(M):
+    d = si.layer_inputs("decode65b_8192x22016", M=M, with_grad=False)
+    K, N, r, c = d["K"], d["N"], d["r"], d["c"]
+    say(f"decode65b GEMV M={M}")
+    state, status = _quantize(d["W"])
+    assert status == 0
+    X, A, B = (dev_bf16(d[k]) for k in ("X_bits", "A_bits", "B_bits"))
+    Y, Z = qn.qlora_linear_fwd(X, state, A, B, c, K, N)
+    ow = OracleWeight(d["W"])
+    groups = np.array([0, 17, 100, N // 64 - 1])
+    cols, Wc = ow.columns(groups)
+    Xf, Af, Bf = (d[k].astype(np.float64) for k in ("X", "A", "B"))
+    Zr = Xf @ Af
+    Yr = Xf @ Wc.astype(np.float64) + c * (Zr @ Bf[:, cols])
+    e = rel_err(host(Y)[:, cols], Yr)
+    say(f"GEMV M={M} err={e:.2e}")
+    assert e <= TOL and rel_err(host(Z), Zr) <= TOL

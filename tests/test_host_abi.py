@@ -1,0 +1,98 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares, the size queries match the pages' closed forms, and argument
+errors are rejected before anything is launched.  No GPU work is issued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_nf4_quantized_10_amd as qn
+from oracle import nf4_oracle as o
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora_nf4.h")
+
+
+def _declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    declared = _declared_functions()
+    assert "nf4_quantize" in declared and "qlora_linear_bwd" in declared
+    L = qn.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(qn.C_FUNCTIONS) == declared
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 63, 64, 65, 4096, 16384, 16385, 4096 * 4096, 8192 * 22016])
+def test_nf4_sizes_match_storage_bill(P):
+    s = qn.nf4_sizes(P)
+    n1, n2 = o.counts(P)
+    assert (s["n1"], s["n2"], s["code_bytes"]) == (n1, n2, (P + 1) // 2)
+    bits = 8 * s["code_bytes"] + 8 * s["n1"] + 32 * s["n2"] + 32
+    assert bits == o.storage_bits(P)
+    assert s["quant_workspace_bytes"] >= 4 * n1 + 8 * n2
+
+
+def test_nf4_sizes_rejects_empty():
+    with pytest.raises(qn.NF4Error) as e:
+        qn.nf4_sizes(0)
+    assert e.value.code == qn.NF4_EINVAL
+
+
+@pytest.mark.parametrize("shape", [(0, 64, 64, 8), (4, 64, 63, 8), (4, 12, 64, 8), (4, 64, 64, 4),
+                                   (4, 64, 64, 264), (4, 0, 64, 8)])
+def test_layer_shapes_rejected(shape):
+    with pytest.raises(qn.NF4Error):
+        qn.qlora_workspace_bytes(*shape)
+
+
+def test_layer_workspace_sizes_are_positive():
+    for shape in [(16, 256, 256, 8), (4096, 4096, 4096, 64), (1, 8192, 22016, 64), (2048, 22016, 8192, 64)]:
+        f, b = qn.qlora_workspace_bytes(*shape)
+        assert f >= 0 and b > 0 and f % 256 == 0 and b % 256 == 0
+
+
+def test_entry_points_reject_bad_arguments_before_launch():
+    L = qn.lib()
+    st = qn._State(64, 0x1000, 0x2000, 0x3000, 0x4000)
+    # NULL weights / state / workspace / status
+    assert L.nf4_quantize(None, ctypes.byref(st), 0x10000, 1 << 20, 0x5000, None) == qn.NF4_EINVAL
+    assert L.nf4_quantize(0x100, None, 0x10000, 1 << 20, 0x5000, None) == qn.NF4_EINVAL
+    # misaligned weights, too small a workspace
+    assert L.nf4_quantize(0x104, ctypes.byref(st), 0x10000, 1 << 20, 0x5000, None) == qn.NF4_EINVAL
+    assert L.nf4_quantize(0x100, ctypes.byref(st), 0x10000, 8, 0x5000, None) == qn.NF4_EINVAL
+    # bad output dtype for the decoder
+    assert L.nf4_dequantize(ctypes.byref(st), 0x100, 7, None, None) == qn.NF4_EINVAL
+    # layer: numel mismatch, N % 64, NULL output
+    st2 = qn._State(64 * 64, 0x1000, 0x2000, 0x3000, 0x4000)
+    args = (0x100, ctypes.byref(st2), 0x200, 0x300, ctypes.c_float(1.0), 0x400, 0x500, 0x10000, 1 << 30, None)
+    assert L.qlora_linear_fwd(4, 64, 32, 8, *args) == qn.NF4_EINVAL
+    assert L.qlora_linear_fwd(4, 32, 64, 8, *args) == qn.NF4_EINVAL
+    bad = (0x100, ctypes.byref(st2), 0x200, 0x300, ctypes.c_float(1.0), None, 0x500, 0x10000, 1 << 30, None)
+    assert L.qlora_linear_fwd(4, 64, 64, 8, *bad) == qn.NF4_EINVAL
+    small_ws = (0x100, ctypes.byref(st2), 0x200, 0x300, ctypes.c_float(1.0), 0x400, 0x500, 0x10000, 0, None)
+    f, _ = qn.qlora_workspace_bytes(4, 64, 64, 8)
+    if f > 0:
+        assert L.qlora_linear_fwd(4, 64, 64, 8, *small_ws) == qn.NF4_EINVAL
+    assert L.qlora_linear_bwd(4, 64, 64, 8, 0x100, 0x100, 0x100, ctypes.byref(st2), 0x200, 0x300,
+                              ctypes.c_float(1.0), None, None, 0x600, 0x10000, 1 << 30, None) == qn.NF4_EINVAL
+
+
+def test_timer_ids_validated():
+    L = qn.lib()
+    assert L.qlora_timer_enable(99, 1) == qn.NF4_EINVAL
+    assert L.qlora_timer_enable(-1, 1) == qn.NF4_EINVAL
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    assert L.qlora_timer_read(3, ctypes.byref(ms), ctypes.byref(n)) == qn.NF4_OK and n.value == 0
+
+
+def test_error_strings():
+    L = qn.lib()
+    for code in (0, 1, 2, 4, 8, 6):
+        assert L.nf4_error_string(code)
