@@ -1,0 +1,298 @@
+"""Benchmark of the QLoRA NF4 linear layer on one MI355X.
+
+One step = nf4_quantize(W) -> qlora_linear_fwd -> qlora_linear_bwd on the
+7B-attention-shaped projection (M = 4096 tokens, K = N = 4096, r = 64,
+alpha = 16), inputs resident in HBM.  `value` is the forward+backward
+algorithmic TFLOP/s of the whole step (the quantize time is inside the step,
+its flops are not counted).  Three input sets are rotated so that the 256 MB
+Infinity Cache cannot hold a step's inputs from the previous step.
+
+Also reported (not part of `value`): the roofline of the dominant kernel
+(timed live with HIP events on the launch stream), the memory-bound paths in
+GB/s (quantize, bf16 dequantize, small-M dequant-GEMV at M = 1/8/16 on the
+65B MLP shape), and the CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--copy-probe]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "QLoRA linear fwd+bwd TFLOP/s and NF4 dequant-GEMV GB/s, % of roofline"
+KERNEL_SOURCES = {"fwd_gemm": "gemm.hip", "bwd_dx": "gemm.hip", "fwd_gemv": "gemm.hip",
+                  "quant_pass1": "quantize.hip", "dequant": "quantize.hip"}
+
+
+def layer_flops(M, K, N, r):
+    fwd = 2 * M * K * N + 2 * M * K * r + 2 * M * r * N
+    bwd = 2 * M * N * K + 4 * M * N * r + 4 * M * K * r
+    return fwd, bwd
+
+
+def kernel_flops(name, M, K, N, r):
+    if name == "fwd_gemm":
+        return 2 * M * K * N + 2 * M * r * N       # X·Ŵ plus the Z·(cB) extension
+    if name == "bwd_dx":
+        return 2 * M * N * K + 2 * M * r * K       # G·Ŵᵀ plus the dZ·Aᵀ extension
+    raise KeyError(name)
+
+
+def src_hash(fname):
+    with open(os.path.join(ROOT, "bit_nf4_quantized_10_amd", "csrc", fname), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(kernel):
+    """HBM bytes per launch from the committed PMC summary of this kernel, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_attn7b_4096_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path, encoding="utf-8").read()
+    m_hash = re.search(r"source_sha256_16:\s*(\w+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != src_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return float(m_bytes.group(1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not supported "
+              "(see DESIGN.md for how the path would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_nf4_quantized_10_amd as qn
+    import synth_inputs as si
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    wl = "attn7b_4096"
+    sets = []
+    for i in range(3):
+        d = si.layer_inputs(wl, matrix=0)   # same values, distinct buffers
+        bf = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+        sets.append({"W": torch.from_numpy(d["W"]).to(dev).reshape(-1), "X": bf(d["X_bits"]),
+                     "A": bf(d["A_bits"]), "B": bf(d["B_bits"]), "G": bf(d["G_bits"])})
+    M, K, N, r, c = d["M"], d["K"], d["N"], d["r"], d["c"]
+    P = K * N
+    sizes = qn.nf4_sizes(P)
+    fwd_ws, bwd_ws = qn.qlora_workspace_bytes(M, K, N, r)
+    qws = torch.empty(sizes["quant_workspace_bytes"], dtype=torch.uint8, device=dev)
+    fws = torch.empty(max(fwd_ws, 256), dtype=torch.uint8, device=dev)
+    bws = torch.empty(max(bwd_ws, 256), dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    outs = []
+    for s in sets:
+        outs.append({"state": qn.empty_state(P, dev),
+                     "Y": torch.empty(M, N, dtype=torch.bfloat16, device=dev),
+                     "Z": torch.empty(M, r, dtype=torch.bfloat16, device=dev),
+                     "dX": torch.empty(M, K, dtype=torch.bfloat16, device=dev),
+                     "dA": torch.empty(K, r, dtype=torch.float32, device=dev),
+                     "dB": torch.empty(r, N, dtype=torch.float32, device=dev)})
+
+    def step(i):
+        s, o = sets[i % 3], outs[i % 3]
+        qn.nf4_quantize(s["W"], o["state"], qws, status)
+        qn.qlora_linear_fwd(s["X"], o["state"], s["A"], s["B"], c, K, N, o["Y"], o["Z"], fws)
+        qn.qlora_linear_bwd(s["G"], s["X"], o["Z"], o["state"], s["A"], s["B"], c, K, N, True,
+                            o["dX"], o["dA"], o["dB"], bws)
+
+    # warmup, with every kernel timed once to find the dominant one
+    for k in qn.KERNEL_IDS:
+        qn.qlora_timer_enable(k, True)
+    for i in range(max(args.warmup, 1)):
+        step(i)
+    torch.cuda.synchronize()
+    per_kernel = {}
+    for k in qn.KERNEL_IDS:
+        ms, n = qn.qlora_timer_read(k)
+        qn.qlora_timer_enable(k, False)
+        if n:
+            per_kernel[k] = ms / n
+    dominant = max(("fwd_gemm", "bwd_dx"), key=lambda k: per_kernel.get(k, 0.0))
+    if qn.nf4_status_read(status) != 0:
+        raise RuntimeError("quantize reported a bad status")
+
+    # timed region
+    qn.qlora_timer_enable(dominant, True)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    dom_ms, dom_n = qn.qlora_timer_read(dominant)
+    qn.qlora_timer_enable(dominant, False)
+    dom_avg = dom_ms / max(dom_n, 1)
+
+    fwd_f, bwd_f = layer_flops(M, K, N, r)
+    value = (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
+    dflops = kernel_flops(dominant, M, K, N, r)
+    achieved = dflops / (dom_avg * 1e-3) / 1e12
+    traffic = read_traffic(dominant)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic, "kernel": dominant, "avg_ms": round(dom_avg, 4),
+                "launches": dom_n, "flops_per_launch": dflops}
+
+    components = {"kernel_avg_ms_warmup": {k: round(v, 4) for k, v in per_kernel.items()}}
+    if not args.no_components:
+        components.update(bench_components(torch, qn, si, dev, sets, outs, qws, status))
+    if args.copy_probe:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        components["copy_probe_bytes"] = {"read": a.numel() * 4, "write": a.numel() * 4}
+
+    cpu = None if args.no_cpu else cpu_baseline(wl)
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl, "M": M, "K": K, "N": N, "r": r, "alpha": 16.0,
+                   "step": "nf4_quantize + qlora_linear_fwd + qlora_linear_bwd",
+                   "flops_fwd": fwd_f, "flops_bwd": bwd_f, "input_sets_rotated": 3,
+                   "wall_s": round(wall, 3)},
+        "roofline": roofline, "cpu_baseline": cpu, "components": components,
+    }
+    print(json.dumps(line))
+
+
+def _time_kernel(qn, torch, name, fn, reps):
+    qn.qlora_timer_enable(name, True)
+    for i in range(reps):
+        fn(i)
+    torch.cuda.synchronize()
+    ms, n = qn.qlora_timer_read(name)
+    qn.qlora_timer_enable(name, False)
+    return ms / max(n, 1)
+
+
+def bench_components(torch, qn, si, dev, sets, outs, qws, status):
+    res = {}
+    P = sets[0]["W"].numel()
+    n1, n2 = qn.nf4_sizes(P)["n1"], qn.nf4_sizes(P)["n2"]
+    # quantize: fp32 read, codes + int8 codes + fp32 scales written
+    qbytes = 4 * P + (P + 1) // 2 + n1 + 4 * n2 + 4
+    ms = _time_kernel(qn, torch, "quant_pass1",
+                      lambda i: qn.nf4_quantize(sets[i % 3]["W"], outs[i % 3]["state"], qws, status), 10)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for i in range(10):
+        qn.nf4_quantize(sets[i % 3]["W"], outs[i % 3]["state"], qws, status)
+    ev[1].record()
+    torch.cuda.synchronize()
+    full_ms = ev[0].elapsed_time(ev[1]) / 10
+    res["quantize_attn7b"] = {"bytes": qbytes, "pass1_ms": round(ms, 4), "call_ms": round(full_ms, 4),
+                              "GBps_call": round(qbytes / (full_ms * 1e-3) / 1e9, 1),
+                              "frac_hbm_call": round(qbytes / (full_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    # bf16 dequantize
+    dbytes = (P + 1) // 2 + n1 + 4 * n2 + 4 + 2 * P
+    outs_bf = [torch.empty(P, dtype=torch.bfloat16, device=dev) for _ in range(8)]
+    ms = _time_kernel(qn, torch, "dequant",
+                      lambda i: qn.nf4_dequantize(outs[i % 3]["state"], "bf16", out=outs_bf[i % 8]), 16)
+    res["dequant_bf16_attn7b"] = {"bytes": dbytes, "ms": round(ms, 4),
+                                  "GBps": round(dbytes / (ms * 1e-3) / 1e9, 1),
+                                  "frac_hbm": round(dbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del outs_bf
+    # small-M dequant-GEMV on the 65B MLP shape
+    d = si.layer_inputs("decode65b_8192x22016", M=16, with_grad=False)
+    K, N, r, c = d["K"], d["N"], d["r"], d["c"]
+    Pg = K * N
+    states = []
+    for i in range(3):
+        W = torch.from_numpy(d["W"]).to(dev).reshape(-1)
+        st, _ = qn.nf4_quantize(W)
+        states.append(st)
+        del W
+    bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+    A, B = bf(d["A_bits"]), bf(d["B_bits"])
+    sg = qn.nf4_sizes(Pg)
+    gemv = {}
+    for M in (1, 8, 16):
+        X = bf(d["X_bits"][:M])
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        Z = torch.empty(M, r, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(qn.qlora_workspace_bytes(M, K, N, r)[0], 256), dtype=torch.uint8, device=dev)
+        gbytes = Pg // 2 + sg["n1"] + 4 * sg["n2"] + 4 + 2 * M * K + 2 * K * r + 2 * r * N + 2 * M * N + 2 * M * r
+        fn = lambda i: qn.qlora_linear_fwd(X, states[i % 3], A, B, c, K, N, Y, Z, ws)
+        for i in range(3):
+            fn(i)
+        ev[0].record()
+        for i in range(12):
+            fn(i)
+        ev[1].record()
+        torch.cuda.synchronize()
+        call_ms = ev[0].elapsed_time(ev[1]) / 12
+        kms = _time_kernel(qn, torch, "fwd_gemv", fn, 12)
+        gemv[f"M{M}"] = {"bytes": gbytes, "call_ms": round(call_ms, 4), "gemv_kernel_ms": round(kms, 4),
+                         "GBps_call": round(gbytes / (call_ms * 1e-3) / 1e9, 1),
+                         "frac_hbm_call": round(gbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    res["gemv_decode65b"] = gemv
+    return res
+
+
+def cpu_baseline(wl):
+    """The oracle as it stands, on the host cores: quantize of the full weight
+    plus forward+backward on a 256-row sample of the tokens, scaled to the full
+    step (the oracle's layer cost is linear in M)."""
+    import synth_inputs as si
+    from oracle import nf4_oracle as o
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    d = si.layer_inputs(wl, matrix=0)
+    M, K, N, r, c = d["M"], d["K"], d["N"], d["r"], d["c"]
+    Ms = 256
+    t0 = time.perf_counter()
+    st = o.quantize(d["W"].ravel())
+    t_q = time.perf_counter() - t0
+    W_hat = o.dequantize(st, "bf16").reshape(K, N)
+    t1 = time.perf_counter()
+    X, A, B, G = d["X"][:Ms], d["A"], d["B"], d["G"][:Ms]
+    o.layer_forward(X, W_hat, A, B, c)
+    o.layer_backward(G, X, W_hat, A, B, c)
+    t_l = time.perf_counter() - t1
+    fwd_f, bwd_f = layer_flops(M, K, N, r)
+    step_s = t_q + t_l * (M / Ms)
+    return {"value": round((fwd_f + bwd_f) / step_s / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"full-weight quantize ({t_q:.2f} s) + fwd/bwd on {Ms} of {M} token rows "
+                      f"({t_l:.2f} s), layer time scaled by {M // Ms}; est. step {step_s:.2f} s"}
+
+
+if __name__ == "__main__":
+    main()
