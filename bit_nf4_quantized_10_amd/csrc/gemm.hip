@@ -356,7 +356,6 @@ hipError_t launch_reduce(const float* part, int64_t splits, int64_t count, float
 }
 
 // Tile shapes.
-constexpr int kBigBM = 128, kBigBN = 128;           // fwd / dX
 constexpr int kTallBM = 128, kTallBN = 64;          // rows large, cols = r
 constexpr int kWideBM = 64, kWideBN = 128;          // rows = r, cols large
 constexpr int kGemvBM = 16, kGemvBN = 256;          // M <= 16 forward
@@ -441,12 +440,7 @@ hipError_t launch_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
     t.stop();
     return launch_reduce(ypart, p.y_splits, M * N, 1.0f, nullptr, Y, stream);
   }
-  FwdArgs f{X, W, Z, B, c, Y, nullptr, M, K, N, r, p.y_per};
-  dim3 grid(static_cast<unsigned>(ceil_div(N, kBigBN)), static_cast<unsigned>(ceil_div(M, kBigBM)), 1);
-  Timer t(QK_FWD_GEMM, stream);
-  hipLaunchKernelGGL((qlora_fwd_kernel<kBigBM, kBigBN, 2, 2>), grid, dim3(256), 0, stream, f);
-  t.stop();
-  return hipGetLastError();
+  return launch_fwd_big(M, K, N, r, X, W, Z, B, c, Y, stream);
 }
 
 hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* X,
@@ -492,11 +486,7 @@ hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
   }
   // dX = G Ŵᵀ + dZ Aᵀ
   if (dX != nullptr) {
-    DxArgs d{G, W, dz16, A, dX, M, K, N, r};
-    dim3 grid(static_cast<unsigned>(ceil_div(K, kBigBN)), static_cast<unsigned>(ceil_div(M, kBigBM)), 1);
-    Timer t(QK_BWD_DX, stream);
-    hipLaunchKernelGGL((qlora_dx_kernel<kBigBM, kBigBN, 2, 2>), grid, dim3(256), 0, stream, d);
-    t.stop();
+    if ((e = launch_dx_big(M, K, N, r, G, W, dz16, A, dX, stream)) != hipSuccess) return e;
   }
   return hipGetLastError();
 }

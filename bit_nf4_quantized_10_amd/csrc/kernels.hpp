@@ -47,4 +47,10 @@ hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
                       const uint16_t* B, float c, uint16_t* dX, float* dA, float* dB, void* ws,
                       hipStream_t stream);
 
+hipError_t launch_fwd_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W,
+                          const uint16_t* Z, const uint16_t* B, float c, uint16_t* Y, hipStream_t stream);
+
+hipError_t launch_dx_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, NF4View W,
+                         const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream);
+
 }  // namespace qn
