@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "QLoRA linear fwd+bwd TFLOP/s and NF4 dequant-GEMV GB/s, % of roofline"
-KERNEL_SOURCES = {"fwd_gemm": "gemm.hip", "bwd_dx": "gemm.hip", "fwd_gemv": "gemm.hip",
+KERNEL_SOURCES = {"fwd_gemm": "gemm_big.hip", "bwd_dx": "gemm_big.hip", "fwd_gemv": "skinny.hip",
                   "quant_pass1": "quantize.hip", "dequant": "quantize.hip"}
 
 

@@ -71,4 +71,39 @@ __device__ __forceinline__ void decode8(uint32_t w, float ahat, const float* lut
   }
 }
 
+// ---- raw buffer access: loads whose offset is at or past the byte count
+// return zeros, so masked loads need no branches (an offset of 0x80000000
+// marks a masked lane; every tensor is smaller than 2 GiB).
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kMasked = 0x80000000u;
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0x7fffffff ? bytes : 0x7fffffff;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(n),
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 ld_b128(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint2 ld_b64(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t ld_b32(Rsrc r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+__device__ __forceinline__ float ld_f32(Rsrc r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ int ld_i8(Rsrc r, uint32_t off) {
+  return static_cast<int>(static_cast<int8_t>(__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0)));
+}
+
+// The 16 reconstructions RNE_bf16(fl32(C[j] * ahat)) of one block, written
+// as 32 bytes (entry j at byte 2j) to 16-byte aligned LDS.
+__device__ __forceinline__ void write_block_table(uint16_t* tab, float ahat) {
+  uint32_t w[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w[j] = pack_bf16x2(__fmul_rn(kNF4[2 * j], ahat), __fmul_rn(kNF4[2 * j + 1], ahat));
+  reinterpret_cast<uint4*>(tab)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  reinterpret_cast<uint4*>(tab)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
 }  // namespace qn

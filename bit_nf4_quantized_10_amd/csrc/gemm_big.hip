@@ -4,27 +4,32 @@
 //
 // Workgroup: 256 threads (4 waves, 2 x 2), output tile 256 x 256, each wave
 // 128 x 128 as 8 x 8 tiles of v_mfma_f32_16x16x32_bf16 (256 fp32 accumulators
-// per lane, one wave per SIMD).  The reduction advances 64 elements per LDS
-// stage with two stages in flight: while the MFMAs consume stage s, the
-// global loads of stage s+1 are outstanding; the loaded codes are then decoded
-// to bf16 and written to the other LDS buffer.
+// per lane, one wave per SIMD).  The reduction advances 64 elements per stage;
+// LDS holds two stages.  In iteration s the workgroup
+//   - copies the activation tile of stage s+1 from global memory straight into
+//     LDS (buffer loads with the LDS destination, no registers involved);
+//   - loads the code words and block scales of stage s+2 into registers;
+//   - builds the bf16 block tables of stage s+1 (16 entries RNE(fl32(C[j]*â))
+//     per 64-weight block row) and decodes stage s+1 into the other weight
+//     buffer by table lookups (no per-weight multiply or conversion);
+//   - runs the 128 MFMAs of stage s;
+// then waits for its loads and synchronises once.
 //
 // LDS layout of one operand stage: 256 rows x 64 bf16 (128 bytes per row), the
-// eight 16-byte chunks of row r stored at chunk ^ ((r ^ r >> 3) & 7).  The
-// swizzle keeps both the 16-byte fragment reads (16 consecutive rows, one
-// chunk) and the decoder's writes (rows 8 apart, one chunk) free of bank
-// conflicts within each group of 8 lanes.
+// eight 16-byte chunks of row r stored at chunk ^ ((r ^ r >> 3) & 7), which
+// keeps the fragment reads (16 consecutive rows, one chunk) and the decoder's
+// writes (rows 8 apart, one chunk) free of bank conflicts per 8 lanes.
 //
 // Weight operand:
-//  - forward (reduction over k, codes packed along n): each thread loads one
-//    32-bit code word (8 consecutive n) from each of 8 consecutive k-rows,
-//    transposes the 8 x 8 nibble matrix in registers (three byte/nibble
-//    butterfly stages), and decodes each column's 8 k-values with their 8
-//    row scales into one 16-byte LDS chunk;
-//  - backward dX (reduction over n, the packed direction): each thread owns
-//    one k-row and decodes its 64 consecutive n (exactly one 64-weight block,
-//    one scale) into 8 LDS chunks.
-// Decoding is ŵ = RNE_bf16(fl32(C[code] * â)), bit-identical to nf4_dequantize.
+//  - forward (reduction over k, codes packed along n): thread (rg, cg) owns
+//    k-rows 8rg..8rg+7 and columns 8cg..8cg+7 of the stage; it builds the
+//    table of one (row, block) pair that the 8 threads of its group share
+//    (all in one wave) and writes each column's 8 k-values as one chunk;
+//  - backward dX (reduction over n, the packed direction): thread t owns
+//    k-row t and the stage's 64 n, exactly one block and one table.
+// Rows at or past K get an all-zero table and the matching activation
+// chunks are masked, so tails add exact zeros.  Every global load is a raw
+// buffer load, so masked lanes need no branches.
 //
 // The MFMA is issued as D = Ŵ-fragment x activation-fragment, so each lane
 // holds 4 consecutive output columns of one output row: 8-byte bf16 stores.
@@ -40,45 +45,17 @@ constexpr int kBN = 256;
 constexpr int kBK = 64;
 constexpr int kThreads = 256;
 constexpr int kTileBytes = 256 * 128;
-constexpr int kLutOffset = 4 * kTileBytes;
-constexpr int kQ2Offset = kLutOffset + 16 * 4;
-constexpr int kLdsBytes = kQ2Offset + 256 * 4;
+constexpr int kTabBytes = 256 * 32;
+constexpr int kOffA = 0;                           // 2 stages of activation tiles
+constexpr int kOffB = 2 * kTileBytes;              // 2 stages of weight tiles
+constexpr int kOffT = 4 * kTileBytes;              // 2 stages of block tables
+constexpr int kOffQ = kOffT + 2 * kTabBytes;       // fl32(q/127) table
+constexpr int kLdsBytes = kOffQ + 256 * 4;
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 4); }
 
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
-}
-
-// 8 x 8 nibble transpose: afterwards r[j] holds, at bits 4i..4i+3, what r[i]
-// held at bits 4j..4j+3.
-__device__ __forceinline__ void transpose8x8_nibbles(uint32_t (&r)[8]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {   // swap the off-diagonal 4 x 4 blocks (16-bit halves)
-    const uint32_t a = r[i], b = r[i + 4];
-    r[i] = perm(b, a, 0x05040100u);
-    r[i + 4] = perm(b, a, 0x07060302u);
-  }
-#pragma unroll
-  for (int h = 0; h < 8; h += 4)   // swap the off-diagonal 2 x 2 blocks (bytes)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t a = r[h + i], b = r[h + i + 2];
-      r[h + i] = perm(b, a, 0x06020400u);
-      r[h + i + 2] = perm(b, a, 0x07030501u);
-    }
-#pragma unroll
-  for (int i = 0; i < 8; i += 2) {  // swap single nibbles
-    const uint32_t a = r[i], b = r[i + 1];
-    r[i] = (a & 0x0F0F0F0Fu) | ((b & 0x0F0F0F0Fu) << 4);
-    r[i + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
-  }
-}
-
-__device__ __forceinline__ float lut_mul(const float* lut, uint32_t d, int shift, float s) {
-  return __fmul_rn(lut[(d >> shift) & 15u], s);
-}
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 struct BigArgs {
   const uint16_t* act;     // X (forward) or G (backward): rows m, reduction contiguous
@@ -91,272 +68,390 @@ struct BigArgs {
   int64_t M, K, N, r;
 };
 
-struct StageRegs {
-  uint4 x[8];
+// Registers carried from the load of a stage to its decode.
+struct WRegs {
   uint32_t w[8];
-  int q[8];
-  float s2[8];
+  int q;
+  float s2;
 };
 
-// Activation operand of one stage: 256 rows x 64 reduction elements, row-major
-// source.  Thread t loads chunk t&7 of rows t/8 + 32i.
-__device__ __forceinline__ void load_act(StageRegs& R, const uint16_t* __restrict__ src, int64_t ld, int64_t rows,
-                                         int64_t red, int64_t m0, int64_t k0, int t) {
-  const int c = t & 7;
-  const int64_t k = k0 + 8 * c;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t m = m0 + (t >> 3) + 32 * i;
-    R.x[i] = (m < rows && k < red) ? *reinterpret_cast<const uint4*>(src + m * ld + k) : make_uint4(0, 0, 0, 0);
-  }
+__device__ __forceinline__ uint32_t nib(uint32_t w, int t) { return (w >> (8 * (t >> 1) + ((t & 1) ? 0 : 4))) & 15u; }
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void store_act(const StageRegs& R, char* sA, int t) {
-  const int c = t & 7;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(sA + lds_off((t >> 3) + 32 * i, c)) = R.x[i];
+__device__ __forceinline__ uint32_t ld32s(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint4 ld128s(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-// Forward weight stage: rows k0 + 8*rg + i, columns n0 + 8*cg .. +7.
-__device__ __forceinline__ void load_w_fwd(StageRegs& R, const BigArgs& a, int64_t n0, int64_t k0, int t) {
-  const int rg = t >> 5, cg = t & 31;
-  const int64_t n = n0 + 8 * cg;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t k = k0 + 8 * rg + i;
-    if (k < a.K && n < a.N) {
-      const int64_t e = k * a.N + n;
-      R.w[i] = *reinterpret_cast<const uint32_t*>(a.W.codes + (e >> 1));
-      R.q[i] = a.W.qabsmax[e >> 6];
-      R.s2[i] = a.W.absmax2[e >> 14];
-    } else {
-      R.w[i] = 0x77777777u;  // code 7 decodes to 0
-      R.q[i] = 0;
-      R.s2[i] = 0.0f;
+template <bool kForward, bool kKTail>
+struct Big {
+  const BigArgs& a;
+  char* smem;
+  int t, lane, wave;            // wave is wave-uniform (scalar)
+  int64_t m0, c0, red;
+  Rsrc r_act, r_codes, r_q, r_s2;
+  float off;
+  uint32_t act_voff[8];         // byte offset of this lane's activation chunk, stage 0
+  int act_lim[8];               // forward tail: chunk valid while k0 < act_lim
+  uint32_t w_voff[8];           // forward: code word of row i at stage 0; backward: [0] = row start
+  uint32_t q_voff;              // second-level code of this thread's table at stage 0
+  int64_t tab_e0;               // flat weight index of this thread's table block at stage 0
+  int tab_row, tab_blk;
+  bool tab_ok;
+
+  __device__ Big(const BigArgs& args, char* s) : a(args), smem(s) {
+    t = threadIdx.x;
+    lane = t & 63;
+    wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Give
+    // XCD x the contiguous run of tiles [x*T/8, (x+1)*T/8) in row-major order,
+    // so the workgroups sharing an activation row-tile and a weight
+    // column-tile sit behind the same L2.
+    {
+      const int64_t ntx = gridDim.x, total = static_cast<int64_t>(gridDim.x) * gridDim.y;
+      const int64_t id = static_cast<int64_t>(blockIdx.y) * ntx + blockIdx.x;
+      const int64_t per = (total + 7) / 8, xcd = id % 8, slot = id / 8;
+      int64_t tile = xcd * per + slot;
+      // the last XCD may own fewer tiles; fold the overflow back onto the ids
+      // that would otherwise be unused (keeps the map a bijection)
+      if (total % 8 != 0 || tile >= total) tile = id;
+      m0 = (tile / ntx) * kBM;
+      c0 = (tile % ntx) * kBN;
     }
-  }
-}
-
-__device__ __forceinline__ void store_w_fwd(StageRegs& R, char* sB, const float* lut, const float* q2t, float off,
-                                            int t) {
-  const int rg = t >> 5, cg = t & 31;
-  float sc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) sc[i] = __fadd_rn(__fmul_rn(q2t[R.q[i] + 128], R.s2[i]), off);
-  uint32_t r[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = R.w[i];
-  transpose8x8_nibbles(r);
-  // input nibble position p holds column p^1 (first code of a byte in the
-  // high nibble), so column tc now sits in r[tc ^ 1], nibble i = row i.
-#pragma unroll
-  for (int tc = 0; tc < 8; ++tc) {
-    const uint32_t d = r[tc ^ 1];
-    uint4 o;
-    o.x = pack_bf16x2(lut_mul(lut, d, 0, sc[0]), lut_mul(lut, d, 4, sc[1]));
-    o.y = pack_bf16x2(lut_mul(lut, d, 8, sc[2]), lut_mul(lut, d, 12, sc[3]));
-    o.z = pack_bf16x2(lut_mul(lut, d, 16, sc[4]), lut_mul(lut, d, 20, sc[5]));
-    o.w = pack_bf16x2(lut_mul(lut, d, 24, sc[6]), lut_mul(lut, d, 28, sc[7]));
-    *reinterpret_cast<uint4*>(sB + lds_off(8 * cg + tc, rg)) = o;
-  }
-}
-
-// Backward weight stage (Ŵᵀ): row k = kc0 + t, reduction n0 .. n0+63 (one block).
-__device__ __forceinline__ void load_w_bwd(StageRegs& R, const BigArgs& a, int64_t kc0, int64_t n0, int t) {
-  const int64_t k = kc0 + t;
-  if (k < a.K) {
-    const int64_t e = k * a.N + n0;
-    const uint4 lo = *reinterpret_cast<const uint4*>(a.W.codes + (e >> 1));
-    const uint4 hi = *reinterpret_cast<const uint4*>(a.W.codes + (e >> 1) + 16);
-    R.w[0] = lo.x; R.w[1] = lo.y; R.w[2] = lo.z; R.w[3] = lo.w;
-    R.w[4] = hi.x; R.w[5] = hi.y; R.w[6] = hi.z; R.w[7] = hi.w;
-    R.q[0] = a.W.qabsmax[e >> 6];
-    R.s2[0] = a.W.absmax2[e >> 14];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) R.w[i] = 0x77777777u;
-    R.q[0] = 0;
-    R.s2[0] = 0.0f;
-  }
-}
-
-__device__ __forceinline__ void store_w_bwd(const StageRegs& R, char* sB, const float* lut, const float* q2t,
-                                            float off, int t) {
-  const float s = __fadd_rn(__fmul_rn(q2t[R.q[0] + 128], R.s2[0]), off);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint32_t d = R.w[c];
-    uint4 o;  // byte b: high nibble = element 2b, low nibble = element 2b+1
-    o.x = pack_bf16x2(lut_mul(lut, d, 4, s), lut_mul(lut, d, 0, s));
-    o.y = pack_bf16x2(lut_mul(lut, d, 12, s), lut_mul(lut, d, 8, s));
-    o.z = pack_bf16x2(lut_mul(lut, d, 20, s), lut_mul(lut, d, 16, s));
-    o.w = pack_bf16x2(lut_mul(lut, d, 28, s), lut_mul(lut, d, 24, s));
-    *reinterpret_cast<uint4*>(sB + lds_off(t, c)) = o;
-  }
-}
-
-__device__ __forceinline__ void compute_stage(const char* sA, const char* sB, f32x4 (&acc)[8][8], int wm, int wn,
-                                              int lane) {
-  const int q = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    bf16x8 af[8], bw[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      af[i] = *reinterpret_cast<const bf16x8*>(sA + lds_off(wm * 128 + 16 * i + q, ks * 4 + g));
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      bw[j] = *reinterpret_cast<const bf16x8*>(sB + lds_off(wn * 128 + 16 * j + q, ks * 4 + g));
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = mfma16x16x32(bw[j], af[i], acc[i][j]);
-  }
-}
-
-// Lane (q, g) holds, for tile (i, j), output row 16i+q and columns 16j+4g..+3.
-__device__ __forceinline__ void store_out(const f32x4 (&acc)[8][8], uint16_t* out, int64_t ld, int64_t rows,
-                                          int64_t cols, int64_t m0, int64_t c0, int wm, int wn, int lane) {
-  const int q = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t m = m0 + wm * 128 + 16 * i + q;
-    if (m >= rows) continue;
+    red = kForward ? a.K : a.N;
+    const int64_t P = a.K * a.N;
+    r_act = make_rsrc(a.act, a.M * a.act_ld * 2);
+    r_codes = make_rsrc(a.W.codes, (P + 1) / 2);
+    r_q = make_rsrc(a.W.qabsmax, (P + 63) / 64);
+    r_s2 = make_rsrc(a.W.absmax2, ((P + 16383) / 16384) * 4);
+    off = a.W.offset[0];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int64_t n = c0 + wn * 128 + 16 * j + 4 * g;
-      if (n < cols) {
-        uint2 v;
-        v.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-        v.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-        *reinterpret_cast<uint2*>(out + m * ld + n) = v;
-      }
+      // row = wave*64 + 8j + lane/8, whose swizzle is (lane/8) ^ j
+      const int chunk = (lane & 7) ^ (lane >> 3) ^ j;
+      const int64_t m = m0 + wave * 64 + 8 * j + (lane >> 3);
+      act_voff[j] = m < a.M ? static_cast<uint32_t>((m * a.act_ld + 8 * chunk) * 2) : kMasked;
+      act_lim[j] = static_cast<int>(red - 8 * chunk);
+    }
+    if (kForward) {
+      const int rg = t >> 5, cg = t & 31;
+      const int64_t col = c0 + 8 * cg;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        w_voff[i] = col < a.N ? static_cast<uint32_t>(((8 * rg + i) * a.N + col) >> 1) : kMasked;
+      tab_row = 8 * rg + (cg & 7);
+      tab_blk = cg >> 3;
+      tab_ok = c0 + 64 * tab_blk < a.N;
+      tab_e0 = tab_row * a.N + c0 + 64 * tab_blk;
+    } else {
+      const int64_t k = c0 + t;
+      w_voff[0] = k < a.K ? static_cast<uint32_t>((k * a.N) >> 1) : kMasked;
+      tab_row = t;
+      tab_blk = 0;
+      tab_ok = k < a.K;
+      tab_e0 = k * a.N;
+    }
+    q_voff = tab_ok ? static_cast<uint32_t>(tab_e0 >> 6) : kMasked;
+  }
+
+  __device__ char* sA(int b) const { return smem + kOffA + b * kTileBytes; }
+  __device__ char* sB(int b) const { return smem + kOffB + b * kTileBytes; }
+  __device__ uint16_t* tabs(int b) const { return reinterpret_cast<uint16_t*>(smem + kOffT + b * kTabBytes); }
+  __device__ const float* q2t() const { return reinterpret_cast<const float*>(smem + kOffQ); }
+
+  // Activation stage s -> LDS buffer b, straight from global memory.
+  __device__ void copy_act(int64_t s, int b) const {
+    const int64_t k0 = s * kBK;
+    const uint32_t soff = static_cast<uint32_t>(k0 * 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t v = (!kKTail || k0 < act_lim[j]) ? act_voff[j] : kMasked;
+      char* dst = sA(b) + (wave * 64 + 8 * j) * 128;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_act, (lds_ptr_t)(dst), 16, v, soff, 0, 0);
     }
   }
-}
 
-__device__ __forceinline__ void stage_tables(char* smem) {
-  float* lut = reinterpret_cast<float*>(smem + kLutOffset);
-  float* q2t = reinterpret_cast<float*>(smem + kQ2Offset);
-  const int t = threadIdx.x;
-  q2t[t] = q2_value(t - 128);
-  if (t < 16) lut[t] = kNF4[t];
-}
+  // Code words and the table's second-level code / scale of stage s.
+  __device__ void load_w(WRegs& R, int64_t s) const {
+    const int64_t k0 = s * kBK;
+    if (kForward) {
+      const uint32_t soff = static_cast<uint32_t>((k0 * a.N) >> 1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) R.w[i] = ld32s(r_codes, w_voff[i], soff);
+      R.q = static_cast<int>(static_cast<int8_t>(
+          __builtin_amdgcn_raw_buffer_load_b8(r_q, q_voff, static_cast<uint32_t>((k0 * a.N) >> 6), 0)));
+      const int64_t e = tab_e0 + k0 * a.N;
+      R.s2 = ld_f32(r_s2, tab_ok ? static_cast<uint32_t>((e >> 14) * 4) : kMasked);
+    } else {
+      const uint32_t soff = static_cast<uint32_t>(k0 >> 1);
+      const uint4 lo = ld128s(r_codes, w_voff[0], soff);
+      const uint4 hi = ld128s(r_codes, w_voff[0], soff + 16);
+      R.w[0] = lo.x; R.w[1] = lo.y; R.w[2] = lo.z; R.w[3] = lo.w;
+      R.w[4] = hi.x; R.w[5] = hi.y; R.w[6] = hi.z; R.w[7] = hi.w;
+      R.q = static_cast<int>(static_cast<int8_t>(
+          __builtin_amdgcn_raw_buffer_load_b8(r_q, q_voff, static_cast<uint32_t>(k0 >> 6), 0)));
+      const int64_t e = tab_e0 + k0;
+      R.s2 = ld_f32(r_s2, tab_ok ? static_cast<uint32_t>((e >> 14) * 4) : kMasked);
+    }
+  }
 
-template <bool kForward>
+  // Build this thread's table for stage s into table buffer b.
+  __device__ void build_table(const WRegs& R, int64_t s, int b) const {
+    const int64_t krow = kForward ? s * kBK + tab_row : c0 + tab_row;
+    float ahat = __fadd_rn(__fmul_rn(q2t()[R.q + 128], R.s2), off);
+    if (krow >= a.K) ahat = 0.0f;   // rows past K decode to zero
+    write_block_table(tabs(b) + (kForward ? (tab_row * 4 + tab_blk) : tab_row) * 16, ahat);
+  }
+
+  // Split code words into byte-wise doubled nibbles: ix[2c] holds 2*code of
+  // the even (high-nibble) elements of word c in its 4 bytes, ix[2c+1] those
+  // of the odd (low-nibble) elements, so a lookup address is table + 1 byte.
+  __device__ void split_codes(const WRegs& R, uint32_t (&ix)[16]) const {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      ix[2 * c] = (R.w[c] >> 3) & 0x1E1E1E1Eu;
+      ix[2 * c + 1] = (R.w[c] << 1) & 0x1E1E1E1Eu;
+    }
+  }
+
+  // Decode part `part` (0..7) of this thread's share of a stage into weight
+  // buffer b: forward column `part` of the thread's 8 columns (8 rows, one
+  // table each); backward chunk `part` of its row (8 elements, one table).
+  __device__ void decode_part(const uint32_t (&ix)[16], int b, int part) const {
+    const char* tb = reinterpret_cast<const char*>(tabs(b));
+    char* dst = sB(b);
+    uint32_t d[4];
+    if (kForward) {
+      const int rg = t >> 5, cg = t & 31;
+      const char* trow = tb + ((8 * rg) * 4 + (cg >> 3)) * 32;   // table of row 8rg + i at trow + 128 i
+      const int sh = 8 * (part >> 1);
+      const int odd = part & 1;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t i0 = (ix[2 * (2 * p) + odd] >> sh) & 0xFFu;
+        const uint32_t i1 = (ix[2 * (2 * p + 1) + odd] >> sh) & 0xFFu;
+        const uint32_t lo = *reinterpret_cast<const uint16_t*>(trow + (2 * p) * 128 + i0);
+        const uint32_t hi = *reinterpret_cast<const uint16_t*>(trow + (2 * p + 1) * 128 + i1);
+        d[p] = lo | (hi << 16);
+      }
+      *reinterpret_cast<uint4*>(dst + lds_off(8 * cg + part, rg)) = make_uint4(d[0], d[1], d[2], d[3]);
+    } else {
+      const char* tr = tb + tab_row * 32;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        // elements 2p (high nibble of byte p) and 2p+1 (low nibble)
+        const uint32_t i0 = (ix[2 * part] >> (8 * p)) & 0xFFu;
+        const uint32_t i1 = (ix[2 * part + 1] >> (8 * p)) & 0xFFu;
+        const uint32_t lo = *reinterpret_cast<const uint16_t*>(tr + i0);
+        const uint32_t hi = *reinterpret_cast<const uint16_t*>(tr + i1);
+        d[p] = lo | (hi << 16);
+      }
+      *reinterpret_cast<uint4*>(dst + lds_off(t, part)) = make_uint4(d[0], d[1], d[2], d[3]);
+    }
+  }
+
+  // One stage of MFMAs from buffer b: 4 substeps of 16 reduction elements,
+  // each 4 activation x 4 weight fragments (32 rows x 16 values; lane l holds
+  // row l%32, values 8*(l/32)..+7) and 16 v_mfma_f32_32x32x16_bf16.
+  struct Frags {
+    bf16x8 a[4], w[4];
+  };
+  __device__ void load_frags(int b, int ks, Frags& F) const {
+    const int r32 = lane & 31, h = lane >> 5, wm = wave >> 1, wn = wave & 1;
+    const char* A = sA(b);
+    const char* Bt = sB(b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      F.a[i] = *reinterpret_cast<const bf16x8*>(A + lds_off(wm * 128 + 32 * i + r32, 2 * ks + h));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      F.w[j] = *reinterpret_cast<const bf16x8*>(Bt + lds_off(wn * 128 + 32 * j + r32, 2 * ks + h));
+  }
+  __device__ static void mma(const Frags& F, f32x16 (&acc)[4][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(F.w[j], F.a[i], acc[i][j]);
+  }
+  __device__ void compute(int b, f32x16 (&acc)[4][4]) const {
+    Frags F;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      load_frags(b, ks, F);
+      mma(F, acc);
+    }
+  }
+};
+
+template <bool kForward, bool kKTail>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void qlora_big_kernel(BigArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  // stage buffer b: activation tile at 2b*T, weight tile at (2b+1)*T
-  auto sA = [&](int b) { return smem + (2 * b) * kTileBytes; };
-  auto sB = [&](int b) { return smem + (2 * b + 1) * kTileBytes; };
-  const float* lut = reinterpret_cast<const float*>(smem + kLutOffset);
-  const float* q2t = reinterpret_cast<const float*>(smem + kQ2Offset);
-  stage_tables(smem);
+  Big<kForward, kKTail> k(a, smem);
+  {
+    float* q2t = reinterpret_cast<float*>(smem + kOffQ);
+    q2t[k.t] = q2_value(k.t - 128);
+  }
+  const int64_t nst = (k.red + kBK - 1) / kBK;
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kBN;   // n0 (forward) or k0 (backward)
-  const int64_t red = kForward ? a.K : a.N;
-  const int64_t nst = (red + kBK - 1) / kBK;
-  const float off = a.W.offset[0];
-
-  f32x4 acc[8][8];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  StageRegs R;
-  load_act(R, a.act, a.act_ld, a.M, red, m0, 0, t);
-  if (kForward)
-    load_w_fwd(R, a, c0, 0, t);
-  else
-    load_w_bwd(R, a, c0, 0, t);
-  __syncthreads();  // tables staged
-  store_act(R, sA(0), t);
-  if (kForward)
-    store_w_fwd(R, sB(0), lut, q2t, off, t);
-  else
-    store_w_bwd(R, sB(0), lut, q2t, off, t);
+  // prologue: stage 0 into buffer 0, stage 1 weights into registers
+  WRegs cur, nxt;
+  k.copy_act(0, 0);
+  k.load_w(cur, 0);
+  k.load_w(nxt, 1);
+  __syncthreads();                 // q2t staged
+  k.build_table(cur, 0, 0);
+  {
+    uint32_t ix[16];
+    k.split_codes(cur, ix);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) k.decode_part(ix, 0, p);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  cur = nxt;
 
   for (int64_t s = 0; s < nst; ++s) {
-    const int cur = static_cast<int>(s & 1);
-    const bool more = s + 1 < nst;
-    if (more) {
-      const int64_t k0 = (s + 1) * kBK;
-      load_act(R, a.act, a.act_ld, a.M, red, m0, k0, t);
-      if (kForward)
-        load_w_fwd(R, a, c0, k0, t);
-      else
-        load_w_bwd(R, a, c0, k0, t);
+    const int b = static_cast<int>(s & 1);
+    // (stage s+1 and s+2 accesses past the end are masked or never read)
+    k.copy_act(s + 1, b ^ 1);
+    k.load_w(nxt, s + 2);
+    k.build_table(cur, s + 1, b ^ 1);
+    uint32_t ix[16];
+    k.split_codes(cur, ix);
+    // MFMAs of stage s, with the fragments of substep ks+1 and two decode
+    // parts of stage s+1 issued in the shadow of substep ks.
+    typename Big<kForward, kKTail>::Frags F0, F1;
+    k.load_frags(b, 0, F0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 3) k.load_frags(b, ks + 1, F1);
+      k.decode_part(ix, b ^ 1, 2 * ks);
+      k.decode_part(ix, b ^ 1, 2 * ks + 1);
+      Big<kForward, kKTail>::mma(F0, acc);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);     // DS write
+      if (ks < 3) F0 = F1;
     }
-    compute_stage(sA(cur), sB(cur), acc, wm, wn, lane);
-    if (more) {
-      store_act(R, sA(cur ^ 1), t);
-      if (kForward)
-        store_w_fwd(R, sB(cur ^ 1), lut, q2t, off, t);
-      else
-        store_w_bwd(R, sB(cur ^ 1), lut, q2t, off, t);
-    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    cur = nxt;
   }
 
   // LoRA extension: r more reduction steps with (Z, c·B) or (dZ, A).
+  const int lane = k.lane, t = k.t;
   for (int64_t j0 = 0; j0 < a.r; j0 += kBK) {
-    load_act(R, a.ext_a, a.r, a.M, a.r, m0, j0, t);
-    store_act(R, sA(0), t);
+    {
+      // activation side: rows m0 + row, reduction j0 .. j0+63 of ext_a (ld r)
+      const Rsrc re = make_rsrc(a.ext_a, a.M * a.r * 2);
+      const int c = t & 7;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int row = (t >> 3) + 32 * i;
+        const int64_t m = k.m0 + row, j = j0 + 8 * c;
+        const uint4 v = ld_b128(re, (m < a.M && j < a.r) ? static_cast<uint32_t>((m * a.r + j) * 2) : kMasked);
+        *reinterpret_cast<uint4*>(k.sA(0) + lds_off(row, c)) = v;
+      }
+    }
     if (kForward) {
-      // B tile row n = c0 + t, chunk jc holds c*B[j0 + 8jc + e][n]
-      const int64_t n = c0 + t;
+      // row n = c0 + t, chunk jc holds c*B[j0 + 8jc + e][n]
+      const int64_t n = k.c0 + t;
+      const Rsrc rb = make_rsrc(a.ext_b, a.r * a.N * 2);
 #pragma unroll
       for (int jc = 0; jc < 8; ++jc) {
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int64_t j = j0 + 8 * jc + e;
-          v[e] = (j < a.r && n < a.N) ? a.c * bf16_bits_to_f32(a.ext_b[j * a.N + n]) : 0.0f;
+          const bool ok = j < a.r && n < a.N;
+          const uint32_t raw = ld_b32(rb, ok ? static_cast<uint32_t>((j * a.N + n) * 2) & ~3u : kMasked);
+          const uint32_t bits = ((j * a.N + n) & 1) ? (raw >> 16) : (raw & 0xffffu);
+          v[e] = ok ? a.c * bf16_bits_to_f32(bits) : 0.0f;
         }
         uint4 o;
         o.x = pack_bf16x2(v[0], v[1]);
         o.y = pack_bf16x2(v[2], v[3]);
         o.z = pack_bf16x2(v[4], v[5]);
         o.w = pack_bf16x2(v[6], v[7]);
-        *reinterpret_cast<uint4*>(sB(0) + lds_off(t, jc)) = o;
+        *reinterpret_cast<uint4*>(k.sB(0) + lds_off(t, jc)) = o;
       }
     } else {
       // A-matrix row k = c0 + t, reduction j contiguous
-      const int64_t k = c0 + t;
+      const int64_t kr = k.c0 + t;
+      const Rsrc ra = make_rsrc(a.ext_b, a.K * a.r * 2);
 #pragma unroll
       for (int jc = 0; jc < 8; ++jc) {
         const int64_t j = j0 + 8 * jc;
-        const uint4 v = (k < a.K && j < a.r) ? *reinterpret_cast<const uint4*>(a.ext_b + k * a.r + j)
-                                             : make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(sB(0) + lds_off(t, jc)) = v;
+        const uint4 v = ld_b128(ra, (kr < a.K && j < a.r) ? static_cast<uint32_t>((kr * a.r + j) * 2) : kMasked);
+        *reinterpret_cast<uint4*>(k.sB(0) + lds_off(t, jc)) = v;
       }
     }
     __syncthreads();
-    compute_stage(sA(0), sB(0), acc, wm, wn, lane);
+    k.compute(0, acc);
     __syncthreads();
   }
 
-  store_out(acc, a.out, kForward ? a.N : a.K, a.M, kForward ? a.N : a.K, m0, c0, wm, wn, lane);
+  // Lane l holds, for tile (i, j), output row 32i + l%32 and, for each jj,
+  // the 4 columns 32j + 8jj + 4(l/32) .. +3.
+  const int r32 = lane & 31, h = lane >> 5, wm = k.wave >> 1, wn = k.wave & 1;
+  const int64_t cols = kForward ? a.N : a.K;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = k.m0 + wm * 128 + 32 * i + r32;
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int64_t n = k.c0 + wn * 128 + 32 * j + 8 * jj + 4 * h;
+        if (n < cols) {
+          uint2 v;
+          v.x = pack_bf16x2(acc[i][j][4 * jj], acc[i][j][4 * jj + 1]);
+          v.y = pack_bf16x2(acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]);
+          *reinterpret_cast<uint2*>(a.out + m * cols + n) = v;
+        }
+      }
+  }
 }
 
-template <bool kForward>
-hipError_t launch_big(const BigArgs& a, hipStream_t stream) {
+template <bool kForward, bool kKTail>
+hipError_t launch_big_t(const BigArgs& a, hipStream_t stream) {
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_big_kernel<kForward>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_big_kernel<kForward, kKTail>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
     configured = true;
   }
   const int64_t cols = kForward ? a.N : a.K;
   dim3 grid(static_cast<unsigned>((cols + kBN - 1) / kBN), static_cast<unsigned>((a.M + kBM - 1) / kBM), 1);
-  hipLaunchKernelGGL((qlora_big_kernel<kForward>), grid, dim3(kThreads), kLdsBytes, stream, a);
+  hipLaunchKernelGGL((qlora_big_kernel<kForward, kKTail>), grid, dim3(kThreads), kLdsBytes, stream, a);
   return hipGetLastError();
+}
+
+template <bool kForward>
+hipError_t launch_big(const BigArgs& a, hipStream_t stream) {
+  const int64_t red = kForward ? a.K : a.N;
+  return (red % kBK) ? launch_big_t<kForward, true>(a, stream) : launch_big_t<kForward, false>(a, stream);
 }
 
 }  // namespace

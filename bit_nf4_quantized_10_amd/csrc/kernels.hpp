@@ -38,6 +38,25 @@ struct NF4View {
 int64_t fwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r);
 int64_t bwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r);
 
+// Split plans of the rank-r products and of the small-M GEMV (sizes in bytes).
+struct SkinnyPlan {
+  int64_t z_splits, z_per, dz_splits, dz_per, da_splits, da_per, db_splits, db_per;
+  int64_t at_bytes, z_part, dz_part, da_part, db_part;
+  int64_t gv_rows_per_wave, gv_splits, gv_part;
+};
+SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N, int64_t r);
+
+hipError_t launch_lora_down(int64_t M, int64_t K, int64_t r, const uint16_t* X, const uint16_t* A, uint16_t* Z,
+                            const SkinnyPlan& p, void* at_ws, void* part_ws, hipStream_t stream);
+hipError_t launch_gemv(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W, const uint16_t* Z,
+                       const uint16_t* B, float c, uint16_t* Y, const SkinnyPlan& p, void* part_ws,
+                       hipStream_t stream);
+hipError_t launch_dz(int64_t M, int64_t N, int64_t r, const uint16_t* G, const uint16_t* B, float c, uint16_t* dZ,
+                     const SkinnyPlan& p, void* part_ws, hipStream_t stream);
+hipError_t launch_colsums(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const uint16_t* G,
+                          const uint16_t* Z, const uint16_t* dZ, float c, float* dA, float* dB, const SkinnyPlan& p,
+                          void* da_ws, void* db_ws, hipStream_t stream);
+
 hipError_t launch_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W,
                       const uint16_t* A, const uint16_t* B, float c, uint16_t* Y, uint16_t* Z,
                       void* ws, hipStream_t stream);

@@ -1,0 +1,52 @@
+// Orchestration of the layer entry points: workspace carving and the kernel
+// sequence of the forward and backward passes.
+//   forward : Aᵀ <- A; Z = X A (split rows/K, fixed-order reduce);
+//             M <= 16: dequant-GEMV partials, then sum + c Z B;
+//             else   : fused dequant-GEMM with the LoRA extension.
+//   backward: dZ = c G Bᵀ; dA = Xᵀ dZ; dB = c Zᵀ G; dX = G Ŵᵀ + dZ Aᵀ.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qn {
+
+namespace {
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
+int64_t fwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r) {
+  const SkinnyPlan p = plan_skinny(M, K, N, r);
+  return p.at_bytes + p.z_part + (M <= 16 ? p.gv_part : 0);
+}
+
+int64_t bwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r) {
+  const SkinnyPlan p = plan_skinny(M, K, N, r);
+  return p.dz_part + align256(M * r * 2) + p.da_part + p.db_part;
+}
+
+hipError_t launch_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W, const uint16_t* A,
+                      const uint16_t* B, float c, uint16_t* Y, uint16_t* Z, void* ws, hipStream_t stream) {
+  const SkinnyPlan p = plan_skinny(M, K, N, r);
+  char* base = static_cast<char*>(ws);
+  hipError_t e = launch_lora_down(M, K, r, X, A, Z, p, base, base + p.at_bytes, stream);
+  if (e != hipSuccess) return e;
+  if (M <= 16) return launch_gemv(M, K, N, r, X, W, Z, B, c, Y, p, base + p.at_bytes + p.z_part, stream);
+  return launch_fwd_big(M, K, N, r, X, W, Z, B, c, Y, stream);
+}
+
+hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* X,
+                      const uint16_t* Z, NF4View W, const uint16_t* A, const uint16_t* B, float c, uint16_t* dX,
+                      float* dA, float* dB, void* ws, hipStream_t stream) {
+  const SkinnyPlan p = plan_skinny(M, K, N, r);
+  char* base = static_cast<char*>(ws);
+  void* dz_part = base;
+  uint16_t* dz16 = reinterpret_cast<uint16_t*>(base + p.dz_part);
+  void* da_part = base + p.dz_part + align256(M * r * 2);
+  void* db_part = static_cast<char*>(da_part) + p.da_part;
+  hipError_t e = launch_dz(M, N, r, G, B, c, dz16, p, dz_part, stream);
+  if (e != hipSuccess) return e;
+  if ((e = launch_colsums(M, K, N, r, X, G, Z, dz16, c, dA, dB, p, da_part, db_part, stream)) != hipSuccess) return e;
+  if (dX != nullptr) return launch_dx_big(M, K, N, r, G, W, dz16, A, dX, stream);
+  return hipGetLastError();
+}
+
+}  // namespace qn
