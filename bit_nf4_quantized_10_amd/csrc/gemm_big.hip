@@ -66,6 +66,7 @@ struct BigArgs {
   float c;                 // forward: LoRA scale
   uint16_t* out;           // Y (M x N) or dX (M x K)
   int64_t M, K, N, r;
+  const uint16_t* wdense;  // dense path: Ŵᵀ (N x K, forward) or Ŵ (K x N, backward), bf16
 };
 
 // Registers carried from the load of a stage to its decode.
@@ -290,74 +291,99 @@ struct Big {
   }
 };
 
+// Dense core: both operands are bf16 matrices with the reduction contiguous
+// (activations M x red and the dequantized weight rows x red), copied into
+// LDS by buffer loads with the LDS destination; no decode in the loop.
 template <bool kForward, bool kKTail>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void qlora_big_kernel(BigArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  Big<kForward, kKTail> k(a, smem);
-  {
-    float* q2t = reinterpret_cast<float*>(smem + kOffQ);
-    q2t[k.t] = q2_value(k.t - 128);
-  }
-  const int64_t nst = (k.red + kBK - 1) / kBK;
+struct Dense {
+  const BigArgs& a;
+  char* smem;
+  int t, lane, wave;
+  int64_t m0, c0, red;
+  Rsrc r_act, r_w;
+  uint32_t act_voff[8], w_voff[8];
+  int lim[8];
 
-  f32x16 acc[4][4];
+  __device__ Dense(const BigArgs& args, char* s) : a(args), smem(s) {
+    t = threadIdx.x;
+    lane = t & 63;
+    wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    {
+      const int64_t ntx = gridDim.x, total = static_cast<int64_t>(gridDim.x) * gridDim.y;
+      const int64_t id = static_cast<int64_t>(blockIdx.y) * ntx + blockIdx.x;
+      const int64_t per = (total + 7) / 8, xcd = id % 8, slot = id / 8;
+      int64_t tile = xcd * per + slot;
+      if (total % 8 != 0 || tile >= total) tile = id;
+      m0 = (tile / ntx) * kBM;
+      c0 = (tile % ntx) * kBN;
+    }
+    red = kForward ? a.K : a.N;
+    const int64_t wrows = kForward ? a.N : a.K;
+    r_act = make_rsrc(a.act, a.M * red * 2);
+    r_w = make_rsrc(a.wdense, wrows * red * 2);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 8; ++j) {
+      const int chunk = (lane & 7) ^ (lane >> 3) ^ j;   // row = wave*64 + 8j + lane/8
+      const int64_t m = m0 + wave * 64 + 8 * j + (lane >> 3);
+      const int64_t n = c0 + wave * 64 + 8 * j + (lane >> 3);
+      act_voff[j] = m < a.M ? static_cast<uint32_t>((m * red + 8 * chunk) * 2) : kMasked;
+      w_voff[j] = n < wrows ? static_cast<uint32_t>((n * red + 8 * chunk) * 2) : kMasked;
+      lim[j] = static_cast<int>(red - 8 * chunk);
+    }
+  }
+
+  __device__ char* sA(int b) const { return smem + kOffA + b * kTileBytes; }
+  __device__ char* sB(int b) const { return smem + kOffB + b * kTileBytes; }
+
+  __device__ void copy(int64_t s, int b) const {
+    const int64_t k0 = s * kBK;
+    const uint32_t soff = static_cast<uint32_t>(k0 * 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool ok = !kKTail || k0 < lim[j];
+      char* da = sA(b) + (wave * 64 + 8 * j) * 128;
+      char* dw = sB(b) + (wave * 64 + 8 * j) * 128;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_act, (lds_ptr_t)(da), 16, ok ? act_voff[j] : kMasked, soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr_t)(dw), 16, ok ? w_voff[j] : kMasked, soff, 0, 0);
+    }
+  }
+
+  struct Frags {
+    bf16x8 a[4], w[4];
+  };
+  __device__ void load_frags(int b, int ks, Frags& F) const {
+    const int r32 = lane & 31, h = lane >> 5, wm = wave >> 1, wn = wave & 1;
+    const char* A = sA(b);
+    const char* Bt = sB(b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      F.a[i] = *reinterpret_cast<const bf16x8*>(A + lds_off(wm * 128 + 32 * i + r32, 2 * ks + h));
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  // prologue: stage 0 into buffer 0, stage 1 weights into registers
-  WRegs cur, nxt;
-  k.copy_act(0, 0);
-  k.load_w(cur, 0);
-  k.load_w(nxt, 1);
-  __syncthreads();                 // q2t staged
-  k.build_table(cur, 0, 0);
-  {
-    uint32_t ix[16];
-    k.split_codes(cur, ix);
-#pragma unroll
-    for (int p = 0; p < 8; ++p) k.decode_part(ix, 0, p);
+      F.w[j] = *reinterpret_cast<const bf16x8*>(Bt + lds_off(wn * 128 + 32 * j + r32, 2 * ks + h));
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  cur = nxt;
-
-  for (int64_t s = 0; s < nst; ++s) {
-    const int b = static_cast<int>(s & 1);
-    // (stage s+1 and s+2 accesses past the end are masked or never read)
-    k.copy_act(s + 1, b ^ 1);
-    k.load_w(nxt, s + 2);
-    k.build_table(cur, s + 1, b ^ 1);
-    uint32_t ix[16];
-    k.split_codes(cur, ix);
-    // MFMAs of stage s, with the fragments of substep ks+1 and two decode
-    // parts of stage s+1 issued in the shadow of substep ks.
-    typename Big<kForward, kKTail>::Frags F0, F1;
-    k.load_frags(b, 0, F0);
+  __device__ static void mma(const Frags& F, f32x16 (&acc)[4][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(F.w[j], F.a[i], acc[i][j]);
+  }
+  __device__ void compute(int b, f32x16 (&acc)[4][4]) const {
+    Frags F0, F1;
+    load_frags(b, 0, F0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      if (ks < 3) k.load_frags(b, ks + 1, F1);
-      k.decode_part(ix, b ^ 1, 2 * ks);
-      k.decode_part(ix, b ^ 1, 2 * ks + 1);
-      Big<kForward, kKTail>::mma(F0, acc);
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);     // DS write
+      if (ks < 3) load_frags(b, ks + 1, F1);
+      mma(F0, acc);
       if (ks < 3) F0 = F1;
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    cur = nxt;
   }
+};
 
-  // LoRA extension: r more reduction steps with (Z, c·B) or (dZ, A).
+// LoRA extension (r more reduction steps with (Z, c·B) or (dZ, A)) and the
+// bf16 store of the accumulators; shared by the fused and dense kernels.
+template <bool kForward, class Core>
+__device__ __forceinline__ void finish(const Core& k, const BigArgs& a, f32x16 (&acc)[4][4]) {
   const int lane = k.lane, t = k.t;
   for (int64_t j0 = 0; j0 < a.r; j0 += kBK) {
     {
@@ -434,6 +460,101 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 }
 
 template <bool kForward, bool kKTail>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void qlora_big_kernel(BigArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  Big<kForward, kKTail> k(a, smem);
+  {
+    float* q2t = reinterpret_cast<float*>(smem + kOffQ);
+    q2t[k.t] = q2_value(k.t - 128);
+  }
+  const int64_t nst = (k.red + kBK - 1) / kBK;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // prologue: stage 0 into buffer 0, stage 1 weights into registers
+  WRegs cur, nxt;
+  k.copy_act(0, 0);
+  k.load_w(cur, 0);
+  k.load_w(nxt, 1);
+  __syncthreads();                 // q2t staged
+  k.build_table(cur, 0, 0);
+  {
+    uint32_t ix[16];
+    k.split_codes(cur, ix);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) k.decode_part(ix, 0, p);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  cur = nxt;
+
+  for (int64_t s = 0; s < nst; ++s) {
+    const int b = static_cast<int>(s & 1);
+    // (stage s+1 and s+2 accesses past the end are masked or never read)
+    k.copy_act(s + 1, b ^ 1);
+    k.load_w(nxt, s + 2);
+    k.build_table(cur, s + 1, b ^ 1);
+    uint32_t ix[16];
+    k.split_codes(cur, ix);
+    // MFMAs of stage s, with the fragments of substep ks+1 and two decode
+    // parts of stage s+1 issued in the shadow of substep ks.
+    typename Big<kForward, kKTail>::Frags F0, F1;
+    k.load_frags(b, 0, F0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 3) k.load_frags(b, ks + 1, F1);
+      k.decode_part(ix, b ^ 1, 2 * ks);
+      k.decode_part(ix, b ^ 1, 2 * ks + 1);
+      Big<kForward, kKTail>::mma(F0, acc);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);     // DS write
+      if (ks < 3) F0 = F1;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    cur = nxt;
+  }
+
+  finish<kForward>(k, a, acc);
+}
+
+template <bool kForward, bool kKTail>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void qlora_dense_kernel(BigArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  Dense<kForward, kKTail> k(a, smem);
+  const int64_t nst = (k.red + kBK - 1) / kBK;
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  k.copy(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int64_t s = 0; s < nst; ++s) {
+    const int b = static_cast<int>(s & 1);
+    k.copy(s + 1, b ^ 1);   // past the end: offsets fall outside the buffers or are never read
+    k.compute(b, acc);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  finish<kForward>(k, a, acc);
+}
+
+template <bool kForward, bool kKTail>
 hipError_t launch_big_t(const BigArgs& a, hipStream_t stream) {
   static bool configured = false;
   if (!configured) {
@@ -454,11 +575,50 @@ hipError_t launch_big(const BigArgs& a, hipStream_t stream) {
   return (red % kBK) ? launch_big_t<kForward, true>(a, stream) : launch_big_t<kForward, false>(a, stream);
 }
 
+template <bool kForward, bool kKTail>
+hipError_t launch_dense_t(const BigArgs& a, hipStream_t stream) {
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_dense_kernel<kForward, kKTail>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 4 * kTileBytes);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  const int64_t cols = kForward ? a.N : a.K;
+  dim3 grid(static_cast<unsigned>((cols + kBN - 1) / kBN), static_cast<unsigned>((a.M + kBM - 1) / kBM), 1);
+  hipLaunchKernelGGL((qlora_dense_kernel<kForward, kKTail>), grid, dim3(kThreads), 4 * kTileBytes, stream, a);
+  return hipGetLastError();
+}
+
+template <bool kForward>
+hipError_t launch_dense(const BigArgs& a, hipStream_t stream) {
+  const int64_t red = kForward ? a.K : a.N;
+  return (red % kBK) ? launch_dense_t<kForward, true>(a, stream) : launch_dense_t<kForward, false>(a, stream);
+}
+
 }  // namespace
+
+hipError_t launch_fwd_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const uint16_t* WhatT,
+                            const uint16_t* Z, const uint16_t* B, float c, uint16_t* Y, hipStream_t stream) {
+  BigArgs a{X, K, NF4View{}, Z, B, c, Y, M, K, N, r, WhatT};
+  Timer t(QK_FWD_GEMM, stream);
+  hipError_t e = launch_dense<true>(a, stream);
+  t.stop();
+  return e;
+}
+
+hipError_t launch_dx_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* What,
+                           const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream) {
+  BigArgs a{G, N, NF4View{}, dZ, A, 1.0f, dX, M, K, N, r, What};
+  Timer t(QK_BWD_DX, stream);
+  hipError_t e = launch_dense<false>(a, stream);
+  t.stop();
+  return e;
+}
 
 hipError_t launch_fwd_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W,
                           const uint16_t* Z, const uint16_t* B, float c, uint16_t* Y, hipStream_t stream) {
-  BigArgs a{X, K, W, Z, B, c, Y, M, K, N, r};
+  BigArgs a{X, K, W, Z, B, c, Y, M, K, N, r, nullptr};
   Timer t(QK_FWD_GEMM, stream);
   hipError_t e = launch_big<true>(a, stream);
   t.stop();
@@ -467,7 +627,7 @@ hipError_t launch_fwd_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint
 
 hipError_t launch_dx_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, NF4View W,
                          const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream) {
-  BigArgs a{G, N, W, dZ, A, 1.0f, dX, M, K, N, r};
+  BigArgs a{G, N, W, dZ, A, 1.0f, dX, M, K, N, r, nullptr};
   Timer t(QK_BWD_DX, stream);
   hipError_t e = launch_big<false>(a, stream);
   t.stop();

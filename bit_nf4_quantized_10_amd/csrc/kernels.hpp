@@ -72,4 +72,14 @@ hipError_t launch_fwd_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint
 hipError_t launch_dx_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, NF4View W,
                          const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream);
 
+hipError_t launch_fwd_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const uint16_t* WhatT,
+                            const uint16_t* Z, const uint16_t* B, float c, uint16_t* Y, hipStream_t stream);
+hipError_t launch_dx_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* What,
+                           const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream);
+
+// Dequantize a K x N weight to bf16, either as stored (K x N) or transposed (N x K).
+hipError_t launch_dequant_bf16(const uint8_t* codes, const int8_t* qabsmax, const float* absmax2,
+                               const float* offset, int64_t K, int64_t N, bool transposed, uint16_t* out,
+                               hipStream_t stream);
+
 }  // namespace qn

@@ -11,16 +11,24 @@ namespace qn {
 
 namespace {
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// From this many tokens on, the weight is dequantized once to bf16 and the
+// product runs as a dense bf16 GEMM; below, the fused kernel decodes the
+// packed codes inside its k-loop (each weight tile is then decoded by fewer
+// row-tiles, so the one-off decode pass does not pay for itself).
+constexpr int64_t kDenseMinM = 512;
+bool use_dense(int64_t M) { return M >= kDenseMinM; }
+int64_t dense_bytes(int64_t M, int64_t K, int64_t N) { return use_dense(M) ? align256(K * N * 2) : 0; }
 }  // namespace
 
 int64_t fwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r) {
   const SkinnyPlan p = plan_skinny(M, K, N, r);
-  return p.at_bytes + p.z_part + (M <= 16 ? p.gv_part : 0);
+  return p.at_bytes + p.z_part + (M <= 16 ? p.gv_part : 0) + dense_bytes(M, K, N);
 }
 
 int64_t bwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r) {
   const SkinnyPlan p = plan_skinny(M, K, N, r);
-  return p.dz_part + align256(M * r * 2) + p.da_part + p.db_part;
+  return p.dz_part + align256(M * r * 2) + p.da_part + p.db_part + dense_bytes(M, K, N);
 }
 
 hipError_t launch_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W, const uint16_t* A,
@@ -30,6 +38,11 @@ hipError_t launch_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
   hipError_t e = launch_lora_down(M, K, r, X, A, Z, p, base, base + p.at_bytes, stream);
   if (e != hipSuccess) return e;
   if (M <= 16) return launch_gemv(M, K, N, r, X, W, Z, B, c, Y, p, base + p.at_bytes + p.z_part, stream);
+  if (use_dense(M)) {
+    uint16_t* wt = reinterpret_cast<uint16_t*>(base + p.at_bytes + p.z_part);
+    if ((e = launch_dequant_bf16(W.codes, W.qabsmax, W.absmax2, W.offset, K, N, true, wt, stream)) != hipSuccess) return e;
+    return launch_fwd_dense(M, K, N, r, X, wt, Z, B, c, Y, stream);
+  }
   return launch_fwd_big(M, K, N, r, X, W, Z, B, c, Y, stream);
 }
 
@@ -45,7 +58,15 @@ hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
   hipError_t e = launch_dz(M, N, r, G, B, c, dz16, p, dz_part, stream);
   if (e != hipSuccess) return e;
   if ((e = launch_colsums(M, K, N, r, X, G, Z, dz16, c, dA, dB, p, da_part, db_part, stream)) != hipSuccess) return e;
-  if (dX != nullptr) return launch_dx_big(M, K, N, r, G, W, dz16, A, dX, stream);
+  if (dX != nullptr) {
+    if (use_dense(M)) {
+      uint16_t* wd = reinterpret_cast<uint16_t*>(static_cast<char*>(db_part) + p.db_part);
+      if ((e = launch_dequant_bf16(W.codes, W.qabsmax, W.absmax2, W.offset, K, N, false, wd, stream)) != hipSuccess)
+        return e;
+      return launch_dx_dense(M, K, N, r, G, wd, dz16, A, dX, stream);
+    }
+    return launch_dx_big(M, K, N, r, G, W, dz16, A, dX, stream);
+  }
   return hipGetLastError();
 }
 

@@ -276,6 +276,56 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_dequant_kernel(
   }
 }
 
+// Transposed decoder for a K x N weight: out[n][k] = RNE_bf16(fl32(C[j] * â))
+// (the same values nf4_dequant_kernel writes at [k][n]).  Workgroup tile:
+// 64 k x 128 n, staged through LDS so both the code reads (along n) and the
+// bf16 writes (along k) are row-contiguous.
+constexpr int kTPad = 66;  // bf16 per LDS row (64 k + 2): 132-byte rows
+
+__global__ __launch_bounds__(256) void nf4_dequant_t_kernel(const uint8_t* __restrict__ codes,
+                                                            const int8_t* __restrict__ qabsmax,
+                                                            const float* __restrict__ absmax2,
+                                                            const float* __restrict__ offset, int64_t K, int64_t N,
+                                                            uint16_t* __restrict__ out) {
+  __shared__ float s_lut[16];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * kTPad];
+  const int t = threadIdx.x;
+  if (t < 16) s_lut[t] = kNF4[t];
+  __syncthreads();
+  const int64_t k0 = static_cast<int64_t>(blockIdx.y) * 64, n0 = static_cast<int64_t>(blockIdx.x) * 128;
+  const float off = offset[0];
+  {
+    const int kk = t >> 2, part = t & 3;           // row k0+kk, columns n0 + 32*part .. +31 (one block)
+    const int64_t k = k0 + kk, nb = n0 + 32 * part;
+    const bool ok = k < K && nb < N;
+    float ahat = 0.0f;
+    uint32_t w[4] = {0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
+    if (ok) {
+      const int64_t e0 = k * N + nb;
+      ahat = absmax_hat(qabsmax[e0 >> 6], absmax2[e0 >> 14], off);
+      const uint4 v = *reinterpret_cast<const uint4*>(codes + (e0 >> 1));
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float v[8];
+      decode8(w[c], ahat, s_lut, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tile[(32 * part + 8 * c + e) * kTPad + kk] = static_cast<uint16_t>(pack_bf16x2(v[e], 0.0f));
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = t + 256 * i, nn = id >> 3, c = id & 7;
+    const int64_t n = n0 + nn, k = k0 + 8 * c;
+    if (n < N && k < K) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(tile + nn * kTPad + 8 * c);
+      *reinterpret_cast<uint4*>(out + n * K + k) = make_uint4(src[0], src[1], src[2], src[3]);
+    }
+  }
+}
+
 __global__ void nf4_status_clear_kernel(int32_t* status) { status[0] = 0; }
 
 // ----------------------------------------------------------------- launchers
@@ -309,6 +359,17 @@ hipError_t launch_dequantize(const uint8_t* codes, const int8_t* qabsmax, const 
   Timer t(QK_DEQUANT, stream);
   hipLaunchKernelGGL(nf4_dequant_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kQuantThreads), 0,
                      stream, codes, qabsmax, absmax2, offset, P, out, out_dtype, status);
+  t.stop();
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_bf16(const uint8_t* codes, const int8_t* qabsmax, const float* absmax2,
+                               const float* offset, int64_t K, int64_t N, bool transposed, uint16_t* out,
+                               hipStream_t stream) {
+  if (!transposed) return launch_dequantize(codes, qabsmax, absmax2, offset, K * N, out, NF4_OUT_BF16, nullptr, stream);
+  Timer t(QK_DEQUANT, stream);
+  dim3 grid(static_cast<unsigned>((N + 127) / 128), static_cast<unsigned>((K + 63) / 64));
+  hipLaunchKernelGGL(nf4_dequant_t_kernel, grid, dim3(256), 0, stream, codes, qabsmax, absmax2, offset, K, N, out);
   t.stop();
   return hipGetLastError();
 }

@@ -197,6 +197,8 @@ LAYER_SHAPES = [
     (17, 256, 256, 8, 2.0),      # large-M path, ragged M
     (130, 264, 320, 24, 0.25),   # ragged M, K % 32 != 0, N % 128 != 0, r % 32 != 0
     (256, 512, 512, 64, 0.25),
+    (600, 264, 320, 24, 0.5),    # dequantize-then-GEMM path (M >= 512), ragged everywhere
+    (1024, 512, 768, 64, 0.25),  # dequantize-then-GEMM path, two row tiles x three column tiles
 ]
 
 
@@ -246,7 +248,7 @@ def _integer_case(M, K, N, r, seed):
     return dict(W=W, X=X, A=A, B=B, G=G, Xb=bits(X), Ab=bits(A), Bb=bits(B), Gb=bits(G), c=0.5)
 
 
-@pytest.mark.parametrize("M,K,N,r", [(16, 256, 256, 8), (96, 320, 384, 16)])
+@pytest.mark.parametrize("M,K,N,r", [(16, 256, 256, 8), (96, 320, 384, 16), (520, 256, 320, 16)])
 def test_layer_exact_integer_case_bit_exact(M, K, N, r):
     say(f"exact-integer layer M={M} K={K} N={N} r={r}")
     case = _integer_case(M, K, N, r, seed=M + N)
