@@ -62,12 +62,32 @@ struct BigArgs {
   int64_t act_ld;          // K (forward) or N (backward)
   NF4View W;
   const uint16_t* ext_a;   // Z (forward) or dZ (backward), M x r bf16
-  const uint16_t* ext_b;   // B (forward, r x N) or A (backward, K x r)
-  float c;                 // forward: LoRA scale
+  const uint16_t* ext_b;   // (c B)ᵀ in bf16 (forward, N x r) or A (backward, K x r)
   uint16_t* out;           // Y (M x N) or dX (M x K)
   int64_t M, K, N, r;
   const uint16_t* wdense;  // dense path: Ŵᵀ (N x K, forward) or Ŵ (K x N, backward), bf16
 };
+
+#ifndef QN_TILE_GROUP
+#define QN_TILE_GROUP 4
+#endif
+constexpr int64_t kGroup = QN_TILE_GROUP;
+
+// Workgroup -> output tile origin.  Workgroups are dealt to the 8 XCDs
+// round-robin (id % 8); XCD x takes the x-th contiguous run of tile numbers,
+// and tile numbers walk groups of kGroup row-tiles column by column, so the
+// tiles of one XCD form a compact block whose activation rows and weight
+// columns are shared in that XCD's L2.  A bijection for any grid.
+__device__ __forceinline__ void tile_origin(int64_t& m0, int64_t& c0) {
+  const int64_t ntx = gridDim.x, nty = gridDim.y, total = ntx * nty;
+  const int64_t id = static_cast<int64_t>(blockIdx.y) * ntx + blockIdx.x;
+  const int64_t t = (total % 8 == 0) ? (id % 8) * (total / 8) + id / 8 : id;
+  const int64_t g = t / (kGroup * ntx), first = g * kGroup;
+  const int64_t gm = nty - first < kGroup ? nty - first : kGroup;
+  const int64_t w = t - g * kGroup * ntx;
+  m0 = (first + w % gm) * kBM;
+  c0 = (w / gm) * kBN;
+}
 
 // Registers carried from the load of a stage to its decode.
 struct WRegs {
@@ -111,21 +131,7 @@ struct Big {
     t = threadIdx.x;
     lane = t & 63;
     wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Give
-    // XCD x the contiguous run of tiles [x*T/8, (x+1)*T/8) in row-major order,
-    // so the workgroups sharing an activation row-tile and a weight
-    // column-tile sit behind the same L2.
-    {
-      const int64_t ntx = gridDim.x, total = static_cast<int64_t>(gridDim.x) * gridDim.y;
-      const int64_t id = static_cast<int64_t>(blockIdx.y) * ntx + blockIdx.x;
-      const int64_t per = (total + 7) / 8, xcd = id % 8, slot = id / 8;
-      int64_t tile = xcd * per + slot;
-      // the last XCD may own fewer tiles; fold the overflow back onto the ids
-      // that would otherwise be unused (keeps the map a bijection)
-      if (total % 8 != 0 || tile >= total) tile = id;
-      m0 = (tile / ntx) * kBM;
-      c0 = (tile % ntx) * kBN;
-    }
+    tile_origin(m0, c0);
     red = kForward ? a.K : a.N;
     const int64_t P = a.K * a.N;
     r_act = make_rsrc(a.act, a.M * a.act_ld * 2);
@@ -308,15 +314,7 @@ struct Dense {
     t = threadIdx.x;
     lane = t & 63;
     wave = __builtin_amdgcn_readfirstlane(t >> 6);
-    {
-      const int64_t ntx = gridDim.x, total = static_cast<int64_t>(gridDim.x) * gridDim.y;
-      const int64_t id = static_cast<int64_t>(blockIdx.y) * ntx + blockIdx.x;
-      const int64_t per = (total + 7) / 8, xcd = id % 8, slot = id / 8;
-      int64_t tile = xcd * per + slot;
-      if (total % 8 != 0 || tile >= total) tile = id;
-      m0 = (tile / ntx) * kBM;
-      c0 = (tile % ntx) * kBN;
-    }
+    tile_origin(m0, c0);
     red = kForward ? a.K : a.N;
     const int64_t wrows = kForward ? a.N : a.K;
     r_act = make_rsrc(a.act, a.M * red * 2);
@@ -380,56 +378,30 @@ struct Dense {
   }
 };
 
-// LoRA extension (r more reduction steps with (Z, c·B) or (dZ, A)) and the
-// bf16 store of the accumulators; shared by the fused and dense kernels.
+// LoRA extension: r more reduction steps over (Z, (c B)ᵀ) in the forward or
+// (dZ, A) in the backward; both operands are row-major with r contiguous
+// (M x r and cols x r), staged into the 64-wide LDS layout of the main loop.
+// Then the bf16 store: the tile goes through LDS (row-major, 512 bytes per
+// row, 16-byte chunk q of row R at q ^ (R & 31)) so that every global store
+// writes whole 512-byte row segments.  Shared by the fused and dense kernels;
+// the main loop has released LDS when this starts.
 template <bool kForward, class Core>
 __device__ __forceinline__ void finish(const Core& k, const BigArgs& a, f32x16 (&acc)[4][4]) {
   const int lane = k.lane, t = k.t;
+  const int64_t cols = kForward ? a.N : a.K;
+  const Rsrc re = make_rsrc(a.ext_a, a.M * a.r * 2);
+  const Rsrc rb = make_rsrc(a.ext_b, cols * a.r * 2);
   for (int64_t j0 = 0; j0 < a.r; j0 += kBK) {
-    {
-      // activation side: rows m0 + row, reduction j0 .. j0+63 of ext_a (ld r)
-      const Rsrc re = make_rsrc(a.ext_a, a.M * a.r * 2);
-      const int c = t & 7;
+    const int c = t & 7;
+    const int64_t j = j0 + 8 * c;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int row = (t >> 3) + 32 * i;
-        const int64_t m = k.m0 + row, j = j0 + 8 * c;
-        const uint4 v = ld_b128(re, (m < a.M && j < a.r) ? static_cast<uint32_t>((m * a.r + j) * 2) : kMasked);
-        *reinterpret_cast<uint4*>(k.sA(0) + lds_off(row, c)) = v;
-      }
-    }
-    if (kForward) {
-      // row n = c0 + t, chunk jc holds c*B[j0 + 8jc + e][n]
-      const int64_t n = k.c0 + t;
-      const Rsrc rb = make_rsrc(a.ext_b, a.r * a.N * 2);
-#pragma unroll
-      for (int jc = 0; jc < 8; ++jc) {
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int64_t j = j0 + 8 * jc + e;
-          const bool ok = j < a.r && n < a.N;
-          const uint32_t raw = ld_b32(rb, ok ? static_cast<uint32_t>((j * a.N + n) * 2) & ~3u : kMasked);
-          const uint32_t bits = ((j * a.N + n) & 1) ? (raw >> 16) : (raw & 0xffffu);
-          v[e] = ok ? a.c * bf16_bits_to_f32(bits) : 0.0f;
-        }
-        uint4 o;
-        o.x = pack_bf16x2(v[0], v[1]);
-        o.y = pack_bf16x2(v[2], v[3]);
-        o.z = pack_bf16x2(v[4], v[5]);
-        o.w = pack_bf16x2(v[6], v[7]);
-        *reinterpret_cast<uint4*>(k.sB(0) + lds_off(t, jc)) = o;
-      }
-    } else {
-      // A-matrix row k = c0 + t, reduction j contiguous
-      const int64_t kr = k.c0 + t;
-      const Rsrc ra = make_rsrc(a.ext_b, a.K * a.r * 2);
-#pragma unroll
-      for (int jc = 0; jc < 8; ++jc) {
-        const int64_t j = j0 + 8 * jc;
-        const uint4 v = ld_b128(ra, (kr < a.K && j < a.r) ? static_cast<uint32_t>((kr * a.r + j) * 2) : kMasked);
-        *reinterpret_cast<uint4*>(k.sB(0) + lds_off(t, jc)) = v;
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int row = (t >> 3) + 32 * i;
+      const int64_t m = k.m0 + row, n = k.c0 + row;
+      const uint4 v = ld_b128(re, (m < a.M && j < a.r) ? static_cast<uint32_t>((m * a.r + j) * 2) : kMasked);
+      const uint4 w = ld_b128(rb, (n < cols && j < a.r) ? static_cast<uint32_t>((n * a.r + j) * 2) : kMasked);
+      *reinterpret_cast<uint4*>(k.sA(0) + lds_off(row, c)) = v;
+      *reinterpret_cast<uint4*>(k.sB(0) + lds_off(row, c)) = w;
     }
     __syncthreads();
     k.compute(0, acc);
@@ -438,24 +410,35 @@ __device__ __forceinline__ void finish(const Core& k, const BigArgs& a, f32x16 (
 
   // Lane l holds, for tile (i, j), output row 32i + l%32 and, for each jj,
   // the 4 columns 32j + 8jj + 4(l/32) .. +3.
-  const int r32 = lane & 31, h = lane >> 5, wm = k.wave >> 1, wn = k.wave & 1;
-  const int64_t cols = kForward ? a.N : a.K;
+  char* st = k.sA(0);
+  {
+    const int r32 = lane & 31, h = lane >> 5, wm = k.wave >> 1, wn = k.wave & 1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t m = k.m0 + wm * 128 + 32 * i + r32;
-    if (m >= a.M) continue;
+    for (int i = 0; i < 4; ++i) {
+      const int R = wm * 128 + 32 * i + r32;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int64_t n = k.c0 + wn * 128 + 32 * j + 8 * jj + 4 * h;
-        if (n < cols) {
+        for (int jj = 0; jj < 4; ++jj) {
+          const int q = wn * 16 + 4 * j + jj;
           uint2 v;
           v.x = pack_bf16x2(acc[i][j][4 * jj], acc[i][j][4 * jj + 1]);
           v.y = pack_bf16x2(acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]);
-          *reinterpret_cast<uint2*>(a.out + m * cols + n) = v;
+          *reinterpret_cast<uint2*>(st + R * 512 + ((q ^ r32) << 4) + 8 * h) = v;
         }
-      }
+    }
+  }
+  __syncthreads();
+  {
+    const int q = lane & 31;
+    const int64_t n = k.c0 + 8 * q;
+#pragma unroll 4
+    for (int u = 0; u < 32; ++u) {
+      const int R = k.wave * 64 + 2 * u + (lane >> 5);
+      const int64_t m = k.m0 + R;
+      const uint4 v = *reinterpret_cast<const uint4*>(st + R * 512 + ((q ^ (R & 31)) << 4));
+      if (m < a.M && n < cols) *reinterpret_cast<uint4*>(a.out + m * cols + n) = v;
+    }
   }
 }
 
@@ -599,8 +582,8 @@ hipError_t launch_dense(const BigArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const uint16_t* WhatT,
-                            const uint16_t* Z, const uint16_t* B, float c, uint16_t* Y, hipStream_t stream) {
-  BigArgs a{X, K, NF4View{}, Z, B, c, Y, M, K, N, r, WhatT};
+                            const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream) {
+  BigArgs a{X, K, NF4View{}, Z, cBt, Y, M, K, N, r, WhatT};
   Timer t(QK_FWD_GEMM, stream);
   hipError_t e = launch_dense<true>(a, stream);
   t.stop();
@@ -609,7 +592,7 @@ hipError_t launch_fwd_dense(int64_t M, int64_t K, int64_t N, int64_t r, const ui
 
 hipError_t launch_dx_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* What,
                            const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream) {
-  BigArgs a{G, N, NF4View{}, dZ, A, 1.0f, dX, M, K, N, r, What};
+  BigArgs a{G, N, NF4View{}, dZ, A, dX, M, K, N, r, What};
   Timer t(QK_BWD_DX, stream);
   hipError_t e = launch_dense<false>(a, stream);
   t.stop();
@@ -617,8 +600,8 @@ hipError_t launch_dx_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uin
 }
 
 hipError_t launch_fwd_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W,
-                          const uint16_t* Z, const uint16_t* B, float c, uint16_t* Y, hipStream_t stream) {
-  BigArgs a{X, K, W, Z, B, c, Y, M, K, N, r, nullptr};
+                          const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream) {
+  BigArgs a{X, K, W, Z, cBt, Y, M, K, N, r, nullptr};
   Timer t(QK_FWD_GEMM, stream);
   hipError_t e = launch_big<true>(a, stream);
   t.stop();
@@ -627,7 +610,7 @@ hipError_t launch_fwd_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint
 
 hipError_t launch_dx_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, NF4View W,
                          const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream) {
-  BigArgs a{G, N, W, dZ, A, 1.0f, dX, M, K, N, r, nullptr};
+  BigArgs a{G, N, W, dZ, A, dX, M, K, N, r, nullptr};
   Timer t(QK_BWD_DX, stream);
   hipError_t e = launch_big<false>(a, stream);
   t.stop();

@@ -46,8 +46,11 @@ struct SkinnyPlan {
 };
 SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N, int64_t r);
 
+// Z = X A; with cbt != nullptr the same launch also writes cbt = RNE_bf16(c B)ᵀ
+// (N x r), the forward's LoRA extension operand.
 hipError_t launch_lora_down(int64_t M, int64_t K, int64_t r, const uint16_t* X, const uint16_t* A, uint16_t* Z,
-                            const SkinnyPlan& p, void* at_ws, void* part_ws, hipStream_t stream);
+                            const SkinnyPlan& p, void* at_ws, void* part_ws, hipStream_t stream, int64_t N = 0,
+                            const uint16_t* B = nullptr, float c = 1.0f, uint16_t* cbt = nullptr);
 hipError_t launch_gemv(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W, const uint16_t* Z,
                        const uint16_t* B, float c, uint16_t* Y, const SkinnyPlan& p, void* part_ws,
                        hipStream_t stream);
@@ -66,14 +69,15 @@ hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
                       const uint16_t* B, float c, uint16_t* dX, float* dA, float* dB, void* ws,
                       hipStream_t stream);
 
+// cBt: RNE_bf16(c B)ᵀ, N x r
 hipError_t launch_fwd_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W,
-                          const uint16_t* Z, const uint16_t* B, float c, uint16_t* Y, hipStream_t stream);
+                          const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream);
 
 hipError_t launch_dx_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, NF4View W,
                          const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream);
 
 hipError_t launch_fwd_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const uint16_t* WhatT,
-                            const uint16_t* Z, const uint16_t* B, float c, uint16_t* Y, hipStream_t stream);
+                            const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream);
 hipError_t launch_dx_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* What,
                            const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream);
 

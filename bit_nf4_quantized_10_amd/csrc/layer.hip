@@ -2,8 +2,11 @@
 // sequence of the forward and backward passes.
 //   forward : Aᵀ <- A; Z = X A (split rows/K, fixed-order reduce);
 //             M <= 16: dequant-GEMV partials, then sum + c Z B;
-//             else   : fused dequant-GEMM with the LoRA extension.
-//   backward: dZ = c G Bᵀ; dA = Xᵀ dZ; dB = c Zᵀ G; dX = G Ŵᵀ + dZ Aᵀ.
+//             else   : (c B)ᵀ in bf16 (same launch as Aᵀ), then
+//                      M < 512: fused dequant-GEMM with the LoRA extension;
+//                      M >= 512: Ŵᵀ dequantized to bf16, dense GEMM.
+//   backward: dZ = c G Bᵀ; dA = Xᵀ dZ; dB = c Zᵀ G; dX = G Ŵᵀ + dZ Aᵀ
+//             (M >= 512: Ŵ dequantized to bf16 first, dense GEMM).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -21,9 +24,12 @@ bool use_dense(int64_t M) { return M >= kDenseMinM; }
 int64_t dense_bytes(int64_t M, int64_t K, int64_t N) { return use_dense(M) ? align256(K * N * 2) : 0; }
 }  // namespace
 
+// (c B)ᵀ in bf16 for the GEMM kernels' LoRA extension
+int64_t cbt_bytes(int64_t M, int64_t N, int64_t r) { return M > 16 ? align256(N * r * 2) : 0; }
+
 int64_t fwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r) {
   const SkinnyPlan p = plan_skinny(M, K, N, r);
-  return p.at_bytes + p.z_part + (M <= 16 ? p.gv_part : 0) + dense_bytes(M, K, N);
+  return p.at_bytes + p.z_part + (M <= 16 ? p.gv_part : 0) + cbt_bytes(M, N, r) + dense_bytes(M, K, N);
 }
 
 int64_t bwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r) {
@@ -35,15 +41,21 @@ hipError_t launch_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
                       const uint16_t* B, float c, uint16_t* Y, uint16_t* Z, void* ws, hipStream_t stream) {
   const SkinnyPlan p = plan_skinny(M, K, N, r);
   char* base = static_cast<char*>(ws);
-  hipError_t e = launch_lora_down(M, K, r, X, A, Z, p, base, base + p.at_bytes, stream);
-  if (e != hipSuccess) return e;
-  if (M <= 16) return launch_gemv(M, K, N, r, X, W, Z, B, c, Y, p, base + p.at_bytes + p.z_part, stream);
-  if (use_dense(M)) {
-    uint16_t* wt = reinterpret_cast<uint16_t*>(base + p.at_bytes + p.z_part);
-    if ((e = launch_dequant_bf16(W.codes, W.qabsmax, W.absmax2, W.offset, K, N, true, wt, stream)) != hipSuccess) return e;
-    return launch_fwd_dense(M, K, N, r, X, wt, Z, B, c, Y, stream);
+  char* after_z = base + p.at_bytes + p.z_part;
+  if (M <= 16) {
+    hipError_t e = launch_lora_down(M, K, r, X, A, Z, p, base, base + p.at_bytes, stream);
+    if (e != hipSuccess) return e;
+    return launch_gemv(M, K, N, r, X, W, Z, B, c, Y, p, after_z, stream);
   }
-  return launch_fwd_big(M, K, N, r, X, W, Z, B, c, Y, stream);
+  uint16_t* cbt = reinterpret_cast<uint16_t*>(after_z);
+  hipError_t e = launch_lora_down(M, K, r, X, A, Z, p, base, base + p.at_bytes, stream, N, B, c, cbt);
+  if (e != hipSuccess) return e;
+  if (use_dense(M)) {
+    uint16_t* wt = reinterpret_cast<uint16_t*>(after_z + cbt_bytes(M, N, r));
+    if ((e = launch_dequant_bf16(W.codes, W.qabsmax, W.absmax2, W.offset, K, N, true, wt, stream)) != hipSuccess) return e;
+    return launch_fwd_dense(M, K, N, r, X, wt, Z, cbt, Y, stream);
+  }
+  return launch_fwd_big(M, K, N, r, X, W, Z, cbt, Y, stream);
 }
 
 hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* X,

@@ -23,6 +23,9 @@ namespace qn {
 
 namespace {
 
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
 __device__ __forceinline__ uint16_t bf16_of(float x) {
   return static_cast<uint16_t>(pack_bf16x2(x, 0.0f) & 0xffffu);
 }
@@ -32,22 +35,41 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 }
 
 // ------------------------------------------------------------ transpose
-// dst[c][r] = src[r][c] for a rows x cols bf16 matrix (32 x 32 LDS tiles).
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src,
-                                                             uint16_t* __restrict__ dst, int64_t rows,
-                                                             int64_t cols) {
+// dst[c][r] = RNE_bf16(scale * src[r][c]) for a rows x cols bf16 matrix
+// (32 x 32 LDS tiles; scale 1 copies the bits).  One launch serves two such
+// jobs: Aᵀ for the rank-r products and, in the forward, the LoRA extension
+// operand (c B)ᵀ, rounded once to bf16.
+struct TJob {
+  const uint16_t* src;
+  uint16_t* dst;
+  int64_t rows, cols;
+  float scale;
+  int64_t bx, nblk;   // 32-column tiles per tile row, tiles in this job
+};
+
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(TJob j0, TJob j1) {
   __shared__ uint16_t tile[32][33];
-  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 32, c0 = static_cast<int64_t>(blockIdx.x) * 32;
+  const bool second = blockIdx.x >= j0.nblk;
+  const TJob j = second ? j1 : j0;
+  const int64_t b = second ? blockIdx.x - j0.nblk : blockIdx.x;
+  const int64_t r0 = (b / j.bx) * 32, c0 = (b % j.bx) * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   for (int i = ty; i < 32; i += 8) {
     const int64_t r = r0 + i, c = c0 + tx;
-    tile[i][tx] = (r < rows && c < cols) ? src[r * cols + c] : 0;
+    uint16_t v = (r < j.rows && c < j.cols) ? j.src[r * j.cols + c] : 0;
+    if (j.scale != 1.0f) v = bf16_of(j.scale * bf16_bits_to_f32(v));
+    tile[i][tx] = v;
   }
   __syncthreads();
   for (int i = ty; i < 32; i += 8) {
     const int64_t c = c0 + i, r = r0 + tx;
-    if (c < cols && r < rows) dst[c * rows + r] = tile[tx][i];
+    if (c < j.cols && r < j.rows) j.dst[c * j.rows + r] = tile[tx][i];
   }
+}
+
+TJob tjob(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols, float scale) {
+  const int64_t bx = cdiv(cols, 32);
+  return TJob{src, dst, rows, cols, scale, bx, bx * cdiv(rows, 32)};
 }
 
 // ------------------------------------------------------------ row sums
@@ -402,9 +424,6 @@ __global__ __launch_bounds__(64) void gemv_finish_kernel(const float* __restrict
   }
 }
 
-int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
-
 void split_plan(int64_t tiles, int64_t red, int64_t target, int64_t quantum, int64_t* splits, int64_t* per) {
   int64_t s = cdiv(target, tiles);
   const int64_t max_s = cdiv(red, quantum);
@@ -451,10 +470,14 @@ SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N, int64_t r) {
 }
 
 hipError_t launch_lora_down(int64_t M, int64_t K, int64_t r, const uint16_t* X, const uint16_t* A, uint16_t* Z,
-                            const SkinnyPlan& p, void* at_ws, void* part_ws, hipStream_t stream) {
+                            const SkinnyPlan& p, void* at_ws, void* part_ws, hipStream_t stream, int64_t N,
+                            const uint16_t* B, float c, uint16_t* cbt) {
   uint16_t* At = static_cast<uint16_t*>(at_ws);
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(static_cast<unsigned>(cdiv(r, 32)), static_cast<unsigned>(cdiv(K, 32))),
-                     dim3(256), 0, stream, A, At, K, r);
+  const TJob ja = tjob(A, At, K, r, 1.0f);
+  TJob jb = cbt != nullptr ? tjob(B, cbt, r, N, c) : ja;
+  if (cbt == nullptr) jb.nblk = 0;
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(static_cast<unsigned>(ja.nblk + jb.nblk)), dim3(256), 0, stream, ja,
+                     jb);
   float* part = static_cast<float*>(part_ws);
   const int64_t row_tiles = cdiv(M, 16);
   Timer tm(QK_LORA_DOWN, stream);
