@@ -1,38 +1,42 @@
-// Large-M fused dequant-GEMM kernels for gfx950: the forward Y = X Ŵ + c Z B
-// and the backward dX = G Ŵᵀ + dZ Aᵀ (page "QLoRA：冻结的 4-bit 权重怎样参与一次微调",
+// Large-M GEMM kernels for gfx950: the forward Y = X Ŵ + c Z B and the
+// backward dX = G Ŵᵀ + dZ Aᵀ (page "QLoRA：冻结的 4-bit 权重怎样参与一次微调",
 // sections "量化基座与可训练支路怎样相加" and "冻结权重为什么仍然需要输入梯度").
 //
-// Workgroup: 256 threads (4 waves, 2 x 2), output tile 256 x 256, each wave
-// 128 x 128 as 8 x 8 tiles of v_mfma_f32_16x16x32_bf16 (256 fp32 accumulators
-// per lane, one wave per SIMD).  The reduction advances 64 elements per stage;
-// LDS holds two stages.  In iteration s the workgroup
+// Both kernels: workgroup of 256 threads (4 waves, 2 x 2), output tile
+// 256 x 256, each wave 128 x 128 as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16
+// (256 fp32 accumulators per lane in AGPRs, one wave per SIMD).  The LoRA
+// term is r more reduction steps over (Z, (c B)ᵀ) or (dZ, A) after the main
+// loop; the bf16 tile is then stored through LDS as whole rows.
+//
+// qlora_big_kernel (17 <= M < 512) decodes the packed weight inside its
+// reduction loop.  Per 64-element stage the workgroup
 //   - copies the activation tile of stage s+1 from global memory straight into
 //     LDS (buffer loads with the LDS destination, no registers involved);
 //   - loads the code words and block scales of stage s+2 into registers;
 //   - builds the bf16 block tables of stage s+1 (16 entries RNE(fl32(C[j]*â))
 //     per 64-weight block row) and decodes stage s+1 into the other weight
 //     buffer by table lookups (no per-weight multiply or conversion);
-//   - runs the 128 MFMAs of stage s;
-// then waits for its loads and synchronises once.
-//
-// LDS layout of one operand stage: 256 rows x 64 bf16 (128 bytes per row), the
-// eight 16-byte chunks of row r stored at chunk ^ ((r ^ r >> 3) & 7), which
-// keeps the fragment reads (16 consecutive rows, one chunk) and the decoder's
-// writes (rows 8 apart, one chunk) free of bank conflicts per 8 lanes.
-//
-// Weight operand:
-//  - forward (reduction over k, codes packed along n): thread (rg, cg) owns
-//    k-rows 8rg..8rg+7 and columns 8cg..8cg+7 of the stage; it builds the
+//   - runs the 64 MFMAs of stage s;
+// then waits for its loads and synchronises once.  LDS layout of one operand
+// stage: 256 rows x 64 bf16 (128 bytes per row), the eight 16-byte chunks of
+// row r stored at chunk ^ ((r ^ r >> 3) & 7), which keeps the fragment reads
+// and the decoder's writes free of bank conflicts per 8 lanes.
+//  - forward weight (reduction over k, codes packed along n): thread (rg, cg)
+//    owns k-rows 8rg..8rg+7 and columns 8cg..8cg+7 of the stage; it builds the
 //    table of one (row, block) pair that the 8 threads of its group share
-//    (all in one wave) and writes each column's 8 k-values as one chunk;
-//  - backward dX (reduction over n, the packed direction): thread t owns
+//    and writes each column's 8 k-values as one chunk;
+//  - backward weight (reduction over n, the packed direction): thread t owns
 //    k-row t and the stage's 64 n, exactly one block and one table.
 // Rows at or past K get an all-zero table and the matching activation
-// chunks are masked, so tails add exact zeros.  Every global load is a raw
-// buffer load, so masked lanes need no branches.
+// chunks are masked, so tails add exact zeros.
 //
+// qlora_dense_kernel (M >= 512) reads a weight dequantized beforehand to bf16
+// (bit-identical to the fused decode) and streams both operands through a
+// five-slot LDS ring (see Dense below).
+//
+// Every global load is a raw buffer load, so masked lanes need no branches.
 // The MFMA is issued as D = Ŵ-fragment x activation-fragment, so each lane
-// holds 4 consecutive output columns of one output row: 8-byte bf16 stores.
+// holds 4 consecutive output columns of one output row.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -298,8 +302,20 @@ struct Big {
 };
 
 // Dense core: both operands are bf16 matrices with the reduction contiguous
-// (activations M x red and the dequantized weight rows x red), copied into
-// LDS by buffer loads with the LDS destination; no decode in the loop.
+// (activations M x red and the dequantized weight, rows x red).  The
+// reduction advances 32 elements per stage through a ring of kSlots LDS
+// slots (slot = 256 activation rows + 256 weight rows, 64 bytes each, the
+// four 16-byte chunks of row R at chunk ^ ((R >> 1) & 3)).  Copies are
+// buffer loads straight into LDS, issued three to four stages ahead and
+// spread one per four MFMAs, so the memory pipeline never backs up into the
+// MFMA issue stream; one barrier per stage.
+constexpr int kRK = 32;
+constexpr int kRTile = 256 * 64;                 // one operand of one slot
+constexpr int kSlots = 5;
+constexpr int kRingLds = kSlots * 2 * kRTile;    // 160 KB
+
+__device__ __forceinline__ int roff(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
+
 template <bool kForward, bool kKTail>
 struct Dense {
   const BigArgs& a;
@@ -307,8 +323,9 @@ struct Dense {
   int t, lane, wave;
   int64_t m0, c0, red;
   Rsrc r_act, r_w;
-  uint32_t act_voff[8], w_voff[8];
-  int lim[8];
+  uint32_t act_voff[4], w_voff[4];   // copy j: row wave*64 + 16j + lane/4, chunk (lane&3)^((lane>>3)&3)
+  int lim[4];
+  int foffA[2][4], foffW[2][4];      // fragment offsets within a slot, per substep
 
   __device__ Dense(const BigArgs& args, char* s) : a(args), smem(s) {
     t = threadIdx.x;
@@ -319,61 +336,106 @@ struct Dense {
     const int64_t wrows = kForward ? a.N : a.K;
     r_act = make_rsrc(a.act, a.M * red * 2);
     r_w = make_rsrc(a.wdense, wrows * red * 2);
+    const int chunk = (lane & 3) ^ ((lane >> 3) & 3);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int chunk = (lane & 7) ^ (lane >> 3) ^ j;   // row = wave*64 + 8j + lane/8
-      const int64_t m = m0 + wave * 64 + 8 * j + (lane >> 3);
-      const int64_t n = c0 + wave * 64 + 8 * j + (lane >> 3);
+    for (int j = 0; j < 4; ++j) {
+      const int row = wave * 64 + 16 * j + (lane >> 2);
+      const int64_t m = m0 + row, n = c0 + row;
       act_voff[j] = m < a.M ? static_cast<uint32_t>((m * red + 8 * chunk) * 2) : kMasked;
       w_voff[j] = n < wrows ? static_cast<uint32_t>((n * red + 8 * chunk) * 2) : kMasked;
       lim[j] = static_cast<int>(red - 8 * chunk);
     }
+    const int r32 = lane & 31, h = lane >> 5, wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        foffA[ks][i] = roff(wm * 128 + 32 * i + r32, 2 * ks + h);
+        foffW[ks][i] = kRTile + roff(wn * 128 + 32 * i + r32, 2 * ks + h);
+      }
   }
 
-  __device__ char* sA(int b) const { return smem + kOffA + b * kTileBytes; }
-  __device__ char* sB(int b) const { return smem + kOffB + b * kTileBytes; }
+  // 64-wide layout used by the LoRA extension after the main loop
+  __device__ char* sA(int) const { return smem; }
+  __device__ char* sB(int) const { return smem + kTileBytes; }
+  __device__ char* slot(int b) const { return smem + b * 2 * kRTile; }
 
-  __device__ void copy(int64_t s, int b) const {
-    const int64_t k0 = s * kBK;
+  // Copy instruction g (0..3) of half `half` of stage s into slot b: the
+  // activation (even g) or weight (odd g) rows wave*64 + 16j .. +15,
+  // j = 2*half + g/2, 64 bytes each.  Past the reduction end it reads zeros.
+  __device__ void copy_one(int64_t s, int b, int half, int g) const {
+    const int64_t k0 = s * kRK;
     const uint32_t soff = static_cast<uint32_t>(k0 * 2);
+    const int j = 2 * half + (g >> 1);
+    const bool ok = !kKTail || k0 < lim[j];
+    char* dst = slot(b) + (wave * 64 + 16 * j) * 64;
+    if ((g & 1) == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_act, (lds_ptr_t)(dst), 16, ok ? act_voff[j] : kMasked, soff, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr_t)(dst + kRTile), 16, ok ? w_voff[j] : kMasked, soff, 0,
+                                               0);
+  }
+  __device__ void copy_stage(int64_t s, int b) const {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool ok = !kKTail || k0 < lim[j];
-      char* da = sA(b) + (wave * 64 + 8 * j) * 128;
-      char* dw = sB(b) + (wave * 64 + 8 * j) * 128;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_act, (lds_ptr_t)(da), 16, ok ? act_voff[j] : kMasked, soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr_t)(dw), 16, ok ? w_voff[j] : kMasked, soff, 0, 0);
-    }
+    for (int g = 0; g < 8; ++g) copy_one(s, b, g >> 2, g & 3);
   }
 
   struct Frags {
     bf16x8 a[4], w[4];
   };
   __device__ void load_frags(int b, int ks, Frags& F) const {
+    const char* base = slot(b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) F.a[i] = *reinterpret_cast<const bf16x8*>(base + foffA[ks][i]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) F.w[j] = *reinterpret_cast<const bf16x8*>(base + foffW[ks][j]);
+  }
+
+  // 16 MFMAs from Fc; in their shadow, the 8 fragment reads of substep ksn
+  // of slot bn into Fn (all within the first 8 MFMAs, so the last 8 cover
+  // their latency) and the 4 copies of half ch of stage cs into slot cb.
+  // The order is pinned with scheduling barriers.
+  __device__ void half_step(const Frags& Fc, Frags& Fn, int bn, int ksn, int64_t cs, int cb, int ch,
+                            f32x16 (&acc)[4][4]) const {
+    const char* base = slot(bn);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc[g][u] = mfma32x32x16(Fc.w[u], Fc.a[g], acc[g][u]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (g < 2) {
+          const int q = 4 * g + u;
+          if ((q & 1) == 0)
+            Fn.a[q >> 1] = *reinterpret_cast<const bf16x8*>(base + foffA[ksn][q >> 1]);
+          else
+            Fn.w[q >> 1] = *reinterpret_cast<const bf16x8*>(base + foffW[ksn][q >> 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (u == 1) {
+          copy_one(cs, cb, ch, g);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  }
+
+  // One 64-element reduction step from the 64-wide layout at sA(0)/sB(0).
+  __device__ void compute(int, f32x16 (&acc)[4][4]) const {
     const int r32 = lane & 31, h = lane >> 5, wm = wave >> 1, wn = wave & 1;
-    const char* A = sA(b);
-    const char* Bt = sB(b);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      F.a[i] = *reinterpret_cast<const bf16x8*>(A + lds_off(wm * 128 + 32 * i + r32, 2 * ks + h));
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      F.w[j] = *reinterpret_cast<const bf16x8*>(Bt + lds_off(wn * 128 + 32 * j + r32, 2 * ks + h));
-  }
-  __device__ static void mma(const Frags& F, f32x16 (&acc)[4][4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(F.w[j], F.a[i], acc[i][j]);
-  }
-  __device__ void compute(int b, f32x16 (&acc)[4][4]) const {
-    Frags F0, F1;
-    load_frags(b, 0, F0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      if (ks < 3) load_frags(b, ks + 1, F1);
-      mma(F0, acc);
-      if (ks < 3) F0 = F1;
+      Frags F;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        F.a[i] = *reinterpret_cast<const bf16x8*>(sA(0) + lds_off(wm * 128 + 32 * i + r32, 2 * ks + h));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        F.w[j] = *reinterpret_cast<const bf16x8*>(sB(0) + lds_off(wn * 128 + 32 * j + r32, 2 * ks + h));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(F.w[j], F.a[i], acc[i][j]);
     }
   }
 };
@@ -512,11 +574,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   finish<kForward>(k, a, acc);
 }
 
+// s_waitcnt immediates (vmcnt split over bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8; an all-ones field does not wait)
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+
 template <bool kForward, bool kKTail>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void qlora_dense_kernel(BigArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   Dense<kForward, kKTail> k(a, smem);
-  const int64_t nst = (k.red + kBK - 1) / kBK;
+  const int64_t nst = (k.red + kRK - 1) / kRK;
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -524,16 +590,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  k.copy(0, 0);
+  // Barrier B(x) (in the middle of stage x-1) says: every wave has finished
+  // reading slot (x-1) % S and stage x has landed.  Stage x's 8 copies are
+  // issued in two halves between B(x-S+1) and B(x-S+2), into slot x % S,
+  // which B(x-S+1) released.  Each wave then has (S-2) later stages (8
+  // copies each) outstanding when it waits for stage x.  Copies of stages
+  // past the end read zeros or land in slots that are never read.
+  constexpr int S = kSlots;
+  for (int x = 0; x < S - 1; ++x) k.copy_stage(x, x);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) k.copy_one(S - 1, S - 1, 0, g);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(8 * (S - 2) + 4, 15));
+  __builtin_amdgcn_s_barrier();
+  typename Dense<kForward, kKTail>::Frags F0, F1;
+  k.load_frags(0, 0, F0);
+  int b = 0;
+  for (int64_t s = 0; s < nst; ++s) {
+    const int bp = b == 0 ? S - 1 : b - 1;   // slot of stage s + S - 1
+    const int bn = b == S - 1 ? 0 : b + 1;   // slot of stage s + 1
+    k.half_step(F0, F1, b, 1, s + S - 1, bp, 1, acc);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(8 * (S - 2), 0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    k.half_step(F1, F0, bn, 0, s + S, b, 0, acc);
+    b = bn;
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int64_t s = 0; s < nst; ++s) {
-    const int b = static_cast<int>(s & 1);
-    k.copy(s + 1, b ^ 1);   // past the end: offsets fall outside the buffers or are never read
-    k.compute(b, acc);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
   finish<kForward>(k, a, acc);
 }
 
@@ -563,13 +646,13 @@ hipError_t launch_dense_t(const BigArgs& a, hipStream_t stream) {
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_dense_kernel<kForward, kKTail>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 4 * kTileBytes);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kRingLds);
     if (e != hipSuccess) return e;
     configured = true;
   }
   const int64_t cols = kForward ? a.N : a.K;
   dim3 grid(static_cast<unsigned>((cols + kBN - 1) / kBN), static_cast<unsigned>((a.M + kBM - 1) / kBM), 1);
-  hipLaunchKernelGGL((qlora_dense_kernel<kForward, kKTail>), grid, dim3(kThreads), 4 * kTileBytes, stream, a);
+  hipLaunchKernelGGL((qlora_dense_kernel<kForward, kKTail>), grid, dim3(kThreads), kRingLds, stream, a);
   return hipGetLastError();
 }
 

@@ -446,11 +446,14 @@ hipError_t launch_reduce2(const float* part, int64_t splits, int64_t rows, int64
 }  // namespace
 
 // ------------------------------------------------------------ plans
+#ifndef QN_ROWSUM_WAVES
+#define QN_ROWSUM_WAVES 512   // target number of row-sum waves (row tiles x splits)
+#endif
 SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N, int64_t r) {
   SkinnyPlan p{};
   const int64_t row_tiles = cdiv(M, 16);
-  split_plan(row_tiles, K, 512, 128, &p.z_splits, &p.z_per);
-  split_plan(row_tiles, N, 512, 128, &p.dz_splits, &p.dz_per);
+  split_plan(row_tiles, K, QN_ROWSUM_WAVES, 128, &p.z_splits, &p.z_per);
+  split_plan(row_tiles, N, QN_ROWSUM_WAVES, 128, &p.dz_splits, &p.dz_per);
   split_plan(cdiv(K, 64), M, 512, 32, &p.da_splits, &p.da_per);
   split_plan(cdiv(N, 64), M, 512, 32, &p.db_splits, &p.db_per);
   p.at_bytes = round_up(r * K * 2, 256);

@@ -199,6 +199,8 @@ LAYER_SHAPES = [
     (256, 512, 512, 64, 0.25),
     (600, 264, 320, 24, 0.5),    # dequantize-then-GEMM path (M >= 512), ragged everywhere
     (1024, 512, 768, 64, 0.25),  # dequantize-then-GEMM path, two row tiles x three column tiles
+    (520, 64, 128, 8, 1.0),      # dense path with fewer reduction stages than LDS ring slots
+    (512, 4104, 192, 16, 0.5),   # dense path, long reduction with a ragged last stage
 ]
 
 
