@@ -18,7 +18,7 @@ NF4_OK, NF4_EINVAL, NF4_ENONFINITE, NF4_EPADDING, NF4_EHIP = 0, 1, 2, 4, 8
 NF4_OUT_F32, NF4_OUT_BF16 = 0, 1
 KERNEL_IDS = {
     "quant_pass1": 0, "quant_mean": 1, "quant_pass2": 2, "dequant": 3, "lora_down": 4,
-    "fwd_gemm": 5, "fwd_gemv": 6, "bwd_dz": 7, "bwd_dx": 8, "bwd_da": 9, "bwd_db": 10,
+    "fwd_gemm": 5, "fwd_gemv": 6, "bwd_dz": 7, "bwd_dx": 8, "bwd_colsum": 9, "dequant_bf16": 10,
     "reduce": 11,
 }
 C_FUNCTIONS = [

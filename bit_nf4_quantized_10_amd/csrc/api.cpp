@@ -24,9 +24,15 @@ bool state_ok(const nf4_state_t* s) {
          s->absmax2 != nullptr && s->offset != nullptr;
 }
 
+// Kernels address operands with 32-bit buffer offsets and mark masked lanes
+// with offset 2^31; keeping every bf16 operand (X, G, Y, dX and the
+// dequantized weight) under 1 GiB keeps all such offsets below 2^32.
+constexpr int64_t kMaxOperandElems = int64_t(1) << 29;
+
 bool layer_shape_ok(int64_t M, int64_t K, int64_t N, int64_t r) {
   return M >= 1 && K >= 1 && N >= 1 && r >= 1 && N % NF4_BLOCK1 == 0 && K % 8 == 0 && r % 8 == 0 &&
-         r <= 256 && M <= (int64_t(1) << 20) && K <= (int64_t(1) << 24) && N <= (int64_t(1) << 24);
+         r <= 256 && M <= (int64_t(1) << 20) && K <= (int64_t(1) << 24) && N <= (int64_t(1) << 24) &&
+         M * K < kMaxOperandElems && M * N < kMaxOperandElems && K * N < kMaxOperandElems;
 }
 
 // ---------------------------------------------------------------- timers

@@ -58,6 +58,13 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+
 // Decode the 8 nibbles of one little-endian code word (byte i holds codes
 // 2i in the high nibble and 2i+1 in the low nibble) with a per-block scale
 // held in `ahat`, into 8 fp32 reconstructions fl32(C[j] * ahat).  `lut` is
@@ -95,6 +102,12 @@ __device__ __forceinline__ float ld_f32(Rsrc r, uint32_t off) {
 __device__ __forceinline__ int ld_i8(Rsrc r, uint32_t off) {
   return static_cast<int>(static_cast<int8_t>(__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0)));
 }
+
+// s_waitcnt immediate for gfx9: vmcnt split over bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; an all-ones field does not wait.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // The 16 reconstructions RNE_bf16(fl32(C[j] * ahat)) of one block, written
 // as 32 bytes (entry j at byte 2j) to 16-byte aligned LDS.

@@ -59,7 +59,6 @@ constexpr int kLdsBytes = kOffQ + 256 * 4;
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 4); }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 struct BigArgs {
   const uint16_t* act;     // X (forward) or G (backward): rows m, reduction contiguous
@@ -102,11 +101,6 @@ struct WRegs {
 
 __device__ __forceinline__ uint32_t nib(uint32_t w, int t) { return (w >> (8 * (t >> 1) + ((t & 1) ? 0 : 4))) & 15u; }
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 __device__ __forceinline__ uint32_t ld32s(Rsrc r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
@@ -573,10 +567,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   finish<kForward>(k, a, acc);
 }
-
-// s_waitcnt immediates (vmcnt split over bits 3:0 and 15:14, expcnt 6:4,
-// lgkmcnt 11:8; an all-ones field does not wait)
-constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
 template <bool kForward, bool kKTail>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void qlora_dense_kernel(BigArgs a) {

@@ -367,7 +367,7 @@ hipError_t launch_dequant_bf16(const uint8_t* codes, const int8_t* qabsmax, cons
                                const float* offset, int64_t K, int64_t N, bool transposed, uint16_t* out,
                                hipStream_t stream) {
   if (!transposed) return launch_dequantize(codes, qabsmax, absmax2, offset, K * N, out, NF4_OUT_BF16, nullptr, stream);
-  Timer t(QK_DEQUANT, stream);
+  Timer t(QK_DEQUANT_BF16, stream);
   dim3 grid(static_cast<unsigned>((N + 127) / 128), static_cast<unsigned>((K + 63) / 64));
   hipLaunchKernelGGL(nf4_dequant_t_kernel, grid, dim3(256), 0, stream, codes, qabsmax, absmax2, offset, K, N, out);
   t.stop();

@@ -73,152 +73,273 @@ TJob tjob(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols, float 
 }
 
 // ------------------------------------------------------------ row sums
-// out[row][j] = sum_red act[row][red] * wt[j][red] over this wave's split.
-// One wave per (16-row tile, split); r <= 16 * RT.  The reduction runs in
-// chunks of U steps of 32; the next chunk's fragments are loaded before the
-// current chunk's MFMAs so that memory latency overlaps the math.
-template <int RT, int U>
-struct RowFrag {
-  uint4 a[U];
-  uint4 w[U][RT];
+// part[split][m][j] = sum, over this split's share of the reduction, of
+// act[m][k] * wt[j][k]; both operands contiguous along k.  A workgroup owns a
+// 64-row x 64-column output block (columns j0 .. j0+63): four waves of 16 rows
+// x 4 tiles of v_mfma_f32_16x16x32_bf16.  64-wide stages flow through a ring
+// of kRsSlots LDS slots (64 activation rows, then 64 weight rows, 128 bytes
+// each, 16-byte chunk c of row R at c ^ (R & 7)), filled by buffer loads with
+// the LDS destination three stages ahead; one barrier per stage.  The weight
+// rows are shared by the four waves, so each weight slice is fetched once per
+// 64 activation rows.
+constexpr int kRsSlots = 4;
+constexpr int kRsSlot = 2 * 64 * 128;
+
+struct RsArgs {
+  const uint16_t* act;
+  const uint16_t* wt;
+  int64_t M, r, red, per_split, row_blocks, j_chunks;
+  float* part;   // [splits][M][r]
 };
 
-template <int RT, int U>
-__device__ __forceinline__ void rowsum_load(RowFrag<RT, U>& f, Rsrc ra, int64_t arow_off, bool row_ok, Rsrc rw,
-                                            int64_t ld_wt, int64_t r, int64_t kc, int64_t end, int q, int g) {
+__device__ __forceinline__ int rs_off(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+__global__ __launch_bounds__(256) void rowsum_kernel(RsArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kRsSlots * kRsSlot];
+  const int t = threadIdx.x, lane = t & 63, q = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int64_t rb = blockIdx.x % a.row_blocks, rest = blockIdx.x / a.row_blocks;
+  const int64_t m0 = rb * 64, j0 = (rest % a.j_chunks) * 64, split = rest / a.j_chunks;
+  const int64_t beg = split * a.per_split;
+  const int64_t len = min(a.red, beg + a.per_split) - beg;
+  const int64_t nst = (len + 63) / 64;
+  const Rsrc ra = make_rsrc(a.act, a.M * a.red * 2), rw = make_rsrc(a.wt, a.r * a.red * 2);
+  // copy i (0..1) of each operand fills slot rows 16*wave + 8i .. +7; lane -> row
+  // 16*wave + 8i + lane/8, slot position lane & 7, global chunk (lane & 7) ^ (row & 7)
+  uint32_t av[2], wv[2];
+  int lim[2];
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int64_t k = kc + 32 * u + 8 * g;
-    const bool k_ok = k < end;
-    f.a[u] = ld_b128(ra, (row_ok && k_ok) ? static_cast<uint32_t>((arow_off + k) * 2) : kMasked);
+  for (int i = 0; i < 2; ++i) {
+    const int R = 16 * wave + 8 * i + (lane >> 3), c = (lane & 7) ^ (R & 7);
+    const int64_t m = m0 + R, j = j0 + R;
+    av[i] = m < a.M ? static_cast<uint32_t>((m * a.red + beg + 8 * c) * 2) : kMasked;
+    wv[i] = j < a.r ? static_cast<uint32_t>((j * a.red + beg + 8 * c) * 2) : kMasked;
+    lim[i] = static_cast<int>(len - 8 * c);
+  }
+  auto copy = [&](int64_t s, int b) {
+    const int64_t k0 = s * 64;
+    const uint32_t soff = static_cast<uint32_t>(k0 * 2);
+    char* slot = smem + b * kRsSlot;
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const int64_t j = 16 * t + q;
-      f.w[u][t] = ld_b128(rw, (j < r && k_ok) ? static_cast<uint32_t>((j * ld_wt + k) * 2) : kMasked);
+    for (int i = 0; i < 2; ++i) {
+      const bool ok = k0 < lim[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + (16 * wave + 8 * i) * 128), 16,
+                                               ok ? av[i] : kMasked, soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(slot + 8192 + (16 * wave + 8 * i) * 128), 16,
+                                               ok ? wv[i] : kMasked, soff, 0, 0);
+    }
+  };
+  f32x4 acc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] = f32x4{0, 0, 0, 0};
+  // stages past the end read zeros into slots that are never read
+  copy(0, 0);
+  copy(1, 1);
+  copy(2, 2);
+  for (int64_t s = 0; s < nst; ++s) {
+    const int b = static_cast<int>(s & 3);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(8, 0));   // own copies of stage s landed
+    __builtin_amdgcn_s_barrier();                    // everyone's; slot (s-1)&3 released
+    copy(s + 3, (b + 3) & 3);
+    const char* slot = smem + b * kRsSlot;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const bf16x8 af = *reinterpret_cast<const bf16x8*>(slot + rs_off(16 * wave + q, 4 * st + g));
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bf16x8 wf = *reinterpret_cast<const bf16x8*>(slot + 8192 + rs_off(16 * u + q, 4 * st + g));
+        acc[u] = mfma16x16x32(af, wf, acc[u]);
+      }
     }
   }
-}
-
-template <int RT, int U>
-__global__ __launch_bounds__(64) void rowsum_kernel(const uint16_t* __restrict__ act, int64_t ld_act,
-                                                    const uint16_t* __restrict__ wt, int64_t ld_wt,
-                                                    int64_t rows, int64_t r, int64_t red, int64_t per_split,
-                                                    int64_t row_tiles, float* __restrict__ part) {
-  const int lane = threadIdx.x, q = lane & 15, g = lane >> 4;
-  const int64_t tile = blockIdx.x % row_tiles, split = blockIdx.x / row_tiles;
-  const int64_t row = tile * 16 + q;
-  const int64_t beg = split * per_split, end = min(red, beg + per_split);
-  const bool row_ok = row < rows;
-  const Rsrc ra = make_rsrc(act, rows * ld_act * 2), rw = make_rsrc(wt, r * ld_wt * 2);
-  const int64_t arow_off = row * ld_act;
-  f32x4 acc[RT];
+  // lane holds rows 4g + e of column 16u + q
+  float* out = a.part + split * a.M * a.r;
 #pragma unroll
-  for (int t = 0; t < RT; ++t) acc[t] = f32x4{0, 0, 0, 0};
-  RowFrag<RT, U> cur, nxt;
-  rowsum_load<RT, U>(cur, ra, arow_off, row_ok, rw, ld_wt, r, beg, end, q, g);
-  for (int64_t kc = beg; kc < end; kc += 32 * U) {
-    const int64_t kn = kc + 32 * U;
-    rowsum_load<RT, U>(nxt, ra, arow_off, row_ok, rw, ld_wt, r, kn, end, q, g);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int t = 0; t < RT; ++t)
-        acc[t] = mfma16x16x32(__builtin_bit_cast(bf16x8, cur.a[u]), __builtin_bit_cast(bf16x8, cur.w[u][t]), acc[t]);
-    cur = nxt;
-  }
-  // lane holds rows 4g+e of column 16t+q
-  float* out = part + split * rows * r;
-#pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    const int64_t j = 16 * t + q;
+  for (int u = 0; u < 4; ++u) {
+    const int64_t j = j0 + 16 * u + q;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int64_t orow = tile * 16 + 4 * g + e;
-      if (orow < rows && j < r) out[orow * r + j] = acc[t][e];
+      const int64_t m = m0 + 16 * wave + 4 * g + e;
+      if (m < a.M && j < a.r) out[m * a.r + j] = acc[u][e];
     }
   }
 }
 
 // ------------------------------------------------------------ column sums
-// out[col][j] = sum_m act[m][col] * v[m][j] over this workgroup's token split;
-// 64 columns x r (<= 64) per workgroup, 32 tokens per LDS step.
-constexpr int kCsPitch = 40;  // 32 tokens + 8 pad (bf16)
+// part[split][c][j] = sum, over this split's tokens, of act[m][c] * v[m][j]
+// (both token-major).  A workgroup owns a 64-column x 64-j block; its tokens
+// are divided among the 4 waves, and each wave streams 16-token steps (16
+// activation rows of 64 columns and 16 rows of v, 128 bytes each) through its
+// own ring of kCsSlots LDS slots, so waves never wait for each other.  Within
+// a slot, 16-byte chunk c of row R sits at c ^ (((R >> 1) & 1) << 2), which
+// keeps the transposing reads below free of bank conflicts.  The MFMA
+// operands (8 consecutive tokens of one column per lane) come from
+// ds_read_b64_tr_b16: in each 16-lane group, lane L names the 4 values of
+// row L/4, columns 4(L%4) .. +3 of a 4 x 16 block, and receives column L of
+// that block.  The four waves' sums are added in LDS in wave order.
+constexpr int kCsSlots = 8;
+constexpr int kCsSlot = 2 * 16 * 128;
+constexpr int kCsLds = 4 * kCsSlots * kCsSlot;   // 128 KB
 
-__global__ __launch_bounds__(256) void colsum_kernel(const uint16_t* __restrict__ act, int64_t ld_act,
-                                                     const uint16_t* __restrict__ v, int64_t r, int64_t j0,
-                                                     int64_t M, int64_t cols, int64_t per_split, int64_t col_tiles,
-                                                     float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) uint16_t sAct[64 * kCsPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[64 * kCsPitch];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, q = lane & 15, g = lane >> 4;
-  const int64_t ctile = blockIdx.x % col_tiles, split = blockIdx.x / col_tiles;
-  const int64_t c0 = ctile * 64;
-  const int64_t beg = split * per_split, end = min(M, beg + per_split);
-  f32x4 acc[4];
+struct CsJob {
+  const uint16_t* act;   // M x cols, leading dimension ld
+  int64_t ld, cols;
+  const uint16_t* v;     // M x r
+  float* part;           // [splits][cols][r]
+  int64_t col_blocks, j_chunks, per_split, nblk;
+};
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int cs_off(int row, int chunk) { return row * 128 + ((chunk ^ (((row >> 1) & 1) << 2)) << 4); }
+
+__device__ __forceinline__ bf16x8 tr_read2(const char* p0, const char* p1) {
+  typedef __attribute__((address_space(3))) v4i16* lp;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(p0));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(p1));
+  const v4i16 both[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+__global__ __launch_bounds__(256) void colsum_kernel(CsJob j0, CsJob j1, int64_t M, int64_t r) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const bool second = blockIdx.x >= j0.nblk;
+  const CsJob& J = second ? j1 : j0;
+  const int64_t blk = second ? blockIdx.x - j0.nblk : blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int64_t cb = blk % J.col_blocks, rest = blk / J.col_blocks;
+  const int64_t c0 = cb * 64, jb = (rest % J.j_chunks) * 64, split = rest / J.j_chunks;
+  const int64_t mb = split * J.per_split, me = min(M, mb + J.per_split);
+  const int64_t share = (((me - mb) + 63) / 64) * 16;   // tokens per wave, a multiple of 16
+  const int64_t wb = mb + wave * share, we = min(me, wb + share);
+  const int64_t nsteps = we > wb ? (we - wb + 15) / 16 : 0;
+  char* ring = smem + wave * (kCsSlots * kCsSlot);
+  const Rsrc ra = make_rsrc(J.act, M * J.ld * 2), rv = make_rsrc(J.v, M * r * 2);
+  // copy i (0..1) of each operand fills slot rows 8i .. 8i+7: lane -> row
+  // 8i + lane/8, slot position lane & 7, global chunk (lane & 7) ^ swizzle
+  uint32_t av[2], vv[2];
+  int lim[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0, 0, 0, 0};
-  const int lr = t >> 3, lc = t & 7;  // loader: token row lr (0..31), 8-wide chunk lc
-  const Rsrc ra = make_rsrc(act, M * ld_act * 2), rv = make_rsrc(v, M * r * 2);
-  auto load = [&](int64_t m0, uint4& a4, uint4& v4) {
-    const int64_t m = m0 + lr;
-    const bool ok = m < end;
-    a4 = ld_b128(ra, (ok && c0 + 8 * lc < cols) ? static_cast<uint32_t>((m * ld_act + c0 + 8 * lc) * 2) : kMasked);
-    v4 = ld_b128(rv, (ok && j0 + 8 * lc < r) ? static_cast<uint32_t>((m * r + j0 + 8 * lc) * 2) : kMasked);
-  };
-  uint4 a4, v4;
-  load(beg, a4, v4);
-  for (int64_t m0 = beg; m0 < end; m0 += 32) {
-    const uint32_t aw[4] = {a4.x, a4.y, a4.z, a4.w}, vw[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sAct[(8 * lc + e) * kCsPitch + lr] = static_cast<uint16_t>(aw[e >> 1] >> (16 * (e & 1)));
-      sV[(8 * lc + e) * kCsPitch + lr] = static_cast<uint16_t>(vw[e >> 1] >> (16 * (e & 1)));
-    }
-    __syncthreads();
-    load(m0 + 32, a4, v4);
-    const bf16x8 af = *reinterpret_cast<const bf16x8*>(sAct + (16 * wave + q) * kCsPitch + 8 * g);
-#pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + (16 * jt + q) * kCsPitch + 8 * g);
-      acc[jt] = mfma16x16x32(af, vf, acc[jt]);
-    }
-    __syncthreads();
+  for (int i = 0; i < 2; ++i) {
+    const int R = 8 * i + (lane >> 3), c = (lane & 7) ^ (((R >> 1) & 1) << 2);
+    const int64_t m = wb + R;
+    av[i] = c0 + 8 * c < J.cols ? static_cast<uint32_t>((m * J.ld + c0 + 8 * c) * 2) : kMasked;
+    vv[i] = jb + 8 * c < r ? static_cast<uint32_t>((m * r + jb + 8 * c) * 2) : kMasked;
+    lim[i] = static_cast<int>(we - wb - R);   // row valid in step s iff 16 s < lim
   }
-  // wave covers columns 16*wave + 4g + e, j = 16*jt + q
-  float* out = part + split * cols * r;
+  auto copy = [&](int64_t s, int b) {
+    const uint32_t sa = static_cast<uint32_t>(s * 16 * J.ld * 2), sv = static_cast<uint32_t>(s * 16 * r * 2);
+    char* slot = ring + b * kCsSlot;
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    const int64_t j = j0 + 16 * jt + q;
+    for (int i = 0; i < 2; ++i) {
+      const bool ok = 16 * s < lim[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + 8 * i * 128), 16, ok ? av[i] : kMasked, sa, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(slot + 2048 + 8 * i * 128), 16, ok ? vv[i] : kMasked, sv,
+                                               0, 0);
+    }
+  };
+  // transposing-read addresses within a slot: group G = lane/16 reads rows
+  // 8(G>>1) + 4 half + L/4 and columns 16(G&1) + 4(L&3) of 32-column tile ti
+  const int G = lane >> 4, L = lane & 15;
+  int toff[2][2];   // [tile][half], byte offsets
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t col = c0 + 16 * wave + 4 * g + e;
-      if (col < cols && j < r) out[col * r + j] = acc[jt][e];
+  for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int R = 8 * (G >> 1) + 4 * h + (L >> 2);
+      const int col = 32 * ti + 16 * (G & 1) + 4 * (L & 3);
+      toff[ti][h] = cs_off(R, col >> 3) + 2 * (col & 7);
+    }
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  constexpr int S = kCsSlots;
+  for (int x = 0; x < S - 1; ++x) copy(x, x);
+  for (int64_t s = 0; s < nsteps; ++s) {
+    const int b = static_cast<int>(s % S);
+    copy(s + S - 1, static_cast<int>((s + S - 1) % S));   // slot of step s-1, read in full already
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 * (S - 1), 15));
+    const char* slot = ring + b * kCsSlot;
+    bf16x8 fa[2], fv[2];
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      fa[ti] = tr_read2(slot + toff[ti][0], slot + toff[ti][1]);
+      fv[ti] = tr_read2(slot + 2048 + toff[ti][0], slot + 2048 + toff[ti][1]);
+    }
+    // D[j][c]: each lane holds column c = 32 ci + lane%32 and j = 32 vj + 8jj + 4(lane/32) + e
+#pragma unroll
+    for (int vj = 0; vj < 2; ++vj)
+#pragma unroll
+      for (int ci = 0; ci < 2; ++ci) acc[vj][ci] = mfma32x32x16(fv[vj], fa[ci], acc[vj][ci]);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  // each wave's 64 x 64 block, [c][j] fp32, into the start of its own ring
+  {
+    float* mine = reinterpret_cast<float*>(ring);
+    const int h = lane >> 5, cl = lane & 31;
+#pragma unroll
+    for (int vj = 0; vj < 2; ++vj)
+#pragma unroll
+      for (int ci = 0; ci < 2; ++ci)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int c = 32 * ci + cl, j = 32 * vj + 8 * jj + 4 * h;
+          *reinterpret_cast<f32x4*>(mine + c * 64 + j) =
+              f32x4{acc[vj][ci][4 * jj], acc[vj][ci][4 * jj + 1], acc[vj][ci][4 * jj + 2], acc[vj][ci][4 * jj + 3]};
+        }
+  }
+  __syncthreads();
+  {
+    const int c = t >> 2, jq = 16 * (t & 3);
+    float* out = J.part + split * J.cols * r;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = jq + 4 * u;
+      f32x4 s4 = *reinterpret_cast<const f32x4*>(smem + (c * 64 + j) * 4);
+#pragma unroll
+      for (int w = 1; w < 4; ++w) s4 += *reinterpret_cast<const f32x4*>(smem + w * (kCsSlots * kCsSlot) + (c * 64 + j) * 4);
+      if (c0 + c < J.cols && jb + j < r) *reinterpret_cast<f32x4*>(out + (c0 + c) * r + jb + j) = s4;
     }
   }
 }
 
-// out = scale * sum_s part[s] (fixed order), optionally transposed from
-// [rows][cols] to [cols][rows]; fp32 and/or bf16 outputs.
-__global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ part, int splits, int64_t rows,
-                                                     int64_t cols, float scale, bool transpose,
-                                                     float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16) {
-  const int64_t count = rows * cols;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+// out = scale * sum_s part[s] in split order, optionally transposed from
+// [rows][cols] to [cols][rows]; fp32 and/or bf16 outputs.  Two jobs per launch.
+struct RdJob {
+  const float* part;
+  int64_t splits, rows, cols;
+  float scale;
+  int transpose;
+  float* out_f32;
+  uint16_t* out_bf16;
+  int64_t nblk;
+};
+
+__global__ __launch_bounds__(256) void reduce_kernel(RdJob j0, RdJob j1) {
+  const bool second = blockIdx.x >= j0.nblk;
+  const RdJob& J = second ? j1 : j0;
+  const int64_t blk = second ? blockIdx.x - j0.nblk : blockIdx.x;
+  const int64_t count = J.rows * J.cols;
+  for (int64_t i = blk * 256 + threadIdx.x; i < count; i += J.nblk * 256) {
     float s = 0.0f;
-    int k = 0;
-    for (; k + 8 <= splits; k += 8) {
+    int64_t k = 0;
+    for (; k + 8 <= J.splits; k += 8) {
       float v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = part[(k + u) * count + i];
+      for (int u = 0; u < 8; ++u) v[u] = J.part[(k + u) * count + i];
 #pragma unroll
       for (int u = 0; u < 8; ++u) s += v[u];
     }
-    for (; k < splits; ++k) s += part[k * count + i];
-    s *= scale;
-    const int64_t o = transpose ? (i % cols) * rows + i / cols : i;
-    if (out_f32) out_f32[o] = s;
-    if (out_bf16) out_bf16[o] = bf16_of(s);
+    for (; k < J.splits; ++k) s += J.part[k * count + i];
+    s *= J.scale;
+    const int64_t o = J.transpose ? (i % J.cols) * J.rows + i / J.cols : i;
+    if (J.out_f32) J.out_f32[o] = s;
+    if (J.out_bf16) J.out_bf16[o] = bf16_of(s);
   }
 }
 
@@ -432,14 +553,28 @@ void split_plan(int64_t tiles, int64_t red, int64_t target, int64_t quantum, int
   *splits = cdiv(red, *per);
 }
 
-hipError_t launch_reduce2(const float* part, int64_t splits, int64_t rows, int64_t cols, float scale, bool transpose,
-                          float* out_f32, uint16_t* out_bf16, hipStream_t stream) {
+RdJob rdjob(const float* part, int64_t splits, int64_t rows, int64_t cols, float scale, bool transpose, float* out_f32,
+            uint16_t* out_bf16) {
   int64_t blocks = cdiv(rows * cols, 256);
-  if (blocks > 4096) blocks = 4096;
+  if (blocks > 2048) blocks = 2048;
+  return RdJob{part, splits, rows, cols, scale, transpose ? 1 : 0, out_f32, out_bf16, blocks};
+}
+
+hipError_t launch_reduce(const RdJob& ja, const RdJob* jb, hipStream_t stream) {
+  RdJob second = jb != nullptr ? *jb : ja;
+  if (jb == nullptr) second.nblk = 0;
   Timer tm(QK_REDUCE, stream);
-  hipLaunchKernelGGL(reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, part,
-                     static_cast<int>(splits), rows, cols, scale, transpose, out_f32, out_bf16);
+  hipLaunchKernelGGL(reduce_kernel, dim3(static_cast<unsigned>(ja.nblk + second.nblk)), dim3(256), 0, stream, ja,
+                     second);
   tm.stop();
+  return hipGetLastError();
+}
+
+hipError_t launch_rowsum(const uint16_t* act, const uint16_t* wt, int64_t M, int64_t r, int64_t red, int64_t splits,
+                         int64_t per, float* part, hipStream_t stream) {
+  const RsArgs a{act, wt, M, r, red, per, cdiv(M, 64), cdiv(r, 64), part};
+  hipLaunchKernelGGL(rowsum_kernel, dim3(static_cast<unsigned>(a.row_blocks * a.j_chunks * splits)), dim3(256), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -447,15 +582,22 @@ hipError_t launch_reduce2(const float* part, int64_t splits, int64_t rows, int64
 
 // ------------------------------------------------------------ plans
 #ifndef QN_ROWSUM_WAVES
-#define QN_ROWSUM_WAVES 512   // target number of row-sum waves (row tiles x splits)
+#define QN_ROWSUM_WAVES 512   // target number of row-sum workgroups
 #endif
 SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N, int64_t r) {
   SkinnyPlan p{};
-  const int64_t row_tiles = cdiv(M, 16);
-  split_plan(row_tiles, K, QN_ROWSUM_WAVES, 128, &p.z_splits, &p.z_per);
-  split_plan(row_tiles, N, QN_ROWSUM_WAVES, 128, &p.dz_splits, &p.dz_per);
-  split_plan(cdiv(K, 64), M, 512, 32, &p.da_splits, &p.da_per);
-  split_plan(cdiv(N, 64), M, 512, 32, &p.db_splits, &p.db_per);
+  // row sums: 64-row blocks x 64-wide column chunks, split along the
+  // reduction into multiples of 256 until ~512 workgroups (2 per CU)
+  const int64_t rs_tiles = cdiv(M, 64) * cdiv(r, 64);
+  split_plan(rs_tiles, K, QN_ROWSUM_WAVES, 256, &p.z_splits, &p.z_per);
+  split_plan(rs_tiles, N, QN_ROWSUM_WAVES, 256, &p.dz_splits, &p.dz_per);
+  // column sums: 64-column blocks of dA and dB together, split along the
+  // tokens (multiples of 64) until ~256 workgroups (1 per CU)
+  const int64_t cs_tiles = (cdiv(K, 64) + cdiv(N, 64)) * cdiv(r, 64);
+  int64_t cs_splits, cs_per;
+  split_plan(cs_tiles, M, 256, 64, &cs_splits, &cs_per);
+  p.da_splits = p.db_splits = cs_splits;
+  p.da_per = p.db_per = cs_per;
   p.at_bytes = round_up(r * K * 2, 256);
   p.z_part = round_up(p.z_splits * M * r * 4, 256);
   p.dz_part = round_up(p.dz_splits * M * r * 4, 256);
@@ -482,16 +624,12 @@ hipError_t launch_lora_down(int64_t M, int64_t K, int64_t r, const uint16_t* X, 
   hipLaunchKernelGGL(transpose_bf16_kernel, dim3(static_cast<unsigned>(ja.nblk + jb.nblk)), dim3(256), 0, stream, ja,
                      jb);
   float* part = static_cast<float*>(part_ws);
-  const int64_t row_tiles = cdiv(M, 16);
   Timer tm(QK_LORA_DOWN, stream);
-  if (r <= 64)
-    hipLaunchKernelGGL((rowsum_kernel<4, 4>), dim3(static_cast<unsigned>(row_tiles * p.z_splits)), dim3(64), 0, stream, X,
-                       K, At, K, M, r, K, p.z_per, row_tiles, part);
-  else
-    hipLaunchKernelGGL((rowsum_kernel<16, 1>), dim3(static_cast<unsigned>(row_tiles * p.z_splits)), dim3(64), 0, stream,
-                       X, K, At, K, M, r, K, p.z_per, row_tiles, part);
+  hipError_t e = launch_rowsum(X, At, M, r, K, p.z_splits, p.z_per, part, stream);
   tm.stop();
-  return launch_reduce2(part, p.z_splits, M, r, 1.0f, false, nullptr, Z, stream);
+  if (e != hipSuccess) return e;
+  const RdJob jz = rdjob(part, p.z_splits, M, r, 1.0f, false, nullptr, Z);
+  return launch_reduce(jz, nullptr, stream);
 }
 
 hipError_t launch_gemv(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W, const uint16_t* Z,
@@ -513,46 +651,38 @@ hipError_t launch_gemv(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_
 hipError_t launch_dz(int64_t M, int64_t N, int64_t r, const uint16_t* G, const uint16_t* B, float c, uint16_t* dZ,
                      const SkinnyPlan& p, void* part_ws, hipStream_t stream) {
   float* part = static_cast<float*>(part_ws);
-  const int64_t row_tiles = cdiv(M, 16);
   Timer tm(QK_BWD_DZ, stream);
-  if (r <= 64)
-    hipLaunchKernelGGL((rowsum_kernel<4, 4>), dim3(static_cast<unsigned>(row_tiles * p.dz_splits)), dim3(64), 0, stream,
-                       G, N, B, N, M, r, N, p.dz_per, row_tiles, part);
-  else
-    hipLaunchKernelGGL((rowsum_kernel<16, 1>), dim3(static_cast<unsigned>(row_tiles * p.dz_splits)), dim3(64), 0, stream,
-                       G, N, B, N, M, r, N, p.dz_per, row_tiles, part);
+  hipError_t e = launch_rowsum(G, B, M, r, N, p.dz_splits, p.dz_per, part, stream);
   tm.stop();
-  return launch_reduce2(part, p.dz_splits, M, r, c, false, nullptr, dZ, stream);
+  if (e != hipSuccess) return e;
+  const RdJob jz = rdjob(part, p.dz_splits, M, r, c, false, nullptr, dZ);
+  return launch_reduce(jz, nullptr, stream);
 }
 
 // dA = Xᵀ dZ (K x r) and dB = c Zᵀ G (r x N).
 hipError_t launch_colsums(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const uint16_t* G,
                           const uint16_t* Z, const uint16_t* dZ, float c, float* dA, float* dB, const SkinnyPlan& p,
                           void* da_ws, void* db_ws, hipStream_t stream) {
-  hipError_t e;
-  {
-    const int64_t tiles = cdiv(K, 64);
-    Timer tm(QK_BWD_DA, stream);
-    for (int64_t j0 = 0; j0 < r; j0 += 64)
-      hipLaunchKernelGGL(colsum_kernel, dim3(static_cast<unsigned>(tiles * p.da_splits)), dim3(256), 0, stream, X, K,
-                         dZ, r, j0, M, K, p.da_per, tiles, static_cast<float*>(da_ws));
-    tm.stop();
-    if ((e = launch_reduce2(static_cast<float*>(da_ws), p.da_splits, K, r, 1.0f, false, dA, nullptr, stream)) !=
-        hipSuccess)
-      return e;
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&colsum_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kCsLds);
+    if (e != hipSuccess) return e;
+    configured = true;
   }
-  {
-    const int64_t tiles = cdiv(N, 64);
-    Timer tm(QK_BWD_DB, stream);
-    for (int64_t j0 = 0; j0 < r; j0 += 64)
-      hipLaunchKernelGGL(colsum_kernel, dim3(static_cast<unsigned>(tiles * p.db_splits)), dim3(256), 0, stream, G, N,
-                         Z, r, j0, M, N, p.db_per, tiles, static_cast<float*>(db_ws));
-    tm.stop();
-    if ((e = launch_reduce2(static_cast<float*>(db_ws), p.db_splits, N, r, c, true, dB, nullptr, stream)) !=
-        hipSuccess)
-      return e;
-  }
-  return hipGetLastError();
+  const int64_t jc = cdiv(r, 64);
+  CsJob ja{X, K, K, dZ, static_cast<float*>(da_ws), cdiv(K, 64), jc, p.da_per, 0};
+  CsJob jb{G, N, N, Z, static_cast<float*>(db_ws), cdiv(N, 64), jc, p.db_per, 0};
+  ja.nblk = ja.col_blocks * jc * p.da_splits;
+  jb.nblk = jb.col_blocks * jc * p.db_splits;
+  Timer tm(QK_BWD_COLSUM, stream);
+  hipLaunchKernelGGL(colsum_kernel, dim3(static_cast<unsigned>(ja.nblk + jb.nblk)), dim3(256), kCsLds, stream, ja, jb, M, r);
+  tm.stop();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const RdJob ra = rdjob(static_cast<float*>(da_ws), p.da_splits, K, r, 1.0f, false, dA, nullptr);
+  const RdJob rb = rdjob(static_cast<float*>(db_ws), p.db_splits, N, r, c, true, dB, nullptr);
+  return launch_reduce(ra, &rb, stream);
 }
 
 }  // namespace qn

@@ -46,14 +46,18 @@ def test_nf4_sizes_rejects_empty():
 
 
 @pytest.mark.parametrize("shape", [(0, 64, 64, 8), (4, 64, 63, 8), (4, 12, 64, 8), (4, 64, 64, 4),
-                                   (4, 64, 64, 264), (4, 0, 64, 8)])
+                                   (4, 64, 64, 264), (4, 0, 64, 8),
+                                   (1 << 20, 1 << 9, 64, 8),       # X of 2^29 elements (1 GiB)
+                                   (4, 1 << 15, 1 << 14, 8),       # weight of 2^29 elements
+                                   (1 << 16, 64, 1 << 13, 8)])     # Y of 2^29 elements
 def test_layer_shapes_rejected(shape):
     with pytest.raises(qn.NF4Error):
         qn.qlora_workspace_bytes(*shape)
 
 
 def test_layer_workspace_sizes_are_positive():
-    for shape in [(16, 256, 256, 8), (4096, 4096, 4096, 64), (1, 8192, 22016, 64), (2048, 22016, 8192, 64)]:
+    for shape in [(16, 256, 256, 8), (4096, 4096, 4096, 64), (1, 8192, 22016, 64), (2048, 22016, 8192, 64),
+                  ((1 << 20) - 8, 256, 64, 8)]:
         f, b = qn.qlora_workspace_bytes(*shape)
         assert f >= 0 and b > 0 and f % 256 == 0 and b % 256 == 0
 
