@@ -82,8 +82,12 @@ TJob tjob(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols, float 
 // the LDS destination three stages ahead; one barrier per stage.  The weight
 // rows are shared by the four waves, so each weight slice is fetched once per
 // 64 activation rows.
-constexpr int kRsSlots = 4;
+#ifndef QN_RS_SLOTS
+#define QN_RS_SLOTS 4
+#endif
+constexpr int kRsSlots = QN_RS_SLOTS;
 constexpr int kRsSlot = 2 * 64 * 128;
+constexpr int kRsLds = kRsSlots * kRsSlot;
 
 struct RsArgs {
   const uint16_t* act;
@@ -95,7 +99,7 @@ struct RsArgs {
 __device__ __forceinline__ int rs_off(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
 
 __global__ __launch_bounds__(256) void rowsum_kernel(RsArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[kRsSlots * kRsSlot];
+  extern __shared__ __attribute__((aligned(16))) char smem[];
   const int t = threadIdx.x, lane = t & 63, q = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t rb = blockIdx.x % a.row_blocks, rest = blockIdx.x / a.row_blocks;
@@ -132,16 +136,20 @@ __global__ __launch_bounds__(256) void rowsum_kernel(RsArgs a) {
   f32x4 acc[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] = f32x4{0, 0, 0, 0};
-  // stages past the end read zeros into slots that are never read
-  copy(0, 0);
-  copy(1, 1);
-  copy(2, 2);
+  // Stage x goes to slot x % S, S - 1 stages ahead (4 copies per wave per
+  // stage); no copies are issued past the last stage.
+  constexpr int S = kRsSlots;
+  for (int x = 0; x < S - 1; ++x)
+    if (x < nst) copy(x, x);
+  int b = 0;
   for (int64_t s = 0; s < nst; ++s) {
-    const int b = static_cast<int>(s & 3);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(8, 0));   // own copies of stage s landed
-    __builtin_amdgcn_s_barrier();                    // everyone's; slot (s-1)&3 released
-    copy(s + 3, (b + 3) & 3);
+    // own copies of stage s landed (later stages may still be in flight)
+    if (s + S - 2 < nst) __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 * (S - 2), 0));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_barrier();   // everyone's; slot of stage s-1 released
+    if (s + S - 1 < nst) copy(s + S - 1, b == 0 ? S - 1 : b - 1);
     const char* slot = smem + b * kRsSlot;
+    b = b == S - 1 ? 0 : b + 1;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const bf16x8 af = *reinterpret_cast<const bf16x8*>(slot + rs_off(16 * wave + q, 4 * st + g));
@@ -177,7 +185,13 @@ __global__ __launch_bounds__(256) void rowsum_kernel(RsArgs a) {
 // ds_read_b64_tr_b16: in each 16-lane group, lane L names the 4 values of
 // row L/4, columns 4(L%4) .. +3 of a 4 x 16 block, and receives column L of
 // that block.  The four waves' sums are added in LDS in wave order.
-constexpr int kCsSlots = 8;
+#ifndef QN_CS_SLOTS
+#define QN_CS_SLOTS 8
+#endif
+#ifndef QN_CS_WGS
+#define QN_CS_WGS 256
+#endif
+constexpr int kCsSlots = QN_CS_SLOTS;
 constexpr int kCsSlot = 2 * 16 * 128;
 constexpr int kCsLds = 4 * kCsSlots * kCsSlot;   // 128 KB
 
@@ -259,11 +273,16 @@ __global__ __launch_bounds__(256) void colsum_kernel(CsJob j0, CsJob j1, int64_t
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   constexpr int S = kCsSlots;
-  for (int x = 0; x < S - 1; ++x) copy(x, x);
+  for (int x = 0; x < S - 1; ++x)
+    if (x < nsteps) copy(x, x);
   for (int64_t s = 0; s < nsteps; ++s) {
     const int b = static_cast<int>(s % S);
-    copy(s + S - 1, static_cast<int>((s + S - 1) % S));   // slot of step s-1, read in full already
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 * (S - 1), 15));
+    if (s + S - 1 < nsteps) {
+      copy(s + S - 1, static_cast<int>((s + S - 1) % S));   // slot of step s-1, read in full already
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 * (S - 1), 15));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
+    }
     const char* slot = ring + b * kCsSlot;
     bf16x8 fa[2], fv[2];
 #pragma unroll
@@ -346,7 +365,34 @@ __global__ __launch_bounds__(256) void reduce_kernel(RdJob j0, RdJob j1) {
 // ------------------------------------------------------------ small-M GEMV
 constexpr int kGvWaves = 4;
 constexpr int kGvCols = 256;    // columns per workgroup slab (16 per lane)
-constexpr int kGvTab = 32 * 4 * 16;  // bf16 entries of one wave's tables for one 32-row step
+// One wave's block tables for one 32-row step: row r (4 tables of 16 bf16,
+// 128 bytes) at byte r * 128 + 128 * (r / 8), so that the four rows 8g + c
+// (g = 0..3) that one lookup instruction touches fall on both halves of the
+// 64 LDS banks.
+constexpr int kGvTabBytes = 32 * 128 + 4 * 128;
+#ifndef QN_GV_DEPTH
+#define QN_GV_DEPTH 3
+#endif
+constexpr int kGvDepth = QN_GV_DEPTH;   // 32-row steps of code loads in flight per wave
+__device__ __forceinline__ int gv_row(int r) { return r * 128 + 128 * (r >> 3); }
+
+// base + byte b of w, one VALU instruction (SDWA byte select on the second operand)
+__device__ __forceinline__ uint32_t add_byte(uint32_t base, uint32_t w, int b) {
+  uint32_t r;
+  switch (b) {
+    case 0: asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(base), "v"(w)); break;
+    case 1: asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(base), "v"(w)); break;
+    case 2: asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(base), "v"(w)); break;
+    default: asm("v_add_u32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(base), "v"(w)); break;
+  }
+  return r;
+}
+
+// 16-bit LDS load from a byte address
+__device__ __forceinline__ uint32_t lds_u16(uint32_t addr) {
+  typedef __attribute__((address_space(3))) const uint16_t* lp;
+  return *reinterpret_cast<lp>(static_cast<uintptr_t>(addr));
+}
 
 __device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
   return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
@@ -381,83 +427,117 @@ struct GvStep {
 // step to its LDS ring, then decodes the current step by table lookups, so no
 // per-weight multiply or conversion is needed; column t of the lane feeds the
 // MFMA of tile t.  part[split][m][n] = sum of the 4 waves (fixed order).
-__global__ __launch_bounds__(256) void gemv_kernel(const uint16_t* __restrict__ X, int64_t M, NF4View W, int64_t K,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemv_kernel(const uint16_t* __restrict__ X, int64_t M, NF4View W, int64_t K,
                                                    int64_t N, int64_t rpw, int64_t slabs, float* __restrict__ part) {
   __shared__ float q2t[256];
-  __shared__ __attribute__((aligned(16))) uint16_t tabs[kGvWaves * 2 * kGvTab];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, q = lane & 15, g = lane >> 4;
+  __shared__ __attribute__((aligned(16))) char tabs[kGvWaves * 2 * kGvTabBytes];
+  const int t = threadIdx.x, lane = t & 63, q = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   q2t[t] = q2_value(t - 128);
   const int64_t slab = blockIdx.x % slabs, split = blockIdx.x / slabs;
   const int64_t n0 = slab * kGvCols;
   const int64_t kw0 = (split * kGvWaves + wave) * rpw;
+  const int64_t kend = min(K, kw0 + rpw);   // this wave's rows; nothing past them is fetched
+  const int64_t rows = kend > kw0 ? kend - kw0 : 0;
   const int64_t P = K * N;
-  const Rsrc rc = make_rsrc(W.codes, (P + 1) / 2);
-  const Rsrc rq = make_rsrc(W.qabsmax, (P + 63) / 64);
+  // descriptors over this wave's rows only: rows past kend read zeros, and the
+  // step advance is a scalar offset (N is a multiple of 64)
+  const int64_t kb0 = kend > kw0 ? kw0 : 0;
+  const Rsrc rc = make_rsrc(W.codes + kb0 * N / 2, rows * N / 2);
+  const Rsrc rq = make_rsrc(W.qabsmax + kb0 * N / 64, rows * N / 64);
   const Rsrc rs = make_rsrc(W.absmax2, ((P + 16383) / 16384) * 4);
   const Rsrc rx = make_rsrc(X, M * K * 2);
   const float off = W.offset[0];
   const int64_t n = n0 + 16 * q;
   const bool n_ok = n < N;
   const int blk = q >> 2;
-  uint16_t* my_tabs = tabs + wave * 2 * kGvTab;
+  char* my_tabs = tabs + wave * 2 * kGvTabBytes;
+  uint32_t voff_w[8], voff_q[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) voff_w[i] = n_ok ? static_cast<uint32_t>(((8 * g + i) * N + n) >> 1) : kMasked;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int64_t nb = n0 + 64 * (2 * (lane & 1) + u);
+    voff_q[u] = nb < N ? static_cast<uint32_t>(((lane >> 1) * N + nb) >> 6) : kMasked;
+  }
+  const uint32_t voff_x = q < M ? static_cast<uint32_t>((q * K + kw0 + 8 * g) * 2) : kMasked;
 
   auto load = [&](GvStep& S, int64_t kk) {
-    const int64_t kb = kw0 + kk + 8 * g;
+    const uint32_t sw = static_cast<uint32_t>((kk * N) >> 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t k = kb + i;
-      S.w[i] = ld_b64(rc, (k < K && n_ok) ? static_cast<uint32_t>((k * N + n) >> 1) : kMasked);
-    }
-    S.x = ld_b128(rx, (q < M && kb < K) ? static_cast<uint32_t>((q * K + kb) * 2) : kMasked);
-    const int64_t kt = kw0 + kk + (lane >> 1);
+    for (int i = 0; i < 8; ++i)
+      S.w[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, voff_w[i], sw, 0));
+    // zero activations past this wave's rows (their codes read as 0, a finite weight)
+    S.x = ld_b128(rx, (kw0 + kk + 8 * g < kend) ? voff_x + static_cast<uint32_t>(kk * 2) : kMasked);
+    const uint32_t sq = static_cast<uint32_t>((kk * N) >> 6);
+    const uint32_t kt = static_cast<uint32_t>(kw0 + kk + (lane >> 1));
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int64_t nb = n0 + 64 * (2 * (lane & 1) + u);
-      const bool ok = kt < K && nb < N;
-      const int64_t e = kt * N + nb;
-      S.q[u] = ld_i8(rq, ok ? static_cast<uint32_t>(e >> 6) : kMasked);
-      S.s2[u] = ld_f32(rs, ok ? static_cast<uint32_t>((e >> 14) * 4) : kMasked);
+      S.q[u] = static_cast<int>(static_cast<int8_t>(__builtin_amdgcn_raw_buffer_load_b8(rq, voff_q[u], sq, 0)));
+      const uint32_t nb = static_cast<uint32_t>(n0 + 64 * (2 * (lane & 1) + u));
+      const bool ok = kt < kend && nb < N;
+      S.s2[u] = ld_f32(rs, ok ? ((kt * static_cast<uint32_t>(N) + nb) >> 14) * 4 : kMasked);
     }
   };
   auto build = [&](const GvStep& S, int buf) {
-    uint16_t* tb = my_tabs + buf * kGvTab + ((lane >> 1) * 4 + 2 * (lane & 1)) * 16;
+    char* tb = my_tabs + buf * kGvTabBytes + gv_row(lane >> 1) + 64 * (lane & 1);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      write_block_table(tb + 16 * u, __fadd_rn(__fmul_rn(q2t[S.q[u] + 128], S.s2[u]), off));
+      write_block_table(reinterpret_cast<uint16_t*>(tb + 32 * u), __fadd_rn(__fmul_rn(q2t[S.q[u] + 128], S.s2[u]), off));
   };
 
   f32x4 acc[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = f32x4{0, 0, 0, 0};
   __syncthreads();  // q2t
-  GvStep cur, nxt;
-  load(cur, 0);
-  build(cur, 0);
-  __syncthreads();
-  int buf = 0;
-  for (int64_t kk = 0; kk < rpw; kk += 32) {
-    const bool more = kk + 32 < rpw;
-    if (more) load(nxt, kk + 32);
-    const uint16_t* tb = my_tabs + buf * kGvTab + (8 * g * 4 + blk) * 16;  // table of row 8g, this lane's block
-    const bf16x8 xf = __builtin_bit_cast(bf16x8, cur.x);
+  // kGvDepth steps of loads in flight per wave: set u holds step D j + u and
+  // is refilled with step D (j+1) + u as soon as it has been decoded.  Each
+  // wave's tables live in its own LDS ring, so no workgroup barrier is needed
+  // (LDS operations of one wave complete in order).
+  GvStep R[kGvDepth];
 #pragma unroll
-    for (int tile = 0; tile < 16; ++tile) {
-      uint32_t fw[4];
+  for (int u = 0; u < kGvDepth; ++u) load(R[u], 32 * u);
+  build(R[0], 0);
+  for (int64_t kk = 0; kk < rpw; kk += 32 * kGvDepth) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t w0 = (tile < 8) ? cur.w[2 * p].x : cur.w[2 * p].y;
-        const uint32_t w1 = (tile < 8) ? cur.w[2 * p + 1].x : cur.w[2 * p + 1].y;
-        const uint32_t lo = tb[(2 * p) * 64 + nib(w0, tile & 7)];
-        const uint32_t hi = tb[(2 * p + 1) * 64 + nib(w1, tile & 7)];
-        fw[p] = lo | (hi << 16);
+    for (int u = 0; u < kGvDepth; ++u) {
+      const int64_t ks = kk + 32 * u;
+      if (ks >= rpw) break;
+      const int buf = static_cast<int>((ks >> 5) & 1);   // tables alternate per 32-row step
+      // table of row 8g + i (i < 8) for this lane's block: tb + 128 i
+      const char* tb = my_tabs + buf * kGvTabBytes + gv_row(8 * g) + 32 * blk;
+      // doubled codes: byte b of ev = 2 * code of column 2b, of od = 2 * code of
+      // column 2b + 1 (x word: columns 0..7, y word: columns 8..15)
+      uint32_t ev[8][2], od[8][2];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ev[i][0] = (R[u].w[i].x >> 3) & 0x1e1e1e1eu;
+        od[i][0] = (R[u].w[i].x << 1) & 0x1e1e1e1eu;
+        ev[i][1] = (R[u].w[i].y >> 3) & 0x1e1e1e1eu;
+        od[i][1] = (R[u].w[i].y << 1) & 0x1e1e1e1eu;
       }
-      acc[tile] = mfma16x16x32(xf, __builtin_bit_cast(bf16x8, make_uint4(fw[0], fw[1], fw[2], fw[3])), acc[tile]);
+      const uint32_t tbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tb));
+      const bf16x8 xf = __builtin_bit_cast(bf16x8, R[u].x);
+#pragma unroll
+      for (int tile = 0; tile < 16; ++tile) {
+        const int h = tile >> 3, col = tile & 7;
+        uint32_t fw[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t a0 = add_byte(tbase, (col & 1) ? od[2 * p][h] : ev[2 * p][h], col >> 1);
+          const uint32_t a1 = add_byte(tbase, (col & 1) ? od[2 * p + 1][h] : ev[2 * p + 1][h], col >> 1);
+          const uint32_t lo = lds_u16(a0 + 2 * p * 128);
+          const uint32_t hi = lds_u16(a1 + (2 * p + 1) * 128);
+          fw[p] = perm(hi, lo, 0x05040100u);
+        }
+        acc[tile] = mfma16x16x32(xf, __builtin_bit_cast(bf16x8, make_uint4(fw[0], fw[1], fw[2], fw[3])), acc[tile]);
+      }
+      if (ks + 32 < rpw) build(R[(u + 1) % kGvDepth], buf ^ 1);
+      load(R[u], ks + 32 * kGvDepth);   // past the k-range: masked, reads zeros
     }
-    if (more) build(nxt, buf ^ 1);
-    __syncthreads();
-    cur = nxt;
-    buf ^= 1;
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   // lane holds Y[m = 4g+e][n + tile]; fixed-order sum: (w0 + w2) + (w1 + w3)
   float* red = reinterpret_cast<float*>(tabs);   // 2 waves x 64 floats x 64 lanes = 32 KB
   if (wave >= 2) {
@@ -572,8 +652,15 @@ hipError_t launch_reduce(const RdJob& ja, const RdJob* jb, hipStream_t stream) {
 
 hipError_t launch_rowsum(const uint16_t* act, const uint16_t* wt, int64_t M, int64_t r, int64_t red, int64_t splits,
                          int64_t per, float* part, hipStream_t stream) {
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rowsum_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kRsLds);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
   const RsArgs a{act, wt, M, r, red, per, cdiv(M, 64), cdiv(r, 64), part};
-  hipLaunchKernelGGL(rowsum_kernel, dim3(static_cast<unsigned>(a.row_blocks * a.j_chunks * splits)), dim3(256), 0,
+  hipLaunchKernelGGL(rowsum_kernel, dim3(static_cast<unsigned>(a.row_blocks * a.j_chunks * splits)), dim3(256), kRsLds,
                      stream, a);
   return hipGetLastError();
 }
@@ -595,7 +682,7 @@ SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N, int64_t r) {
   // tokens (multiples of 64) until ~256 workgroups (1 per CU)
   const int64_t cs_tiles = (cdiv(K, 64) + cdiv(N, 64)) * cdiv(r, 64);
   int64_t cs_splits, cs_per;
-  split_plan(cs_tiles, M, 256, 64, &cs_splits, &cs_per);
+  split_plan(cs_tiles, M, QN_CS_WGS, 64, &cs_splits, &cs_per);
   p.da_splits = p.db_splits = cs_splits;
   p.da_per = p.db_per = cs_per;
   p.at_bytes = round_up(r * K * 2, 256);
