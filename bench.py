@@ -189,9 +189,15 @@ def main():
     print(json.dumps(line))
 
 
-def _time_kernel(qn, torch, name, fn, reps):
+def _time_kernel(qn, torch, name, fn, reps, flush=None):
+    """Average duration of kernel `name` over `reps` calls of fn, timed by the
+    library's HIP events on the launch stream; with `flush`, the 256 MB
+    Infinity Cache is overwritten before every call (outside the timed
+    kernel)."""
     qn.qlora_timer_enable(name, True)
     for i in range(reps):
+        if flush is not None:
+            flush.add_(1)
         fn(i)
     torch.cuda.synchronize()
     ms, n = qn.qlora_timer_read(name)
@@ -199,29 +205,41 @@ def _time_kernel(qn, torch, name, fn, reps):
     return ms / max(n, 1)
 
 
+def _time_calls(torch, fn, reps, flush):
+    """Average wall time of one call, each call bracketed by its own events
+    after a cache flush."""
+    total = 0.0
+    for i in range(reps):
+        flush.add_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        total += e0.elapsed_time(e1)
+    return total / reps
+
+
 def bench_components(torch, qn, si, dev, sets, outs, qws, status):
+    """The memory-bound paths, each call preceded by a write of a 512 MB buffer
+    so that no input or output is served from the Infinity Cache."""
     res = {}
+    flush = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
     P = sets[0]["W"].numel()
     n1, n2 = qn.nf4_sizes(P)["n1"], qn.nf4_sizes(P)["n2"]
     # quantize: fp32 read, codes + int8 codes + fp32 scales written
     qbytes = 4 * P + (P + 1) // 2 + n1 + 4 * n2 + 4
-    ms = _time_kernel(qn, torch, "quant_pass1",
-                      lambda i: qn.nf4_quantize(sets[i % 3]["W"], outs[i % 3]["state"], qws, status), 10)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record()
-    for i in range(10):
-        qn.nf4_quantize(sets[i % 3]["W"], outs[i % 3]["state"], qws, status)
-    ev[1].record()
-    torch.cuda.synchronize()
-    full_ms = ev[0].elapsed_time(ev[1]) / 10
+    qfn = lambda i: qn.nf4_quantize(sets[i % 3]["W"], outs[i % 3]["state"], qws, status)
+    ms = _time_kernel(qn, torch, "quant_pass1", qfn, 10, flush)
+    full_ms = _time_calls(torch, qfn, 10, flush)
     res["quantize_attn7b"] = {"bytes": qbytes, "pass1_ms": round(ms, 4), "call_ms": round(full_ms, 4),
                               "GBps_call": round(qbytes / (full_ms * 1e-3) / 1e9, 1),
                               "frac_hbm_call": round(qbytes / (full_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     # bf16 dequantize
     dbytes = (P + 1) // 2 + n1 + 4 * n2 + 4 + 2 * P
-    outs_bf = [torch.empty(P, dtype=torch.bfloat16, device=dev) for _ in range(8)]
+    outs_bf = [torch.empty(P, dtype=torch.bfloat16, device=dev) for _ in range(3)]
     ms = _time_kernel(qn, torch, "dequant",
-                      lambda i: qn.nf4_dequantize(outs[i % 3]["state"], "bf16", out=outs_bf[i % 8]), 16)
+                      lambda i: qn.nf4_dequantize(outs[i % 3]["state"], "bf16", out=outs_bf[i % 3]), 16, flush)
     res["dequant_bf16_attn7b"] = {"bytes": dbytes, "ms": round(ms, 4),
                                   "GBps": round(dbytes / (ms * 1e-3) / 1e9, 1),
                                   "frac_hbm": round(dbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -231,7 +249,7 @@ def bench_components(torch, qn, si, dev, sets, outs, qws, status):
     K, N, r, c = d["K"], d["N"], d["r"], d["c"]
     Pg = K * N
     states = []
-    for i in range(3):
+    for i in range(2):
         W = torch.from_numpy(d["W"]).to(dev).reshape(-1)
         st, _ = qn.nf4_quantize(W)
         states.append(st)
@@ -246,27 +264,23 @@ def bench_components(torch, qn, si, dev, sets, outs, qws, status):
         Z = torch.empty(M, r, dtype=torch.bfloat16, device=dev)
         ws = torch.empty(max(qn.qlora_workspace_bytes(M, K, N, r)[0], 256), dtype=torch.uint8, device=dev)
         gbytes = Pg // 2 + sg["n1"] + 4 * sg["n2"] + 4 + 2 * M * K + 2 * K * r + 2 * r * N + 2 * M * N + 2 * M * r
-        fn = lambda i: qn.qlora_linear_fwd(X, states[i % 3], A, B, c, K, N, Y, Z, ws)
-        for i in range(3):
+        fn = lambda i: qn.qlora_linear_fwd(X, states[i % 2], A, B, c, K, N, Y, Z, ws)
+        for i in range(2):
             fn(i)
-        ev[0].record()
-        for i in range(12):
-            fn(i)
-        ev[1].record()
-        torch.cuda.synchronize()
-        call_ms = ev[0].elapsed_time(ev[1]) / 12
-        kms = _time_kernel(qn, torch, "fwd_gemv", fn, 12)
+        call_ms = _time_calls(torch, fn, 12, flush)
+        kms = _time_kernel(qn, torch, "fwd_gemv", fn, 12, flush)
         gemv[f"M{M}"] = {"bytes": gbytes, "call_ms": round(call_ms, 4), "gemv_kernel_ms": round(kms, 4),
                          "GBps_call": round(gbytes / (call_ms * 1e-3) / 1e9, 1),
-                         "frac_hbm_call": round(gbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                         "frac_hbm_call": round(gbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "GBps_kernel": round(gbytes / (kms * 1e-3) / 1e9, 1)}
     res["gemv_decode65b"] = gemv
     return res
 
 
-def cpu_baseline(wl):
-    """The oracle as it stands, on the host cores: quantize of the full weight
-    plus forward+backward on a 256-row sample of the tokens, scaled to the full
-    step (the oracle's layer cost is linear in M)."""
+def cpu_baseline(wl, reps=3):
+    """The oracle as it stands, on the host cores, on the full workload:
+    quantize of the 4096 x 4096 weight, then forward and backward at all 4096
+    token rows (fp64 numpy); median of `reps` runs."""
     import synth_inputs as si
     from oracle import nf4_oracle as o
     try:
@@ -276,22 +290,19 @@ def cpu_baseline(wl):
         threads = os.cpu_count() or 1
     d = si.layer_inputs(wl, matrix=0)
     M, K, N, r, c = d["M"], d["K"], d["N"], d["r"], d["c"]
-    Ms = 256
-    t0 = time.perf_counter()
-    st = o.quantize(d["W"].ravel())
-    t_q = time.perf_counter() - t0
-    W_hat = o.dequantize(st, "bf16").reshape(K, N)
-    t1 = time.perf_counter()
-    X, A, B, G = d["X"][:Ms], d["A"], d["B"], d["G"][:Ms]
-    o.layer_forward(X, W_hat, A, B, c)
-    o.layer_backward(G, X, W_hat, A, B, c)
-    t_l = time.perf_counter() - t1
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        st = o.quantize(d["W"].ravel())
+        W_hat = o.dequantize(st, "bf16").reshape(K, N)
+        o.layer_forward(d["X"], W_hat, d["A"], d["B"], c)
+        o.layer_backward(d["G"], d["X"], W_hat, d["A"], d["B"], c)
+        times.append(time.perf_counter() - t0)
+    step_s = sorted(times)[len(times) // 2]
     fwd_f, bwd_f = layer_flops(M, K, N, r)
-    step_s = t_q + t_l * (M / Ms)
     return {"value": round((fwd_f + bwd_f) / step_s / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"full-weight quantize ({t_q:.2f} s) + fwd/bwd on {Ms} of {M} token rows "
-                      f"({t_l:.2f} s), layer time scaled by {M // Ms}; est. step {step_s:.2f} s"}
+            "sample": f"full workload (quantize + fwd + bwd, M={M}), median of {reps} runs: {step_s:.2f} s per step"}
 
 
 if __name__ == "__main__":

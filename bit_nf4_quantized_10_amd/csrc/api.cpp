@@ -59,14 +59,20 @@ hipEvent_t take_event(TimerSlot& s) {
 
 namespace qn {
 
-Timer::Timer(int kernel_id, hipStream_t stream) : id_(kernel_id), stream_(stream), stop_event_(nullptr) {
+Timer::Timer(int kernel_id, hipStream_t stream, bool packet)
+    : id_(kernel_id), stream_(stream), stop_event_(nullptr), start_event_(nullptr), packet_stop_(nullptr) {
   std::lock_guard<std::mutex> lk(g_timer_mu);
   TimerSlot& s = g_timers[id_];
   if (!s.enabled) return;
   hipEvent_t a = take_event(s), b = take_event(s);
   if (a == nullptr || b == nullptr) return;
-  (void)hipEventRecord(a, stream_);
   s.pending.emplace_back(a, b);
+  if (packet) {
+    start_event_ = a;
+    packet_stop_ = b;
+    return;
+  }
+  (void)hipEventRecord(a, stream_);
   stop_event_ = b;
 }
 

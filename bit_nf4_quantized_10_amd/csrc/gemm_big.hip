@@ -37,6 +37,8 @@
 // Every global load is a raw buffer load, so masked lanes need no branches.
 // The MFMA is issued as D = Ŵ-fragment x activation-fragment, so each lane
 // holds 4 consecutive output columns of one output row.
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -611,7 +613,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 }
 
 template <bool kForward, bool kKTail>
-hipError_t launch_big_t(const BigArgs& a, hipStream_t stream) {
+hipError_t launch_big_t(const BigArgs& a, hipStream_t stream, const Timer& tm) {
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_big_kernel<kForward, kKTail>),
@@ -621,18 +623,19 @@ hipError_t launch_big_t(const BigArgs& a, hipStream_t stream) {
   }
   const int64_t cols = kForward ? a.N : a.K;
   dim3 grid(static_cast<unsigned>((cols + kBN - 1) / kBN), static_cast<unsigned>((a.M + kBM - 1) / kBM), 1);
-  hipLaunchKernelGGL((qlora_big_kernel<kForward, kKTail>), grid, dim3(kThreads), kLdsBytes, stream, a);
+  hipExtLaunchKernelGGL((qlora_big_kernel<kForward, kKTail>), grid, dim3(kThreads), kLdsBytes, stream, tm.start(),
+                        tm.end(), 0, a);
   return hipGetLastError();
 }
 
 template <bool kForward>
-hipError_t launch_big(const BigArgs& a, hipStream_t stream) {
+hipError_t launch_big(const BigArgs& a, hipStream_t stream, const Timer& tm) {
   const int64_t red = kForward ? a.K : a.N;
-  return (red % kBK) ? launch_big_t<kForward, true>(a, stream) : launch_big_t<kForward, false>(a, stream);
+  return (red % kBK) ? launch_big_t<kForward, true>(a, stream, tm) : launch_big_t<kForward, false>(a, stream, tm);
 }
 
 template <bool kForward, bool kKTail>
-hipError_t launch_dense_t(const BigArgs& a, hipStream_t stream) {
+hipError_t launch_dense_t(const BigArgs& a, hipStream_t stream, const Timer& tm) {
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_dense_kernel<kForward, kKTail>),
@@ -642,14 +645,15 @@ hipError_t launch_dense_t(const BigArgs& a, hipStream_t stream) {
   }
   const int64_t cols = kForward ? a.N : a.K;
   dim3 grid(static_cast<unsigned>((cols + kBN - 1) / kBN), static_cast<unsigned>((a.M + kBM - 1) / kBM), 1);
-  hipLaunchKernelGGL((qlora_dense_kernel<kForward, kKTail>), grid, dim3(kThreads), kRingLds, stream, a);
+  hipExtLaunchKernelGGL((qlora_dense_kernel<kForward, kKTail>), grid, dim3(kThreads), kRingLds, stream, tm.start(),
+                        tm.end(), 0, a);
   return hipGetLastError();
 }
 
 template <bool kForward>
-hipError_t launch_dense(const BigArgs& a, hipStream_t stream) {
+hipError_t launch_dense(const BigArgs& a, hipStream_t stream, const Timer& tm) {
   const int64_t red = kForward ? a.K : a.N;
-  return (red % kBK) ? launch_dense_t<kForward, true>(a, stream) : launch_dense_t<kForward, false>(a, stream);
+  return (red % kRK) ? launch_dense_t<kForward, true>(a, stream, tm) : launch_dense_t<kForward, false>(a, stream, tm);
 }
 
 }  // namespace
@@ -657,37 +661,29 @@ hipError_t launch_dense(const BigArgs& a, hipStream_t stream) {
 hipError_t launch_fwd_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const uint16_t* WhatT,
                             const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream) {
   BigArgs a{X, K, NF4View{}, Z, cBt, Y, M, K, N, r, WhatT};
-  Timer t(QK_FWD_GEMM, stream);
-  hipError_t e = launch_dense<true>(a, stream);
-  t.stop();
-  return e;
+  const Timer t(QK_FWD_GEMM, stream, true);
+  return launch_dense<true>(a, stream, t);
 }
 
 hipError_t launch_dx_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* What,
                            const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream) {
   BigArgs a{G, N, NF4View{}, dZ, A, dX, M, K, N, r, What};
-  Timer t(QK_BWD_DX, stream);
-  hipError_t e = launch_dense<false>(a, stream);
-  t.stop();
-  return e;
+  const Timer t(QK_BWD_DX, stream, true);
+  return launch_dense<false>(a, stream, t);
 }
 
 hipError_t launch_fwd_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W,
                           const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream) {
   BigArgs a{X, K, W, Z, cBt, Y, M, K, N, r, nullptr};
-  Timer t(QK_FWD_GEMM, stream);
-  hipError_t e = launch_big<true>(a, stream);
-  t.stop();
-  return e;
+  const Timer t(QK_FWD_GEMM, stream, true);
+  return launch_big<true>(a, stream, t);
 }
 
 hipError_t launch_dx_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, NF4View W,
                          const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream) {
   BigArgs a{G, N, W, dZ, A, dX, M, K, N, r, nullptr};
-  Timer t(QK_BWD_DX, stream);
-  hipError_t e = launch_big<false>(a, stream);
-  t.stop();
-  return e;
+  const Timer t(QK_BWD_DX, stream, true);
+  return launch_big<false>(a, stream, t);
 }
 
 }  // namespace qn

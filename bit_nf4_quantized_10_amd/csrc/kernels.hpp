@@ -8,15 +8,24 @@ namespace qn {
 
 // Optional per-kernel event timer (see qlora_timer_enable).  Construct right
 // before a launch, call stop() right after it; a no-op unless enabled.
+// Per-kernel timing for qlora_timer_*: when kernel_id's timer is enabled,
+// an event pair brackets the launches between construction and stop().  With
+// packet = true the pair is instead handed to one launch through start() /
+// end() (hipExtLaunchKernelGGL records it in the dispatch packet itself, so
+// it measures that kernel alone); stop() then does nothing.
 class Timer {
  public:
-  Timer(int kernel_id, hipStream_t stream);
+  Timer(int kernel_id, hipStream_t stream, bool packet = false);
   void stop();
+  hipEvent_t start() const { return static_cast<hipEvent_t>(start_event_); }
+  hipEvent_t end() const { return static_cast<hipEvent_t>(packet_stop_); }
 
  private:
   int id_;
   hipStream_t stream_;
   void* stop_event_;
+  void* start_event_;
+  void* packet_stop_;
 };
 
 hipError_t launch_quantize(const float* W, int64_t P, uint8_t* codes, int8_t* qabsmax,
