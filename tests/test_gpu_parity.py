@@ -350,8 +350,16 @@ def test_full_size_attn7b():
     _full_size_check("attn7b_4096")
 
 
-def test_full_size_mlp7b_down():
-    _full_size_check("mlp7b_4096x11008", matrix=2)
+@pytest.mark.parametrize("matrix", [0, 1, 2])   # up, gate (4096 x 11008) and down (11008 x 4096)
+def test_full_size_mlp7b(matrix):
+    _full_size_check("mlp7b_4096x11008", matrix=matrix)
+
+
+# the seven linears of a 65B block at M = 2048: q, k, v, o (8192 x 8192),
+# gate, up (8192 x 22016), down (22016 x 8192)
+@pytest.mark.parametrize("matrix", range(7))
+def test_full_size_block65b(matrix):
+    _full_size_check("block65b_m2048", matrix=matrix, row_samples=32, col_groups=2)
 
 
 @pytest.mark.parametrize("M", [1, 8, 16])
