@@ -274,6 +274,17 @@ def bench_components(torch, qn, si, dev, sets, outs, qws, status):
                          "frac_hbm_call": round(gbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "GBps_kernel": round(gbytes / (kms * 1e-3) / 1e9, 1)}
     res["gemv_decode65b"] = gemv
+    # what plain streaming reaches on this device, as context for the HBM fractions
+    # (the fractions above are against the 8 TB/s specification)
+    big = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    out = torch.empty_like(big)
+    rd = min(_time_calls(torch, lambda i: big.sum(), 3, flush) for _ in range(2))
+    wr = min(_time_calls(torch, lambda i: out.fill_(1.0), 3, flush) for _ in range(2))
+    res["device_streaming_ceiling"] = {
+        "read_GBps": round(big.numel() * 4 / (rd * 1e-3) / 1e9, 1),
+        "write_GBps": round(big.numel() * 4 / (wr * 1e-3) / 1e9, 1),
+        "how": "torch sum / fill of a 1 GiB fp32 tensor, cache flushed before each call"}
+    del big, out
     return res
 
 

@@ -53,6 +53,7 @@ struct SkinnyPlan {
   int64_t at_bytes, z_part, dz_part, da_part, db_part;
   int64_t gv_rows_per_wave, gv_splits, gv_part;
 };
+void plan_gemv(int64_t M, int64_t K, int64_t N, SkinnyPlan* p);
 SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N, int64_t r);
 
 // Z = X A; with cbt != nullptr the same launch also writes cbt = RNE_bf16(c B)ᵀ
