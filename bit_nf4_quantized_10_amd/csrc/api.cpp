@@ -92,7 +92,7 @@ int nf4_sizes(int64_t numel, int64_t* code_bytes, int64_t* n1, int64_t* n2, int6
   if (code_bytes) *code_bytes = (numel + 1) / 2;
   if (n1) *n1 = a;
   if (n2) *n2 = b;
-  if (quant_workspace_bytes) *quant_workspace_bytes = align256(4 * a) + align256(8 * b);
+  if (quant_workspace_bytes) *quant_workspace_bytes = align256(4 * a) + align256(8 * b) + align256(4 * b);
   return NF4_OK;
 }
 
@@ -103,12 +103,13 @@ int nf4_quantize(const float* W, const nf4_state_t* out, void* workspace, int64_
   int64_t n1, n2, need;
   nf4_sizes(out->numel, nullptr, &n1, &n2, &need);
   if (workspace_bytes < need) return NF4_EINVAL;
-  if (n2 > 0x7fffffff) return NF4_EINVAL;
+  if (out->numel >= (int64_t(1) << 29)) return NF4_EINVAL;   // fp32 input under 2 GiB (32-bit buffer offsets)
   char* ws = static_cast<char*>(workspace);
   float* ws_absmax = reinterpret_cast<float*>(ws);
   double* ws_gsum = reinterpret_cast<double*>(ws + align256(4 * n1));
+  int32_t* ws_flags = reinterpret_cast<int32_t*>(ws + align256(4 * n1) + align256(8 * n2));
   hipError_t e = qn::launch_quantize(W, out->numel, out->codes, out->qabsmax, out->absmax2, out->offset,
-                                     ws_absmax, ws_gsum, status, static_cast<hipStream_t>(stream));
+                                     ws_absmax, ws_gsum, ws_flags, status, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? NF4_OK : NF4_EHIP;
 }
 

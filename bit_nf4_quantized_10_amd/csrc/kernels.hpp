@@ -30,7 +30,7 @@ class Timer {
 
 hipError_t launch_quantize(const float* W, int64_t P, uint8_t* codes, int8_t* qabsmax,
                            float* absmax2, float* offset, float* ws_absmax, double* ws_gsum,
-                           int32_t* status, hipStream_t stream);
+                           int32_t* ws_flags, int32_t* status, hipStream_t stream);
 
 hipError_t launch_dequantize(const uint8_t* codes, const int8_t* qabsmax, const float* absmax2,
                              const float* offset, int64_t P, void* out, int out_dtype,

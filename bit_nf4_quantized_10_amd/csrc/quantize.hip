@@ -18,6 +18,8 @@
 // padded by 2^-12, far below the 0.08 gap between midpoints), so each weight
 // costs one double comparison.  The same argument, with the 255 midpoints of
 // the linear 8-bit code, decides the second-level codes.
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -54,12 +56,15 @@ __device__ __forceinline__ double nf4_midpoint(int j) {
 // group's absmax values.
 __global__ __launch_bounds__(kQuantThreads) void nf4_quant_pass1_kernel(
     const float* __restrict__ W, int64_t P, uint8_t* __restrict__ codes,
-    float* __restrict__ absmax, double* __restrict__ group_sum, int32_t* __restrict__ status) {
+    float* __restrict__ absmax, double* __restrict__ group_sum, int32_t* __restrict__ flags,
+    int32_t* __restrict__ status) {
   __shared__ uint8_t s_bin[256];
   __shared__ double s_mid[16];
   __shared__ float s_abs[kBlock2];
+  __shared__ int s_bad;
 
   const int tid = threadIdx.x;
+  if (tid == 0) s_bad = 0;
   {
     // bin b covers estimates in [b/128 - 1, (b+1)/128 - 1); its entry is the
     // number of midpoints below the padded lower edge.
@@ -78,19 +83,30 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quant_pass1_kernel(
   const int sub = lane & 7;
   bool bad = false;
 
+  // all of this thread's 64 weights are requested before any is used (raw
+  // buffer loads: elements past P read as +0)
+  const Rsrc rw = make_rsrc(W, P * 4);
+  uint4 raw[16];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int64_t block = static_cast<int64_t>(blockIdx.x) * kBlock2 + wave * 64 + it * 8 + (lane >> 3);
+    const uint32_t off = static_cast<uint32_t>((block * kBlock1 + sub * 8) * 4);
+    raw[2 * it] = ld_b128(rw, off);
+    raw[2 * it + 1] = ld_b128(rw, off + 16);
+  }
+
+#pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int bl = wave * 64 + it * 8 + (lane >> 3);   // block within the group
     const int64_t block = static_cast<int64_t>(blockIdx.x) * kBlock2 + bl;
     const int64_t e0 = block * kBlock1 + sub * 8;
     float w[8];
-    if (e0 + 8 <= P) {
-      const float4 v0 = *reinterpret_cast<const float4*>(W + e0);
-      const float4 v1 = *reinterpret_cast<const float4*>(W + e0 + 4);
-      w[0] = v0.x; w[1] = v0.y; w[2] = v0.z; w[3] = v0.w;
-      w[4] = v1.x; w[5] = v1.y; w[6] = v1.z; w[7] = v1.w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = (e0 + i < P) ? W[e0 + i] : 0.0f;
+    {
+      const uint4 v0 = raw[2 * it], v1 = raw[2 * it + 1];
+      w[0] = __builtin_bit_cast(float, v0.x); w[1] = __builtin_bit_cast(float, v0.y);
+      w[2] = __builtin_bit_cast(float, v0.z); w[3] = __builtin_bit_cast(float, v0.w);
+      w[4] = __builtin_bit_cast(float, v1.x); w[5] = __builtin_bit_cast(float, v1.y);
+      w[6] = __builtin_bit_cast(float, v1.z); w[7] = __builtin_bit_cast(float, v1.w);
     }
     float m = 0.0f;
 #pragma unroll
@@ -129,8 +145,14 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quant_pass1_kernel(
       s_abs[bl] = (block < n1) ? a : 0.0f;
     }
   }
-  if (bad) atomicOr(status, NF4_ENONFINITE);
+  if (bad) s_bad = 1;
   __syncthreads();
+  // This group's non-finite flag, for pass 2 to report; the status word is
+  // cleared here (pass 2, the only writer, runs after this kernel).
+  if (tid == 0) {
+    flags[blockIdx.x] = s_bad ? NF4_ENONFINITE : 0;
+    if (blockIdx.x == 0) status[0] = 0;
+  }
 
   if (wave == 0) {
     // stride-halving fp64 sum of the 256 values (pairs i, i+128; i, i+64; ...)
@@ -146,9 +168,9 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quant_pass1_kernel(
 // power of two), divided by n1 in fp64 and rounded to fp32.  One workgroup.
 // Thread t first sums {x[t + s*T]} for s < L/T in stride-halving order,
 // computed as the adjacent-pairwise sum of the bit-reversed sequence.
-__global__ __launch_bounds__(kQuantThreads) void nf4_quant_mean_kernel(
-    const double* __restrict__ group_sum, int64_t n2, int64_t n1, float* __restrict__ offset) {
-  __shared__ double s_x[kQuantThreads];
+// The fixed-tree fp64 sum of the n2 group sums, returned to every thread
+// (s_x: kQuantThreads doubles of LDS).
+__device__ double tree_sum_groups(const double* __restrict__ group_sum, int64_t n2, double* s_x) {
   const int tid = threadIdx.x;
   int64_t L = 1;
   while (L < n2) L <<= 1;
@@ -180,20 +202,78 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quant_mean_kernel(
     if (tid < h) s_x[tid] = s_x[tid] + s_x[tid + h];
     __syncthreads();
   }
-  if (tid == 0) offset[0] = __double2float_rn(__ddiv_rn(s_x[0], static_cast<double>(n1)));
+  const double total = s_x[0];
+  __syncthreads();
+  return total;
 }
+
+// The same sum for n2 <= 8 * kQuantThreads without a stack: thread t holds
+// x[t + 256 s] for s < S = L / 256 (S <= 8, a power of two) and combines
+// them with strides S/2, S/4, ..., 1 before the shared-memory levels.
+__device__ double tree_sum_groups_small(const double* __restrict__ group_sum, int64_t n2, double* s_x) {
+  const int tid = threadIdx.x;
+  int64_t L = 1;
+  while (L < n2) L <<= 1;
+  const int S = L > kQuantThreads ? static_cast<int>(L / kQuantThreads) : 1;
+  double v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t idx = tid + static_cast<int64_t>(i) * kQuantThreads;
+    v[i] = (i < S && idx < n2) ? group_sum[idx] : 0.0;
+  }
+#pragma unroll
+  for (int h = 4; h >= 1; h >>= 1)
+    if (h < S)
+#pragma unroll
+      for (int i = 0; i < h; ++i) v[i] = v[i] + v[i + h];
+  s_x[tid] = v[0];
+  __syncthreads();
+  for (int h = kQuantThreads / 2; h >= 1; h >>= 1) {
+    if (tid < h) s_x[tid] = s_x[tid] + s_x[tid + h];
+    __syncthreads();
+  }
+  const double total = s_x[0];
+  __syncthreads();
+  return total;
+}
+
+__device__ __forceinline__ float offset_of(double total, int64_t n1) {
+  return __double2float_rn(__ddiv_rn(total, static_cast<double>(n1)));
+}
+
+__global__ __launch_bounds__(kQuantThreads) void nf4_quant_mean_kernel(
+    const double* __restrict__ group_sum, int64_t n2, int64_t n1, float* __restrict__ offset) {
+  __shared__ double s_x[kQuantThreads];
+  const double total = tree_sum_groups(group_sum, n2, s_x);
+  if (threadIdx.x == 0) offset[0] = offset_of(total, n1);
+}
+
+// Up to this many groups, every pass-2 workgroup sums the group sums itself
+// (the same tree; the values are in L2) instead of waiting for a separate
+// single-workgroup launch.
+constexpr int64_t kSelfMeanGroups = 8 * kQuantThreads;
 
 // Pass 2: one workgroup per group of 256 first-level scales.  c = a - offset
 // (fp32), s2 = max |c| (1 if zero), q = nearest fl32(q/127) to c / s2 with
 // ties to the smaller q.  Also checks that the reconstructed scale is finite.
 __global__ __launch_bounds__(kQuantThreads) void nf4_quant_pass2_kernel(
-    const float* __restrict__ absmax, int64_t n1, const float* __restrict__ offset,
-    int8_t* __restrict__ qabsmax, float* __restrict__ absmax2, int32_t* __restrict__ status) {
+    const float* __restrict__ absmax, int64_t n1, const double* __restrict__ group_sum, int64_t n2,
+    float* __restrict__ offset, int8_t* __restrict__ qabsmax, float* __restrict__ absmax2,
+    const int32_t* __restrict__ flags, int32_t* __restrict__ status) {
   __shared__ float s_red[kQuantThreads / 64];
+  __shared__ double s_x[kQuantThreads];
+  __shared__ int s_bad;
   const int tid = threadIdx.x;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * kBlock2 + tid;
   const bool valid = idx < n1;
-  const float off = offset[0];
+  if (tid == 0) s_bad = 0;
+  float off;
+  if (n2 <= kSelfMeanGroups) {
+    off = offset_of(tree_sum_groups_small(group_sum, n2, s_x), n1);
+    if (blockIdx.x == 0 && tid == 0) offset[0] = off;
+  } else {
+    off = offset[0];   // written by nf4_quant_mean_kernel
+  }
   const float c = valid ? __fsub_rn(absmax[idx], off) : 0.0f;
   float m = fabsf(c);
   for (int h = 32; h >= 1; h >>= 1) m = fmaxf(m, __shfl_xor(m, h, 64));
@@ -201,9 +281,8 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quant_pass2_kernel(
   __syncthreads();
   float s2 = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   if (s2 == 0.0f) s2 = 1.0f;
-  if (!valid) return;
 
-  const float est = __fdiv_rn(c, s2);
+  const float est = __fdiv_rn(c, s2);   // (threads past n1 compute on c = 0 and store nothing)
   int q = static_cast<int>(rintf(est * static_cast<float>(kLevels2)));
   q = min(max(q, -kLevels2), kLevels2);
   const double cd = c, sd = s2;
@@ -214,65 +293,126 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quant_pass2_kernel(
     if (q > -kLevels2 && cd <= mid(q - 1) * sd) --q;
   for (int it = 0; it < 2; ++it)
     if (q < kLevels2 && cd > mid(q) * sd) ++q;
-  qabsmax[idx] = static_cast<int8_t>(q);
+  if (valid) {
+    qabsmax[idx] = static_cast<int8_t>(q);
+    if (!is_finite_bits(absmax_hat(q, s2, off))) s_bad = 1;
+  }
   if (tid == 0) absmax2[blockIdx.x] = s2;
-  if (!is_finite_bits(absmax_hat(q, s2, off))) atomicOr(status, NF4_ENONFINITE);
+  __syncthreads();
+  if (tid == 0 && (s_bad || flags[blockIdx.x] != 0)) atomicOr(status, NF4_ENONFINITE);
 }
 
-// Decoder: each thread turns one 32-bit code word (8 weights) into fp32 or
-// bf16 reconstructions; grid-stride over the words.
+// Decoder.  The whole code words (8 weights each) are cut into tiles of
+// 256 * U words; thread t handles words tile * 256 * U + t + 256 * u, u < U,
+// so every load and every 16-byte store of a wave is contiguous.  Workgroups
+// stride over the tiles and request the next tile's codes and scales before
+// decoding and storing the current one.  The decoded second-level values
+// fl32(q / 127) come from a table in LDS, one division per thread at start.
+// A final partial word (P % 8 != 0) is decoded by one thread on its own.
+// Words per thread per tile, and the most workgroups a launch uses (8 per
+// CU; larger tensors loop over their tiles).
+#ifndef QN_DQ_U
+#define QN_DQ_U 4
+#endif
+#ifndef QN_DQ_GRID
+#define QN_DQ_GRID 2048
+#endif
+
+template <int U>
+struct DqTile {
+  uint32_t wd[U];
+  int q[U];
+  float s2[U];
+};
+
+template <int U>
+__device__ __forceinline__ void dq_load(DqTile<U>& t, int64_t tile, int64_t words, Rsrc rc, Rsrc rq, Rsrc rs) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t wi = tile * (kQuantThreads * U) + threadIdx.x + static_cast<int64_t>(u) * kQuantThreads;
+    const bool in = wi < words;
+    t.wd[u] = ld_b32(rc, in ? static_cast<uint32_t>(wi * 4) : kMasked);
+    t.q[u] = ld_i8(rq, in ? static_cast<uint32_t>(wi >> 3) : kMasked);
+    t.s2[u] = ld_f32(rs, in ? static_cast<uint32_t>((wi >> 11) * 4) : kMasked);
+  }
+}
+
+template <bool kBf16>
+__device__ __forceinline__ void dq_store(void* out, int64_t e0, const float v[8]) {
+  if (kBf16) {
+    uint4 pk;
+    pk.x = pack_bf16x2(v[0], v[1]);
+    pk.y = pack_bf16x2(v[2], v[3]);
+    pk.z = pack_bf16x2(v[4], v[5]);
+    pk.w = pack_bf16x2(v[6], v[7]);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + e0) = pk;
+  } else {
+    float* o = static_cast<float*>(out) + e0;
+    *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+template <int U, bool kBf16>
+__device__ __forceinline__ void dq_decode(const DqTile<U>& t, int64_t tile, int64_t words, const float* s_lut,
+                                          const float* s_q2, float off, void* out) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t wi = tile * (kQuantThreads * U) + threadIdx.x + static_cast<int64_t>(u) * kQuantThreads;
+    if (wi < words) {
+      const float ahat = __fadd_rn(__fmul_rn(s_q2[t.q[u] + kLevels2], t.s2[u]), off);
+      float v[8];
+      decode8(t.wd[u], ahat, s_lut, v);
+      dq_store<kBf16>(out, wi * 8, v);
+    }
+  }
+}
+
+template <int U, bool kBf16>
 __global__ __launch_bounds__(kQuantThreads) void nf4_dequant_kernel(
     const uint8_t* __restrict__ codes, const int8_t* __restrict__ qabsmax,
     const float* __restrict__ absmax2, const float* __restrict__ offset, int64_t P,
-    void* __restrict__ out, int out_dtype, int32_t* __restrict__ status) {
+    void* __restrict__ out, int32_t* __restrict__ status) {
   __shared__ float s_lut[16];
-  if (threadIdx.x < 16) s_lut[threadIdx.x] = kNF4[threadIdx.x];
-  __syncthreads();
-  const float off = offset[0];
-  const int64_t words = (P + 7) / 8;
+  __shared__ float s_q2[2 * kLevels2 + 2];
+  const int tid = threadIdx.x;
+  const int64_t n1 = (P + kBlock1 - 1) / kBlock1;
   const int64_t code_bytes = (P + 1) / 2;
-  for (int64_t wi = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; wi < words;
-       wi += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t e0 = wi * 8;
-    uint32_t word;
-    if (e0 + 8 <= P) {
-      word = *reinterpret_cast<const uint32_t*>(codes + wi * 4);
-    } else {
-      word = 0;
-      for (int b = 0; b < 4; ++b)
-        if (wi * 4 + b < code_bytes) word |= static_cast<uint32_t>(codes[wi * 4 + b]) << (8 * b);
-      if ((P & 1) && status) {
-        const uint32_t last = codes[code_bytes - 1];
-        if ((last & 15u) != 7u) atomicOr(status, NF4_EPADDING);
-      }
-    }
-    const int64_t block = e0 / kBlock1;
-    const float ahat = absmax_hat(qabsmax[block], absmax2[block / kBlock2], off);
+  const int64_t words = P >> 3;   // whole words
+  const Rsrc rc = make_rsrc(codes, words * 4);
+  const Rsrc rq = make_rsrc(qabsmax, n1);
+  const Rsrc rs = make_rsrc(absmax2, ((n1 + kBlock2 - 1) / kBlock2) * 4);
+  const int64_t tiles = (words + kQuantThreads * U - 1) / (kQuantThreads * U);
+  int64_t tile = blockIdx.x;
+  DqTile<U> cur;
+  dq_load(cur, tile, words, rc, rq, rs);
+  if (tid < 16) s_lut[tid] = kNF4[tid];
+  if (tid <= 2 * kLevels2) s_q2[tid] = q2_value(tid - kLevels2);
+  const float off = offset[0];
+  __syncthreads();
+  if (blockIdx.x == 0 && tid == 0 && (P & 7)) {
+    uint32_t word = 0;
+    for (int b = 0; b < 4; ++b)
+      if (words * 4 + b < code_bytes) word |= static_cast<uint32_t>(codes[words * 4 + b]) << (8 * b);
+    // odd P: the pad nibble (low half of the last byte) must be code 7
+    if ((P & 1) && status && (codes[code_bytes - 1] & 15u) != 7u) atomicOr(status, NF4_EPADDING);
     float v[8];
-    decode8(word, ahat, s_lut, v);
-    if (out_dtype == NF4_OUT_BF16) {
-      uint16_t* o = static_cast<uint16_t*>(out) + e0;
-      if (e0 + 8 <= P) {
-        uint4 pk;
-        pk.x = pack_bf16x2(v[0], v[1]);
-        pk.y = pack_bf16x2(v[2], v[3]);
-        pk.z = pack_bf16x2(v[4], v[5]);
-        pk.w = pack_bf16x2(v[6], v[7]);
-        *reinterpret_cast<uint4*>(o) = pk;
-      } else {
-        for (int i = 0; i < 8; ++i)
-          if (e0 + i < P) o[i] = static_cast<uint16_t>(pack_bf16x2(v[i], 0.0f) & 0xffffu);
-      }
-    } else {
-      float* o = static_cast<float*>(out) + e0;
-      if (e0 + 8 <= P) {
-        *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
-        *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
-      } else {
-        for (int i = 0; i < 8; ++i)
-          if (e0 + i < P) o[i] = v[i];
-      }
+    decode8(word, absmax_hat(qabsmax[n1 - 1], absmax2[(n1 - 1) / kBlock2], off), s_lut, v);
+    for (int i = 0; i < 8; ++i) {
+      const int64_t e = words * 8 + i;
+      if (e >= P) break;
+      if (kBf16) static_cast<uint16_t*>(out)[e] = static_cast<uint16_t>(pack_bf16x2(v[i], 0.0f) & 0xffffu);
+      else static_cast<float*>(out)[e] = v[i];
     }
+  }
+  // two register tiles in turn, so no copy waits on loads still in flight
+  DqTile<U> nxt;
+  for (; tile < tiles; tile += 2 * static_cast<int64_t>(gridDim.x)) {
+    dq_load(nxt, tile + gridDim.x, words, rc, rq, rs);
+    dq_decode<U, kBf16>(cur, tile, words, s_lut, s_q2, off, out);
+    if (tile + gridDim.x >= tiles) break;
+    dq_load(cur, tile + 2 * static_cast<int64_t>(gridDim.x), words, rc, rq, rs);
+    dq_decode<U, kBf16>(nxt, tile + gridDim.x, words, s_lut, s_q2, off, out);
   }
 }
 
@@ -326,26 +466,26 @@ __global__ __launch_bounds__(256) void nf4_dequant_t_kernel(const uint8_t* __res
   }
 }
 
-__global__ void nf4_status_clear_kernel(int32_t* status) { status[0] = 0; }
 
 // ----------------------------------------------------------------- launchers
 hipError_t launch_quantize(const float* W, int64_t P, uint8_t* codes, int8_t* qabsmax,
                            float* absmax2, float* offset, float* ws_absmax, double* ws_gsum,
-                           int32_t* status, hipStream_t stream) {
+                           int32_t* ws_flags, int32_t* status, hipStream_t stream) {
   const int64_t n1 = (P + kBlock1 - 1) / kBlock1;
   const int64_t n2 = (n1 + kBlock2 - 1) / kBlock2;
-  hipLaunchKernelGGL(nf4_status_clear_kernel, dim3(1), dim3(1), 0, stream, status);
   Timer t1(QK_QUANT_PASS1, stream);
   hipLaunchKernelGGL(nf4_quant_pass1_kernel, dim3(static_cast<unsigned>(n2)), dim3(kQuantThreads), 0,
-                     stream, W, P, codes, ws_absmax, ws_gsum, status);
+                     stream, W, P, codes, ws_absmax, ws_gsum, ws_flags, status);
   t1.stop();
-  Timer t2(QK_QUANT_MEAN, stream);
-  hipLaunchKernelGGL(nf4_quant_mean_kernel, dim3(1), dim3(kQuantThreads), 0, stream, ws_gsum, n2, n1,
-                     offset);
-  t2.stop();
+  if (n2 > kSelfMeanGroups) {
+    Timer t2(QK_QUANT_MEAN, stream);
+    hipLaunchKernelGGL(nf4_quant_mean_kernel, dim3(1), dim3(kQuantThreads), 0, stream, ws_gsum, n2, n1,
+                       offset);
+    t2.stop();
+  }
   Timer t3(QK_QUANT_PASS2, stream);
   hipLaunchKernelGGL(nf4_quant_pass2_kernel, dim3(static_cast<unsigned>(n2)), dim3(kQuantThreads), 0,
-                     stream, ws_absmax, n1, offset, qabsmax, absmax2, status);
+                     stream, ws_absmax, n1, ws_gsum, n2, offset, qabsmax, absmax2, ws_flags, status);
   t3.stop();
   return hipGetLastError();
 }
@@ -353,13 +493,16 @@ hipError_t launch_quantize(const float* W, int64_t P, uint8_t* codes, int8_t* qa
 hipError_t launch_dequantize(const uint8_t* codes, const int8_t* qabsmax, const float* absmax2,
                              const float* offset, int64_t P, void* out, int out_dtype,
                              int32_t* status, hipStream_t stream) {
-  const int64_t words = (P + 7) / 8;
-  int64_t blocks = (words + kQuantThreads - 1) / kQuantThreads;
-  if (blocks > 65536) blocks = 65536;
-  Timer t(QK_DEQUANT, stream);
-  hipLaunchKernelGGL(nf4_dequant_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kQuantThreads), 0,
-                     stream, codes, qabsmax, absmax2, offset, P, out, out_dtype, status);
-  t.stop();
+  constexpr int U = QN_DQ_U;
+  const int64_t tiles = (P / 8 + kQuantThreads * U - 1) / (kQuantThreads * U);
+  const int64_t blocks = tiles < 1 ? 1 : (tiles < QN_DQ_GRID ? tiles : QN_DQ_GRID);
+  const Timer t(QK_DEQUANT, stream, true);
+  if (out_dtype == NF4_OUT_BF16)
+    hipExtLaunchKernelGGL((nf4_dequant_kernel<U, true>), dim3(static_cast<unsigned>(blocks)), dim3(kQuantThreads),
+                          0, stream, t.start(), t.end(), 0, codes, qabsmax, absmax2, offset, P, out, status);
+  else
+    hipExtLaunchKernelGGL((nf4_dequant_kernel<U, false>), dim3(static_cast<unsigned>(blocks)), dim3(kQuantThreads),
+                          0, stream, t.start(), t.end(), 0, codes, qabsmax, absmax2, offset, P, out, status);
   return hipGetLastError();
 }
 

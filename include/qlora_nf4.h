@@ -78,7 +78,8 @@ int nf4_sizes(int64_t numel, int64_t* code_bytes, int64_t* n1, int64_t* n2,
  * device int32 that the call first sets to 0; the GPU ORs NF4_ENONFINITE into
  * it if a weight is NaN/Inf or a reconstructed scale overflows (the page
  * rejects both).  Codes use the exact first-level absmax; the offset is the
- * fp64 fixed-tree mean rounded to fp32. */
+ * fp64 fixed-tree mean rounded to fp32.  P must be below 2^29 (the fp32
+ * input under 2 GiB); NF4_EINVAL otherwise. */
 int nf4_quantize(const float* W, const nf4_state_t* out, void* workspace,
                  int64_t workspace_bytes, int32_t* status, void* stream);
 

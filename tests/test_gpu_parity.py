@@ -166,6 +166,14 @@ def test_quantize_decode65b_sampled_bit_exact():
     packed = got["codes_packed"].reshape(-1, 32)[blocks]
     exp = ((codes[:, 0::2] << 4) | codes[:, 1::2]).astype(np.uint8)
     np.testing.assert_array_equal(packed, exp)
+    # the decoder at this size loops over its tiles; sampled blocks of both outputs
+    import torch
+    idx = torch.from_numpy(blocks).cuda()
+    for dt in ("fp32", "bf16"):
+        full = qn.nf4_dequantize(state, dt).view(-1, 64)
+        got_w = host(full[idx].contiguous().reshape(-1)).reshape(len(blocks), 64)
+        del full
+        np.testing.assert_array_equal(got_w, ow.weights_of_blocks(blocks, dt))
 
 
 # -------------------------------------------------------------------- layer
