@@ -19,9 +19,12 @@ void counts(int64_t P, int64_t* n1, int64_t* n2) {
   *n2 = (*n1 + NF4_BLOCK2 - 1) / NF4_BLOCK2;
 }
 
+// The encoder and decoders move packed codes and second-level codes as
+// 32-bit words and the scales as fp32, so those buffers must be aligned.
 bool state_ok(const nf4_state_t* s) {
   return s != nullptr && s->numel >= 1 && s->codes != nullptr && s->qabsmax != nullptr &&
-         s->absmax2 != nullptr && s->offset != nullptr;
+         s->absmax2 != nullptr && s->offset != nullptr && aligned16(s->codes) && aligned16(s->qabsmax) &&
+         (reinterpret_cast<uintptr_t>(s->absmax2) & 3u) == 0 && (reinterpret_cast<uintptr_t>(s->offset) & 3u) == 0;
 }
 
 // Kernels address operands with 32-bit buffer offsets and mark masked lanes

@@ -42,6 +42,13 @@ __device__ __forceinline__ float dpp_max_row8(float x) {
   return x;
 }
 
+// One bin of the encoder's lookup: the midpoint m_L it may straddle and L.
+struct __attribute__((aligned(16))) BinEntry {
+  double mid;
+  int L;
+  int pad;
+};
+
 // Midpoint between NF4 codes j and j+1, exact in double; +4 for j = 15 so a
 // comparison against it is always false.
 __device__ __forceinline__ double nf4_midpoint(int j) {
@@ -49,6 +56,11 @@ __device__ __forceinline__ double nf4_midpoint(int j) {
 }
 
 }  // namespace
+
+#ifndef QN_P1_DEPTH
+#define QN_P1_DEPTH 3
+#endif
+constexpr int kP1Depth = QN_P1_DEPTH;
 
 // Pass 1: one workgroup per group of 256 blocks (16384 weights).  Each lane
 // owns 8 consecutive weights; 8 lanes form a block.  Writes the packed codes,
@@ -58,21 +70,19 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quant_pass1_kernel(
     const float* __restrict__ W, int64_t P, uint8_t* __restrict__ codes,
     float* __restrict__ absmax, double* __restrict__ group_sum, int32_t* __restrict__ flags,
     int32_t* __restrict__ status) {
-  __shared__ uint8_t s_bin[256];
-  __shared__ double s_mid[16];
+  __shared__ BinEntry s_tab[256];
   __shared__ float s_abs[kBlock2];
   __shared__ int s_bad;
 
   const int tid = threadIdx.x;
   if (tid == 0) s_bad = 0;
   {
-    // bin b covers estimates in [b/128 - 1, (b+1)/128 - 1); its entry is the
-    // number of midpoints below the padded lower edge.
+    // bin b covers estimates in [b/128 - 1, (b+1)/128 - 1); its entry holds
+    // L, the number of midpoints below the padded lower edge, and m_L.
     const double lo = static_cast<double>(tid) / 128.0 - 1.0 - kBinPad;
     int cnt = 0;
     for (int j = 0; j < 15; ++j) cnt += nf4_midpoint(j) < lo ? 1 : 0;
-    s_bin[tid] = static_cast<uint8_t>(cnt);
-    if (tid < 16) s_mid[tid] = nf4_midpoint(tid);
+    s_tab[tid] = BinEntry{nf4_midpoint(cnt), cnt, 0};
   }
   __syncthreads();
 
@@ -83,20 +93,27 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quant_pass1_kernel(
   const int sub = lane & 7;
   bool bad = false;
 
-  // all of this thread's 64 weights are requested before any is used (raw
-  // buffer loads: elements past P read as +0)
+  // The thread's 8 steps of 8 weights are loaded kP1Depth steps ahead of
+  // their use, so the encoding of early steps overlaps the later loads (raw
+  // buffer loads: elements past P read as +0).
   const Rsrc rw = make_rsrc(W, P * 4);
   uint4 raw[16];
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {
+  auto load_step = [&](int it) {
     const int64_t block = static_cast<int64_t>(blockIdx.x) * kBlock2 + wave * 64 + it * 8 + (lane >> 3);
     const uint32_t off = static_cast<uint32_t>((block * kBlock1 + sub * 8) * 4);
     raw[2 * it] = ld_b128(rw, off);
     raw[2 * it + 1] = ld_b128(rw, off + 16);
-  }
+  };
+#pragma unroll
+  for (int it = 0; it < kP1Depth; ++it) load_step(it);
 
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
+    if (kP1Depth < 8) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (it + kP1Depth < 8) load_step(it + kP1Depth);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     const int bl = wave * 64 + it * 8 + (lane >> 3);   // block within the group
     const int64_t block = static_cast<int64_t>(blockIdx.x) * kBlock2 + bl;
     const int64_t e0 = block * kBlock1 + sub * 8;
@@ -116,19 +133,28 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quant_pass1_kernel(
     }
     m = dpp_max_row8(m);
     const float a = (m == 0.0f) ? 1.0f : m;
-    // fp32 estimate of w / a; tiny scales are lifted by 2^64 first so that
-    // the reciprocal stays finite (exact power-of-two scaling).
-    const float lift = (a < 0x1p-100f) ? 0x1p64f : 1.0f;
-    const float inv = 1.0f / (a * lift);
+    // fp32 estimate of w / a, used only to pick the bin (its error, a few
+    // ulp, is far inside the bin padding).  Scales outside [2^-100, 2^100]
+    // are first brought inside by an exact power of two, so that the
+    // reciprocal is a normal number.
+    const float lift = (a < 0x1p-100f) ? 0x1p64f : ((a > 0x1p100f) ? 0x1p-64f : 1.0f);
+    const float inv = __builtin_amdgcn_rcpf(a * lift);
     const double ad = static_cast<double>(a);
+    int bin[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // truncation, then the clamp, gives the floor's bin for every estimate
+      // in [-1 - 2^-20, 1 + 2^-20]
+      const int b = static_cast<int>(fmaf((w[i] * lift) * inv, 128.0f, 128.0f));
+      bin[i] = min(max(b, 0), 255);
+    }
+    BinEntry ent[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ent[i] = s_tab[bin[i]];
     uint32_t word = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float est = (w[i] * lift) * inv;
-      int bin = static_cast<int>(floorf(fmaf(est, 128.0f, 128.0f)));
-      bin = min(max(bin, 0), 255);
-      const int L = s_bin[bin];
-      const int code = L + ((static_cast<double>(w[i]) > s_mid[L] * ad) ? 1 : 0);
+      const int code = ent[i].L + ((static_cast<double>(w[i]) > ent[i].mid * ad) ? 1 : 0);
       // byte i/2 of the little-endian word: even i -> high nibble
       word |= static_cast<uint32_t>(code) << (8 * (i >> 1) + ((i & 1) ? 0 : 4));
     }
@@ -164,142 +190,140 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_quant_pass1_kernel(
   }
 }
 
-// Offset: stride-halving fp64 sum of the n2 group sums (zero-padded to a
-// power of two), divided by n1 in fp64 and rounded to fp32.  One workgroup.
-// Thread t first sums {x[t + s*T]} for s < L/T in stride-halving order,
-// computed as the adjacent-pairwise sum of the bit-reversed sequence.
-// The fixed-tree fp64 sum of the n2 group sums, returned to every thread
-// (s_x: kQuantThreads doubles of LDS).
-__device__ double tree_sum_groups(const double* __restrict__ group_sum, int64_t n2, double* s_x) {
-  const int tid = threadIdx.x;
-  int64_t L = 1;
-  while (L < n2) L <<= 1;
-  double v = 0.0;
-  if (L <= kQuantThreads) {
-    v = (tid < n2) ? group_sum[tid] : 0.0;
-  } else {
-    const int64_t S = L / kQuantThreads;
-    int lg = 0;
-    while ((int64_t(1) << lg) < S) ++lg;
-    double stack[40];
-    for (int64_t i = 0; i < S; ++i) {
-      int64_t s = 0;
-      for (int b = 0; b < lg; ++b) s |= ((i >> b) & 1) << (lg - 1 - b);
-      const int64_t idx = tid + s * kQuantThreads;
-      double x = (idx < n2) ? group_sum[idx] : 0.0;
-      int l = 0;
-      while ((i >> l) & 1) {
-        x = stack[l] + x;
-        ++l;
-      }
-      stack[l] = x;
-    }
-    v = stack[lg];
-  }
-  s_x[tid] = v;
-  __syncthreads();
-  for (int h = kQuantThreads / 2; h >= 1; h >>= 1) {
-    if (tid < h) s_x[tid] = s_x[tid] + s_x[tid + h];
-    __syncthreads();
-  }
-  const double total = s_x[0];
-  __syncthreads();
-  return total;
-}
+// The offset is the mean of the n1 first-level scales: the stride-halving
+// fp64 sum of the n2 group sums (zero-padded to a power of two L; pass 1
+// summed each group's 256 values the same way), divided by n1 in fp64 and
+// rounded to fp32.  With T threads, thread t holds x[t + T s] for
+// s < S = L / T and combines them with strides S/2, ..., 1 in registers;
+// the levels T/2, ..., 1 then pair threads t and t + h.  Zero padding adds
+// +0 exactly, so any power of two T gives the same sum.
+constexpr int kMaxSumPerThread = 32;
 
-// The same sum for n2 <= 8 * kQuantThreads without a stack: thread t holds
-// x[t + 256 s] for s < S = L / 256 (S <= 8, a power of two) and combines
-// them with strides S/2, S/4, ..., 1 before the shared-memory levels.
-__device__ double tree_sum_groups_small(const double* __restrict__ group_sum, int64_t n2, double* s_x) {
-  const int tid = threadIdx.x;
+template <int T>
+__device__ __forceinline__ double tree_partial(const double* __restrict__ group_sum, int64_t n2, int t) {
   int64_t L = 1;
   while (L < n2) L <<= 1;
-  const int S = L > kQuantThreads ? static_cast<int>(L / kQuantThreads) : 1;
-  double v[8];
+  const int S = L > T ? static_cast<int>(L / T) : 1;   // <= kMaxSumPerThread
+  double v[kMaxSumPerThread];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t idx = tid + static_cast<int64_t>(i) * kQuantThreads;
+  for (int i = 0; i < kMaxSumPerThread; ++i) {
+    const int64_t idx = t + static_cast<int64_t>(i) * T;
     v[i] = (i < S && idx < n2) ? group_sum[idx] : 0.0;
   }
 #pragma unroll
-  for (int h = 4; h >= 1; h >>= 1)
+  for (int h = kMaxSumPerThread / 2; h >= 1; h >>= 1)
     if (h < S)
 #pragma unroll
       for (int i = 0; i < h; ++i) v[i] = v[i] + v[i + h];
-  s_x[tid] = v[0];
-  __syncthreads();
-  for (int h = kQuantThreads / 2; h >= 1; h >>= 1) {
-    if (tid < h) s_x[tid] = s_x[tid] + s_x[tid + h];
-    __syncthreads();
-  }
-  const double total = s_x[0];
-  __syncthreads();
-  return total;
+  return v[0];
 }
 
 __device__ __forceinline__ float offset_of(double total, int64_t n1) {
   return __double2float_rn(__ddiv_rn(total, static_cast<double>(n1)));
 }
 
-__global__ __launch_bounds__(kQuantThreads) void nf4_quant_mean_kernel(
-    const double* __restrict__ group_sum, int64_t n2, int64_t n1, float* __restrict__ offset) {
-  __shared__ double s_x[kQuantThreads];
-  const double total = tree_sum_groups(group_sum, n2, s_x);
-  if (threadIdx.x == 0) offset[0] = offset_of(total, n1);
+// One wave computes the whole sum (n2 <= 64 * kMaxSumPerThread); every
+// lane receives it.
+__device__ __forceinline__ double tree_sum_wave(const double* __restrict__ group_sum, int64_t n2, int lane) {
+  double x = tree_partial<64>(group_sum, n2, lane);
+  for (int h = 32; h >= 1; h >>= 1) x = x + __shfl_down(x, h, 64);
+  return __shfl(x, 0, 64);
 }
 
-// Up to this many groups, every pass-2 workgroup sums the group sums itself
-// (the same tree; the values are in L2) instead of waiting for a separate
-// single-workgroup launch.
-constexpr int64_t kSelfMeanGroups = 8 * kQuantThreads;
+constexpr int kMeanThreads = 1024;
 
-// Pass 2: one workgroup per group of 256 first-level scales.  c = a - offset
+// Separate offset kernel for n2 > 64 * kMaxSumPerThread groups (one
+// workgroup of 1024 threads; n2 <= 1024 * kMaxSumPerThread).
+__global__ __launch_bounds__(kMeanThreads) void nf4_quant_mean_kernel(
+    const double* __restrict__ group_sum, int64_t n2, int64_t n1, float* __restrict__ offset) {
+  __shared__ double s_x[kMeanThreads];
+  const int tid = threadIdx.x;
+  s_x[tid] = tree_partial<kMeanThreads>(group_sum, n2, tid);
+  __syncthreads();
+  for (int h = kMeanThreads / 2; h >= 64; h >>= 1) {
+    if (tid < h) s_x[tid] = s_x[tid] + s_x[tid + h];
+    __syncthreads();
+  }
+  if (tid < 64) {
+    double x = s_x[tid];
+    for (int h = 32; h >= 1; h >>= 1) x = x + __shfl_down(x, h, 64);
+    if (tid == 0) offset[0] = offset_of(x, n1);
+  }
+}
+
+// Up to this many groups every pass-2 wave sums the group sums itself (the
+// values are in L2) instead of waiting for a separate launch.
+constexpr int64_t kSelfMeanGroups = 64 * kMaxSumPerThread;
+
+// Pass 2: one wave per group of 256 first-level scales, 4 groups per
+// workgroup; lane l holds scales 4l .. 4l+3 of its group.  c = a - offset
 // (fp32), s2 = max |c| (1 if zero), q = nearest fl32(q/127) to c / s2 with
-// ties to the smaller q.  Also checks that the reconstructed scale is finite.
-__global__ __launch_bounds__(kQuantThreads) void nf4_quant_pass2_kernel(
+// ties to the smaller q.  Also checks that each reconstructed scale is
+// finite and reports pass 1's non-finite flag of the group.
+constexpr int kPass2Groups = 4;
+
+__global__ __launch_bounds__(64 * kPass2Groups) void nf4_quant_pass2_kernel(
     const float* __restrict__ absmax, int64_t n1, const double* __restrict__ group_sum, int64_t n2,
     float* __restrict__ offset, int8_t* __restrict__ qabsmax, float* __restrict__ absmax2,
     const int32_t* __restrict__ flags, int32_t* __restrict__ status) {
-  __shared__ float s_red[kQuantThreads / 64];
-  __shared__ double s_x[kQuantThreads];
-  __shared__ int s_bad;
-  const int tid = threadIdx.x;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kBlock2 + tid;
-  const bool valid = idx < n1;
-  if (tid == 0) s_bad = 0;
+  // s_mid[k + 127] = midpoint between codes k and k+1, exact in double
+  __shared__ double s_mid[2 * kLevels2];
+  for (int k = threadIdx.x; k < 2 * kLevels2; k += blockDim.x)
+    s_mid[k] = 0.5 * (static_cast<double>(q2_value(k - kLevels2)) + static_cast<double>(q2_value(k - kLevels2 + 1)));
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * kPass2Groups + (threadIdx.x >> 6);
+  if (g >= n2) return;   // whole waves only
+  const Rsrc ra = make_rsrc(absmax, n1 * 4);
+  const int64_t i0 = g * kBlock2 + 4 * lane;
+  const uint4 raw = ld_b128(ra, static_cast<uint32_t>(i0 * 4));   // scales past n1 read as 0
   float off;
   if (n2 <= kSelfMeanGroups) {
-    off = offset_of(tree_sum_groups_small(group_sum, n2, s_x), n1);
-    if (blockIdx.x == 0 && tid == 0) offset[0] = off;
+    off = offset_of(tree_sum_wave(group_sum, n2, lane), n1);
+    if (g == 0 && lane == 0) offset[0] = off;
   } else {
     off = offset[0];   // written by nf4_quant_mean_kernel
   }
-  const float c = valid ? __fsub_rn(absmax[idx], off) : 0.0f;
-  float m = fabsf(c);
-  for (int h = 32; h >= 1; h >>= 1) m = fmaxf(m, __shfl_xor(m, h, 64));
-  if ((tid & 63) == 0) s_red[tid >> 6] = m;
-  __syncthreads();
-  float s2 = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  if (s2 == 0.0f) s2 = 1.0f;
-
-  const float est = __fdiv_rn(c, s2);   // (threads past n1 compute on c = 0 and store nothing)
-  int q = static_cast<int>(rintf(est * static_cast<float>(kLevels2)));
-  q = min(max(q, -kLevels2), kLevels2);
-  const double cd = c, sd = s2;
-  auto mid = [](int k) {  // midpoint between codes k and k+1, exact in double
-    return 0.5 * (static_cast<double>(q2_value(k)) + static_cast<double>(q2_value(k + 1)));
-  };
-  for (int it = 0; it < 2; ++it)
-    if (q > -kLevels2 && cd <= mid(q - 1) * sd) --q;
-  for (int it = 0; it < 2; ++it)
-    if (q < kLevels2 && cd > mid(q) * sd) ++q;
-  if (valid) {
-    qabsmax[idx] = static_cast<int8_t>(q);
-    if (!is_finite_bits(absmax_hat(q, s2, off))) s_bad = 1;
+  const float a[4] = {__builtin_bit_cast(float, raw.x), __builtin_bit_cast(float, raw.y),
+                      __builtin_bit_cast(float, raw.z), __builtin_bit_cast(float, raw.w)};
+  float c[4];
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    c[i] = (i0 + i < n1) ? __fsub_rn(a[i], off) : 0.0f;
+    m = fmaxf(m, fabsf(c[i]));
   }
-  if (tid == 0) absmax2[blockIdx.x] = s2;
-  __syncthreads();
-  if (tid == 0 && (s_bad || flags[blockIdx.x] != 0)) atomicOr(status, NF4_ENONFINITE);
+  for (int h = 32; h >= 1; h >>= 1) m = fmaxf(m, __shfl_xor(m, h, 64));
+  const float s2 = (m == 0.0f) ? 1.0f : m;
+  const double sd = s2;
+  auto mid = [&](int k) { return s_mid[k + kLevels2]; };
+  uint32_t packed = 0;
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // estimate, then the exact corrections against the neighbouring midpoints
+    const float est = __fdiv_rn(c[i], s2);
+    int q = static_cast<int>(rintf(est * static_cast<float>(kLevels2)));
+    q = min(max(q, -kLevels2), kLevels2);
+    const double cd = c[i];
+    for (int it = 0; it < 2; ++it)
+      if (q > -kLevels2 && cd <= mid(q - 1) * sd) --q;
+    for (int it = 0; it < 2; ++it)
+      if (q < kLevels2 && cd > mid(q) * sd) ++q;
+    if (i0 + i < n1 && !is_finite_bits(absmax_hat(q, s2, off))) bad = true;
+    packed |= (static_cast<uint32_t>(q) & 0xffu) << (8 * i);
+  }
+  if (i0 + 4 <= n1) {
+    *reinterpret_cast<uint32_t*>(qabsmax + i0) = packed;
+  } else {
+    for (int i = 0; i < 4; ++i)
+      if (i0 + i < n1) qabsmax[i0 + i] = static_cast<int8_t>(packed >> (8 * i));
+  }
+  const bool any_bad = __any(bad);
+  if (lane == 0) {
+    absmax2[g] = s2;
+    if (any_bad || flags[g] != 0) atomicOr(status, NF4_ENONFINITE);
+  }
 }
 
 // Decoder.  The whole code words (8 weights each) are cut into tiles of
@@ -478,14 +502,15 @@ hipError_t launch_quantize(const float* W, int64_t P, uint8_t* codes, int8_t* qa
                      stream, W, P, codes, ws_absmax, ws_gsum, ws_flags, status);
   t1.stop();
   if (n2 > kSelfMeanGroups) {
+    if (n2 > static_cast<int64_t>(kMeanThreads) * kMaxSumPerThread) return hipErrorInvalidValue;
     Timer t2(QK_QUANT_MEAN, stream);
-    hipLaunchKernelGGL(nf4_quant_mean_kernel, dim3(1), dim3(kQuantThreads), 0, stream, ws_gsum, n2, n1,
-                       offset);
+    hipLaunchKernelGGL(nf4_quant_mean_kernel, dim3(1), dim3(kMeanThreads), 0, stream, ws_gsum, n2, n1, offset);
     t2.stop();
   }
   Timer t3(QK_QUANT_PASS2, stream);
-  hipLaunchKernelGGL(nf4_quant_pass2_kernel, dim3(static_cast<unsigned>(n2)), dim3(kQuantThreads), 0,
-                     stream, ws_absmax, n1, ws_gsum, n2, offset, qabsmax, absmax2, ws_flags, status);
+  hipLaunchKernelGGL(nf4_quant_pass2_kernel, dim3(static_cast<unsigned>((n2 + kPass2Groups - 1) / kPass2Groups)),
+                     dim3(64 * kPass2Groups), 0, stream, ws_absmax, n1, ws_gsum, n2, offset, qabsmax, absmax2,
+                     ws_flags, status);
   t3.stop();
   return hipGetLastError();
 }

@@ -57,7 +57,9 @@ extern "C" {
 #define NF4_BLOCK2  256
 #define NF4_LEVELS2 127
 
-/* The stored, frozen state of one weight tensor (all device pointers). */
+/* The stored, frozen state of one weight tensor (all device pointers;
+ * codes and qabsmax 16-byte aligned, absmax2 and offset 4-byte aligned, or
+ * every entry point taking the state returns NF4_EINVAL). */
 typedef struct nf4_state {
   int64_t  numel;    /* P, the logical number of weights (>= 1)            */
   uint8_t* codes;    /* ceil(P/2) bytes, packed NF4 codes                  */

@@ -75,6 +75,9 @@ def _special_tensors():
     t["all_zero_4096"] = np.zeros(4096, np.float32)
     mags = np.exp(rng.uniform(np.log(1e-30), np.log(1e30), 64 * 300)).astype(np.float32)
     t["mixed_magnitudes"] = (mags * np.sign(rng.standard_normal(mags.size))).astype(np.float32)
+    # scales above 2^100 up to 1e38 (the reconstructed scales stay finite)
+    big = np.exp(rng.uniform(np.log(1e31), np.log(1e38), 64 * 64)).astype(np.float32)
+    t["huge_magnitudes"] = (big * np.sign(rng.standard_normal(big.size))).astype(np.float32)
     sub = (rng.standard_normal(64 * 40) * 1e-40).astype(np.float32)   # subnormal blocks
     t["subnormal"] = sub
     t["outliers_300k"] = si.weight(300, 1000, 7, True).ravel()

@@ -73,6 +73,11 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert L.nf4_quantize(0x100, ctypes.byref(st), 0x10000, 8, 0x5000, None) == qn.NF4_EINVAL
     # bad output dtype for the decoder
     assert L.nf4_dequantize(ctypes.byref(st), 0x100, 7, None, None) == qn.NF4_EINVAL
+    # state buffers moved as words: misaligned codes / second-level codes / scales
+    for bad_state in (qn._State(64, 0x1004, 0x2000, 0x3000, 0x4000), qn._State(64, 0x1000, 0x2001, 0x3000, 0x4000),
+                      qn._State(64, 0x1000, 0x2000, 0x3002, 0x4000)):
+        assert L.nf4_quantize(0x100, ctypes.byref(bad_state), 0x10000, 1 << 20, 0x5000, None) == qn.NF4_EINVAL
+        assert L.nf4_dequantize(ctypes.byref(bad_state), 0x100, qn.NF4_OUT_F32, None, None) == qn.NF4_EINVAL
     # layer: numel mismatch, N % 64, NULL output
     st2 = qn._State(64 * 64, 0x1000, 0x2000, 0x3000, 0x4000)
     args = (0x100, ctypes.byref(st2), 0x200, 0x300, ctypes.c_float(1.0), 0x400, 0x500, 0x10000, 1 << 30, None)
