@@ -77,6 +77,76 @@ __device__ __forceinline__ void transpose8x8_bf16(const uint4 (&in)[8], uint4 (&
 // Nibble of column t (0..7) in a code word: byte t/2, high nibble for even t.
 __device__ __forceinline__ uint32_t nib(uint32_t w, int t) { return (w >> (8 * (t >> 1) + ((t & 1) ? 0 : 4))) & 15u; }
 
+// Split-K partial of Z = X A for M <= 16 over rows [split * 4 rpw, +4 rpw),
+// each wave over the rows its GEMV counterpart streams.  A is read row-major
+// (8 rows of 8 columns per lane, transposed in registers), X rows feed the
+// MFMA as the 16-row operand; lane (q, g) accumulates columns j0 + 8q .. +7.
+// The four waves are added in LDS in a fixed order: (w0 + w2) + (w1 + w3).
+// zpart[split][m][j], fp32.  red: 16 KB of LDS.
+__device__ void gemv_zpart(const uint16_t* __restrict__ X, int64_t M, int64_t K, int64_t rpw,
+                           const uint16_t* __restrict__ A, int64_t r, float* __restrict__ zpart, int64_t split,
+                           float* red) {
+  const int t = threadIdx.x, lane = t & 63, q = lane & 15, g = lane >> 4;
+  const int wave = t >> 6;
+  const int64_t kw0 = (split * kGvWaves + wave) * rpw;
+  const int64_t kend = min(K, kw0 + rpw);
+  const Rsrc rx = make_rsrc(X, M * K * 2), ra = make_rsrc(A, K * r * 2);
+  for (int64_t j0 = 0; j0 < r; j0 += 128) {
+    const int64_t j = j0 + 8 * q;
+    f32x4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = f32x4{0, 0, 0, 0};
+    for (int64_t kb = kw0; kb < kend; kb += 32) {
+      const int64_t k = kb + 8 * g;
+      const uint4 xv = ld_b128(rx, (q < M && k < kend) ? static_cast<uint32_t>((q * K + k) * 2) : kMasked);
+      uint4 rows8[8], cols8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        rows8[i] = ld_b128(ra, (k + i < kend && j < r) ? static_cast<uint32_t>(((k + i) * r + j) * 2) : kMasked);
+      transpose8x8_bf16(rows8, cols8);
+#pragma unroll
+      for (int tc = 0; tc < 8; ++tc)
+        acc[tc] = mfma16x16x32(__builtin_bit_cast(bf16x8, xv), __builtin_bit_cast(bf16x8, cols8[tc]), acc[tc]);
+    }
+    // lane holds Z[m = 4g + e][j + tc]
+    __syncthreads();
+    if (wave >= 2) {
+#pragma unroll
+      for (int tc = 0; tc < 8; ++tc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[((wave - 2) * 32 + tc * 4 + e) * 64 + lane] = acc[tc][e];
+    }
+    __syncthreads();
+    if (wave < 2) {
+#pragma unroll
+      for (int tc = 0; tc < 8; ++tc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[tc][e] += red[(wave * 32 + tc * 4 + e) * 64 + lane];
+    }
+    __syncthreads();
+    if (wave == 1) {
+#pragma unroll
+      for (int tc = 0; tc < 8; ++tc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[(tc * 4 + e) * 64 + lane] = acc[tc][e];
+    }
+    __syncthreads();
+    if (wave == 0 && j < r) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t m = 4 * g + e;
+        if (m >= M) continue;
+        float v[8];
+#pragma unroll
+        for (int tc = 0; tc < 8; ++tc) v[tc] = acc[tc][e] + red[(tc * 4 + e) * 64 + lane];
+        float* o = zpart + (split * M + m) * r + j;
+        *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    }
+  }
+}
+
 struct GvStep {
   uint2 w[8];   // code words of rows 8g..8g+7 (16 columns each)
   uint4 x;      // activation fragment
@@ -92,11 +162,19 @@ struct GvStep {
 // per-weight multiply or conversion is needed; column t of the lane feeds the
 // MFMA of tile t.  part[split][m][n] = sum of the 4 waves (fixed order).
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemv_kernel(const uint16_t* __restrict__ X, int64_t M, NF4View W, int64_t K,
-                                                   int64_t N, int64_t rpw, int64_t slabs, float* __restrict__ part) {
+                                                   int64_t N, int64_t rpw, int64_t slabs, float* __restrict__ part,
+                                                   const uint16_t* __restrict__ A, int64_t r,
+                                                   float* __restrict__ zpart) {
   __shared__ float q2t[256];
   __shared__ __attribute__((aligned(16))) char tabs[kGvWaves * 2 * kGvTabBytes];
   const int t = threadIdx.x, lane = t & 63, q = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int64_t splits = (K + kGvWaves * rpw - 1) / (kGvWaves * rpw);
+  if (blockIdx.x >= slabs * splits) {
+    // the last `splits` workgroups: Z partials over the same row ranges
+    gemv_zpart(X, M, K, rpw, A, r, zpart, blockIdx.x - slabs * splits, reinterpret_cast<float*>(tabs));
+    return;
+  }
   q2t[t] = q2_value(t - 128);
   const int64_t slab = blockIdx.x % slabs, split = blockIdx.x / slabs;
   const int64_t n0 = slab * kGvCols;
@@ -244,21 +322,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // Y = sum_s part[s] + c Z B for M <= 16: one wave per 128 columns; lane
 // (q, g) holds rows 4g..4g+3 of columns n0+8q..+7; the LoRA product runs on
-// MFMA with B transposed in registers.
+// MFMA with B transposed in registers.  Z = RNE_bf16(sum_s zpart[s]) (fixed
+// order) is formed by every wave for the values it needs and written out by
+// wave 0.
 __global__ __launch_bounds__(64) void gemv_finish_kernel(const float* __restrict__ part, int splits, int64_t M,
-                                                         int64_t N, const uint16_t* __restrict__ Z,
-                                                         const uint16_t* __restrict__ B, int64_t r, float c,
-                                                         uint16_t* __restrict__ Y) {
+                                                         int64_t N, const float* __restrict__ zpart,
+                                                         uint16_t* __restrict__ Z, const uint16_t* __restrict__ B,
+                                                         int64_t r, float c, uint16_t* __restrict__ Y) {
   const int lane = threadIdx.x, q = lane & 15, g = lane >> 4;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 128, n = n0 + 8 * q;
   const bool n_ok = n < N;
-  const Rsrc rz = make_rsrc(Z, M * r * 2), rb = make_rsrc(B, r * N * 2);
+  const Rsrc rb = make_rsrc(B, r * N * 2);
   f32x4 accl[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) accl[i] = f32x4{0, 0, 0, 0};
   for (int64_t j0 = 0; j0 < r; j0 += 32) {
     const int64_t jb = j0 + 8 * g;
-    const uint4 zv = ld_b128(rz, (q < M && jb < r) ? static_cast<uint32_t>((q * r + jb) * 2) : kMasked);
+    uint4 zv = make_uint4(0, 0, 0, 0);
+    if (q < M && jb < r) {
+      float zs[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) zs[i] = 0.0f;
+      for (int s = 0; s < splits; ++s) {
+        const float* src = zpart + (s * M + q) * r + jb;
+        const float4 a = *reinterpret_cast<const float4*>(src), b = *reinterpret_cast<const float4*>(src + 4);
+        zs[0] += a.x; zs[1] += a.y; zs[2] += a.z; zs[3] += a.w; zs[4] += b.x; zs[5] += b.y; zs[6] += b.z; zs[7] += b.w;
+      }
+      zv = make_uint4(pack_bf16x2(zs[0], zs[1]), pack_bf16x2(zs[2], zs[3]), pack_bf16x2(zs[4], zs[5]),
+                      pack_bf16x2(zs[6], zs[7]));
+      if (blockIdx.x == 0) *reinterpret_cast<uint4*>(Z + q * r + jb) = zv;
+    }
     uint4 rows8[8], cols8[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -291,7 +384,7 @@ __global__ __launch_bounds__(64) void gemv_finish_kernel(const float* __restrict
 
 }  // namespace
 
-void plan_gemv(int64_t M, int64_t K, int64_t N, SkinnyPlan* p_) {
+void plan_gemv(int64_t M, int64_t K, int64_t N, int64_t r, SkinnyPlan* p_) {
   SkinnyPlan& p = *p_;
   // 4 waves x rows_per_wave rows per workgroup, ~1400 waves in total
   const int64_t slabs = cdiv(N, kGvCols);
@@ -301,20 +394,23 @@ void plan_gemv(int64_t M, int64_t K, int64_t N, SkinnyPlan* p_) {
   p.gv_rows_per_wave = rpw;
   p.gv_splits = cdiv(K, rpw * kGvWaves);
   p.gv_part = round_up(p.gv_splits * M * N * 4, 256);
+  p.gv_zpart = round_up(p.gv_splits * M * r * 4, 256);
 }
 
-hipError_t launch_gemv(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W, const uint16_t* Z,
-                       const uint16_t* B, float c, uint16_t* Y, const SkinnyPlan& p, void* part_ws,
+hipError_t launch_gemv(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W, const uint16_t* A,
+                       const uint16_t* B, float c, uint16_t* Y, uint16_t* Z, const SkinnyPlan& p, void* part_ws,
                        hipStream_t stream) {
   const int64_t slabs = cdiv(N, kGvCols);
   float* part = static_cast<float*>(part_ws);
+  float* zpart = reinterpret_cast<float*>(static_cast<char*>(part_ws) + p.gv_part);
   Timer tm(QK_FWD_GEMV, stream);
-  hipLaunchKernelGGL(gemv_kernel, dim3(static_cast<unsigned>(slabs * p.gv_splits)), dim3(kGvWaves * 64), 0, stream, X,
-                     M, W, K, N, p.gv_rows_per_wave, slabs, part);
+  hipLaunchKernelGGL(gemv_kernel, dim3(static_cast<unsigned>((slabs + 1) * p.gv_splits)), dim3(kGvWaves * 64), 0,
+                     stream, X, M, W, K, N, p.gv_rows_per_wave, slabs, part, A, r, zpart);
   tm.stop();
   Timer te(QK_REDUCE, stream);
-  hipLaunchKernelGGL(gemv_finish_kernel, dim3(static_cast<unsigned>(cdiv(N, 128))), dim3(64), 0, stream, part,
-                     static_cast<int>(p.gv_splits), M, N, Z, B, r, c, Y);
+  hipLaunchKernelGGL(gemv_finish_kernel, dim3(static_cast<unsigned>(cdiv(N, 128))), dim3(64), 0, stream,
+                     static_cast<const float*>(part), static_cast<int>(p.gv_splits), M, N,
+                     static_cast<const float*>(zpart), Z, B, r, c, Y);
   te.stop();
   return hipGetLastError();
 }

@@ -51,9 +51,9 @@ int64_t bwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r);
 struct SkinnyPlan {
   int64_t z_splits, z_per, dz_splits, dz_per, da_splits, da_per, db_splits, db_per;
   int64_t at_bytes, z_part, dz_part, da_part, db_part;
-  int64_t gv_rows_per_wave, gv_splits, gv_part;
+  int64_t gv_rows_per_wave, gv_splits, gv_part, gv_zpart;
 };
-void plan_gemv(int64_t M, int64_t K, int64_t N, SkinnyPlan* p);
+void plan_gemv(int64_t M, int64_t K, int64_t N, int64_t r, SkinnyPlan* p);
 SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N, int64_t r);
 
 // Z = X A; with cbt != nullptr the same launch also writes cbt = RNE_bf16(c B)ᵀ
@@ -61,8 +61,11 @@ SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N, int64_t r);
 hipError_t launch_lora_down(int64_t M, int64_t K, int64_t r, const uint16_t* X, const uint16_t* A, uint16_t* Z,
                             const SkinnyPlan& p, void* at_ws, void* part_ws, hipStream_t stream, int64_t N = 0,
                             const uint16_t* B = nullptr, float c = 1.0f, uint16_t* cbt = nullptr);
-hipError_t launch_gemv(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W, const uint16_t* Z,
-                       const uint16_t* B, float c, uint16_t* Y, const SkinnyPlan& p, void* part_ws,
+// Small-M forward (M <= 16) in two launches: the split-K partials of X Ŵ and
+// of Z = X A (extra workgroups of the same launch), then their fixed-order
+// sums, Z (written out) and Y = X Ŵ + c Z B.  part_ws: gv_part + gv_zpart.
+hipError_t launch_gemv(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W, const uint16_t* A,
+                       const uint16_t* B, float c, uint16_t* Y, uint16_t* Z, const SkinnyPlan& p, void* part_ws,
                        hipStream_t stream);
 hipError_t launch_dz(int64_t M, int64_t N, int64_t r, const uint16_t* G, const uint16_t* B, float c, uint16_t* dZ,
                      const SkinnyPlan& p, void* part_ws, hipStream_t stream);

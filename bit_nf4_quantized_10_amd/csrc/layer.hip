@@ -1,8 +1,9 @@
 // Orchestration of the layer entry points: workspace carving and the kernel
 // sequence of the forward and backward passes.
-//   forward : Aᵀ <- A; Z = X A (split rows/K, fixed-order reduce);
-//             M <= 16: dequant-GEMV partials, then sum + c Z B;
-//             else   : (c B)ᵀ in bf16 (same launch as Aᵀ), then
+//   forward : M <= 16: dequant-GEMV and Z = X A split-K partials (one
+//                      launch), then their sums and c Z B;
+//             else   : Aᵀ and (c B)ᵀ in bf16 (one launch); Z = X A (split
+//                      rows/K, fixed-order reduce); then
 //                      M < 512: fused dequant-GEMM with the LoRA extension;
 //                      M >= 512: Ŵᵀ dequantized to bf16, dense GEMM.
 //   backward: dZ = c G Bᵀ; dA = Xᵀ dZ; dB = c Zᵀ G; dX = G Ŵᵀ + dZ Aᵀ
@@ -29,7 +30,8 @@ int64_t cbt_bytes(int64_t M, int64_t N, int64_t r) { return M > 16 ? align256(N 
 
 int64_t fwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r) {
   const SkinnyPlan p = plan_skinny(M, K, N, r);
-  return p.at_bytes + p.z_part + (M <= 16 ? p.gv_part : 0) + cbt_bytes(M, N, r) + dense_bytes(M, K, N);
+  if (M <= 16) return p.gv_part + p.gv_zpart;
+  return p.at_bytes + p.z_part + cbt_bytes(M, N, r) + dense_bytes(M, K, N);
 }
 
 int64_t bwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r) {
@@ -42,14 +44,11 @@ hipError_t launch_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
   const SkinnyPlan p = plan_skinny(M, K, N, r);
   char* base = static_cast<char*>(ws);
   char* after_z = base + p.at_bytes + p.z_part;
-  if (M <= 16) {
-    hipError_t e = launch_lora_down(M, K, r, X, A, Z, p, base, base + p.at_bytes, stream);
-    if (e != hipSuccess) return e;
-    return launch_gemv(M, K, N, r, X, W, Z, B, c, Y, p, after_z, stream);
-  }
+  hipError_t e;
+  if (M <= 16) return launch_gemv(M, K, N, r, X, W, A, B, c, Y, Z, p, base, stream);
   uint16_t* cbt = reinterpret_cast<uint16_t*>(after_z);
-  hipError_t e = launch_lora_down(M, K, r, X, A, Z, p, base, base + p.at_bytes, stream, N, B, c, cbt);
-  if (e != hipSuccess) return e;
+  if ((e = launch_lora_down(M, K, r, X, A, Z, p, base, base + p.at_bytes, stream, N, B, c, cbt)) != hipSuccess)
+    return e;
   if (use_dense(M)) {
     uint16_t* wt = reinterpret_cast<uint16_t*>(after_z + cbt_bytes(M, N, r));
     if ((e = launch_dequant_bf16(W.codes, W.qabsmax, W.absmax2, W.offset, K, N, true, wt, stream)) != hipSuccess) return e;
@@ -67,19 +66,17 @@ hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
   uint16_t* dz16 = reinterpret_cast<uint16_t*>(base + p.dz_part);
   void* da_part = base + p.dz_part + align256(M * r * 2);
   void* db_part = static_cast<char*>(da_part) + p.da_part;
-  hipError_t e = launch_dz(M, N, r, G, B, c, dz16, p, dz_part, stream);
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if ((e = launch_dz(M, N, r, G, B, c, dz16, p, dz_part, stream)) != hipSuccess) return e;
   if ((e = launch_colsums(M, K, N, r, X, G, Z, dz16, c, dA, dB, p, da_part, db_part, stream)) != hipSuccess) return e;
-  if (dX != nullptr) {
-    if (use_dense(M)) {
-      uint16_t* wd = reinterpret_cast<uint16_t*>(static_cast<char*>(db_part) + p.db_part);
-      if ((e = launch_dequant_bf16(W.codes, W.qabsmax, W.absmax2, W.offset, K, N, false, wd, stream)) != hipSuccess)
-        return e;
-      return launch_dx_dense(M, K, N, r, G, wd, dz16, A, dX, stream);
-    }
-    return launch_dx_big(M, K, N, r, G, W, dz16, A, dX, stream);
+  if (dX == nullptr) return hipGetLastError();
+  if (use_dense(M)) {
+    uint16_t* wd = reinterpret_cast<uint16_t*>(static_cast<char*>(db_part) + p.db_part);
+    if ((e = launch_dequant_bf16(W.codes, W.qabsmax, W.absmax2, W.offset, K, N, false, wd, stream)) != hipSuccess)
+      return e;
+    return launch_dx_dense(M, K, N, r, G, wd, dz16, A, dX, stream);
   }
-  return hipGetLastError();
+  return launch_dx_big(M, K, N, r, G, W, dz16, A, dX, stream);
 }
 
 }  // namespace qn

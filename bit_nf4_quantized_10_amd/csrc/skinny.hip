@@ -427,7 +427,7 @@ SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N, int64_t r) {
   p.dz_part = round_up(p.dz_splits * M * r * 4, 256);
   p.da_part = round_up(p.da_splits * K * r * 4, 256);
   p.db_part = round_up(p.db_splits * N * r * 4, 256);
-  plan_gemv(M, K, N, &p);
+  plan_gemv(M, K, N, r, &p);
   return p;
 }
 

@@ -323,6 +323,39 @@ def test_frozen_state_unchanged_and_deterministic():
     assert outs[0] == outs[1]
 
 
+@pytest.mark.parametrize("M", [8, 64, 600])   # dequant-GEMV, fused kernel, dequantize-then-GEMM
+def test_layer_on_user_stream_sees_prior_work(M):
+    """Every launch of a call goes on the caller's stream: it starts after
+    work enqueued earlier there (a long product, then the overwrite of X and
+    G) and finishes before later work on it.  The outputs must equal a plain
+    run on the new inputs."""
+    import torch
+    K, N, r = 512, 768, 16
+    case = _layer_case(M, K, N, r, 0.5, seed=21)
+    say(f"layer on a user stream after pending work, M={M}")
+    state, status = _quantize(case["W"])
+    assert status == 0
+    X, A, B, G = (dev_bf16(case[k]) for k in ("Xb", "Ab", "Bb", "Gb"))
+    Y0, Z0 = qn.qlora_linear_fwd(X, state, A, B, 0.5, K, N)
+    dX0, dA0, dB0 = qn.qlora_linear_bwd(G, X, Z0, state, A, B, 0.5, K, N)
+    torch.cuda.synchronize()
+    ref = [host(t).tobytes() for t in (Y0, Z0, dX0, dA0, dB0)]
+    Xs, Gs = torch.zeros_like(X), torch.zeros_like(G)
+    big = torch.randn(4096, 4096, device="cuda")
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for _ in range(4):
+            big = big @ big * 1e-2          # keeps the stream busy for a while
+        Xs.copy_(X)
+        Gs.copy_(G)
+        Y, Z = qn.qlora_linear_fwd(Xs, state, A, B, 0.5, K, N, stream=s)
+        dX, dA, dB = qn.qlora_linear_bwd(Gs, Xs, Z, state, A, B, 0.5, K, N, stream=s)
+        outs = [t.clone() for t in (Y, Z, dX, dA, dB)]
+    s.synchronize()
+    assert [host(t).tobytes() for t in outs] == ref
+
+
 # ------------------------------------------------------- full-size workloads
 def _full_size_check(name, matrix=0, M=None, row_samples=48, col_groups=3):
     d = si.layer_inputs(name, matrix=matrix, M=M)
