@@ -285,6 +285,25 @@ def bench_components(torch, qn, si, dev, sets, outs, qws, status):
         "write_GBps": round(big.numel() * 4 / (wr * 1e-3) / 1e9, 1),
         "how": "torch sum / fill of a 1 GiB fp32 tensor, cache flushed before each call"}
     del big, out
+    # the vendor library's plain bf16 GEMM of the same base shape on this
+    # device (torch.matmul -> hipBLASLt), as context for the MFMA fraction
+    Mv, Kv, Nv = 4096, 4096, 4096
+    xa = torch.randn(Mv, Kv, device=dev).to(torch.bfloat16)
+    wb = torch.randn(Kv, Nv, device=dev).to(torch.bfloat16)
+    yv = torch.empty(Mv, Nv, dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        torch.matmul(xa, wb, out=yv)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        torch.matmul(xa, wb, out=yv)
+    e1.record()
+    torch.cuda.synchronize()
+    vms = e0.elapsed_time(e1) / 20
+    res["vendor_gemm_bf16_4096"] = {
+        "ms": round(vms, 4), "TFLOPs": round(2 * Mv * Kv * Nv / (vms * 1e-3) / 1e12, 1),
+        "how": "torch.matmul of 4096x4096 by 4096x4096 bf16 (hipBLASLt), 20 back-to-back calls"}
+    del xa, wb, yv
     return res
 
 

@@ -28,14 +28,16 @@ bool state_ok(const nf4_state_t* s) {
 }
 
 // Kernels address operands with 32-bit buffer offsets and mark masked lanes
-// with offset 2^31; keeping every bf16 operand (X, G, Y, dX and the
-// dequantized weight) under 1 GiB keeps all such offsets below 2^32.
+// with offset 2^31; keeping every bf16 operand (X, G, Y, dX, A, B and the
+// dequantized weight) under 1 GiB, and so every fp32 M x N buffer under
+// 2 GiB, keeps all real offsets below 2^31.
 constexpr int64_t kMaxOperandElems = int64_t(1) << 29;
 
 bool layer_shape_ok(int64_t M, int64_t K, int64_t N, int64_t r) {
   return M >= 1 && K >= 1 && N >= 1 && r >= 1 && N % NF4_BLOCK1 == 0 && K % 8 == 0 && r % 8 == 0 &&
          r <= 256 && M <= (int64_t(1) << 20) && K <= (int64_t(1) << 24) && N <= (int64_t(1) << 24) &&
-         M * K < kMaxOperandElems && M * N < kMaxOperandElems && K * N < kMaxOperandElems;
+         M * K < kMaxOperandElems && M * N < kMaxOperandElems && K * N < kMaxOperandElems &&
+         K * r < kMaxOperandElems && r * N < kMaxOperandElems;
 }
 
 // ---------------------------------------------------------------- timers

@@ -320,66 +320,92 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// Y = sum_s part[s] + c Z B for M <= 16: one wave per 128 columns; lane
-// (q, g) holds rows 4g..4g+3 of columns n0+8q..+7; the LoRA product runs on
-// MFMA with B transposed in registers.  Z = RNE_bf16(sum_s zpart[s]) (fixed
-// order) is formed by every wave for the values it needs and written out by
-// wave 0.
+// Y = sum_s part[s] + c Z B for M <= 16: one wave per 128 columns and row
+// phase e (blockIdx.y); lane (q, g) owns columns n0+8q..+7 and row 4g+e.
+// The LoRA product runs on MFMA with B transposed in registers (every phase
+// computes it; only row 4g+e is kept).  Z = RNE_bf16(sum_s zpart[s]) in a
+// fixed order; workgroup (0, 0) writes it.  The split loops request 8
+// partials at a time before adding them in order.
 __global__ __launch_bounds__(64) void gemv_finish_kernel(const float* __restrict__ part, int splits, int64_t M,
                                                          int64_t N, const float* __restrict__ zpart,
                                                          uint16_t* __restrict__ Z, const uint16_t* __restrict__ B,
                                                          int64_t r, float c, uint16_t* __restrict__ Y) {
   const int lane = threadIdx.x, q = lane & 15, g = lane >> 4;
+  const int e = blockIdx.y;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 128, n = n0 + 8 * q;
   const bool n_ok = n < N;
   const Rsrc rb = make_rsrc(B, r * N * 2);
+  const Rsrc rzp = make_rsrc(zpart, static_cast<int64_t>(splits) * M * r * 4);
+  const Rsrc rp = make_rsrc(part, static_cast<int64_t>(splits) * M * N * 4);
   f32x4 accl[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) accl[i] = f32x4{0, 0, 0, 0};
   for (int64_t j0 = 0; j0 < r; j0 += 32) {
     const int64_t jb = j0 + 8 * g;
-    uint4 zv = make_uint4(0, 0, 0, 0);
-    if (q < M && jb < r) {
-      float zs[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) zs[i] = 0.0f;
-      for (int s = 0; s < splits; ++s) {
-        const float* src = zpart + (s * M + q) * r + jb;
-        const float4 a = *reinterpret_cast<const float4*>(src), b = *reinterpret_cast<const float4*>(src + 4);
-        zs[0] += a.x; zs[1] += a.y; zs[2] += a.z; zs[3] += a.w; zs[4] += b.x; zs[5] += b.y; zs[6] += b.z; zs[7] += b.w;
-      }
-      zv = make_uint4(pack_bf16x2(zs[0], zs[1]), pack_bf16x2(zs[2], zs[3]), pack_bf16x2(zs[4], zs[5]),
-                      pack_bf16x2(zs[6], zs[7]));
-      if (blockIdx.x == 0) *reinterpret_cast<uint4*>(Z + q * r + jb) = zv;
-    }
+    const bool zok = q < M && jb < r;
     uint4 rows8[8], cols8[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       rows8[i] = ld_b128(rb, (jb + i < r && n_ok) ? static_cast<uint32_t>(((jb + i) * N + n) * 2) : kMasked);
+    float zs[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) zs[i] = 0.0f;
+    for (int s0 = 0; s0 < splits; s0 += 8) {
+      uint4 za[8], zb[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t off = (zok && s0 + k < splits) ? static_cast<uint32_t>((((s0 + k) * M + q) * r + jb) * 4) : kMasked;
+        za[k] = ld_b128(rzp, off);
+        zb[k] = ld_b128(rzp, off == kMasked ? kMasked : off + 16);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (s0 + k >= splits) break;
+        zs[0] += __builtin_bit_cast(float, za[k].x); zs[1] += __builtin_bit_cast(float, za[k].y);
+        zs[2] += __builtin_bit_cast(float, za[k].z); zs[3] += __builtin_bit_cast(float, za[k].w);
+        zs[4] += __builtin_bit_cast(float, zb[k].x); zs[5] += __builtin_bit_cast(float, zb[k].y);
+        zs[6] += __builtin_bit_cast(float, zb[k].z); zs[7] += __builtin_bit_cast(float, zb[k].w);
+      }
+    }
+    uint4 zv = make_uint4(0, 0, 0, 0);
+    if (zok) {
+      zv = make_uint4(pack_bf16x2(zs[0], zs[1]), pack_bf16x2(zs[2], zs[3]), pack_bf16x2(zs[4], zs[5]),
+                      pack_bf16x2(zs[6], zs[7]));
+      if (blockIdx.x == 0 && e == 0) *reinterpret_cast<uint4*>(Z + q * r + jb) = zv;
+    }
     transpose8x8_bf16(rows8, cols8);
 #pragma unroll
     for (int tc = 0; tc < 8; ++tc)
       accl[tc] = mfma16x16x32(__builtin_bit_cast(bf16x8, zv), __builtin_bit_cast(bf16x8, cols8[tc]), accl[tc]);
   }
+  const int64_t m = 4 * g + e;
+  if (m >= M || !n_ok) return;
+  float v[8];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int64_t m = 4 * g + e;
-    if (m >= M || !n_ok) continue;
-    float v[8];
+  for (int tc = 0; tc < 8; ++tc) v[tc] = 0.0f;
+  for (int s0 = 0; s0 < splits; s0 += 8) {
+    uint4 pa[8], pb[8];
 #pragma unroll
-    for (int tc = 0; tc < 8; ++tc) v[tc] = 0.0f;
-    for (int s = 0; s < splits; ++s) {
-      const float* src = part + (s * M + m) * N + n;
-      const float4 a = *reinterpret_cast<const float4*>(src), b = *reinterpret_cast<const float4*>(src + 4);
-      v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w; v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t off = (s0 + k < splits) ? static_cast<uint32_t>((((s0 + k) * M + m) * N + n) * 4) : kMasked;
+      pa[k] = ld_b128(rp, off);
+      pb[k] = ld_b128(rp, off == kMasked ? kMasked : off + 16);
     }
-    uint4 o;
-    o.x = pack_bf16x2(v[0] + c * accl[0][e], v[1] + c * accl[1][e]);
-    o.y = pack_bf16x2(v[2] + c * accl[2][e], v[3] + c * accl[3][e]);
-    o.z = pack_bf16x2(v[4] + c * accl[4][e], v[5] + c * accl[5][e]);
-    o.w = pack_bf16x2(v[6] + c * accl[6][e], v[7] + c * accl[7][e]);
-    *reinterpret_cast<uint4*>(Y + m * N + n) = o;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (s0 + k >= splits) break;
+      v[0] += __builtin_bit_cast(float, pa[k].x); v[1] += __builtin_bit_cast(float, pa[k].y);
+      v[2] += __builtin_bit_cast(float, pa[k].z); v[3] += __builtin_bit_cast(float, pa[k].w);
+      v[4] += __builtin_bit_cast(float, pb[k].x); v[5] += __builtin_bit_cast(float, pb[k].y);
+      v[6] += __builtin_bit_cast(float, pb[k].z); v[7] += __builtin_bit_cast(float, pb[k].w);
+    }
   }
+  uint4 o;
+  o.x = pack_bf16x2(v[0] + c * accl[0][e], v[1] + c * accl[1][e]);
+  o.y = pack_bf16x2(v[2] + c * accl[2][e], v[3] + c * accl[3][e]);
+  o.z = pack_bf16x2(v[4] + c * accl[4][e], v[5] + c * accl[5][e]);
+  o.w = pack_bf16x2(v[6] + c * accl[6][e], v[7] + c * accl[7][e]);
+  *reinterpret_cast<uint4*>(Y + m * N + n) = o;
 }
 
 }  // namespace
@@ -408,7 +434,8 @@ hipError_t launch_gemv(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_
                      stream, X, M, W, K, N, p.gv_rows_per_wave, slabs, part, A, r, zpart);
   tm.stop();
   Timer te(QK_REDUCE, stream);
-  hipLaunchKernelGGL(gemv_finish_kernel, dim3(static_cast<unsigned>(cdiv(N, 128))), dim3(64), 0, stream,
+  const unsigned phases = static_cast<unsigned>(M < 4 ? M : 4);   // rows 4g + e, e < phases
+  hipLaunchKernelGGL(gemv_finish_kernel, dim3(static_cast<unsigned>(cdiv(N, 128)), phases), dim3(64), 0, stream,
                      static_cast<const float*>(part), static_cast<int>(p.gv_splits), M, N,
                      static_cast<const float*>(zpart), Z, B, r, c, Y);
   te.stop();

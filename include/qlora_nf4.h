@@ -107,9 +107,9 @@ int qlora_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r,
  * bf16, B: r x N bf16, c = alpha / r.  Ŵ is exactly the bf16 weight that
  * nf4_dequantize(W, NF4_OUT_BF16) returns.  Z is written for the backward
  * pass.  Requirements: M, K, N, r >= 1, N % 64 == 0, K % 8 == 0, r % 8 == 0,
- * r <= 256, M <= 2^20, K, N <= 2^24, each of M*K, M*N and K*N below 2^29
- * elements (every bf16 operand under 1 GiB, so that 32-bit buffer offsets
- * suffice), all pointers 16-byte aligned, workspace >= fwd_bytes.  The
+ * r <= 256, M <= 2^20, K, N <= 2^24, each of M*K, M*N, K*N, K*r and r*N
+ * below 2^29 elements (every bf16 operand under 1 GiB, so that 32-bit
+ * buffer offsets suffice), all pointers 16-byte aligned, workspace >= fwd_bytes.  The
  * state is only read.  M <= 16 runs the memory-bound dequant-GEMV kernels;
  * M >= 512 dequantizes Ŵ to bf16 in the workspace and runs a dense GEMM. */
 int qlora_linear_fwd(int64_t M, int64_t K, int64_t N, int64_t r,

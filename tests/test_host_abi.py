@@ -49,7 +49,9 @@ def test_nf4_sizes_rejects_empty():
                                    (4, 64, 64, 264), (4, 0, 64, 8),
                                    (1 << 20, 1 << 9, 64, 8),       # X of 2^29 elements (1 GiB)
                                    (4, 1 << 15, 1 << 14, 8),       # weight of 2^29 elements
-                                   (1 << 16, 64, 1 << 13, 8)])     # Y of 2^29 elements
+                                   (1 << 16, 64, 1 << 13, 8),      # Y of 2^29 elements
+                                   (1, 8, 1 << 21, 256),           # B (r x N) of 2^29 elements
+                                   (1, 1 << 21, 64, 256)])         # A (K x r) of 2^29 elements
 def test_layer_shapes_rejected(shape):
     with pytest.raises(qn.NF4Error):
         qn.qlora_workspace_bytes(*shape)
