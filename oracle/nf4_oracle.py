@@ -58,6 +58,10 @@ Parity status of each function (see the tests under tests/):
   nf4_codebook, first_level_absmax, nf4_codes, pack_nibbles, unpack_nibbles,
   storage_bits, layer_forward, layer_backward, bf16_round: pinned to printed
   page values, exact rational brute force, closed forms or finite differences.
+  merge: pinned by the P1 merge example ([0.53, -0.44] -> codes [15, 1],
+  -0.368982, output -0.207964) and exact special cases (c = 0, B = 0,
+  power-of-two rank-1 increments).  sgd_step: pinned by the P1 update of the
+  worked layer example (a, b after one step; the loss falls).
   tree_offset: pinned by exactly-summable inputs and the fsum error bound.
   linear_absmax_table / linear_absmax_codes: pinned by the P2 §6 example,
   exact rational brute force and special cases.  The CHOICE of this codebook
@@ -77,7 +81,7 @@ __all__ = [
     "double_quantize", "reconstruct_absmax", "quantize", "dequantize",
     "reconstruct_weights",
     "bf16_round", "layer_forward", "layer_backward", "storage_bits",
-    "counts",
+    "counts", "merge", "sgd_step",
 ]
 
 # [P1] "从 NF4 索引打包成字节": the sixteen reconstruction values, ascending.
@@ -320,6 +324,37 @@ def layer_backward(G, X, W_hat, A, B, c):
     dB = float(c) * (Z.T @ G)
     dX = G @ W_hat.T + dZ @ A.T
     return dX, dA, dB, dZ
+
+
+def merge(state: dict, A, B, c, K: int, N: int) -> np.ndarray:
+    """Merged fp32 weight for re-export ([P1] "Merge 后还是不是训练时的函数":
+    the trained function is Ŵ plus the adapter, merged in high precision,
+    then re-quantized as a new step).  Reading: Ŵ is the fp32 reconstruction
+    (R5); the increment c A B is accumulated in float64, t = 0 .. r-1 in
+    order (each product of two fp32 or bf16 values is exact in float64, one
+    rounding per addition), scaled by c in float64, added to ŵ in float64
+    and rounded once to fp32.  A: K x r, B: r x N (fp32 or bf16 values)."""
+    w = dequantize(state, "fp32").astype(np.float64).reshape(K, N)
+    A = np.asarray(A, dtype=np.float64).reshape(K, -1)
+    B = np.asarray(B, dtype=np.float64).reshape(A.shape[1], N)
+    acc = np.zeros((K, N), dtype=np.float64)
+    for t in range(A.shape[1]):
+        acc = acc + np.outer(A[:, t], B[t])
+    return (w + np.float64(c) * acc).astype(np.float32)
+
+
+def sgd_step(param, grad, lr, master=None):
+    """One plain SGD update of an adapter tensor ([P1] "一次完整反向与有限差分":
+    only the adapter is updated, v <- v - lr * g, and the loss must fall).
+    Reading: the step is taken in fp32, p' = fl32(p - fl32(lr * g)), on the
+    fp32 master copy when one is kept (else on the bf16 value read as fp32);
+    the bf16 parameter is RNE_bf16(p').  Returns (bf16 values as fp32,
+    the new fp32 master or None)."""
+    g = np.asarray(grad, dtype=np.float32)
+    base = np.asarray(master if master is not None else param, dtype=np.float32)
+    step = (np.float32(lr) * g).astype(np.float32)
+    new = (base - step).astype(np.float32)
+    return bf16_round(new), (new if master is not None else None)
 
 
 def storage_bits(P: int, double_quant: bool = True) -> int:

@@ -111,6 +111,83 @@ def test_merge_requantize_example():
     assert abs(y - float(g["output_approx"])) < tol
 
 
+def test_merge_page_example():
+    """The merge of the worked adapter: increment [0.03, 0.06], merged
+    [0.53, -0.44] (within the fp32 rounding of the fp32 adapter values), the
+    output still -0.35; re-quantized: codes [15, 1], -0.368982, -0.207964."""
+    g = load("p1_merge_increment.txt")
+    st = o.quantize(np.array(floats(g["weight"]), np.float32))
+    A = np.array(floats(g["A"]), np.float32).reshape(2, 1)
+    B = np.array(floats(g["B"]), np.float32).reshape(1, 1)
+    merged = o.merge(st, A, B, float(g["c"]), 2, 1).ravel()
+    for got, want in zip(merged, floats(g["merged"])):
+        w32 = np.float32(want)
+        assert abs(float(got) - float(w32)) <= abs(float(np.spacing(w32)))   # one fp32 ulp
+    inc = merged.astype(np.float64) - o.dequantize(st, "fp32").astype(np.float64)
+    assert np.allclose(inc, floats(g["increment"]), rtol=0, atol=1e-7)
+    y = float(np.dot(floats(g["x"]), merged.astype(np.float64)))
+    assert abs(y - float(g["merged_output"])) < 1e-7
+    r = load("p1_merge_requant.txt")
+    st2 = o.quantize(merged)
+    assert st2["codes"].tolist() == ints(r["codes"])
+    rec = o.dequantize(st2, "fp32")
+    tol = float(r["approx_tol"])
+    assert abs(float(rec[1]) - float(r["restored_1_approx"])) < tol
+    y2 = float(np.dot(floats(r["output_x"]), rec.astype(np.float64)))
+    assert abs(y2 - float(r["output_approx"])) < tol
+
+
+def test_merge_exact_rational_and_special_cases():
+    """With values whose float64 sums are exact (small integers times powers
+    of two), merge must equal the exactly rounded fp32 of ŵ + c Σ_t A B; with
+    c = 0 or B = 0 it must return Ŵ (not W)."""
+    rng = np.random.default_rng(11)
+    K, N, r = 3, 64, 5
+    W = (rng.standard_normal(K * N) * 0.3).astype(np.float32)
+    st = o.quantize(W)
+    w_hat = o.dequantize(st, "fp32").reshape(K, N)
+    A = (rng.integers(-64, 65, (K, r)) * 2.0 ** -7).astype(np.float32)
+    B = (rng.integers(-64, 65, (r, N)) * 2.0 ** -9).astype(np.float32)
+    c = 0.75
+    got = o.merge(st, A, B, c, K, N)
+    for k in range(K):
+        for n in range(N):
+            s = sum(Fraction(float(A[k, t])) * Fraction(float(B[t, n])) for t in range(r))
+            assert got[k, n] == exact_round_f32(Fraction(float(w_hat[k, n])) + Fraction(c) * s)
+    assert np.array_equal(o.merge(st, A, B, 0.0, K, N), w_hat)
+    assert np.array_equal(o.merge(st, A, np.zeros_like(B), c, K, N), w_hat)
+    assert not np.array_equal(o.merge(st, A, np.zeros_like(B), c, K, N), W.reshape(K, N))
+
+
+def test_sgd_page_example():
+    """One step on the worked adapter with fp32 masters gives a = [0.12025,
+    0.2405], b = 0.33375 (to fp32 rounding) and a lower loss."""
+    g = load("p1_sgd_update.txt")
+    lr = float(g["learning_rate"])
+    a0 = np.array(floats(g["A"]), np.float32)
+    b0 = np.array(floats(g["B"]), np.float32)
+    _, a1 = o.sgd_step(a0, np.array(floats(g["dA"]), np.float32), lr, master=a0)
+    _, b1 = o.sgd_step(b0, np.array(floats(g["dB"]), np.float32), lr, master=b0)
+    assert np.allclose(a1, floats(g["A_updated"]), rtol=0, atol=2e-8)
+    assert np.allclose(b1, floats(g["B_updated"]), rtol=0, atol=3e-8)
+    e, X, W_hat, A, B, c, target = _layer_example()
+    loss = lambda A_, B_: 0.5 * float((o.layer_forward(X, W_hat, A_, B_, c)[0][0, 0] - target) ** 2)
+    assert loss(a1.reshape(2, 1), b1.reshape(1, 1)) < loss(A, B)
+
+
+def test_sgd_exact_cases():
+    """Power-of-two steps are exact; without a master the bf16 value itself is
+    stepped and rounded to bf16 (ties to even)."""
+    p = np.array([1.0, -0.5, 0.25, 3.0], np.float32)
+    g = np.array([0.5, 0.25, -1.0, 0.0], np.float32)
+    bf, new = o.sgd_step(p, g, 0.5, master=p.copy())
+    assert new.tolist() == [0.75, -0.625, 0.75, 3.0] and bf.tolist() == new.tolist()
+    # 1 - 2^-9: not a bf16 value; RNE to bf16 rounds to 1.0 (tie between 1 - 2^-8 and 1 -> even = 1.0)
+    bf, new = o.sgd_step(np.array([1.0], np.float32), np.array([2.0 ** -8], np.float32), 0.5)
+    assert new is None and bf.tolist() == [1.0]
+    assert exact_round_bf16(1.0 - 2.0 ** -9) == 1.0
+
+
 def _layer_example():
     g = load("p1_layer_example.txt")
     st = o.quantize(np.array(floats(g["weight"]), np.float32))
@@ -445,6 +522,43 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     assert _fd_agrees(o.layer_backward)
     for bad in (bwd_no_c, bwd_dropped_term, bwd_transposed):
         assert not _fd_agrees(bad), bad.__name__
+    # 4. merge mistakes: the raw W instead of Ŵ, c dropped, B's columns reversed
+    orig_merge = o.merge
+
+    def merge_raw_w(state, A, B, c, K, N):
+        w = state["_W_for_planted_test"].astype(np.float64).reshape(K, N)
+        inc = np.asarray(A, np.float64) @ np.asarray(B, np.float64)
+        return (w + c * inc).astype(np.float32)
+
+    def merge_no_c(state, A, B, c, K, N):
+        return orig_merge(state, A, B, 1.0, K, N)
+
+    def merge_flipped(state, A, B, c, K, N):
+        return orig_merge(state, A, np.asarray(B)[:, ::-1], c, K, N)
+
+    assert _merge_pins_hold(orig_merge)
+    for bad in (merge_raw_w, merge_no_c, merge_flipped):
+        assert not _merge_pins_hold(bad), bad.__name__
+
+
+def _merge_pins_hold(merge) -> bool:
+    """The exact-rational merge pin (c = 0.75, integer-scaled values) and
+    the c = 0 case, for a given merge function."""
+    rng = np.random.default_rng(11)
+    K, N, r = 3, 64, 5
+    W = (rng.standard_normal(K * N) * 0.3).astype(np.float32)
+    st = dict(o.quantize(W))
+    st["_W_for_planted_test"] = W
+    w_hat = o.dequantize(st, "fp32").reshape(K, N)
+    A = (rng.integers(-64, 65, (K, r)) * 2.0 ** -7).astype(np.float32)
+    B = (rng.integers(-64, 65, (r, N)) * 2.0 ** -9).astype(np.float32)
+    got = merge(st, A, B, 0.75, K, N)
+    for k in range(K):
+        for n in range(N):
+            s = sum(Fraction(float(A[k, t])) * Fraction(float(B[t, n])) for t in range(r))
+            if got[k, n] != exact_round_f32(Fraction(float(w_hat[k, n])) + Fraction(0.75) * s):
+                return False
+    return bool(np.array_equal(merge(st, A, B, 0.0, K, N), w_hat))
 
 
 def _fd_agrees(backward) -> bool:
