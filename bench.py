@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP64_PEAK_TFLOPS = 78.6      # MI355X fp64 vector (FMA counted as two flops)
 METRIC = "QLoRA linear fwd+bwd TFLOP/s and NF4 dequant-GEMV GB/s, % of roofline"
 KERNEL_SOURCES = {"fwd_gemm": "gemm_big.hip", "bwd_dx": "gemm_big.hip", "fwd_gemv": "skinny.hip",
                   "quant_pass1": "quantize.hip", "dequant": "quantize.hip"}
@@ -285,6 +286,20 @@ def bench_components(torch, qn, si, dev, sets, outs, qws, status):
         "write_GBps": round(big.numel() * 4 / (wr * 1e-3) / 1e9, 1),
         "how": "torch sum / fill of a 1 GiB fp32 tensor, cache flushed before each call"}
     del big, out
+    # adapter merge for re-export at the bench workload's shape: fp64 FMA bound
+    # (2 K N r flops), plus the re-quantize of the merged weight
+    dm = si.layer_inputs("attn7b_4096", with_weight=False, with_grad=False)
+    Km, Nm, rm, cm = dm["K"], dm["N"], dm["r"], dm["c"]
+    stm = outs[0]["state"]
+    Amd = torch.from_numpy(np.ascontiguousarray(dm["A_bits"]).view(np.int16)).view(torch.bfloat16).to(dev)
+    Bmd = torch.from_numpy(np.ascontiguousarray(dm["B_bits"]).view(np.int16)).view(torch.bfloat16).to(dev)
+    wm = qn.qlora_merge(stm, Amd, Bmd, cm, Km, Nm)
+    mms = _time_kernel(qn, torch, "merge", lambda i: qn.qlora_merge(stm, Amd, Bmd, cm, Km, Nm, out=wm), 10, flush)
+    mfl = 2 * Km * Nm * rm
+    res["merge_attn7b"] = {"ms": round(mms, 4), "fp64_TFLOPs": round(mfl / (mms * 1e-3) / 1e12, 2),
+                           "frac_fp64_peak": round(mfl / (mms * 1e-3) / 1e12 / FP64_PEAK_TFLOPS, 4),
+                           "flops": mfl}
+    del wm, Amd, Bmd
     # the vendor library's plain bf16 GEMM of the same base shape on this
     # device (torch.matmul -> hipBLASLt), as context for the MFMA fraction
     Mv, Kv, Nv = 4096, 4096, 4096

@@ -19,12 +19,12 @@ NF4_OUT_F32, NF4_OUT_BF16 = 0, 1
 KERNEL_IDS = {
     "quant_pass1": 0, "quant_mean": 1, "quant_pass2": 2, "dequant": 3, "lora_down": 4,
     "fwd_gemm": 5, "fwd_gemv": 6, "bwd_dz": 7, "bwd_dx": 8, "bwd_colsum": 9, "dequant_bf16": 10,
-    "reduce": 11,
+    "reduce": 11, "merge": 12, "sgd": 13,
 }
 C_FUNCTIONS = [
     "nf4_sizes", "nf4_quantize", "nf4_dequantize", "qlora_workspace_bytes",
     "qlora_linear_fwd", "qlora_linear_bwd", "nf4_status_read", "qlora_timer_enable",
-    "qlora_timer_read", "nf4_error_string",
+    "qlora_timer_read", "qlora_merge", "qlora_sgd_step", "nf4_error_string",
 ]
 
 
@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.nf4_status_read.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), vp]
         L.qlora_timer_enable.argtypes = [ctypes.c_int, ctypes.c_int]
         L.qlora_timer_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+        L.qlora_merge.argtypes = [i64, i64, i64, sp, vp, vp, ctypes.c_int, ctypes.c_float, vp, vp]
+        L.qlora_sgd_step.argtypes = [i64, i64, i64, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
         L.nf4_error_string.argtypes = [ctypes.c_int]
         L.nf4_error_string.restype = ctypes.c_char_p
         for name in C_FUNCTIONS[:-1]:
@@ -152,6 +154,50 @@ def nf4_dequantize(state: NF4State, out_dtype: str = "bf16", out=None, status=No
                                 NF4_OUT_BF16 if out_dtype == "bf16" else NF4_OUT_F32,
                                 _ptr(status), _stream(stream)), "nf4_dequantize")
     return out
+
+
+NF4_AB_BF16, NF4_AB_F32 = 0, 1
+
+
+def qlora_merge(state: NF4State, A, B, c: float, K: int, N: int, out=None, stream=None):
+    """W' = fl32(ŵ + c A B) as a K*N fp32 tensor (A: K x r, B: r x N, both
+    bf16 or both fp32); pass it to nf4_quantize to re-quantize."""
+    import torch
+    r = A.shape[1]
+    if A.dtype != B.dtype or A.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("A and B must both be bf16 or both fp32")
+    for t, n in ((A, "A"), (B, "B")):
+        _require_cuda(t, n, A.dtype)
+    if tuple(A.shape) != (K, r) or tuple(B.shape) != (r, N):
+        raise ValueError("A must be K x r and B r x N")
+    if out is None:
+        out = torch.empty(K * N, dtype=torch.float32, device=A.device)
+    st = state.c_struct()
+    _check(lib().qlora_merge(K, N, r, ctypes.byref(st), A.data_ptr(), B.data_ptr(),
+                             NF4_AB_F32 if A.dtype == torch.float32 else NF4_AB_BF16, ctypes.c_float(c),
+                             out.data_ptr(), _stream(stream)), "qlora_merge")
+    return out
+
+
+def qlora_merge_requantize(state: NF4State, A, B, c: float, K: int, N: int, stream=None):
+    """Merge, then re-quantize: returns (new NF4State, device status word)."""
+    return nf4_quantize(qlora_merge(state, A, B, c, K, N, stream=stream), stream=stream)
+
+
+def qlora_sgd_step(A, B, dA, dB, lr: float, A_master=None, B_master=None, stream=None) -> None:
+    """In-place SGD step on the bf16 adapter (optionally through fp32 masters)."""
+    import torch
+    K, r = A.shape
+    N = B.shape[1]
+    for t, n, dt in ((A, "A", torch.bfloat16), (B, "B", torch.bfloat16), (dA, "dA", torch.float32),
+                     (dB, "dB", torch.float32)):
+        _require_cuda(t, n, dt)
+    for m, n in ((A_master, "A_master"), (B_master, "B_master")):
+        if m is not None:
+            _require_cuda(m, n, torch.float32)
+    _check(lib().qlora_sgd_step(K, N, r, A.data_ptr(), B.data_ptr(), dA.data_ptr(), dB.data_ptr(),
+                                ctypes.c_float(lr), _ptr(A_master), _ptr(B_master), _stream(stream)),
+           "qlora_sgd_step")
 
 
 def nf4_status_read(status, stream=None) -> int:

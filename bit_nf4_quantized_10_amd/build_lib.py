@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqlora_nf4.so")
-SOURCES = ["quantize.hip", "gemm_big.hip", "skinny.hip", "gemv.hip", "layer.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "gemm_big.hip", "skinny.hip", "gemv.hip", "layer.hip", "adapter.hip", "api.cpp"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -164,6 +164,34 @@ int qlora_linear_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t*
   return e == hipSuccess ? NF4_OK : NF4_EHIP;
 }
 
+int qlora_merge(int64_t K, int64_t N, int64_t r, const nf4_state_t* W, const void* A, const void* B, int ab_dtype,
+                float c, float* W_merged, void* stream) {
+  if (K < 1 || N < 1 || r < 1 || r > 65536 || !state_ok(W) || W->numel != K * N) return NF4_EINVAL;
+  if (K * N >= kMaxOperandElems || K * r >= kMaxOperandElems || r * N >= kMaxOperandElems) return NF4_EINVAL;
+  if (ab_dtype != NF4_AB_BF16 && ab_dtype != NF4_AB_F32) return NF4_EINVAL;
+  if (A == nullptr || B == nullptr || W_merged == nullptr || !aligned16(W_merged)) return NF4_EINVAL;
+  const uintptr_t elem_mask = ab_dtype == NF4_AB_F32 ? 3u : 1u;
+  if ((reinterpret_cast<uintptr_t>(A) & elem_mask) != 0 || (reinterpret_cast<uintptr_t>(B) & elem_mask) != 0)
+    return NF4_EINVAL;
+  qn::NF4View v{W->codes, W->qabsmax, W->absmax2, W->offset};
+  hipError_t e = qn::launch_merge(K, N, r, v, A, B, ab_dtype == NF4_AB_F32, c, W_merged,
+                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4_OK : NF4_EHIP;
+}
+
+int qlora_sgd_step(int64_t K, int64_t N, int64_t r, uint16_t* A, uint16_t* B, const float* dA, const float* dB,
+                   float lr, float* A_master, float* B_master, void* stream) {
+  if (K < 1 || N < 1 || r < 1 || K * r >= kMaxOperandElems || r * N >= kMaxOperandElems) return NF4_EINVAL;
+  if (A == nullptr || B == nullptr || dA == nullptr || dB == nullptr) return NF4_EINVAL;
+  if ((A_master == nullptr) != (B_master == nullptr)) return NF4_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(A) & 1u) || (reinterpret_cast<uintptr_t>(B) & 1u) ||
+      (reinterpret_cast<uintptr_t>(dA) & 3u) || (reinterpret_cast<uintptr_t>(dB) & 3u) ||
+      (reinterpret_cast<uintptr_t>(A_master) & 3u) || (reinterpret_cast<uintptr_t>(B_master) & 3u))
+    return NF4_EINVAL;
+  hipError_t e = qn::launch_sgd(K, N, r, A, B, dA, dB, lr, A_master, B_master, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4_OK : NF4_EHIP;
+}
+
 int nf4_status_read(const int32_t* status, int32_t* host_value, void* stream) {
   if (status == nullptr || host_value == nullptr) return NF4_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -43,6 +43,13 @@ struct NF4View {
   const float* offset;
 };
 
+// W' = fl32(ŵ + c A B) (fp64 accumulation; A, B fp32 when f32_ab, else bf16).
+hipError_t launch_merge(int64_t K, int64_t N, int64_t r, NF4View W, const void* A, const void* B, bool f32_ab,
+                        float c, float* out, hipStream_t stream);
+// One SGD step on A (K x r) and B (r x N), optionally through fp32 masters.
+hipError_t launch_sgd(int64_t K, int64_t N, int64_t r, uint16_t* A, uint16_t* B, const float* dA, const float* dB,
+                      float lr, float* A_master, float* B_master, hipStream_t stream);
+
 // Workspace needs (bytes) of the layer kernels; the C ABI adds them up.
 int64_t fwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r);
 int64_t bwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r);

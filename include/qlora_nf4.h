@@ -131,6 +131,38 @@ int qlora_linear_bwd(int64_t M, int64_t K, int64_t N, int64_t r,
                      float c, uint16_t* dX, float* dA, float* dB,
                      void* workspace, int64_t workspace_bytes, void* stream);
 
+/* Element types of the adapter matrices passed to qlora_merge. */
+#define NF4_AB_BF16 0
+#define NF4_AB_F32  1
+
+/* Merge the adapter into the frozen base for re-export (page section
+ * "Merge 后还是不是训练时的函数": the trained function is Ŵ + cAB, merged in
+ * high precision; re-quantizing the result is a separate step, done by
+ * passing W_merged to nf4_quantize):
+ *   W_merged[k][n] = fl32(ŵ[k][n] + c * sum_t A[k][t] B[t][n])
+ * with ŵ the fp32 reconstruction nf4_dequantize(W, NF4_OUT_F32) returns, the
+ * sum accumulated in fp64 for t = 0 .. r-1 in order, c * sum and the addition
+ * in fp64, and one rounding to fp32.  A: K x r, B: r x N, row-major, of
+ * element type ab_dtype (NF4_AB_BF16 or NF4_AB_F32, e.g. fp32 master copies),
+ * aligned to their element size; W_merged: K x N fp32, 16-byte aligned,
+ * caller-owned.  Requirements: K, N, r >= 1, r <= 65536, W->numel == K*N,
+ * K*N, K*r and r*N below 2^29.  Any N is allowed (blocks run over the flat
+ * index).  NF4_EINVAL otherwise.  The state is only read. */
+int qlora_merge(int64_t K, int64_t N, int64_t r, const nf4_state_t* W, const void* A, const void* B,
+                int ab_dtype, float c, float* W_merged, void* stream);
+
+/* One plain SGD step on the adapter after qlora_linear_bwd (page section
+ * "一次完整反向与有限差分": only A and B move, v <- v - lr * g):
+ *   p' = fl32(p - fl32(lr * g)),  bf16 parameter <- RNE_bf16(p')
+ * where p is the fp32 master copy when A_master / B_master are given (both
+ * or neither; they are updated to p'), else the bf16 parameter itself.
+ * A, B: bf16 K x r and r x N (updated in place); dA, dB: fp32 gradients of
+ * the same shapes (as qlora_linear_bwd returns them).  Requirements: K, N,
+ * r >= 1, K*r and r*N below 2^29, each pointer aligned to its element size.
+ * NF4_EINVAL otherwise. */
+int qlora_sgd_step(int64_t K, int64_t N, int64_t r, uint16_t* A, uint16_t* B, const float* dA, const float* dB,
+                   float lr, float* A_master, float* B_master, void* stream);
+
 /* Synchronise `stream`, then copy the device status word to *host_value.
  * Returns NF4_EHIP if the copy fails, else NF4_OK. */
 int nf4_status_read(const int32_t* status, int32_t* host_value, void* stream);
@@ -148,7 +180,9 @@ int nf4_status_read(const int32_t* status, int32_t* host_value, void* stream);
 #define QK_BWD_COLSUM   9   /* dA = Xᵀ dZ and dB = c Zᵀ G partials      */
 #define QK_DEQUANT_BF16 10  /* Ŵ (or Ŵᵀ) to bf16 for the M >= 512 GEMMs */
 #define QK_REDUCE       11  /* fixed-order split reductions             */
-#define QK_NUM_KERNELS  12
+#define QK_MERGE        12  /* adapter merge W' = fl32(ŵ + cAB)          */
+#define QK_SGD          13  /* adapter SGD step                          */
+#define QK_NUM_KERNELS  14
 
 /* When enabled, the library records a pair of hipEvents on the launch
  * stream around every launch of kernel `kernel_id`.  qlora_timer_read

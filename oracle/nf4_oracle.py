@@ -326,18 +326,21 @@ def layer_backward(G, X, W_hat, A, B, c):
     return dX, dA, dB, dZ
 
 
-def merge(state: dict, A, B, c, K: int, N: int) -> np.ndarray:
+def merge(state: dict, A, B, c, K: int, N: int, rows=None) -> np.ndarray:
     """Merged fp32 weight for re-export ([P1] "Merge 后还是不是训练时的函数":
     the trained function is Ŵ plus the adapter, merged in high precision,
     then re-quantized as a new step).  Reading: Ŵ is the fp32 reconstruction
     (R5); the increment c A B is accumulated in float64, t = 0 .. r-1 in
     order (each product of two fp32 or bf16 values is exact in float64, one
     rounding per addition), scaled by c in float64, added to ŵ in float64
-    and rounded once to fp32.  A: K x r, B: r x N (fp32 or bf16 values)."""
+    and rounded once to fp32.  A: K x r, B: r x N (fp32 or bf16 values).
+    ``rows`` (optional) restricts the result to those rows of W'."""
     w = dequantize(state, "fp32").astype(np.float64).reshape(K, N)
     A = np.asarray(A, dtype=np.float64).reshape(K, -1)
     B = np.asarray(B, dtype=np.float64).reshape(A.shape[1], N)
-    acc = np.zeros((K, N), dtype=np.float64)
+    if rows is not None:
+        w, A = w[rows], A[rows]
+    acc = np.zeros(w.shape, dtype=np.float64)
     for t in range(A.shape[1]):
         acc = acc + np.outer(A[:, t], B[t])
     return (w + np.float64(c) * acc).astype(np.float32)

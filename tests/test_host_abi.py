@@ -107,3 +107,24 @@ def test_error_strings():
     L = qn.lib()
     for code in (0, 1, 2, 4, 8, 6):
         assert L.nf4_error_string(code)
+
+
+def test_adapter_entry_points_reject_bad_arguments():
+    L = qn.lib()
+    st = qn._State(64 * 64, 0x1000, 0x2000, 0x3000, 0x4000)
+    ok = (64, 64, 8, ctypes.byref(st), 0x100, 0x200, qn.NF4_AB_BF16, ctypes.c_float(1.0), 0x300, None)
+    bad_cases = [
+        (64, 32, 8) + ok[3:],                                   # numel != K*N
+        (64, 64, 0) + ok[3:],                                   # r = 0
+        ok[:6] + (7,) + ok[7:],                                 # unknown A/B dtype
+        ok[:4] + (None,) + ok[5:],                              # NULL A
+        ok[:8] + (0x304,) + ok[9:],                             # misaligned output
+        ok[:4] + (0x102,) + (ok[5], qn.NF4_AB_F32) + ok[7:],    # fp32 A not 4-byte aligned
+    ]
+    for args in bad_cases:
+        assert L.qlora_merge(*args) == qn.NF4_EINVAL, args
+    sgd_ok = (64, 64, 8, 0x100, 0x200, 0x300, 0x400, ctypes.c_float(0.1), None, None, None)
+    for args in [(0, 64, 8) + sgd_ok[3:], sgd_ok[:3] + (None,) + sgd_ok[4:],
+                 sgd_ok[:8] + (0x500, None, None),                # one master without the other
+                 sgd_ok[:5] + (0x302,) + sgd_ok[6:]]:             # misaligned fp32 gradient
+        assert L.qlora_sgd_step(*args) == qn.NF4_EINVAL, args
