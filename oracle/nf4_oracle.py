@@ -32,7 +32,9 @@ Pages cited (by title and section):
        [15, 0], scale 0.5, A = [0.1, 0.2]ᵀ, B = [0.3], c = 1, target 1).
      - "Merge 后还是不是训练时的函数": re-quantizing [0.53, -0.44].
 [P2] "SFT（四）：QLoRA的4-bit量化与LoRA微调原理", §6 "先理解最普通的分块量化":
-     a signed absmax integer quantizer with levels [-7, 7] on [-1.2, -0.4, 0.1, 0.85].
+     a signed absmax integer quantizer with levels [-7, 7] on [-1.2, -0.4, 0.1, 0.85];
+     §21.3: double quantization is a switch that further compresses the
+     first-level constants (so a state without it keeps them in fp32).
 [P3] "精读笔记 · QLoRA: Efficient Finetuning of Quantized LLMs", §3.0 (store
      NF4, compute in BF16) and §3.2 (double-quantization accounting).
 
@@ -58,6 +60,9 @@ Parity status of each function (see the tests under tests/):
   nf4_codebook, first_level_absmax, nf4_codes, pack_nibbles, unpack_nibbles,
   storage_bits, layer_forward, layer_backward, bf16_round: pinned to printed
   page values, exact rational brute force, closed forms or finite differences.
+  quantize(double_quant=False) / dequantize of such a state: the codes are
+  those of the double-quantized encoding (R6), and the reconstruction is
+  pinned by exact rational rounding of C[j] * a and the P1 worked block.
   merge: pinned by the P1 merge example ([0.53, -0.44] -> codes [15, 1],
   -0.368982, output -0.207964) and exact special cases (c = 0, B = 0,
   power-of-two rank-1 increments).  sgd_step: pinned by the P1 update of the
@@ -252,14 +257,20 @@ def reconstruct_absmax(q: np.ndarray, s2: np.ndarray, offset) -> np.ndarray:
     return (prod + np.float32(offset)).astype(np.float32)
 
 
-def quantize(W) -> dict:
+def quantize(W, double_quant: bool = True) -> dict:
     """Full encoder: flat fp32 weights -> packed NF4 codes plus double-quantized
     scales.  Also returns the intermediate first-level absmax ``a`` and the
-    unpacked ``codes`` for the tests."""
+    unpacked ``codes`` for the tests.  With double_quant=False the encoding
+    stops at the first level ([P1] "Double Quantization 压缩的是 Scale": one
+    fp32 absmax per 64 weights is the state; [P2] §21.3 names the switch):
+    the stored scales are the exact absmax values and â = a."""
     w32 = np.ascontiguousarray(W, dtype=np.float32).ravel()
     a = first_level_absmax(w32)
     codes = nf4_codes(w32, a)
     payload, length = pack_nibbles(codes)
+    if not double_quant:
+        return {"numel": length, "codes_packed": payload, "absmax": a, "codes": codes,
+                "double_quant": False}
     q, s2, offset = double_quantize(a)
     ahat = reconstruct_absmax(q, s2, offset)
     if not np.all(np.isfinite(ahat)):
@@ -267,7 +278,7 @@ def quantize(W) -> dict:
         raise ValueError("nonfinite reconstruction")
     return {"numel": length, "codes_packed": payload, "qabsmax": q,
             "absmax2": s2, "offset": np.float32(offset), "absmax": a,
-            "codes": codes}
+            "codes": codes, "double_quant": True}
 
 
 def bf16_round(x32: np.ndarray) -> np.ndarray:
@@ -283,7 +294,10 @@ def dequantize(state: dict, out: str = "fp32") -> np.ndarray:
     (the compute dtype, [P3] §3.0).  Unpacks with the page's checks."""
     P = int(state["numel"])
     codes = unpack_nibbles(state["codes_packed"], P)
-    ahat = reconstruct_absmax(state["qabsmax"], state["absmax2"], state["offset"])
+    if state.get("double_quant", True):
+        ahat = reconstruct_absmax(state["qabsmax"], state["absmax2"], state["offset"])
+    else:
+        ahat = np.asarray(state["absmax"], dtype=np.float32)   # single level: â = a
     return reconstruct_weights(codes, np.repeat(ahat, BLOCK1)[:P], out)
 
 

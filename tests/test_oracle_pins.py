@@ -111,6 +111,28 @@ def test_merge_requantize_example():
     assert abs(y - float(g["output_approx"])) < tol
 
 
+def test_single_level_state():
+    """Double quantization off: the codes are those of the double-quantized
+    encoding (they use the exact absmax either way), the stored scales are
+    the exact block maxima, and each weight is the exactly rounded fp32 of
+    C[j] * a; the page's worked block reconstructs to the printed values."""
+    st = o.quantize(np.array([0.0, 0.2, -0.4, 1.0], np.float32), double_quant=False)
+    assert st["codes"].tolist() == [7, 9, 3, 15] and st["codes_packed"].tobytes().hex() == "793f"
+    assert o.dequantize(st, "fp32").tolist() == [0.0, 0.16093020141124725, -0.39491748809814453, 1.0]
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal(64 * 9 + 17) * np.repeat(10.0 ** rng.uniform(-6, 6, 10), 64)[:64 * 9 + 17]).astype(np.float32)
+    single, dq = o.quantize(w, double_quant=False), o.quantize(w)
+    assert np.array_equal(single["codes"], dq["codes"])
+    for b in range(single["absmax"].size):
+        blk = w[64 * b: 64 * b + 64]
+        assert single["absmax"][b] == (np.max(np.abs(blk)) or np.float32(1.0))
+    rec = o.dequantize(single, "fp32")
+    for i in range(w.size):
+        want = exact_round_f32(NF4[int(single["codes"][i])] * Fraction(float(single["absmax"][i // 64])))
+        assert rec[i] == want
+    assert o.storage_bits(64 * 1024, double_quant=False) / (64 * 1024) == 4.5
+
+
 def test_merge_page_example():
     """The merge of the worked adapter: increment [0.03, 0.06], merged
     [0.53, -0.44] (within the fp32 rounding of the fp32 adapter values), the
