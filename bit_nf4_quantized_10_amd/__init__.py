@@ -36,7 +36,7 @@ class NF4Error(RuntimeError):
 
 class _State(ctypes.Structure):
     _fields_ = [("numel", ctypes.c_int64), ("codes", ctypes.c_void_p), ("qabsmax", ctypes.c_void_p),
-                ("absmax2", ctypes.c_void_p), ("offset", ctypes.c_void_p)]
+                ("absmax2", ctypes.c_void_p), ("offset", ctypes.c_void_p), ("absmax", ctypes.c_void_p)]
 
 
 _lib = None
@@ -98,16 +98,23 @@ def _require_cuda(t, name: str, dtype=None) -> None:
 
 @dataclass
 class NF4State:
-    """Frozen NF4 state of one weight tensor (device tensors)."""
+    """Frozen NF4 state of one weight tensor (device tensors).  Double
+    quantized: qabsmax / absmax2 / offset set, absmax None.  Single level
+    (double quantization off): absmax set, the other three None."""
     numel: int
-    codes: "torch.Tensor"     # uint8[ceil(P/2)]
-    qabsmax: "torch.Tensor"   # int8[n1]
-    absmax2: "torch.Tensor"   # float32[n2]
-    offset: "torch.Tensor"    # float32[1]
+    codes: "torch.Tensor"             # uint8[ceil(P/2)]
+    qabsmax: "torch.Tensor | None"    # int8[n1]
+    absmax2: "torch.Tensor | None"    # float32[n2]
+    offset: "torch.Tensor | None"     # float32[1]
+    absmax: "torch.Tensor | None" = None   # float32[n1]
+
+    @property
+    def double_quant(self) -> bool:
+        return self.absmax is None
 
     def c_struct(self) -> _State:
-        return _State(self.numel, self.codes.data_ptr(), self.qabsmax.data_ptr(),
-                      self.absmax2.data_ptr(), self.offset.data_ptr())
+        return _State(self.numel, self.codes.data_ptr(), _ptr(self.qabsmax), _ptr(self.absmax2),
+                      _ptr(self.offset), _ptr(self.absmax))
 
 
 def nf4_sizes(numel: int) -> dict:
@@ -116,23 +123,28 @@ def nf4_sizes(numel: int) -> dict:
     return dict(zip(("code_bytes", "n1", "n2", "quant_workspace_bytes"), (o.value for o in out)))
 
 
-def empty_state(numel: int, device="cuda") -> NF4State:
+def empty_state(numel: int, device="cuda", double_quant: bool = True) -> NF4State:
     import torch
     s = nf4_sizes(numel)
-    return NF4State(numel, torch.empty(s["code_bytes"], dtype=torch.uint8, device=device),
+    codes = torch.empty(s["code_bytes"], dtype=torch.uint8, device=device)
+    if not double_quant:
+        return NF4State(numel, codes, None, None, None, torch.empty(s["n1"], dtype=torch.float32, device=device))
+    return NF4State(numel, codes,
                     torch.empty(s["n1"], dtype=torch.int8, device=device),
                     torch.empty(s["n2"], dtype=torch.float32, device=device),
                     torch.empty(1, dtype=torch.float32, device=device))
 
 
-def nf4_quantize(W, state: NF4State | None = None, workspace=None, status=None, stream=None):
-    """Encode fp32 weights (any shape, flattened row-major) into an NF4State.
+def nf4_quantize(W, state: NF4State | None = None, workspace=None, status=None, stream=None,
+                 double_quant: bool = True):
+    """Encode fp32 weights (any shape, flattened row-major) into an NF4State
+    (single level when double_quant is False or the given state has absmax).
     Returns (state, status) where status is the device int32 status word."""
     import torch
     _require_cuda(W, "W", torch.float32)
     P = W.numel()
     if state is None:
-        state = empty_state(P, W.device)
+        state = empty_state(P, W.device, double_quant)
     sizes = nf4_sizes(P)
     if workspace is None:
         workspace = torch.empty(sizes["quant_workspace_bytes"], dtype=torch.uint8, device=W.device)

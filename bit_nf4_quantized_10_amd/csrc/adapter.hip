@@ -76,7 +76,8 @@ __global__ __launch_bounds__(256) void qlora_merge_kernel(int64_t K, int64_t N, 
     }
     __syncthreads();
   }
-  const float off = W.offset[0];
+  const bool single = W.absmax != nullptr;   // no second level: â = absmax[block]
+  const float off = single ? 0.0f : W.offset[0];
   const double cd = static_cast<double>(c);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(256) void qlora_merge_kernel(int64_t K, int64_t N, 
       const int64_t e = k * N + n;
       const uint32_t byte = W.codes[e >> 1];
       const uint32_t code = (e & 1) ? (byte & 15u) : (byte >> 4);
-      const float ahat = absmax_hat(W.qabsmax[e >> 6], W.absmax2[e >> 14], off);
+      const float ahat = single ? W.absmax[e >> 6] : absmax_hat(W.qabsmax[e >> 6], W.absmax2[e >> 14], off);
       const float w = __fmul_rn(kNF4[code], ahat);
       out[e] = __double2float_rn(__dadd_rn(static_cast<double>(w), __dmul_rn(cd, acc[i][l])));
     }

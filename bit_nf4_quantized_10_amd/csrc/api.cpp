@@ -22,10 +22,13 @@ void counts(int64_t P, int64_t* n1, int64_t* n2) {
 // The encoder and decoders move packed codes and second-level codes as
 // 32-bit words and the scales as fp32, so those buffers must be aligned.
 bool state_ok(const nf4_state_t* s) {
-  return s != nullptr && s->numel >= 1 && s->codes != nullptr && s->qabsmax != nullptr &&
-         s->absmax2 != nullptr && s->offset != nullptr && aligned16(s->codes) && aligned16(s->qabsmax) &&
+  if (s == nullptr || s->numel < 1 || s->codes == nullptr || !aligned16(s->codes)) return false;
+  if (s->absmax != nullptr) return (reinterpret_cast<uintptr_t>(s->absmax) & 3u) == 0;   // single level
+  return s->qabsmax != nullptr && s->absmax2 != nullptr && s->offset != nullptr && aligned16(s->qabsmax) &&
          (reinterpret_cast<uintptr_t>(s->absmax2) & 3u) == 0 && (reinterpret_cast<uintptr_t>(s->offset) & 3u) == 0;
 }
+
+qn::NF4View view_of(const nf4_state_t* s) { return qn::NF4View{s->codes, s->qabsmax, s->absmax2, s->offset, s->absmax}; }
 
 // Kernels address operands with 32-bit buffer offsets and mark masked lanes
 // with offset 2^31; keeping every bf16 operand (X, G, Y, dX, A, B and the
@@ -113,7 +116,7 @@ int nf4_quantize(const float* W, const nf4_state_t* out, void* workspace, int64_
   float* ws_absmax = reinterpret_cast<float*>(ws);
   double* ws_gsum = reinterpret_cast<double*>(ws + align256(4 * n1));
   int32_t* ws_flags = reinterpret_cast<int32_t*>(ws + align256(4 * n1) + align256(8 * n2));
-  hipError_t e = qn::launch_quantize(W, out->numel, out->codes, out->qabsmax, out->absmax2, out->offset,
+  hipError_t e = qn::launch_quantize(W, out->numel, out->codes, out->qabsmax, out->absmax2, out->offset, out->absmax,
                                      ws_absmax, ws_gsum, ws_flags, status, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? NF4_OK : NF4_EHIP;
 }
@@ -121,8 +124,8 @@ int nf4_quantize(const float* W, const nf4_state_t* out, void* workspace, int64_
 int nf4_dequantize(const nf4_state_t* state, void* out, int out_dtype, int32_t* status, void* stream) {
   if (!state_ok(state) || out == nullptr || !aligned16(out)) return NF4_EINVAL;
   if (out_dtype != NF4_OUT_F32 && out_dtype != NF4_OUT_BF16) return NF4_EINVAL;
-  hipError_t e = qn::launch_dequantize(state->codes, state->qabsmax, state->absmax2, state->offset,
-                                       state->numel, out, out_dtype, status, static_cast<hipStream_t>(stream));
+  hipError_t e = qn::launch_dequantize(view_of(state), state->numel, out, out_dtype, status,
+                                       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? NF4_OK : NF4_EHIP;
 }
 
@@ -142,7 +145,7 @@ int qlora_linear_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t*
       !aligned16(W->codes) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return NF4_EINVAL;
   if (workspace_bytes < qn::fwd_workspace_bytes(M, K, N, r)) return NF4_EINVAL;
-  qn::NF4View v{W->codes, W->qabsmax, W->absmax2, W->offset};
+  const qn::NF4View v = view_of(W);
   hipError_t e = qn::launch_fwd(M, K, N, r, X, v, A, B, c, Y, Z, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? NF4_OK : NF4_EHIP;
 }
@@ -158,7 +161,7 @@ int qlora_linear_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t*
       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return NF4_EINVAL;
   if (workspace_bytes < qn::bwd_workspace_bytes(M, K, N, r)) return NF4_EINVAL;
-  qn::NF4View v{W->codes, W->qabsmax, W->absmax2, W->offset};
+  const qn::NF4View v = view_of(W);
   hipError_t e = qn::launch_bwd(M, K, N, r, G, X, Z, v, A, B, c, dX, dA, dB, workspace,
                                 static_cast<hipStream_t>(stream));
   return e == hipSuccess ? NF4_OK : NF4_EHIP;
@@ -173,7 +176,7 @@ int qlora_merge(int64_t K, int64_t N, int64_t r, const nf4_state_t* W, const voi
   const uintptr_t elem_mask = ab_dtype == NF4_AB_F32 ? 3u : 1u;
   if ((reinterpret_cast<uintptr_t>(A) & elem_mask) != 0 || (reinterpret_cast<uintptr_t>(B) & elem_mask) != 0)
     return NF4_EINVAL;
-  qn::NF4View v{W->codes, W->qabsmax, W->absmax2, W->offset};
+  const qn::NF4View v = view_of(W);
   hipError_t e = qn::launch_merge(K, N, r, v, A, B, ab_dtype == NF4_AB_F32, c, W_merged,
                                   static_cast<hipStream_t>(stream));
   return e == hipSuccess ? NF4_OK : NF4_EHIP;

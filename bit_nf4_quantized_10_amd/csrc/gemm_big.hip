@@ -119,6 +119,8 @@ struct Big {
   int64_t m0, c0, red;
   Rsrc r_act, r_codes, r_q, r_s2;
   float off;
+  bool single;   // state without a second level: â = absmax[block]
+  int s_shift;   // flat weight index -> index of its stored scale
   uint32_t act_voff[8];         // byte offset of this lane's activation chunk, stage 0
   int act_lim[8];               // forward tail: chunk valid while k0 < act_lim
   uint32_t w_voff[8];           // forward: code word of row i at stage 0; backward: [0] = row start
@@ -136,9 +138,11 @@ struct Big {
     const int64_t P = a.K * a.N;
     r_act = make_rsrc(a.act, a.M * a.act_ld * 2);
     r_codes = make_rsrc(a.W.codes, (P + 1) / 2);
-    r_q = make_rsrc(a.W.qabsmax, (P + 63) / 64);
-    r_s2 = make_rsrc(a.W.absmax2, ((P + 16383) / 16384) * 4);
-    off = a.W.offset[0];
+    single = a.W.absmax != nullptr;
+    r_q = make_rsrc(a.W.qabsmax, single ? 0 : (P + 63) / 64);
+    r_s2 = single ? make_rsrc(a.W.absmax, ((P + 63) / 64) * 4) : make_rsrc(a.W.absmax2, ((P + 16383) / 16384) * 4);
+    s_shift = single ? 6 : 14;
+    off = single ? 0.0f : a.W.offset[0];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       // row = wave*64 + 8j + lane/8, whose swizzle is (lane/8) ^ j
@@ -195,7 +199,7 @@ struct Big {
       R.q = static_cast<int>(static_cast<int8_t>(
           __builtin_amdgcn_raw_buffer_load_b8(r_q, q_voff, static_cast<uint32_t>((k0 * a.N) >> 6), 0)));
       const int64_t e = tab_e0 + k0 * a.N;
-      R.s2 = ld_f32(r_s2, tab_ok ? static_cast<uint32_t>((e >> 14) * 4) : kMasked);
+      R.s2 = ld_f32(r_s2, tab_ok ? static_cast<uint32_t>((e >> s_shift) * 4) : kMasked);
     } else {
       const uint32_t soff = static_cast<uint32_t>(k0 >> 1);
       const uint4 lo = ld128s(r_codes, w_voff[0], soff);
@@ -205,14 +209,14 @@ struct Big {
       R.q = static_cast<int>(static_cast<int8_t>(
           __builtin_amdgcn_raw_buffer_load_b8(r_q, q_voff, static_cast<uint32_t>(k0 >> 6), 0)));
       const int64_t e = tab_e0 + k0;
-      R.s2 = ld_f32(r_s2, tab_ok ? static_cast<uint32_t>((e >> 14) * 4) : kMasked);
+      R.s2 = ld_f32(r_s2, tab_ok ? static_cast<uint32_t>((e >> s_shift) * 4) : kMasked);
     }
   }
 
   // Build this thread's table for stage s into table buffer b.
   __device__ void build_table(const WRegs& R, int64_t s, int b) const {
     const int64_t krow = kForward ? s * kBK + tab_row : c0 + tab_row;
-    float ahat = __fadd_rn(__fmul_rn(q2t()[R.q + 128], R.s2), off);
+    float ahat = single ? R.s2 : __fadd_rn(__fmul_rn(q2t()[R.q + 128], R.s2), off);
     if (krow >= a.K) ahat = 0.0f;   // rows past K decode to zero
     write_block_table(tabs(b) + (kForward ? (tab_row * 4 + tab_blk) : tab_row) * 16, ahat);
   }

@@ -186,10 +186,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // step advance is a scalar offset (N is a multiple of 64)
   const int64_t kb0 = kend > kw0 ? kw0 : 0;
   const Rsrc rc = make_rsrc(W.codes + kb0 * N / 2, rows * N / 2);
-  const Rsrc rq = make_rsrc(W.qabsmax + kb0 * N / 64, rows * N / 64);
-  const Rsrc rs = make_rsrc(W.absmax2, ((P + 16383) / 16384) * 4);
+  // a state without a second level stores one fp32 scale per block: â = that
+  const bool single = W.absmax != nullptr;
+  const Rsrc rq = single ? make_rsrc(nullptr, 0) : make_rsrc(W.qabsmax + kb0 * N / 64, rows * N / 64);
+  const Rsrc rs = single ? make_rsrc(W.absmax, ((P + 63) / 64) * 4) : make_rsrc(W.absmax2, ((P + 16383) / 16384) * 4);
+  const int s_shift = single ? 6 : 14;
   const Rsrc rx = make_rsrc(X, M * K * 2);
-  const float off = W.offset[0];
+  const float off = single ? 0.0f : W.offset[0];
   const int64_t n = n0 + 16 * q;
   const bool n_ok = n < N;
   const int blk = q >> 2;
@@ -218,14 +221,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       S.q[u] = static_cast<int>(static_cast<int8_t>(__builtin_amdgcn_raw_buffer_load_b8(rq, voff_q[u], sq, 0)));
       const uint32_t nb = static_cast<uint32_t>(n0 + 64 * (2 * (lane & 1) + u));
       const bool ok = kt < kend && nb < N;
-      S.s2[u] = ld_f32(rs, ok ? ((kt * static_cast<uint32_t>(N) + nb) >> 14) * 4 : kMasked);
+      S.s2[u] = ld_f32(rs, ok ? ((kt * static_cast<uint32_t>(N) + nb) >> s_shift) * 4 : kMasked);
     }
   };
   auto build = [&](const GvStep& S, int buf) {
     char* tb = my_tabs + buf * kGvTabBytes + gv_row(lane >> 1) + 64 * (lane & 1);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      write_block_table(reinterpret_cast<uint16_t*>(tb + 32 * u), __fadd_rn(__fmul_rn(q2t[S.q[u] + 128], S.s2[u]), off));
+      write_block_table(reinterpret_cast<uint16_t*>(tb + 32 * u),
+                        single ? S.s2[u] : __fadd_rn(__fmul_rn(q2t[S.q[u] + 128], S.s2[u]), off));
   };
 
   f32x4 acc[16];

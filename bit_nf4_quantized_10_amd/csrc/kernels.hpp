@@ -28,20 +28,24 @@ class Timer {
   void* packet_stop_;
 };
 
-hipError_t launch_quantize(const float* W, int64_t P, uint8_t* codes, int8_t* qabsmax,
-                           float* absmax2, float* offset, float* ws_absmax, double* ws_gsum,
-                           int32_t* ws_flags, int32_t* status, hipStream_t stream);
-
-hipError_t launch_dequantize(const uint8_t* codes, const int8_t* qabsmax, const float* absmax2,
-                             const float* offset, int64_t P, void* out, int out_dtype,
-                             int32_t* status, hipStream_t stream);
-
+// The read-only view of a stored weight the kernels decode.  With absmax
+// non-null the state has no second level: â = absmax[block] (fp32); else
+// â = fl32(fl32(fl32(q / 127) * absmax2[block / 256]) + offset).
 struct NF4View {
   const uint8_t* codes;
   const int8_t* qabsmax;
   const float* absmax2;
   const float* offset;
+  const float* absmax;
 };
+
+// absmax_out non-null: single-level encoding (the fp32 first-level scales are
+// the stored state; qabsmax, absmax2 and offset are not written).
+hipError_t launch_quantize(const float* W, int64_t P, uint8_t* codes, int8_t* qabsmax,
+                           float* absmax2, float* offset, float* absmax_out, float* ws_absmax, double* ws_gsum,
+                           int32_t* ws_flags, int32_t* status, hipStream_t stream);
+
+hipError_t launch_dequantize(NF4View W, int64_t P, void* out, int out_dtype, int32_t* status, hipStream_t stream);
 
 // W' = fl32(ŵ + c A B) (fp64 accumulation; A, B fp32 when f32_ab, else bf16).
 hipError_t launch_merge(int64_t K, int64_t N, int64_t r, NF4View W, const void* A, const void* B, bool f32_ab,
@@ -102,8 +106,6 @@ hipError_t launch_dx_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uin
                            const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream);
 
 // Dequantize a K x N weight to bf16, either as stored (K x N) or transposed (N x K).
-hipError_t launch_dequant_bf16(const uint8_t* codes, const int8_t* qabsmax, const float* absmax2,
-                               const float* offset, int64_t K, int64_t N, bool transposed, uint16_t* out,
-                               hipStream_t stream);
+hipError_t launch_dequant_bf16(NF4View W, int64_t K, int64_t N, bool transposed, uint16_t* out, hipStream_t stream);
 
 }  // namespace qn

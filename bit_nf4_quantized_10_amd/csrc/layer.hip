@@ -51,7 +51,7 @@ hipError_t launch_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
     return e;
   if (use_dense(M)) {
     uint16_t* wt = reinterpret_cast<uint16_t*>(after_z + cbt_bytes(M, N, r));
-    if ((e = launch_dequant_bf16(W.codes, W.qabsmax, W.absmax2, W.offset, K, N, true, wt, stream)) != hipSuccess) return e;
+    if ((e = launch_dequant_bf16(W, K, N, true, wt, stream)) != hipSuccess) return e;
     return launch_fwd_dense(M, K, N, r, X, wt, Z, cbt, Y, stream);
   }
   return launch_fwd_big(M, K, N, r, X, W, Z, cbt, Y, stream);
@@ -72,7 +72,7 @@ hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
   if (dX == nullptr) return hipGetLastError();
   if (use_dense(M)) {
     uint16_t* wd = reinterpret_cast<uint16_t*>(static_cast<char*>(db_part) + p.db_part);
-    if ((e = launch_dequant_bf16(W.codes, W.qabsmax, W.absmax2, W.offset, K, N, false, wd, stream)) != hipSuccess)
+    if ((e = launch_dequant_bf16(W, K, N, false, wd, stream)) != hipSuccess)
       return e;
     return launch_dx_dense(M, K, N, r, G, wd, dz16, A, dX, stream);
   }

@@ -326,6 +326,17 @@ __global__ __launch_bounds__(64 * kPass2Groups) void nf4_quant_pass2_kernel(
   }
 }
 
+// Single-level encoding: OR the groups' non-finite flags (pass 1) into the
+// status word that pass 1 cleared.  One workgroup.
+__global__ __launch_bounds__(kQuantThreads) void nf4_quant_flags_kernel(const int32_t* __restrict__ flags, int64_t n2,
+                                                                        int32_t* __restrict__ status) {
+  int f = 0;
+  for (int64_t g = threadIdx.x; g < n2; g += kQuantThreads) f |= flags[g];
+  if (__syncthreads_or(f)) {
+    if (threadIdx.x == 0) atomicOr(status, NF4_ENONFINITE);
+  }
+}
+
 // Decoder.  The whole code words (8 weights each) are cut into tiles of
 // 256 * U words; thread t handles words tile * 256 * U + t + 256 * u, u < U,
 // so every load and every 16-byte store of a wave is contiguous.  Workgroups
@@ -349,15 +360,18 @@ struct DqTile {
   float s2[U];
 };
 
+// sshift: word index -> index of its scale (11: one per 256 blocks of 8
+// words; 3: one per block, for a state without a second level).
 template <int U>
-__device__ __forceinline__ void dq_load(DqTile<U>& t, int64_t tile, int64_t words, Rsrc rc, Rsrc rq, Rsrc rs) {
+__device__ __forceinline__ void dq_load(DqTile<U>& t, int64_t tile, int64_t words, Rsrc rc, Rsrc rq, Rsrc rs,
+                                        int sshift) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t wi = tile * (kQuantThreads * U) + threadIdx.x + static_cast<int64_t>(u) * kQuantThreads;
     const bool in = wi < words;
     t.wd[u] = ld_b32(rc, in ? static_cast<uint32_t>(wi * 4) : kMasked);
     t.q[u] = ld_i8(rq, in ? static_cast<uint32_t>(wi >> 3) : kMasked);
-    t.s2[u] = ld_f32(rs, in ? static_cast<uint32_t>((wi >> 11) * 4) : kMasked);
+    t.s2[u] = ld_f32(rs, in ? static_cast<uint32_t>((wi >> sshift) * 4) : kMasked);
   }
 }
 
@@ -379,12 +393,12 @@ __device__ __forceinline__ void dq_store(void* out, int64_t e0, const float v[8]
 
 template <int U, bool kBf16>
 __device__ __forceinline__ void dq_decode(const DqTile<U>& t, int64_t tile, int64_t words, const float* s_lut,
-                                          const float* s_q2, float off, void* out) {
+                                          const float* s_q2, float off, bool single, void* out) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t wi = tile * (kQuantThreads * U) + threadIdx.x + static_cast<int64_t>(u) * kQuantThreads;
     if (wi < words) {
-      const float ahat = __fadd_rn(__fmul_rn(s_q2[t.q[u] + kLevels2], t.s2[u]), off);
+      const float ahat = single ? t.s2[u] : __fadd_rn(__fmul_rn(s_q2[t.q[u] + kLevels2], t.s2[u]), off);
       float v[8];
       decode8(t.wd[u], ahat, s_lut, v);
       dq_store<kBf16>(out, wi * 8, v);
@@ -393,26 +407,27 @@ __device__ __forceinline__ void dq_decode(const DqTile<U>& t, int64_t tile, int6
 }
 
 template <int U, bool kBf16>
-__global__ __launch_bounds__(kQuantThreads) void nf4_dequant_kernel(
-    const uint8_t* __restrict__ codes, const int8_t* __restrict__ qabsmax,
-    const float* __restrict__ absmax2, const float* __restrict__ offset, int64_t P,
-    void* __restrict__ out, int32_t* __restrict__ status) {
+__global__ __launch_bounds__(kQuantThreads) void nf4_dequant_kernel(NF4View W, int64_t P, void* __restrict__ out,
+                                                                    int32_t* __restrict__ status) {
   __shared__ float s_lut[16];
   __shared__ float s_q2[2 * kLevels2 + 2];
   const int tid = threadIdx.x;
   const int64_t n1 = (P + kBlock1 - 1) / kBlock1;
   const int64_t code_bytes = (P + 1) / 2;
   const int64_t words = P >> 3;   // whole words
+  const uint8_t* __restrict__ codes = W.codes;
+  const bool single = W.absmax != nullptr;   // no second level: â = absmax[block]
   const Rsrc rc = make_rsrc(codes, words * 4);
-  const Rsrc rq = make_rsrc(qabsmax, n1);
-  const Rsrc rs = make_rsrc(absmax2, ((n1 + kBlock2 - 1) / kBlock2) * 4);
+  const Rsrc rq = make_rsrc(W.qabsmax, single ? 0 : n1);
+  const Rsrc rs = single ? make_rsrc(W.absmax, n1 * 4) : make_rsrc(W.absmax2, ((n1 + kBlock2 - 1) / kBlock2) * 4);
+  const int sshift = single ? 3 : 11;
   const int64_t tiles = (words + kQuantThreads * U - 1) / (kQuantThreads * U);
   int64_t tile = blockIdx.x;
   DqTile<U> cur;
-  dq_load(cur, tile, words, rc, rq, rs);
+  dq_load(cur, tile, words, rc, rq, rs, sshift);
   if (tid < 16) s_lut[tid] = kNF4[tid];
   if (tid <= 2 * kLevels2) s_q2[tid] = q2_value(tid - kLevels2);
-  const float off = offset[0];
+  const float off = single ? 0.0f : W.offset[0];
   __syncthreads();
   if (blockIdx.x == 0 && tid == 0 && (P & 7)) {
     uint32_t word = 0;
@@ -421,7 +436,8 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_dequant_kernel(
     // odd P: the pad nibble (low half of the last byte) must be code 7
     if ((P & 1) && status && (codes[code_bytes - 1] & 15u) != 7u) atomicOr(status, NF4_EPADDING);
     float v[8];
-    decode8(word, absmax_hat(qabsmax[n1 - 1], absmax2[(n1 - 1) / kBlock2], off), s_lut, v);
+    decode8(word, single ? W.absmax[n1 - 1] : absmax_hat(W.qabsmax[n1 - 1], W.absmax2[(n1 - 1) / kBlock2], off),
+            s_lut, v);
     for (int i = 0; i < 8; ++i) {
       const int64_t e = words * 8 + i;
       if (e >= P) break;
@@ -432,11 +448,11 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_dequant_kernel(
   // two register tiles in turn, so no copy waits on loads still in flight
   DqTile<U> nxt;
   for (; tile < tiles; tile += 2 * static_cast<int64_t>(gridDim.x)) {
-    dq_load(nxt, tile + gridDim.x, words, rc, rq, rs);
-    dq_decode<U, kBf16>(cur, tile, words, s_lut, s_q2, off, out);
+    dq_load(nxt, tile + gridDim.x, words, rc, rq, rs, sshift);
+    dq_decode<U, kBf16>(cur, tile, words, s_lut, s_q2, off, single, out);
     if (tile + gridDim.x >= tiles) break;
-    dq_load(cur, tile + 2 * static_cast<int64_t>(gridDim.x), words, rc, rq, rs);
-    dq_decode<U, kBf16>(nxt, tile + gridDim.x, words, s_lut, s_q2, off, out);
+    dq_load(cur, tile + 2 * static_cast<int64_t>(gridDim.x), words, rc, rq, rs, sshift);
+    dq_decode<U, kBf16>(nxt, tile + gridDim.x, words, s_lut, s_q2, off, single, out);
   }
 }
 
@@ -446,10 +462,7 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_dequant_kernel(
 // bf16 writes (along k) are row-contiguous.
 constexpr int kTPad = 66;  // bf16 per LDS row (64 k + 2): 132-byte rows
 
-__global__ __launch_bounds__(256) void nf4_dequant_t_kernel(const uint8_t* __restrict__ codes,
-                                                            const int8_t* __restrict__ qabsmax,
-                                                            const float* __restrict__ absmax2,
-                                                            const float* __restrict__ offset, int64_t K, int64_t N,
+__global__ __launch_bounds__(256) void nf4_dequant_t_kernel(NF4View W, int64_t K, int64_t N,
                                                             uint16_t* __restrict__ out) {
   __shared__ float s_lut[16];
   __shared__ __attribute__((aligned(16))) uint16_t tile[128 * kTPad];
@@ -457,7 +470,8 @@ __global__ __launch_bounds__(256) void nf4_dequant_t_kernel(const uint8_t* __res
   if (t < 16) s_lut[t] = kNF4[t];
   __syncthreads();
   const int64_t k0 = static_cast<int64_t>(blockIdx.y) * 64, n0 = static_cast<int64_t>(blockIdx.x) * 128;
-  const float off = offset[0];
+  const bool single = W.absmax != nullptr;   // no second level: â = absmax[block]
+  const float off = single ? 0.0f : W.offset[0];
   {
     const int kk = t >> 2, part = t & 3;           // row k0+kk, columns n0 + 32*part .. +31 (one block)
     const int64_t k = k0 + kk, nb = n0 + 32 * part;
@@ -466,8 +480,8 @@ __global__ __launch_bounds__(256) void nf4_dequant_t_kernel(const uint8_t* __res
     uint32_t w[4] = {0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
     if (ok) {
       const int64_t e0 = k * N + nb;
-      ahat = absmax_hat(qabsmax[e0 >> 6], absmax2[e0 >> 14], off);
-      const uint4 v = *reinterpret_cast<const uint4*>(codes + (e0 >> 1));
+      ahat = single ? W.absmax[e0 >> 6] : absmax_hat(W.qabsmax[e0 >> 6], W.absmax2[e0 >> 14], off);
+      const uint4 v = *reinterpret_cast<const uint4*>(W.codes + (e0 >> 1));
       w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
     }
 #pragma unroll
@@ -493,14 +507,22 @@ __global__ __launch_bounds__(256) void nf4_dequant_t_kernel(const uint8_t* __res
 
 // ----------------------------------------------------------------- launchers
 hipError_t launch_quantize(const float* W, int64_t P, uint8_t* codes, int8_t* qabsmax,
-                           float* absmax2, float* offset, float* ws_absmax, double* ws_gsum,
+                           float* absmax2, float* offset, float* absmax_out, float* ws_absmax, double* ws_gsum,
                            int32_t* ws_flags, int32_t* status, hipStream_t stream) {
   const int64_t n1 = (P + kBlock1 - 1) / kBlock1;
   const int64_t n2 = (n1 + kBlock2 - 1) / kBlock2;
   Timer t1(QK_QUANT_PASS1, stream);
   hipLaunchKernelGGL(nf4_quant_pass1_kernel, dim3(static_cast<unsigned>(n2)), dim3(kQuantThreads), 0,
-                     stream, W, P, codes, ws_absmax, ws_gsum, ws_flags, status);
+                     stream, W, P, codes, absmax_out != nullptr ? absmax_out : ws_absmax, ws_gsum, ws_flags, status);
   t1.stop();
+  if (absmax_out != nullptr) {
+    // single-level state: the exact absmax values are the stored scales; only
+    // the groups' non-finite flags remain to be reported
+    Timer t3(QK_QUANT_PASS2, stream);
+    hipLaunchKernelGGL(nf4_quant_flags_kernel, dim3(1), dim3(kQuantThreads), 0, stream, ws_flags, n2, status);
+    t3.stop();
+    return hipGetLastError();
+  }
   if (n2 > kSelfMeanGroups) {
     if (n2 > static_cast<int64_t>(kMeanThreads) * kMaxSumPerThread) return hipErrorInvalidValue;
     Timer t2(QK_QUANT_MEAN, stream);
@@ -515,29 +537,25 @@ hipError_t launch_quantize(const float* W, int64_t P, uint8_t* codes, int8_t* qa
   return hipGetLastError();
 }
 
-hipError_t launch_dequantize(const uint8_t* codes, const int8_t* qabsmax, const float* absmax2,
-                             const float* offset, int64_t P, void* out, int out_dtype,
-                             int32_t* status, hipStream_t stream) {
+hipError_t launch_dequantize(NF4View W, int64_t P, void* out, int out_dtype, int32_t* status, hipStream_t stream) {
   constexpr int U = QN_DQ_U;
   const int64_t tiles = (P / 8 + kQuantThreads * U - 1) / (kQuantThreads * U);
   const int64_t blocks = tiles < 1 ? 1 : (tiles < QN_DQ_GRID ? tiles : QN_DQ_GRID);
   const Timer t(QK_DEQUANT, stream, true);
   if (out_dtype == NF4_OUT_BF16)
     hipExtLaunchKernelGGL((nf4_dequant_kernel<U, true>), dim3(static_cast<unsigned>(blocks)), dim3(kQuantThreads),
-                          0, stream, t.start(), t.end(), 0, codes, qabsmax, absmax2, offset, P, out, status);
+                          0, stream, t.start(), t.end(), 0, W, P, out, status);
   else
     hipExtLaunchKernelGGL((nf4_dequant_kernel<U, false>), dim3(static_cast<unsigned>(blocks)), dim3(kQuantThreads),
-                          0, stream, t.start(), t.end(), 0, codes, qabsmax, absmax2, offset, P, out, status);
+                          0, stream, t.start(), t.end(), 0, W, P, out, status);
   return hipGetLastError();
 }
 
-hipError_t launch_dequant_bf16(const uint8_t* codes, const int8_t* qabsmax, const float* absmax2,
-                               const float* offset, int64_t K, int64_t N, bool transposed, uint16_t* out,
-                               hipStream_t stream) {
-  if (!transposed) return launch_dequantize(codes, qabsmax, absmax2, offset, K * N, out, NF4_OUT_BF16, nullptr, stream);
+hipError_t launch_dequant_bf16(NF4View W, int64_t K, int64_t N, bool transposed, uint16_t* out, hipStream_t stream) {
+  if (!transposed) return launch_dequantize(W, K * N, out, NF4_OUT_BF16, nullptr, stream);
   Timer t(QK_DEQUANT_BF16, stream);
   dim3 grid(static_cast<unsigned>((N + 127) / 128), static_cast<unsigned>((K + 63) / 64));
-  hipLaunchKernelGGL(nf4_dequant_t_kernel, grid, dim3(256), 0, stream, codes, qabsmax, absmax2, offset, K, N, out);
+  hipLaunchKernelGGL(nf4_dequant_t_kernel, grid, dim3(256), 0, stream, W, K, N, out);
   t.stop();
   return hipGetLastError();
 }

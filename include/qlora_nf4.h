@@ -57,15 +57,21 @@ extern "C" {
 #define NF4_BLOCK2  256
 #define NF4_LEVELS2 127
 
-/* The stored, frozen state of one weight tensor (all device pointers;
- * codes and qabsmax 16-byte aligned, absmax2 and offset 4-byte aligned, or
- * every entry point taking the state returns NF4_EINVAL). */
+/* The stored, frozen state of one weight tensor (all device pointers).
+ * Double-quantized (absmax == NULL): codes, qabsmax, absmax2 and offset are
+ * used; codes and qabsmax 16-byte aligned, absmax2 and offset 4-byte aligned.
+ * Single-level (absmax != NULL; the pages' configuration with double
+ * quantization switched off): codes and absmax are used, one fp32 scale per
+ * 64-block, â = absmax; qabsmax, absmax2 and offset are ignored (may be NULL).
+ * Any other combination makes every entry point taking the state return
+ * NF4_EINVAL. */
 typedef struct nf4_state {
   int64_t  numel;    /* P, the logical number of weights (>= 1)            */
   uint8_t* codes;    /* ceil(P/2) bytes, packed NF4 codes                  */
   int8_t*  qabsmax;  /* n1 = ceil(P/64) second-level codes                 */
   float*   absmax2;  /* n2 = ceil(n1/256) fp32 second-level scales         */
   float*   offset;   /* 1 fp32, the mean of the first-level absmax values  */
+  float*   absmax;   /* NULL, or n1 fp32 first-level scales (no second level) */
 } nf4_state_t;
 
 /* Host only.  Sizes of the state of a P-weight tensor (closed forms of the
@@ -75,7 +81,10 @@ int nf4_sizes(int64_t numel, int64_t* code_bytes, int64_t* n1, int64_t* n2,
               int64_t* quant_workspace_bytes);
 
 /* Encode P fp32 weights (device, 16-byte aligned) into `out` (all buffers
- * sized per nf4_sizes; out->numel must equal P).  `workspace` is device
+ * sized per nf4_sizes; out->numel must equal P).  With out->absmax non-NULL
+ * the encoding stops at the first level: the exact per-block absmax values
+ * are written there and nothing else is (storage 8*ceil(P/2) + 32*n1 bits,
+ * page section "Double Quantization 压缩的是 Scale").  `workspace` is device
  * memory of at least quant_workspace_bytes, 256-byte aligned.  `status` is a
  * device int32 that the call first sets to 0; the GPU ORs NF4_ENONFINITE into
  * it if a weight is NaN/Inf or a reconstructed scale overflows (the page
@@ -86,7 +95,8 @@ int nf4_quantize(const float* W, const nf4_state_t* out, void* workspace,
                  int64_t workspace_bytes, int32_t* status, void* stream);
 
 /* Decode a state to P weights: ŵ = fl32(C[j] * â) with
- * â = fl32(fl32(fl32(q/127) * s2) + offset), written as fp32
+ * â = fl32(fl32(fl32(q/127) * s2) + offset) (or â = absmax for a
+ * single-level state), written as fp32
  * (NF4_OUT_F32) or round-to-nearest-even bf16 (NF4_OUT_BF16).  `out` is
  * device memory of P elements, 16-byte aligned.  `status` (device int32,
  * may be NULL) receives NF4_EPADDING if P is odd and the last pad nibble is

@@ -77,7 +77,9 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert L.nf4_dequantize(ctypes.byref(st), 0x100, 7, None, None) == qn.NF4_EINVAL
     # state buffers moved as words: misaligned codes / second-level codes / scales
     for bad_state in (qn._State(64, 0x1004, 0x2000, 0x3000, 0x4000), qn._State(64, 0x1000, 0x2001, 0x3000, 0x4000),
-                      qn._State(64, 0x1000, 0x2000, 0x3002, 0x4000)):
+                      qn._State(64, 0x1000, 0x2000, 0x3002, 0x4000),
+                      qn._State(64, 0x1000, None, None, None, 0x5002),     # single level, misaligned scales
+                      qn._State(64, 0x1000, None, 0x3000, 0x4000, None)):  # double quantized without codes q
         assert L.nf4_quantize(0x100, ctypes.byref(bad_state), 0x10000, 1 << 20, 0x5000, None) == qn.NF4_EINVAL
         assert L.nf4_dequantize(ctypes.byref(bad_state), 0x100, qn.NF4_OUT_F32, None, None) == qn.NF4_EINVAL
     # layer: numel mismatch, N % 64, NULL output
