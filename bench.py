@@ -300,6 +300,48 @@ def bench_components(torch, qn, si, dev, sets, outs, qws, status):
                            "frac_fp64_peak": round(mfl / (mms * 1e-3) / 1e12 / FP64_PEAK_TFLOPS, 4),
                            "flops": mfl}
     del wm, Amd, Bmd
+    # grouped q, k, v of the 7B block (3 x 4096 columns sharing X, r = 64 each)
+    # against three separate linears, fwd + bwd each way
+    Kg, Ng, rg, cg, Mg = 4096, 4096, 64, 0.25, 4096
+    gst = [outs[i]["state"] for i in range(3)]
+    Xg = sets[0]["X"]
+    Ag = torch.cat([sets[i]["A"] for i in range(3)], dim=1).contiguous()
+    Bg = torch.cat([sets[i]["B"] for i in range(3)], dim=1).contiguous()
+    Gg = torch.cat([sets[i]["G"] for i in range(3)], dim=1).contiguous()
+    Ns = [Ng] * 3
+    fgw, bgw = qn.qlora_grouped_workspace_bytes(Mg, Kg, Ns, rg)
+    gws = torch.empty(max(fgw, bgw), dtype=torch.uint8, device=dev)
+    Yg = torch.empty(Mg, 3 * Ng, dtype=torch.bfloat16, device=dev)
+    Zg = torch.empty(Mg, 3 * rg, dtype=torch.bfloat16, device=dev)
+    dXg = torch.empty(Mg, Kg, dtype=torch.bfloat16, device=dev)
+    dAg = torch.empty(Kg, 3 * rg, dtype=torch.float32, device=dev)
+    dBg = torch.empty(rg, 3 * Ng, dtype=torch.float32, device=dev)
+
+    def grouped(i):
+        qn.qlora_grouped_fwd(Xg, gst, Ag, Bg, cg, Kg, Ns, Yg, Zg, gws)
+        qn.qlora_grouped_bwd(Gg, Xg, Zg, gst, Ag, Bg, cg, Kg, Ns, True, dXg, dAg, dBg, gws)
+
+    fsw, bsw = qn.qlora_workspace_bytes(Mg, Kg, Ng, rg)
+    sws = torch.empty(max(fsw, bsw), dtype=torch.uint8, device=dev)
+
+    def separate(i):
+        for j in range(3):
+            o = outs[j]
+            qn.qlora_linear_fwd(Xg, gst[j], sets[j]["A"], sets[j]["B"], cg, Kg, Ng, o["Y"], o["Z"], sws)
+            qn.qlora_linear_bwd(sets[j]["G"], Xg, o["Z"], gst[j], sets[j]["A"], sets[j]["B"], cg, Kg, Ng, True,
+                                o["dX"], o["dA"], o["dB"], sws)
+
+    for fn in (grouped, separate):
+        fn(0)
+    gms = _time_calls(torch, grouped, 5, flush)
+    sms = _time_calls(torch, separate, 5, flush)
+    gfl = 3 * sum(layer_flops(Mg, Kg, Ng, rg))
+    res["grouped_qkv_attn7b"] = {"grouped_ms": round(gms, 4), "separate_ms": round(sms, 4),
+                                 "grouped_TFLOPs": round(gfl / (gms * 1e-3) / 1e12, 1),
+                                 "separate_TFLOPs": round(gfl / (sms * 1e-3) / 1e12, 1),
+                                 "how": "fwd + bwd of q, k, v (3 x 4096 x 4096, r = 64, M = 4096): one grouped "
+                                        "call each way vs three single-linear calls each way, cache flushed"}
+    del gws, sws, Yg, Zg, dXg, dAg, dBg, Ag, Bg, Gg
     # the vendor library's plain bf16 GEMM of the same base shape on this
     # device (torch.matmul -> hipBLASLt), as context for the MFMA fraction
     Mv, Kv, Nv = 4096, 4096, 4096

@@ -24,7 +24,8 @@ KERNEL_IDS = {
 C_FUNCTIONS = [
     "nf4_sizes", "nf4_quantize", "nf4_dequantize", "qlora_workspace_bytes",
     "qlora_linear_fwd", "qlora_linear_bwd", "nf4_status_read", "qlora_timer_enable",
-    "qlora_timer_read", "qlora_merge", "qlora_sgd_step", "nf4_error_string",
+    "qlora_timer_read", "qlora_merge", "qlora_sgd_step", "qlora_grouped_workspace_bytes",
+    "qlora_grouped_fwd", "qlora_grouped_bwd", "nf4_error_string",
 ]
 
 
@@ -64,6 +65,12 @@ def lib() -> ctypes.CDLL:
         L.qlora_timer_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
         L.qlora_merge.argtypes = [i64, i64, i64, sp, vp, vp, ctypes.c_int, ctypes.c_float, vp, vp]
         L.qlora_sgd_step.argtypes = [i64, i64, i64, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
+        i64p = ctypes.POINTER(i64)
+        L.qlora_grouped_workspace_bytes.argtypes = [i64, i64, ctypes.c_int, i64p, i64, i64p, i64p]
+        L.qlora_grouped_fwd.argtypes = [i64, i64, ctypes.c_int, i64p, i64, vp, sp, vp, vp, ctypes.c_float,
+                                        vp, vp, vp, i64, vp]
+        L.qlora_grouped_bwd.argtypes = [i64, i64, ctypes.c_int, i64p, i64, vp, vp, vp, sp, vp, vp, ctypes.c_float,
+                                        vp, vp, vp, vp, i64, vp]
         L.nf4_error_string.argtypes = [ctypes.c_int]
         L.nf4_error_string.restype = ctypes.c_char_p
         for name in C_FUNCTIONS[:-1]:
@@ -166,6 +173,70 @@ def nf4_dequantize(state: NF4State, out_dtype: str = "bf16", out=None, status=No
                                 NF4_OUT_BF16 if out_dtype == "bf16" else NF4_OUT_F32,
                                 _ptr(status), _stream(stream)), "nf4_dequantize")
     return out
+
+
+def _group_args(states, Ns):
+    g = len(Ns)
+    if len(states) != g or not 1 <= g <= 8:
+        raise ValueError("one state per member, 1 to 8 members")
+    return g, (ctypes.c_int64 * g)(*Ns), (_State * g)(*[s.c_struct() for s in states])
+
+
+def qlora_grouped_workspace_bytes(M: int, K: int, Ns, r: int) -> tuple[int, int]:
+    f, b = ctypes.c_int64(), ctypes.c_int64()
+    arr = (ctypes.c_int64 * len(Ns))(*Ns)
+    _check(lib().qlora_grouped_workspace_bytes(M, K, len(Ns), arr, r, ctypes.byref(f), ctypes.byref(b)),
+           "qlora_grouped_workspace_bytes")
+    return f.value, b.value
+
+
+def qlora_grouped_fwd(X, states, A, B, c: float, K: int, Ns, Y=None, Z=None, workspace=None, stream=None):
+    """Members sharing X, side by side: A = [A_i] (K x g r), B = [B_i] (r x sum N),
+    returns (Y = [Y_i] (M x sum N), Z = [Z_i] (M x g r))."""
+    import torch
+    g, Narr, Sarr = _group_args(states, Ns)
+    M = X.shape[0]
+    r = A.shape[1] // g
+    Ntot = sum(Ns)
+    for t, n in ((X, "X"), (A, "A"), (B, "B")):
+        _require_cuda(t, n, torch.bfloat16)
+    if Y is None:
+        Y = torch.empty(M, Ntot, dtype=torch.bfloat16, device=X.device)
+    if Z is None:
+        Z = torch.empty(M, g * r, dtype=torch.bfloat16, device=X.device)
+    if workspace is None:
+        workspace = torch.empty(max(qlora_grouped_workspace_bytes(M, K, Ns, r)[0], 256), dtype=torch.uint8,
+                                device=X.device)
+    _check(lib().qlora_grouped_fwd(M, K, g, Narr, r, X.data_ptr(), Sarr, A.data_ptr(), B.data_ptr(),
+                                   ctypes.c_float(c), Y.data_ptr(), Z.data_ptr(), workspace.data_ptr(),
+                                   workspace.numel(), _stream(stream)), "qlora_grouped_fwd")
+    return Y, Z
+
+
+def qlora_grouped_bwd(G, X, Z, states, A, B, c: float, K: int, Ns, need_dx: bool = True, dX=None, dA=None,
+                      dB=None, workspace=None, stream=None):
+    """Returns (dX or None, dA = [dA_i] (K x g r fp32), dB = [dB_i] (r x sum N fp32))."""
+    import torch
+    g, Narr, Sarr = _group_args(states, Ns)
+    M = X.shape[0]
+    r = A.shape[1] // g
+    Ntot = sum(Ns)
+    for t, n in ((G, "G"), (X, "X"), (Z, "Z"), (A, "A"), (B, "B")):
+        _require_cuda(t, n, torch.bfloat16)
+    if need_dx and dX is None:
+        dX = torch.empty(M, K, dtype=torch.bfloat16, device=X.device)
+    if dA is None:
+        dA = torch.empty(K, g * r, dtype=torch.float32, device=X.device)
+    if dB is None:
+        dB = torch.empty(r, Ntot, dtype=torch.float32, device=X.device)
+    if workspace is None:
+        workspace = torch.empty(max(qlora_grouped_workspace_bytes(M, K, Ns, r)[1], 256), dtype=torch.uint8,
+                                device=X.device)
+    _check(lib().qlora_grouped_bwd(M, K, g, Narr, r, G.data_ptr(), X.data_ptr(), Z.data_ptr(), Sarr,
+                                   A.data_ptr(), B.data_ptr(), ctypes.c_float(c),
+                                   dX.data_ptr() if need_dx else None, dA.data_ptr(), dB.data_ptr(),
+                                   workspace.data_ptr(), workspace.numel(), _stream(stream)), "qlora_grouped_bwd")
+    return (dX if need_dx else None), dA, dB
 
 
 NF4_AB_BF16, NF4_AB_F32 = 0, 1

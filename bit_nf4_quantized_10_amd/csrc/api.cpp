@@ -167,6 +167,67 @@ int qlora_linear_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t*
   return e == hipSuccess ? NF4_OK : NF4_EHIP;
 }
 
+static bool grouped_shape_ok(int64_t M, int64_t K, int g, const int64_t* N, int64_t r, int64_t* Ntot) {
+  if (g < 1 || g > qn::kMaxGroupMembers || N == nullptr || r < 1) return false;
+  int64_t tot = 0;
+  for (int i = 0; i < g; ++i) {
+    if (N[i] < 256 || N[i] % 256 != 0 || N[i] > (int64_t(1) << 24)) return false;
+    tot += N[i];
+  }
+  *Ntot = tot;
+  return layer_shape_ok(M, K, tot, g * r);
+}
+
+static bool grouped_states_ok(const nf4_state_t* W, int g, int64_t K, const int64_t* N, qn::NF4View* views) {
+  if (W == nullptr) return false;
+  for (int i = 0; i < g; ++i) {
+    if (!state_ok(&W[i]) || W[i].numel != K * N[i]) return false;
+    views[i] = view_of(&W[i]);
+  }
+  return true;
+}
+
+int qlora_grouped_workspace_bytes(int64_t M, int64_t K, int g, const int64_t* N, int64_t r, int64_t* fwd_bytes,
+                                  int64_t* bwd_bytes) {
+  int64_t Ntot;
+  if (!grouped_shape_ok(M, K, g, N, r, &Ntot)) return NF4_EINVAL;
+  if (fwd_bytes) *fwd_bytes = qn::grouped_fwd_workspace_bytes(M, K, g, N, r);
+  if (bwd_bytes) *bwd_bytes = qn::grouped_bwd_workspace_bytes(M, K, g, N, r);
+  return NF4_OK;
+}
+
+int qlora_grouped_fwd(int64_t M, int64_t K, int g, const int64_t* N, int64_t r, const uint16_t* X,
+                      const nf4_state_t* W, const uint16_t* A, const uint16_t* B, float c, uint16_t* Y, uint16_t* Z,
+                      void* workspace, int64_t workspace_bytes, void* stream) {
+  int64_t Ntot;
+  qn::NF4View views[qn::kMaxGroupMembers];
+  if (!grouped_shape_ok(M, K, g, N, r, &Ntot) || !grouped_states_ok(W, g, K, N, views)) return NF4_EINVAL;
+  if (!X || !A || !B || !Y || !Z || !workspace) return NF4_EINVAL;
+  if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y) || !aligned16(Z) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return NF4_EINVAL;
+  if (workspace_bytes < qn::grouped_fwd_workspace_bytes(M, K, g, N, r)) return NF4_EINVAL;
+  hipError_t e = qn::launch_grouped_fwd(M, K, g, N, r, X, views, A, B, c, Y, Z, workspace,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4_OK : NF4_EHIP;
+}
+
+int qlora_grouped_bwd(int64_t M, int64_t K, int g, const int64_t* N, int64_t r, const uint16_t* G, const uint16_t* X,
+                      const uint16_t* Z, const nf4_state_t* W, const uint16_t* A, const uint16_t* B, float c,
+                      uint16_t* dX, float* dA, float* dB, void* workspace, int64_t workspace_bytes, void* stream) {
+  int64_t Ntot;
+  qn::NF4View views[qn::kMaxGroupMembers];
+  if (!grouped_shape_ok(M, K, g, N, r, &Ntot) || !grouped_states_ok(W, g, K, N, views)) return NF4_EINVAL;
+  if (!G || !X || !Z || !A || !B || !dA || !dB || !workspace) return NF4_EINVAL;
+  if (!aligned16(G) || !aligned16(X) || !aligned16(Z) || !aligned16(A) || !aligned16(B) || !aligned16(dA) ||
+      !aligned16(dB) || (dX && !aligned16(dX)) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return NF4_EINVAL;
+  if (workspace_bytes < qn::grouped_bwd_workspace_bytes(M, K, g, N, r)) return NF4_EINVAL;
+  hipError_t e = qn::launch_grouped_bwd(M, K, g, N, r, G, X, Z, views, A, B, c, dX, dA, dB, workspace,
+                                        static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NF4_OK : NF4_EHIP;
+}
+
 int qlora_merge(int64_t K, int64_t N, int64_t r, const nf4_state_t* W, const void* A, const void* B, int ab_dtype,
                 float c, float* W_merged, void* stream) {
   if (K < 1 || N < 1 || r < 1 || r > 65536 || !state_ok(W) || W->numel != K * N) return NF4_EINVAL;

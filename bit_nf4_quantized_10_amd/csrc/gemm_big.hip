@@ -71,6 +71,13 @@ struct BigArgs {
   uint16_t* out;           // Y (M x N) or dX (M x K)
   int64_t M, K, N, r;
   const uint16_t* wdense;  // dense path: Ŵᵀ (N x K, forward) or Ŵ (K x N, backward), bf16
+  // Forward over the concatenated columns of a group of linears sharing X:
+  // ext_a is then M x (ngroups r) (row stride ext_a_ld) and output columns
+  // c >= gend[i] (member i+1 onwards) take their Z from column block i+1.
+  // Zero / unset: one linear, ext_a row stride r.
+  int64_t ext_a_ld;
+  int ngroups;
+  int64_t gend[kMaxGroupMembers];
 };
 
 #ifndef QN_TILE_GROUP
@@ -451,7 +458,11 @@ template <bool kForward, class Core>
 __device__ __forceinline__ void finish(const Core& k, const BigArgs& a, f32x16 (&acc)[4][4]) {
   const int lane = k.lane, t = k.t;
   const int64_t cols = kForward ? a.N : a.K;
-  const Rsrc re = make_rsrc(a.ext_a, a.M * a.r * 2);
+  const int64_t lda = a.ext_a_ld ? a.ext_a_ld : a.r;
+  int64_t zoff = 0;   // grouped forward: this tile's member's block of Z columns
+  if (kForward)
+    for (int i = 0; i < a.ngroups; ++i) zoff += k.c0 >= a.gend[i] ? a.r : 0;
+  const Rsrc re = make_rsrc(a.ext_a + zoff, (a.M * lda - zoff) * 2);
   const Rsrc rb = make_rsrc(a.ext_b, cols * a.r * 2);
   for (int64_t j0 = 0; j0 < a.r; j0 += kBK) {
     const int c = t & 7;
@@ -460,7 +471,7 @@ __device__ __forceinline__ void finish(const Core& k, const BigArgs& a, f32x16 (
     for (int i = 0; i < 8; ++i) {
       const int row = (t >> 3) + 32 * i;
       const int64_t m = k.m0 + row, n = k.c0 + row;
-      const uint4 v = ld_b128(re, (m < a.M && j < a.r) ? static_cast<uint32_t>((m * a.r + j) * 2) : kMasked);
+      const uint4 v = ld_b128(re, (m < a.M && j < a.r) ? static_cast<uint32_t>((m * lda + j) * 2) : kMasked);
       const uint4 w = ld_b128(rb, (n < cols && j < a.r) ? static_cast<uint32_t>((n * a.r + j) * 2) : kMasked);
       *reinterpret_cast<uint4*>(k.sA(0) + lds_off(row, c)) = v;
       *reinterpret_cast<uint4*>(k.sB(0) + lds_off(row, c)) = w;
@@ -665,6 +676,17 @@ hipError_t launch_dense(const BigArgs& a, hipStream_t stream, const Timer& tm) {
 hipError_t launch_fwd_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const uint16_t* WhatT,
                             const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream) {
   BigArgs a{X, K, NF4View{}, Z, cBt, Y, M, K, N, r, WhatT};
+  const Timer t(QK_FWD_GEMM, stream, true);
+  return launch_dense<true>(a, stream, t);
+}
+
+hipError_t launch_fwd_dense_grouped(int64_t M, int64_t K, int64_t Ntot, int64_t r, const uint16_t* X,
+                                    const uint16_t* WhatT, const uint16_t* Zcat, int g, const int64_t* gend,
+                                    const uint16_t* cBt, uint16_t* Y, hipStream_t stream) {
+  BigArgs a{X, K, NF4View{}, Zcat, cBt, Y, M, K, Ntot, r, WhatT};
+  a.ext_a_ld = g * r;
+  a.ngroups = g - 1;
+  for (int i = 0; i + 1 < g; ++i) a.gend[i] = gend[i];
   const Timer t(QK_FWD_GEMM, stream, true);
   return launch_dense<true>(a, stream, t);
 }

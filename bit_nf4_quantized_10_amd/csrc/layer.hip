@@ -79,4 +79,72 @@ hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
   return launch_dx_big(M, K, N, r, G, W, dz16, A, dX, stream);
 }
 
+// ------------------------------------------------------------ grouped linears
+// g members sharing X with their outputs side by side (Y, G: M x Ntot;
+// A, dA: K x g r; B, dB: r x Ntot; Z: M x g r).  Every member is
+// dequantized to bf16 into one stacked weight and the product runs as one
+// dense GEMM over all Ntot columns (forward) or over all Ntot reduction
+// columns (dX), with one Z = X A over all g r columns.
+int64_t grouped_fwd_workspace_bytes(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r) {
+  const GroupPlan gp = plan_grouped(M, K, g, Ns, r);
+  int64_t Ntot = 0;
+  for (int i = 0; i < g; ++i) Ntot += Ns[i];
+  return gp.zp.at_bytes + gp.zp.z_part + align256(Ntot * r * 2) + align256(Ntot * K * 2);
+}
+
+int64_t grouped_bwd_workspace_bytes(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r) {
+  const GroupPlan gp = plan_grouped(M, K, g, Ns, r);
+  int64_t Ntot = 0;
+  for (int i = 0; i < g; ++i) Ntot += Ns[i];
+  return gp.dz_part + align256(M * g * r * 2) + gp.da_part + gp.db_part_total + align256(K * Ntot * 2);
+}
+
+hipError_t launch_grouped_fwd(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r, const uint16_t* X,
+                              const NF4View* W, const uint16_t* A, const uint16_t* B, float c, uint16_t* Y,
+                              uint16_t* Z, void* ws, hipStream_t stream) {
+  const GroupPlan gp = plan_grouped(M, K, g, Ns, r);
+  int64_t Ntot = 0;
+  for (int i = 0; i < g; ++i) Ntot += Ns[i];
+  char* base = static_cast<char*>(ws);
+  char* zpart = base + gp.zp.at_bytes;
+  uint16_t* cbt = reinterpret_cast<uint16_t*>(zpart + gp.zp.z_part);
+  uint16_t* wt = reinterpret_cast<uint16_t*>(zpart + gp.zp.z_part + align256(Ntot * r * 2));
+  hipError_t e = launch_lora_down(M, K, g * r, X, A, Z, gp.zp, base, zpart, stream, Ntot, B, c, cbt, r);
+  if (e != hipSuccess) return e;
+  int64_t gend[kMaxGroupMembers];
+  int64_t off = 0;
+  for (int i = 0; i < g; ++i) {
+    if ((e = launch_dequant_bf16(W[i], K, Ns[i], true, wt + off * K, stream)) != hipSuccess) return e;
+    off += Ns[i];
+    gend[i] = off;
+  }
+  return launch_fwd_dense_grouped(M, K, Ntot, r, X, wt, Z, g, gend, cbt, Y, stream);
+}
+
+hipError_t launch_grouped_bwd(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r, const uint16_t* G,
+                              const uint16_t* X, const uint16_t* Z, const NF4View* W, const uint16_t* A,
+                              const uint16_t* B, float c, uint16_t* dX, float* dA, float* dB, void* ws,
+                              hipStream_t stream) {
+  const GroupPlan gp = plan_grouped(M, K, g, Ns, r);
+  int64_t Ntot = 0;
+  for (int i = 0; i < g; ++i) Ntot += Ns[i];
+  char* base = static_cast<char*>(ws);
+  uint16_t* dz16 = reinterpret_cast<uint16_t*>(base + gp.dz_part);
+  char* da_ws = base + gp.dz_part + align256(M * g * r * 2);
+  char* db_ws = da_ws + gp.da_part;
+  uint16_t* wd = reinterpret_cast<uint16_t*>(db_ws + gp.db_part_total);
+  hipError_t e = launch_dz_grouped(M, g, Ns, Ntot, r, G, B, c, dz16, gp, base, stream);
+  if (e != hipSuccess) return e;
+  if ((e = launch_colsums_grouped(M, K, g, Ns, Ntot, r, X, G, Z, dz16, c, dA, dB, gp, da_ws, db_ws, stream)) !=
+      hipSuccess)
+    return e;
+  if (dX == nullptr) return hipGetLastError();
+  int64_t off = 0;
+  for (int i = 0; i < g; ++i) {
+    if ((e = launch_dequant_bf16(W[i], K, Ns[i], false, wd + off, stream, Ntot)) != hipSuccess) return e;
+    off += Ns[i];
+  }
+  return launch_dx_dense(M, K, Ntot, g * r, G, wd, dz16, A, dX, stream);
+}
+
 }  // namespace qn

@@ -391,9 +391,13 @@ __device__ __forceinline__ void dq_store(void* out, int64_t e0, const float v[8]
   }
 }
 
+// ncols = 0: the output is the flat P-element tensor; else the weight is
+// K x ncols and lands in columns 0 .. ncols-1 of an output with row stride
+// out_ld (ncols a multiple of 8, so a word never straddles two rows).
 template <int U, bool kBf16>
 __device__ __forceinline__ void dq_decode(const DqTile<U>& t, int64_t tile, int64_t words, const float* s_lut,
-                                          const float* s_q2, float off, bool single, void* out) {
+                                          const float* s_q2, float off, bool single, void* out, uint32_t ncols,
+                                          int64_t out_ld) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t wi = tile * (kQuantThreads * U) + threadIdx.x + static_cast<int64_t>(u) * kQuantThreads;
@@ -401,14 +405,20 @@ __device__ __forceinline__ void dq_decode(const DqTile<U>& t, int64_t tile, int6
       const float ahat = single ? t.s2[u] : __fadd_rn(__fmul_rn(s_q2[t.q[u] + kLevels2], t.s2[u]), off);
       float v[8];
       decode8(t.wd[u], ahat, s_lut, v);
-      dq_store<kBf16>(out, wi * 8, v);
+      int64_t dst = wi * 8;
+      if (ncols != 0) {
+        const uint32_t e0 = static_cast<uint32_t>(wi * 8), k = e0 / ncols;
+        dst = static_cast<int64_t>(k) * out_ld + (e0 - k * ncols);
+      }
+      dq_store<kBf16>(out, dst, v);
     }
   }
 }
 
 template <int U, bool kBf16>
 __global__ __launch_bounds__(kQuantThreads) void nf4_dequant_kernel(NF4View W, int64_t P, void* __restrict__ out,
-                                                                    int32_t* __restrict__ status) {
+                                                                    int32_t* __restrict__ status, uint32_t ncols,
+                                                                    int64_t out_ld) {
   __shared__ float s_lut[16];
   __shared__ float s_q2[2 * kLevels2 + 2];
   const int tid = threadIdx.x;
@@ -449,10 +459,10 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_dequant_kernel(NF4View W, i
   DqTile<U> nxt;
   for (; tile < tiles; tile += 2 * static_cast<int64_t>(gridDim.x)) {
     dq_load(nxt, tile + gridDim.x, words, rc, rq, rs, sshift);
-    dq_decode<U, kBf16>(cur, tile, words, s_lut, s_q2, off, single, out);
+    dq_decode<U, kBf16>(cur, tile, words, s_lut, s_q2, off, single, out, ncols, out_ld);
     if (tile + gridDim.x >= tiles) break;
     dq_load(cur, tile + 2 * static_cast<int64_t>(gridDim.x), words, rc, rq, rs, sshift);
-    dq_decode<U, kBf16>(nxt, tile + gridDim.x, words, s_lut, s_q2, off, single, out);
+    dq_decode<U, kBf16>(nxt, tile + gridDim.x, words, s_lut, s_q2, off, single, out, ncols, out_ld);
   }
 }
 
@@ -537,22 +547,26 @@ hipError_t launch_quantize(const float* W, int64_t P, uint8_t* codes, int8_t* qa
   return hipGetLastError();
 }
 
-hipError_t launch_dequantize(NF4View W, int64_t P, void* out, int out_dtype, int32_t* status, hipStream_t stream) {
+hipError_t launch_dequantize(NF4View W, int64_t P, void* out, int out_dtype, int32_t* status, hipStream_t stream,
+                             int64_t ncols, int64_t out_ld) {
   constexpr int U = QN_DQ_U;
   const int64_t tiles = (P / 8 + kQuantThreads * U - 1) / (kQuantThreads * U);
   const int64_t blocks = tiles < 1 ? 1 : (tiles < QN_DQ_GRID ? tiles : QN_DQ_GRID);
   const Timer t(QK_DEQUANT, stream, true);
   if (out_dtype == NF4_OUT_BF16)
     hipExtLaunchKernelGGL((nf4_dequant_kernel<U, true>), dim3(static_cast<unsigned>(blocks)), dim3(kQuantThreads),
-                          0, stream, t.start(), t.end(), 0, W, P, out, status);
+                          0, stream, t.start(), t.end(), 0, W, P, out, status, static_cast<uint32_t>(ncols), out_ld);
   else
     hipExtLaunchKernelGGL((nf4_dequant_kernel<U, false>), dim3(static_cast<unsigned>(blocks)), dim3(kQuantThreads),
-                          0, stream, t.start(), t.end(), 0, W, P, out, status);
+                          0, stream, t.start(), t.end(), 0, W, P, out, status, static_cast<uint32_t>(ncols), out_ld);
   return hipGetLastError();
 }
 
-hipError_t launch_dequant_bf16(NF4View W, int64_t K, int64_t N, bool transposed, uint16_t* out, hipStream_t stream) {
-  if (!transposed) return launch_dequantize(W, K * N, out, NF4_OUT_BF16, nullptr, stream);
+hipError_t launch_dequant_bf16(NF4View W, int64_t K, int64_t N, bool transposed, uint16_t* out, hipStream_t stream,
+                               int64_t out_ld) {
+  if (!transposed)
+    return launch_dequantize(W, K * N, out, NF4_OUT_BF16, nullptr, stream, out_ld != 0 && out_ld != N ? N : 0,
+                             out_ld);
   Timer t(QK_DEQUANT_BF16, stream);
   dim3 grid(static_cast<unsigned>((N + 127) / 128), static_cast<unsigned>((K + 63) / 64));
   hipLaunchKernelGGL(nf4_dequant_t_kernel, grid, dim3(256), 0, stream, W, K, N, out);

@@ -94,6 +94,7 @@ struct RsArgs {
   const uint16_t* wt;
   int64_t M, r, red, per_split, row_blocks, j_chunks;
   float* part;   // [splits][M][r]
+  int64_t act_ld, wt_ld;   // row strides of act (M x red) and wt (r x red)
 };
 
 __device__ __forceinline__ int rs_off(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
@@ -107,7 +108,8 @@ __global__ __launch_bounds__(256) void rowsum_kernel(RsArgs a) {
   const int64_t beg = split * a.per_split;
   const int64_t len = min(a.red, beg + a.per_split) - beg;
   const int64_t nst = (len + 63) / 64;
-  const Rsrc ra = make_rsrc(a.act, a.M * a.red * 2), rw = make_rsrc(a.wt, a.r * a.red * 2);
+  const Rsrc ra = make_rsrc(a.act, ((a.M - 1) * a.act_ld + a.red) * 2);
+  const Rsrc rw = make_rsrc(a.wt, ((a.r - 1) * a.wt_ld + a.red) * 2);
   // copy i (0..1) of each operand fills slot rows 16*wave + 8i .. +7; lane -> row
   // 16*wave + 8i + lane/8, slot position lane & 7, global chunk (lane & 7) ^ (row & 7)
   uint32_t av[2], wv[2];
@@ -116,8 +118,8 @@ __global__ __launch_bounds__(256) void rowsum_kernel(RsArgs a) {
   for (int i = 0; i < 2; ++i) {
     const int R = 16 * wave + 8 * i + (lane >> 3), c = (lane & 7) ^ (R & 7);
     const int64_t m = m0 + R, j = j0 + R;
-    av[i] = m < a.M ? static_cast<uint32_t>((m * a.red + beg + 8 * c) * 2) : kMasked;
-    wv[i] = j < a.r ? static_cast<uint32_t>((j * a.red + beg + 8 * c) * 2) : kMasked;
+    av[i] = m < a.M ? static_cast<uint32_t>((m * a.act_ld + beg + 8 * c) * 2) : kMasked;
+    wv[i] = j < a.r ? static_cast<uint32_t>((j * a.wt_ld + beg + 8 * c) * 2) : kMasked;
     lim[i] = static_cast<int>(len - 8 * c);
   }
   auto copy = [&](int64_t s, int b) {
@@ -198,9 +200,10 @@ constexpr int kCsLds = 4 * kCsSlots * kCsSlot;   // 128 KB
 struct CsJob {
   const uint16_t* act;   // M x cols, leading dimension ld
   int64_t ld, cols;
-  const uint16_t* v;     // M x r
+  const uint16_t* v;     // M x r, leading dimension v_ld
   float* part;           // [splits][cols][r]
   int64_t col_blocks, j_chunks, per_split, nblk;
+  int64_t r, v_ld;
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -215,7 +218,7 @@ __device__ __forceinline__ bf16x8 tr_read2(const char* p0, const char* p1) {
   return __builtin_bit_cast(bf16x8, both);
 }
 
-__global__ __launch_bounds__(256) void colsum_kernel(CsJob j0, CsJob j1, int64_t M, int64_t r) {
+__global__ __launch_bounds__(256) void colsum_kernel(CsJob j0, CsJob j1, int64_t M) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const bool second = blockIdx.x >= j0.nblk;
   const CsJob& J = second ? j1 : j0;
@@ -229,7 +232,8 @@ __global__ __launch_bounds__(256) void colsum_kernel(CsJob j0, CsJob j1, int64_t
   const int64_t wb = mb + wave * share, we = min(me, wb + share);
   const int64_t nsteps = we > wb ? (we - wb + 15) / 16 : 0;
   char* ring = smem + wave * (kCsSlots * kCsSlot);
-  const Rsrc ra = make_rsrc(J.act, M * J.ld * 2), rv = make_rsrc(J.v, M * r * 2);
+  const int64_t r = J.r;
+  const Rsrc ra = make_rsrc(J.act, ((M - 1) * J.ld + J.cols) * 2), rv = make_rsrc(J.v, ((M - 1) * J.v_ld + r) * 2);
   // copy i (0..1) of each operand fills slot rows 8i .. 8i+7: lane -> row
   // 8i + lane/8, slot position lane & 7, global chunk (lane & 7) ^ swizzle
   uint32_t av[2], vv[2];
@@ -239,11 +243,11 @@ __global__ __launch_bounds__(256) void colsum_kernel(CsJob j0, CsJob j1, int64_t
     const int R = 8 * i + (lane >> 3), c = (lane & 7) ^ (((R >> 1) & 1) << 2);
     const int64_t m = wb + R;
     av[i] = c0 + 8 * c < J.cols ? static_cast<uint32_t>((m * J.ld + c0 + 8 * c) * 2) : kMasked;
-    vv[i] = jb + 8 * c < r ? static_cast<uint32_t>((m * r + jb + 8 * c) * 2) : kMasked;
+    vv[i] = jb + 8 * c < r ? static_cast<uint32_t>((m * J.v_ld + jb + 8 * c) * 2) : kMasked;
     lim[i] = static_cast<int>(we - wb - R);   // row valid in step s iff 16 s < lim
   }
   auto copy = [&](int64_t s, int b) {
-    const uint32_t sa = static_cast<uint32_t>(s * 16 * J.ld * 2), sv = static_cast<uint32_t>(s * 16 * r * 2);
+    const uint32_t sa = static_cast<uint32_t>(s * 16 * J.ld * 2), sv = static_cast<uint32_t>(s * 16 * J.v_ld * 2);
     char* slot = ring + b * kCsSlot;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -337,6 +341,7 @@ struct RdJob {
   float* out_f32;
   uint16_t* out_bf16;
   int64_t nblk;
+  int64_t out_ld;   // row stride of the output (cols, or rows when transposed, for a dense result)
 };
 
 __global__ __launch_bounds__(256) void reduce_kernel(RdJob j0, RdJob j1) {
@@ -356,7 +361,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(RdJob j0, RdJob j1) {
     }
     for (; k < J.splits; ++k) s += J.part[k * count + i];
     s *= J.scale;
-    const int64_t o = J.transpose ? (i % J.cols) * J.rows + i / J.cols : i;
+    const int64_t o = J.transpose ? (i % J.cols) * J.out_ld + i / J.cols : (i / J.cols) * J.out_ld + i % J.cols;
     if (J.out_f32) J.out_f32[o] = s;
     if (J.out_bf16) J.out_bf16[o] = bf16_of(s);
   }
@@ -374,7 +379,7 @@ RdJob rdjob(const float* part, int64_t splits, int64_t rows, int64_t cols, float
             uint16_t* out_bf16) {
   int64_t blocks = cdiv(rows * cols, 256);
   if (blocks > 2048) blocks = 2048;
-  return RdJob{part, splits, rows, cols, scale, transpose ? 1 : 0, out_f32, out_bf16, blocks};
+  return RdJob{part, splits, rows, cols, scale, transpose ? 1 : 0, out_f32, out_bf16, blocks, transpose ? rows : cols};
 }
 
 hipError_t launch_reduce(const RdJob& ja, const RdJob* jb, hipStream_t stream) {
@@ -388,7 +393,7 @@ hipError_t launch_reduce(const RdJob& ja, const RdJob* jb, hipStream_t stream) {
 }
 
 hipError_t launch_rowsum(const uint16_t* act, const uint16_t* wt, int64_t M, int64_t r, int64_t red, int64_t splits,
-                         int64_t per, float* part, hipStream_t stream) {
+                         int64_t per, float* part, hipStream_t stream, int64_t act_ld = 0, int64_t wt_ld = 0) {
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rowsum_kernel),
@@ -396,7 +401,7 @@ hipError_t launch_rowsum(const uint16_t* act, const uint16_t* wt, int64_t M, int
     if (e != hipSuccess) return e;
     configured = true;
   }
-  const RsArgs a{act, wt, M, r, red, per, cdiv(M, 64), cdiv(r, 64), part};
+  const RsArgs a{act, wt, M, r, red, per, cdiv(M, 64), cdiv(r, 64), part, act_ld ? act_ld : red, wt_ld ? wt_ld : red};
   hipLaunchKernelGGL(rowsum_kernel, dim3(static_cast<unsigned>(a.row_blocks * a.j_chunks * splits)), dim3(256), kRsLds,
                      stream, a);
   return hipGetLastError();
@@ -433,10 +438,10 @@ SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N, int64_t r) {
 
 hipError_t launch_lora_down(int64_t M, int64_t K, int64_t r, const uint16_t* X, const uint16_t* A, uint16_t* Z,
                             const SkinnyPlan& p, void* at_ws, void* part_ws, hipStream_t stream, int64_t N,
-                            const uint16_t* B, float c, uint16_t* cbt) {
+                            const uint16_t* B, float c, uint16_t* cbt, int64_t rb) {
   uint16_t* At = static_cast<uint16_t*>(at_ws);
   const TJob ja = tjob(A, At, K, r, 1.0f);
-  TJob jb = cbt != nullptr ? tjob(B, cbt, r, N, c) : ja;
+  TJob jb = cbt != nullptr ? tjob(B, cbt, rb ? rb : r, N, c) : ja;
   if (cbt == nullptr) jb.nblk = 0;
   hipLaunchKernelGGL(transpose_bf16_kernel, dim3(static_cast<unsigned>(ja.nblk + jb.nblk)), dim3(256), 0, stream, ja,
                      jb);
@@ -472,18 +477,114 @@ hipError_t launch_colsums(int64_t M, int64_t K, int64_t N, int64_t r, const uint
     configured = true;
   }
   const int64_t jc = cdiv(r, 64);
-  CsJob ja{X, K, K, dZ, static_cast<float*>(da_ws), cdiv(K, 64), jc, p.da_per, 0};
-  CsJob jb{G, N, N, Z, static_cast<float*>(db_ws), cdiv(N, 64), jc, p.db_per, 0};
+  CsJob ja{X, K, K, dZ, static_cast<float*>(da_ws), cdiv(K, 64), jc, p.da_per, 0, r, r};
+  CsJob jb{G, N, N, Z, static_cast<float*>(db_ws), cdiv(N, 64), jc, p.db_per, 0, r, r};
   ja.nblk = ja.col_blocks * jc * p.da_splits;
   jb.nblk = jb.col_blocks * jc * p.db_splits;
   Timer tm(QK_BWD_COLSUM, stream);
-  hipLaunchKernelGGL(colsum_kernel, dim3(static_cast<unsigned>(ja.nblk + jb.nblk)), dim3(256), kCsLds, stream, ja, jb, M, r);
+  hipLaunchKernelGGL(colsum_kernel, dim3(static_cast<unsigned>(ja.nblk + jb.nblk)), dim3(256), kCsLds, stream, ja, jb, M);
   tm.stop();
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const RdJob ra = rdjob(static_cast<float*>(da_ws), p.da_splits, K, r, 1.0f, false, dA, nullptr);
   const RdJob rb = rdjob(static_cast<float*>(db_ws), p.db_splits, N, r, c, true, dB, nullptr);
   return launch_reduce(ra, &rb, stream);
+}
+
+}  // namespace qn
+
+namespace qn {
+
+// ------------------------------------------------------------ grouped linears
+// g members sharing X, concatenated: member i owns columns off_i .. off_i + N_i
+// of G (M x Ntot) and B (r x Ntot), and columns i r .. i r + r of Z, dZ (M x g r)
+// and A, dA (K x g r).
+GroupPlan plan_grouped(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r) {
+  GroupPlan gp{};
+  int64_t Ntot = 0;
+  for (int i = 0; i < g; ++i) Ntot += Ns[i];
+  const int64_t rt = g * r;
+  gp.zp = plan_skinny(M, K, Ntot, rt);
+  int64_t cs_tiles = cdiv(K, 64) * cdiv(rt, 64);
+  for (int i = 0; i < g; ++i) {
+    const SkinnyPlan pi = plan_skinny(M, K, Ns[i], r);
+    gp.dz_splits[i] = pi.dz_splits;
+    gp.dz_per[i] = pi.dz_per;
+    gp.dz_part = gp.dz_part > pi.dz_part ? gp.dz_part : pi.dz_part;
+    cs_tiles += cdiv(Ns[i], 64) * cdiv(r, 64);
+  }
+  split_plan(cs_tiles, M, QN_CS_WGS, 64, &gp.cs_splits, &gp.cs_per);
+  gp.da_part = round_up(gp.cs_splits * K * rt * 4, 256);
+  gp.db_part_total = 0;
+  for (int i = 0; i < g; ++i) {
+    gp.db_off[i] = gp.db_part_total;
+    gp.db_part_total += round_up(gp.cs_splits * Ns[i] * r * 4, 256);
+  }
+  return gp;
+}
+
+// dZ_i = c G_i B_iᵀ for every member: a row-sum over member i's columns of G
+// and B (row stride Ntot), reduced into column block i of dZ (row stride g r).
+hipError_t launch_dz_grouped(int64_t M, int g, const int64_t* Ns, int64_t Ntot, int64_t r, const uint16_t* G,
+                             const uint16_t* B, float c, uint16_t* dZ, const GroupPlan& gp, void* part_ws,
+                             hipStream_t stream) {
+  float* part = static_cast<float*>(part_ws);
+  int64_t off = 0;
+  for (int i = 0; i < g; ++i) {
+    Timer tm(QK_BWD_DZ, stream);
+    hipError_t e = launch_rowsum(G + off, B + off, M, r, Ns[i], gp.dz_splits[i], gp.dz_per[i], part, stream, Ntot, Ntot);
+    tm.stop();
+    if (e != hipSuccess) return e;
+    RdJob jz = rdjob(part, gp.dz_splits[i], M, r, c, false, nullptr, dZ + i * r);
+    jz.out_ld = g * r;
+    if ((e = launch_reduce(jz, nullptr, stream)) != hipSuccess) return e;
+    off += Ns[i];
+  }
+  return hipSuccess;
+}
+
+// dA = Xᵀ dZ (K x g r, all members at once) and, per member, dB_i = c Z_iᵀ G_i
+// into columns off_i .. of dB (r x Ntot); two column-sum jobs per launch.
+hipError_t launch_colsums_grouped(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t Ntot, int64_t r,
+                                  const uint16_t* X, const uint16_t* G, const uint16_t* Z, const uint16_t* dZ, float c,
+                                  float* dA, float* dB, const GroupPlan& gp, void* da_ws, void* db_ws,
+                                  hipStream_t stream) {
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&colsum_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kCsLds);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  const int64_t rt = g * r;
+  CsJob jobs[kMaxGroupMembers + 1];
+  RdJob rds[kMaxGroupMembers + 1];
+  jobs[0] = CsJob{X, K, K, dZ, static_cast<float*>(da_ws), cdiv(K, 64), cdiv(rt, 64), gp.cs_per, 0, rt, rt};
+  rds[0] = rdjob(static_cast<float*>(da_ws), gp.cs_splits, K, rt, 1.0f, false, dA, nullptr);
+  int64_t off = 0;
+  for (int i = 0; i < g; ++i) {
+    float* part = reinterpret_cast<float*>(static_cast<char*>(db_ws) + gp.db_off[i]);
+    jobs[i + 1] = CsJob{G + off, Ntot, Ns[i], Z + i * r, part, cdiv(Ns[i], 64), cdiv(r, 64), gp.cs_per, 0, r, rt};
+    rds[i + 1] = rdjob(part, gp.cs_splits, Ns[i], r, c, true, dB + off, nullptr);
+    rds[i + 1].out_ld = Ntot;
+    off += Ns[i];
+  }
+  for (int j = 0; j <= g; ++j) jobs[j].nblk = jobs[j].col_blocks * jobs[j].j_chunks * gp.cs_splits;
+  for (int j = 0; j <= g; j += 2) {
+    CsJob second = j + 1 <= g ? jobs[j + 1] : jobs[j];
+    if (j + 1 > g) second.nblk = 0;
+    Timer tm(QK_BWD_COLSUM, stream);
+    hipLaunchKernelGGL(colsum_kernel, dim3(static_cast<unsigned>(jobs[j].nblk + second.nblk)), dim3(256), kCsLds,
+                       stream, jobs[j], second, M);
+    tm.stop();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  for (int j = 0; j <= g; j += 2) {
+    hipError_t e = launch_reduce(rds[j], j + 1 <= g ? &rds[j + 1] : nullptr, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace qn

@@ -173,6 +173,33 @@ int qlora_merge(int64_t K, int64_t N, int64_t r, const nf4_state_t* W, const voi
 int qlora_sgd_step(int64_t K, int64_t N, int64_t r, uint16_t* A, uint16_t* B, const float* dA, const float* dB,
                    float lr, float* A_master, float* B_master, void* stream);
 
+/* Grouped linears sharing one input (e.g. the q, k, v projections, or gate
+ * and up: adapters on several projections of one layer, page
+ * "qlora-4bit-quantization-finetune" section "训练全流程" (Q and V) and page
+ * "SFT（四）" §22.1 (all linear layers); each member is the layer of page
+ * "QLoRA：冻结的 4-bit 权重怎样参与一次微调" section "量化基座与可训练支路怎样相加").  g members (1 <= g <= 8),
+ * member i a K x N[i] weight (state W[i]) with its own rank-r adapter; the
+ * members' outputs and adapters are stored side by side:
+ *   Y = [Y_1 .. Y_g] (M x Ntot, Ntot = sum N[i]),  Z = [Z_1 .. Z_g] (M x g r),
+ *   A = [A_1 .. A_g] (K x g r),                   B = [B_1 .. B_g] (r x Ntot),
+ * and Y_i = X Ŵ_i + c Z_i B_i, Z_i = X A_i, i.e. the layer above per member,
+ * with X read once.  Every N[i] must be a multiple of 256; the concatenated
+ * shape (M, K, Ntot, g r) must meet qlora_linear_fwd's requirements; W is a
+ * host array of g states.  All members are dequantized to a bf16 workspace
+ * and multiplied by one dense GEMM for any M.  Host only: */
+int qlora_grouped_workspace_bytes(int64_t M, int64_t K, int g, const int64_t* N, int64_t r,
+                                  int64_t* fwd_bytes, int64_t* bwd_bytes);
+int qlora_grouped_fwd(int64_t M, int64_t K, int g, const int64_t* N, int64_t r, const uint16_t* X,
+                      const nf4_state_t* W, const uint16_t* A, const uint16_t* B, float c,
+                      uint16_t* Y, uint16_t* Z, void* workspace, int64_t workspace_bytes, void* stream);
+/* Backward of the grouped forward given G = dL/dY (M x Ntot, side by side):
+ * dZ_i = c G_i B_iᵀ, dA = Xᵀ [dZ_1 .. dZ_g] (K x g r fp32), dB = [c Z_iᵀ G_i]
+ * (r x Ntot fp32), dX = sum_i (G_i Ŵ_iᵀ + dZ_i A_iᵀ) (skipped when NULL). */
+int qlora_grouped_bwd(int64_t M, int64_t K, int g, const int64_t* N, int64_t r, const uint16_t* G,
+                      const uint16_t* X, const uint16_t* Z, const nf4_state_t* W, const uint16_t* A,
+                      const uint16_t* B, float c, uint16_t* dX, float* dA, float* dB,
+                      void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Synchronise `stream`, then copy the device status word to *host_value.
  * Returns NF4_EHIP if the copy fails, else NF4_OK. */
 int nf4_status_read(const int32_t* status, int32_t* host_value, void* stream);

@@ -130,3 +130,26 @@ def test_adapter_entry_points_reject_bad_arguments():
                  sgd_ok[:8] + (0x500, None, None),                # one master without the other
                  sgd_ok[:5] + (0x302,) + sgd_ok[6:]]:             # misaligned fp32 gradient
         assert L.qlora_sgd_step(*args) == qn.NF4_EINVAL, args
+
+
+def test_grouped_entry_points_reject_bad_arguments():
+    L = qn.lib()
+    i64 = ctypes.c_int64
+
+    def ws(M, K, Ns, r):
+        f, b = i64(), i64()
+        return L.qlora_grouped_workspace_bytes(M, K, len(Ns), (i64 * max(len(Ns), 1))(*Ns), r,
+                                               ctypes.byref(f), ctypes.byref(b))
+
+    assert ws(64, 256, [256, 512], 8) == qn.NF4_OK
+    for M, K, Ns, r in [(64, 256, [256, 320], 8),        # a member not a multiple of 256 columns
+                        (64, 256, [], 8),                # no member
+                        (64, 256, [256] * 9, 8),         # more than 8 members
+                        (64, 256, [256, 256], 160),      # g r above 256
+                        (64, 12, [256], 8)]:             # K % 8
+        assert ws(M, K, Ns, r) == qn.NF4_EINVAL, (M, K, Ns, r)
+    states = (qn._State * 2)(qn._State(256 * 256, 0x1000, 0x2000, 0x3000, 0x4000),
+                             qn._State(256 * 128, 0x1000, 0x2000, 0x3000, 0x4000))   # numel != K * N[1]
+    Ns = (i64 * 2)(256, 256)
+    assert L.qlora_grouped_fwd(8, 256, 2, Ns, 8, 0x100, states, 0x200, 0x300, ctypes.c_float(1.0), 0x400, 0x500,
+                               0x10000, 1 << 30, None) == qn.NF4_EINVAL
