@@ -58,7 +58,7 @@ Readings where the pages leave a step open (the same list is in the design doc):
 
 Parity status of each function (see the tests under tests/):
   nf4_codebook, first_level_absmax, nf4_codes, pack_nibbles, unpack_nibbles,
-  storage_bits, layer_forward, layer_backward, bf16_round: pinned to printed
+  storage_bits, layer_forward, layer_backward, bf16_round, f16_round: pinned to printed
   page values, exact rational brute force, closed forms or finite differences.
   quantize(double_quant=False) / dequantize of such a state: the codes are
   those of the double-quantized encoding (R6), and the reconstruction is
@@ -86,7 +86,7 @@ __all__ = [
     "double_quantize", "reconstruct_absmax", "quantize", "dequantize",
     "reconstruct_weights",
     "bf16_round", "layer_forward", "layer_backward", "storage_bits",
-    "counts", "merge", "sgd_step",
+    "counts", "merge", "sgd_step", "f16_round",
 ]
 
 # [P1] "从 NF4 索引打包成字节": the sixteen reconstruction values, ascending.
@@ -289,6 +289,14 @@ def bf16_round(x32: np.ndarray) -> np.ndarray:
     return t.to(torch.bfloat16).to(torch.float32).numpy()
 
 
+def f16_round(x32: np.ndarray) -> np.ndarray:
+    """fp32 -> fp16 round-to-nearest-even (values from 65520 up round to
+    inf), returned as float32 values (numpy's conversion is the library
+    routine used for this step); [P2] §20: the other 16-bit compute type."""
+    with np.errstate(over="ignore"):   # overflow to inf is the intended result
+        return np.asarray(x32, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
 def dequantize(state: dict, out: str = "fp32") -> np.ndarray:
     """ŵ = fl32(C[j] * â) per weight (reading R5), optionally rounded to bf16
     (the compute dtype, [P3] §3.0).  Unpacks with the page's checks."""
@@ -312,7 +320,9 @@ def reconstruct_weights(codes, ahat_per_weight, out: str = "fp32") -> np.ndarray
         return w
     if out == "bf16":
         return bf16_round(w)
-    raise ValueError("out must be 'fp32' or 'bf16'")
+    if out == "f16":
+        return f16_round(w)
+    raise ValueError("out must be 'fp32', 'bf16' or 'f16'")
 
 
 def layer_forward(X, W_hat, A, B, c):
@@ -360,18 +370,19 @@ def merge(state: dict, A, B, c, K: int, N: int, rows=None) -> np.ndarray:
     return (w + np.float64(c) * acc).astype(np.float32)
 
 
-def sgd_step(param, grad, lr, master=None):
+def sgd_step(param, grad, lr, master=None, dtype: str = "bf16"):
     """One plain SGD update of an adapter tensor ([P1] "一次完整反向与有限差分":
     only the adapter is updated, v <- v - lr * g, and the loss must fall).
     Reading: the step is taken in fp32, p' = fl32(p - fl32(lr * g)), on the
     fp32 master copy when one is kept (else on the bf16 value read as fp32);
-    the bf16 parameter is RNE_bf16(p').  Returns (bf16 values as fp32,
-    the new fp32 master or None)."""
+    the 16-bit parameter is RNE(p') in bf16 (or fp16 with dtype="f16").
+    Returns (16-bit values as fp32, the new fp32 master or None)."""
     g = np.asarray(grad, dtype=np.float32)
     base = np.asarray(master if master is not None else param, dtype=np.float32)
     step = (np.float32(lr) * g).astype(np.float32)
     new = (base - step).astype(np.float32)
-    return bf16_round(new), (new if master is not None else None)
+    rnd = f16_round if dtype == "f16" else bf16_round
+    return rnd(new), (new if master is not None else None)
 
 
 def storage_bits(P: int, double_quant: bool = True) -> int:

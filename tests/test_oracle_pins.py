@@ -111,6 +111,31 @@ def test_merge_requantize_example():
     assert abs(y - float(g["output_approx"])) < tol
 
 
+def exact_round_f16(x: float) -> float:
+    """Round a value to fp16, nearest with ties to even, by exact rationals
+    over the fp16 grid (subnormal spacing 2^-24; 65520 and up -> inf)."""
+    fx = Fraction(float(x))
+    if abs(fx) >= 65520:
+        return math.copysign(math.inf, float(x))
+    e = max(math.floor(math.log2(abs(fx))) if fx != 0 else -24, -14)
+    q = Fraction(2) ** (e - 10)            # spacing of the binade (or of subnormals)
+    k = fx / q
+    lo = math.floor(k)
+    rem = k - lo
+    n = lo + 1 if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1) else lo
+    return float(n * q)
+
+
+def test_f16_round_exact():
+    vals = [1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11, 2.0 ** -24 * 1.5, 2.0 ** -25, 2.0 ** -26, 65504.0, 65519.99,
+            65520.0, -65536.0, 0.1, -0.16093020141124725, 3.0e-6, 1.0 / 3.0, 1234.567]
+    rng = np.random.default_rng(5)
+    vals += list((rng.standard_normal(300) * 10.0 ** rng.uniform(-7, 4.8, 300)).astype(np.float32))
+    got = o.f16_round(np.array(vals, np.float32))
+    for v, g in zip(vals, got):
+        assert float(g) == exact_round_f16(float(np.float32(v))), v
+
+
 def test_single_level_state():
     """Double quantization off: the codes are those of the double-quantized
     encoding (they use the exact absmax either way), the stored scales are
