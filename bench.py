@@ -342,6 +342,27 @@ def bench_components(torch, qn, si, dev, sets, outs, qws, status):
                                  "how": "fwd + bwd of q, k, v (3 x 4096 x 4096, r = 64, M = 4096): one grouped "
                                         "call each way vs three single-linear calls each way, cache flushed"}
     del gws, sws, Yg, Zg, dXg, dAg, dBg, Ag, Bg, Gg
+    # the same layer step in the fp16 compute type (fp16 MFMA, fp16 Ŵ)
+    Xh, Ah, Bh, Gh = (sets[0][k].to(torch.float16) for k in ("X", "A", "B", "G"))
+    fws16, bws16 = qn.qlora_workspace_bytes(Mg, Kg, Ng, rg)
+    ws16 = torch.empty(max(fws16, bws16), dtype=torch.uint8, device=dev)
+    Yh = torch.empty(Mg, Ng, dtype=torch.float16, device=dev)
+    Zh = torch.empty(Mg, rg, dtype=torch.float16, device=dev)
+    dXh = torch.empty(Mg, Kg, dtype=torch.float16, device=dev)
+    dAh = torch.empty(Kg, rg, dtype=torch.float32, device=dev)
+    dBh = torch.empty(rg, Ng, dtype=torch.float32, device=dev)
+
+    def step16(i):
+        qn.qlora_linear_fwd(Xh, gst[0], Ah, Bh, cg, Kg, Ng, Yh, Zh, ws16)
+        qn.qlora_linear_bwd(Gh, Xh, Zh, gst[0], Ah, Bh, cg, Kg, Ng, True, dXh, dAh, dBh, ws16)
+
+    step16(0)
+    hms = _time_calls(torch, step16, 5, flush)
+    hfl = sum(layer_flops(Mg, Kg, Ng, rg))
+    res["fp16_layer_attn7b"] = {"ms": round(hms, 4), "TFLOPs": round(hfl / (hms * 1e-3) / 1e12, 1),
+                                "how": "qlora_linear_fwd + _bwd in the fp16 compute type, 4096 x 4096, r = 64, "
+                                       "M = 4096, cache flushed"}
+    del Xh, Ah, Bh, Gh, ws16, Yh, Zh, dXh, dAh, dBh
     # the vendor library's plain bf16 GEMM of the same base shape on this
     # device (torch.matmul -> hipBLASLt), as context for the MFMA fraction
     Mv, Kv, Nv = 4096, 4096, 4096

@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libqlora_nf4.so")
 
 NF4_OK, NF4_EINVAL, NF4_ENONFINITE, NF4_EPADDING, NF4_EHIP = 0, 1, 2, 4, 8
-NF4_OUT_F32, NF4_OUT_BF16 = 0, 1
+NF4_OUT_F32, NF4_OUT_BF16, NF4_OUT_F16 = 0, 1, 2
+NF4_COMPUTE_BF16, NF4_COMPUTE_F16 = 0, 1
 KERNEL_IDS = {
     "quant_pass1": 0, "quant_mean": 1, "quant_pass2": 2, "dequant": 3, "lora_down": 4,
     "fwd_gemm": 5, "fwd_gemv": 6, "bwd_dz": 7, "bwd_dx": 8, "bwd_colsum": 9, "dequant_bf16": 10,
@@ -25,7 +26,8 @@ C_FUNCTIONS = [
     "nf4_sizes", "nf4_quantize", "nf4_dequantize", "qlora_workspace_bytes",
     "qlora_linear_fwd", "qlora_linear_bwd", "nf4_status_read", "qlora_timer_enable",
     "qlora_timer_read", "qlora_merge", "qlora_sgd_step", "qlora_grouped_workspace_bytes",
-    "qlora_grouped_fwd", "qlora_grouped_bwd", "nf4_error_string",
+    "qlora_grouped_fwd", "qlora_grouped_bwd", "qlora_linear_fwd_dt", "qlora_linear_bwd_dt", "qlora_sgd_step_dt",
+    "nf4_error_string",
 ]
 
 
@@ -71,6 +73,9 @@ def lib() -> ctypes.CDLL:
                                         vp, vp, vp, i64, vp]
         L.qlora_grouped_bwd.argtypes = [i64, i64, ctypes.c_int, i64p, i64, vp, vp, vp, sp, vp, vp, ctypes.c_float,
                                         vp, vp, vp, vp, i64, vp]
+        L.qlora_linear_fwd_dt.argtypes = [ctypes.c_int] + L.qlora_linear_fwd.argtypes
+        L.qlora_linear_bwd_dt.argtypes = [ctypes.c_int] + L.qlora_linear_bwd.argtypes
+        L.qlora_sgd_step_dt.argtypes = [ctypes.c_int] + L.qlora_sgd_step.argtypes
         L.nf4_error_string.argtypes = [ctypes.c_int]
         L.nf4_error_string.restype = ctypes.c_char_p
         for name in C_FUNCTIONS[:-1]:
@@ -164,14 +169,15 @@ def nf4_quantize(W, state: NF4State | None = None, workspace=None, status=None, 
 
 
 def nf4_dequantize(state: NF4State, out_dtype: str = "bf16", out=None, status=None, stream=None):
+    """ŵ as fp32 ("fp32"), bf16 ("bf16") or fp16 ("f16")."""
     import torch
-    dt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    dt, code = {"bf16": (torch.bfloat16, NF4_OUT_BF16), "f16": (torch.float16, NF4_OUT_F16),
+                "fp32": (torch.float32, NF4_OUT_F32)}[out_dtype]
     if out is None:
         out = torch.empty(state.numel, dtype=dt, device=state.codes.device)
     st = state.c_struct()
-    _check(lib().nf4_dequantize(ctypes.byref(st), out.data_ptr(),
-                                NF4_OUT_BF16 if out_dtype == "bf16" else NF4_OUT_F32,
-                                _ptr(status), _stream(stream)), "nf4_dequantize")
+    _check(lib().nf4_dequantize(ctypes.byref(st), out.data_ptr(), code, _ptr(status), _stream(stream)),
+           "nf4_dequantize")
     return out
 
 
@@ -239,7 +245,25 @@ def qlora_grouped_bwd(G, X, Z, states, A, B, c: float, K: int, Ns, need_dx: bool
     return (dX if need_dx else None), dA, dB
 
 
-NF4_AB_BF16, NF4_AB_F32 = 0, 1
+NF4_AB_BF16, NF4_AB_F32, NF4_AB_F16 = 0, 1, 2
+
+
+class _ComputeMap:
+    """torch dtype -> NF4_COMPUTE_* code (torch is imported lazily)."""
+
+    def __getitem__(self, dt):
+        import torch
+        return {torch.bfloat16: NF4_COMPUTE_BF16, torch.float16: NF4_COMPUTE_F16}[dt]
+
+
+_COMPUTE = _ComputeMap()
+
+
+def _compute_dtype(X):
+    import torch
+    if X.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError(f"the compute type is bf16 or fp16, got {X.dtype}")
+    return X.dtype
 
 
 def qlora_merge(state: NF4State, A, B, c: float, K: int, N: int, out=None, stream=None):
@@ -247,8 +271,8 @@ def qlora_merge(state: NF4State, A, B, c: float, K: int, N: int, out=None, strea
     bf16 or both fp32); pass it to nf4_quantize to re-quantize."""
     import torch
     r = A.shape[1]
-    if A.dtype != B.dtype or A.dtype not in (torch.bfloat16, torch.float32):
-        raise ValueError("A and B must both be bf16 or both fp32")
+    if A.dtype != B.dtype or A.dtype not in (torch.bfloat16, torch.float32, torch.float16):
+        raise ValueError("A and B must both be bf16, both fp16 or both fp32")
     for t, n in ((A, "A"), (B, "B")):
         _require_cuda(t, n, A.dtype)
     if tuple(A.shape) != (K, r) or tuple(B.shape) != (r, N):
@@ -257,7 +281,8 @@ def qlora_merge(state: NF4State, A, B, c: float, K: int, N: int, out=None, strea
         out = torch.empty(K * N, dtype=torch.float32, device=A.device)
     st = state.c_struct()
     _check(lib().qlora_merge(K, N, r, ctypes.byref(st), A.data_ptr(), B.data_ptr(),
-                             NF4_AB_F32 if A.dtype == torch.float32 else NF4_AB_BF16, ctypes.c_float(c),
+                             {torch.float32: NF4_AB_F32, torch.float16: NF4_AB_F16}.get(A.dtype, NF4_AB_BF16),
+                             ctypes.c_float(c),
                              out.data_ptr(), _stream(stream)), "qlora_merge")
     return out
 
@@ -268,19 +293,20 @@ def qlora_merge_requantize(state: NF4State, A, B, c: float, K: int, N: int, stre
 
 
 def qlora_sgd_step(A, B, dA, dB, lr: float, A_master=None, B_master=None, stream=None) -> None:
-    """In-place SGD step on the bf16 adapter (optionally through fp32 masters)."""
+    """In-place SGD step on the bf16 or fp16 adapter (optionally through fp32 masters)."""
     import torch
     K, r = A.shape
     N = B.shape[1]
-    for t, n, dt in ((A, "A", torch.bfloat16), (B, "B", torch.bfloat16), (dA, "dA", torch.float32),
+    pdt = _compute_dtype(A)
+    for t, n, dt in ((A, "A", pdt), (B, "B", pdt), (dA, "dA", torch.float32),
                      (dB, "dB", torch.float32)):
         _require_cuda(t, n, dt)
     for m, n in ((A_master, "A_master"), (B_master, "B_master")):
         if m is not None:
             _require_cuda(m, n, torch.float32)
-    _check(lib().qlora_sgd_step(K, N, r, A.data_ptr(), B.data_ptr(), dA.data_ptr(), dB.data_ptr(),
-                                ctypes.c_float(lr), _ptr(A_master), _ptr(B_master), _stream(stream)),
-           "qlora_sgd_step")
+    _check(lib().qlora_sgd_step_dt(_COMPUTE[pdt], K, N, r, A.data_ptr(), B.data_ptr(), dA.data_ptr(),
+                                   dB.data_ptr(), ctypes.c_float(lr), _ptr(A_master), _ptr(B_master),
+                                   _stream(stream)), "qlora_sgd_step_dt")
 
 
 def nf4_status_read(status, stream=None) -> int:
@@ -297,22 +323,24 @@ def qlora_workspace_bytes(M: int, K: int, N: int, r: int) -> tuple[int, int]:
 
 def qlora_linear_fwd(X, state: NF4State, A, B, c: float, K: int, N: int, Y=None, Z=None,
                      workspace=None, stream=None):
-    """Y = X Ŵ + c (X A) B.  X: M x K bf16, A: K x r, B: r x N.  Returns (Y, Z)."""
+    """Y = X Ŵ + c (X A) B.  X: M x K, A: K x r, B: r x N, all bf16 or all fp16
+    (the compute type).  Returns (Y, Z)."""
     import torch
     M, r = X.shape[0], A.shape[1]
+    dt = _compute_dtype(X)
     for t, n in ((X, "X"), (A, "A"), (B, "B")):
-        _require_cuda(t, n, torch.bfloat16)
+        _require_cuda(t, n, dt)
     if Y is None:
-        Y = torch.empty(M, N, dtype=torch.bfloat16, device=X.device)
+        Y = torch.empty(M, N, dtype=dt, device=X.device)
     if Z is None:
-        Z = torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
+        Z = torch.empty(M, r, dtype=dt, device=X.device)
     if workspace is None:
         workspace = torch.empty(max(qlora_workspace_bytes(M, K, N, r)[0], 256), dtype=torch.uint8,
                                 device=X.device)
     st = state.c_struct()
-    _check(lib().qlora_linear_fwd(M, K, N, r, X.data_ptr(), ctypes.byref(st), A.data_ptr(), B.data_ptr(),
-                                  float(c), Y.data_ptr(), Z.data_ptr(), workspace.data_ptr(),
-                                  workspace.numel(), _stream(stream)), "qlora_linear_fwd")
+    _check(lib().qlora_linear_fwd_dt(_COMPUTE[dt], M, K, N, r, X.data_ptr(), ctypes.byref(st), A.data_ptr(),
+                                     B.data_ptr(), float(c), Y.data_ptr(), Z.data_ptr(), workspace.data_ptr(),
+                                     workspace.numel(), _stream(stream)), "qlora_linear_fwd_dt")
     return Y, Z
 
 
@@ -321,10 +349,11 @@ def qlora_linear_bwd(G, X, Z, state: NF4State, A, B, c: float, K: int, N: int, n
     """dZ = c G Bᵀ, dA = Xᵀ dZ, dB = c Zᵀ G, dX = G Ŵᵀ + dZ Aᵀ.  Returns (dX, dA, dB)."""
     import torch
     M, r = X.shape[0], A.shape[1]
+    dt = _compute_dtype(X)
     for t, n in ((G, "G"), (X, "X"), (Z, "Z"), (A, "A"), (B, "B")):
-        _require_cuda(t, n, torch.bfloat16)
+        _require_cuda(t, n, dt)
     if need_dx and dX is None:
-        dX = torch.empty(M, K, dtype=torch.bfloat16, device=X.device)
+        dX = torch.empty(M, K, dtype=dt, device=X.device)
     if dA is None:
         dA = torch.empty(K, r, dtype=torch.float32, device=X.device)
     if dB is None:
@@ -333,10 +362,10 @@ def qlora_linear_bwd(G, X, Z, state: NF4State, A, B, c: float, K: int, N: int, n
         workspace = torch.empty(max(qlora_workspace_bytes(M, K, N, r)[1], 256), dtype=torch.uint8,
                                 device=X.device)
     st = state.c_struct()
-    _check(lib().qlora_linear_bwd(M, K, N, r, G.data_ptr(), X.data_ptr(), Z.data_ptr(), ctypes.byref(st),
-                                  A.data_ptr(), B.data_ptr(), float(c), _ptr(dX if need_dx else None),
-                                  dA.data_ptr(), dB.data_ptr(), workspace.data_ptr(), workspace.numel(),
-                                  _stream(stream)), "qlora_linear_bwd")
+    _check(lib().qlora_linear_bwd_dt(_COMPUTE[dt], M, K, N, r, G.data_ptr(), X.data_ptr(), Z.data_ptr(),
+                                     ctypes.byref(st), A.data_ptr(), B.data_ptr(), float(c),
+                                     _ptr(dX if need_dx else None), dA.data_ptr(), dB.data_ptr(),
+                                     workspace.data_ptr(), workspace.numel(), _stream(stream)), "qlora_linear_bwd_dt")
     return (dX if need_dx else None), dA, dB
 
 

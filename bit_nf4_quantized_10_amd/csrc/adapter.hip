@@ -13,8 +13,8 @@
 //
 // SGD step (section "一次完整反向与有限差分": only the adapter is updated,
 // v <- v - lr g): p' = fl32(p - fl32(lr * g)) on the fp32 master copy when
-// one is kept, else on the bf16 parameter read as fp32; the bf16 parameter
-// becomes RNE_bf16(p').
+// one is kept, else on the 16-bit parameter read as fp32; the bf16 (or fp16)
+// parameter becomes RNE(p').
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -27,16 +27,18 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 constexpr int kMgTile = 64;   // output tile: 64 rows k x 64 columns n
 constexpr int kMgStep = 32;   // rank steps staged in LDS at a time
 
-template <bool kF32AB>
+// kAB: NF4_AB_BF16, NF4_AB_F32 or NF4_AB_F16 (the adapter's element type).
+template <int kAB>
 __device__ __forceinline__ double ab_value(const void* p, int64_t i) {
-  if (kF32AB) return static_cast<double>(static_cast<const float*>(p)[i]);
+  if (kAB == NF4_AB_F32) return static_cast<double>(static_cast<const float*>(p)[i]);
+  if (kAB == NF4_AB_F16) return static_cast<double>(F16::widen(static_cast<const uint16_t*>(p)[i]));
   return static_cast<double>(bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]));
 }
 
 // Workgroup = one 64 x 64 output tile; thread (tk, tn) owns rows
 // k0 + tk + 16 i and columns n0 + tn + 16 l (i, l < 4), so that the lanes of
 // a wave read 4 distinct A values and 16 consecutive B values per rank step.
-template <bool kF32AB>
+template <int kAB>
 __global__ __launch_bounds__(256) void qlora_merge_kernel(int64_t K, int64_t N, int64_t r, NF4View W,
                                                           const void* __restrict__ A, const void* __restrict__ B,
                                                           float c, float* __restrict__ out) {
@@ -56,10 +58,10 @@ __global__ __launch_bounds__(256) void qlora_merge_kernel(int64_t K, int64_t N, 
       const int idx = t + 256 * j;
       const int kk = idx / kMgStep, tt = idx % kMgStep;
       const int64_t k = k0 + kk, tr = t0 + tt;
-      sA[kk][tt] = (k < K && tr < r) ? ab_value<kF32AB>(A, k * r + tr) : 0.0;
+      sA[kk][tt] = (k < K && tr < r) ? ab_value<kAB>(A, k * r + tr) : 0.0;
       const int tb = idx / kMgTile, nn = idx % kMgTile;
       const int64_t trb = t0 + tb, n = n0 + nn;
-      sB[tb][nn] = (trb < r && n < N) ? ab_value<kF32AB>(B, trb * N + n) : 0.0;
+      sB[tb][nn] = (trb < r && n < N) ? ab_value<kAB>(B, trb * N + n) : 0.0;
     }
     __syncthreads();
     const int steps = static_cast<int>(r - t0 < kMgStep ? r - t0 : kMgStep);
@@ -103,6 +105,7 @@ struct SgdJob {
   float* master;   // may be null
   int64_t count;
   int64_t nblk;
+  int f16;         // parameters are fp16 (else bf16)
 };
 
 __global__ __launch_bounds__(256) void sgd_kernel(SgdJob j0, SgdJob j1, float lr) {
@@ -110,36 +113,39 @@ __global__ __launch_bounds__(256) void sgd_kernel(SgdJob j0, SgdJob j1, float lr
   const SgdJob& J = second ? j1 : j0;
   const int64_t blk = second ? blockIdx.x - j0.nblk : blockIdx.x;
   for (int64_t i = blk * 256 + threadIdx.x; i < J.count; i += J.nblk * 256) {
-    const float base = J.master != nullptr ? J.master[i] : bf16_bits_to_f32(J.param[i]);
+    const float base =
+        J.master != nullptr ? J.master[i] : (J.f16 ? F16::widen(J.param[i]) : Bf16::widen(J.param[i]));
     const float v = __fsub_rn(base, __fmul_rn(lr, J.grad[i]));
     if (J.master != nullptr) J.master[i] = v;
-    J.param[i] = static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xffffu);
+    J.param[i] = static_cast<uint16_t>((J.f16 ? F16::pack2(v, 0.0f) : Bf16::pack2(v, 0.0f)) & 0xffffu);
   }
 }
 
-SgdJob sgd_job(uint16_t* param, const float* grad, float* master, int64_t count) {
+SgdJob sgd_job(uint16_t* param, const float* grad, float* master, int64_t count, int dtype) {
   int64_t blocks = cdiv(count, 256);
   if (blocks > 4096) blocks = 4096;
-  return SgdJob{param, grad, master, count, blocks};
+  return SgdJob{param, grad, master, count, blocks, dtype == kDtypeF16 ? 1 : 0};
 }
 
 }  // namespace
 
-hipError_t launch_merge(int64_t K, int64_t N, int64_t r, NF4View W, const void* A, const void* B, bool f32_ab,
+hipError_t launch_merge(int64_t K, int64_t N, int64_t r, NF4View W, const void* A, const void* B, int ab_dtype,
                         float c, float* out, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(cdiv(N, kMgTile)), static_cast<unsigned>(cdiv(K, kMgTile)));
   Timer tm(QK_MERGE, stream);
-  if (f32_ab)
-    hipLaunchKernelGGL(qlora_merge_kernel<true>, grid, dim3(256), 0, stream, K, N, r, W, A, B, c, out);
+  if (ab_dtype == NF4_AB_F32)
+    hipLaunchKernelGGL(qlora_merge_kernel<NF4_AB_F32>, grid, dim3(256), 0, stream, K, N, r, W, A, B, c, out);
+  else if (ab_dtype == NF4_AB_F16)
+    hipLaunchKernelGGL(qlora_merge_kernel<NF4_AB_F16>, grid, dim3(256), 0, stream, K, N, r, W, A, B, c, out);
   else
-    hipLaunchKernelGGL(qlora_merge_kernel<false>, grid, dim3(256), 0, stream, K, N, r, W, A, B, c, out);
+    hipLaunchKernelGGL(qlora_merge_kernel<NF4_AB_BF16>, grid, dim3(256), 0, stream, K, N, r, W, A, B, c, out);
   tm.stop();
   return hipGetLastError();
 }
 
 hipError_t launch_sgd(int64_t K, int64_t N, int64_t r, uint16_t* A, uint16_t* B, const float* dA, const float* dB,
-                      float lr, float* A_master, float* B_master, hipStream_t stream) {
-  const SgdJob ja = sgd_job(A, dA, A_master, K * r), jb = sgd_job(B, dB, B_master, r * N);
+                      float lr, float* A_master, float* B_master, hipStream_t stream, int dtype) {
+  const SgdJob ja = sgd_job(A, dA, A_master, K * r, dtype), jb = sgd_job(B, dB, B_master, r * N, dtype);
   Timer tm(QK_SGD, stream);
   hipLaunchKernelGGL(sgd_kernel, dim3(static_cast<unsigned>(ja.nblk + jb.nblk)), dim3(256), 0, stream, ja, jb, lr);
   tm.stop();

@@ -30,6 +30,8 @@ bool state_ok(const nf4_state_t* s) {
 
 qn::NF4View view_of(const nf4_state_t* s) { return qn::NF4View{s->codes, s->qabsmax, s->absmax2, s->offset, s->absmax}; }
 
+bool dtype_ok(int d) { return d == NF4_COMPUTE_BF16 || d == NF4_COMPUTE_F16; }
+
 // Kernels address operands with 32-bit buffer offsets and mark masked lanes
 // with offset 2^31; keeping every bf16 operand (X, G, Y, dX, A, B and the
 // dequantized weight) under 1 GiB, and so every fp32 M x N buffer under
@@ -123,7 +125,7 @@ int nf4_quantize(const float* W, const nf4_state_t* out, void* workspace, int64_
 
 int nf4_dequantize(const nf4_state_t* state, void* out, int out_dtype, int32_t* status, void* stream) {
   if (!state_ok(state) || out == nullptr || !aligned16(out)) return NF4_EINVAL;
-  if (out_dtype != NF4_OUT_F32 && out_dtype != NF4_OUT_BF16) return NF4_EINVAL;
+  if (out_dtype != NF4_OUT_F32 && out_dtype != NF4_OUT_BF16 && out_dtype != NF4_OUT_F16) return NF4_EINVAL;
   hipError_t e = qn::launch_dequantize(view_of(state), state->numel, out, out_dtype, status,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? NF4_OK : NF4_EHIP;
@@ -136,25 +138,34 @@ int qlora_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r, int64_t* f
   return NF4_OK;
 }
 
-int qlora_linear_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const nf4_state_t* W,
+int qlora_linear_fwd_dt(int compute_dtype, int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X,
+                        const nf4_state_t* W,
                      const uint16_t* A, const uint16_t* B, float c, uint16_t* Y, uint16_t* Z, void* workspace,
                      int64_t workspace_bytes, void* stream) {
-  if (!layer_shape_ok(M, K, N, r) || !state_ok(W) || W->numel != K * N) return NF4_EINVAL;
+  if (!dtype_ok(compute_dtype) || !layer_shape_ok(M, K, N, r) || !state_ok(W) || W->numel != K * N) return NF4_EINVAL;
   if (!X || !A || !B || !Y || !Z || !workspace) return NF4_EINVAL;
   if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y) || !aligned16(Z) ||
       !aligned16(W->codes) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return NF4_EINVAL;
   if (workspace_bytes < qn::fwd_workspace_bytes(M, K, N, r)) return NF4_EINVAL;
   const qn::NF4View v = view_of(W);
-  hipError_t e = qn::launch_fwd(M, K, N, r, X, v, A, B, c, Y, Z, workspace, static_cast<hipStream_t>(stream));
+  hipError_t e =
+      qn::launch_fwd(M, K, N, r, X, v, A, B, c, Y, Z, workspace, static_cast<hipStream_t>(stream), compute_dtype);
   return e == hipSuccess ? NF4_OK : NF4_EHIP;
 }
 
-int qlora_linear_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* X,
+int qlora_linear_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const nf4_state_t* W,
+                     const uint16_t* A, const uint16_t* B, float c, uint16_t* Y, uint16_t* Z, void* workspace,
+                     int64_t workspace_bytes, void* stream) {
+  return qlora_linear_fwd_dt(NF4_COMPUTE_BF16, M, K, N, r, X, W, A, B, c, Y, Z, workspace, workspace_bytes, stream);
+}
+
+int qlora_linear_bwd_dt(int compute_dtype, int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G,
+                        const uint16_t* X,
                      const uint16_t* Z, const nf4_state_t* W, const uint16_t* A, const uint16_t* B, float c,
                      uint16_t* dX, float* dA, float* dB, void* workspace, int64_t workspace_bytes,
                      void* stream) {
-  if (!layer_shape_ok(M, K, N, r) || !state_ok(W) || W->numel != K * N) return NF4_EINVAL;
+  if (!dtype_ok(compute_dtype) || !layer_shape_ok(M, K, N, r) || !state_ok(W) || W->numel != K * N) return NF4_EINVAL;
   if (!G || !X || !Z || !A || !B || !dA || !dB || !workspace) return NF4_EINVAL;
   if (!aligned16(G) || !aligned16(X) || !aligned16(Z) || !aligned16(A) || !aligned16(B) || !aligned16(dA) ||
       !aligned16(dB) || (dX && !aligned16(dX)) || !aligned16(W->codes) ||
@@ -163,8 +174,16 @@ int qlora_linear_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t*
   if (workspace_bytes < qn::bwd_workspace_bytes(M, K, N, r)) return NF4_EINVAL;
   const qn::NF4View v = view_of(W);
   hipError_t e = qn::launch_bwd(M, K, N, r, G, X, Z, v, A, B, c, dX, dA, dB, workspace,
-                                static_cast<hipStream_t>(stream));
+                                static_cast<hipStream_t>(stream), compute_dtype);
   return e == hipSuccess ? NF4_OK : NF4_EHIP;
+}
+
+int qlora_linear_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* X,
+                     const uint16_t* Z, const nf4_state_t* W, const uint16_t* A, const uint16_t* B, float c,
+                     uint16_t* dX, float* dA, float* dB, void* workspace, int64_t workspace_bytes,
+                     void* stream) {
+  return qlora_linear_bwd_dt(NF4_COMPUTE_BF16, M, K, N, r, G, X, Z, W, A, B, c, dX, dA, dB, workspace,
+                             workspace_bytes, stream);
 }
 
 static bool grouped_shape_ok(int64_t M, int64_t K, int g, const int64_t* N, int64_t r, int64_t* Ntot) {
@@ -232,19 +251,25 @@ int qlora_merge(int64_t K, int64_t N, int64_t r, const nf4_state_t* W, const voi
                 float c, float* W_merged, void* stream) {
   if (K < 1 || N < 1 || r < 1 || r > 65536 || !state_ok(W) || W->numel != K * N) return NF4_EINVAL;
   if (K * N >= kMaxOperandElems || K * r >= kMaxOperandElems || r * N >= kMaxOperandElems) return NF4_EINVAL;
-  if (ab_dtype != NF4_AB_BF16 && ab_dtype != NF4_AB_F32) return NF4_EINVAL;
+  if (ab_dtype != NF4_AB_BF16 && ab_dtype != NF4_AB_F32 && ab_dtype != NF4_AB_F16) return NF4_EINVAL;
   if (A == nullptr || B == nullptr || W_merged == nullptr || !aligned16(W_merged)) return NF4_EINVAL;
   const uintptr_t elem_mask = ab_dtype == NF4_AB_F32 ? 3u : 1u;
   if ((reinterpret_cast<uintptr_t>(A) & elem_mask) != 0 || (reinterpret_cast<uintptr_t>(B) & elem_mask) != 0)
     return NF4_EINVAL;
   const qn::NF4View v = view_of(W);
-  hipError_t e = qn::launch_merge(K, N, r, v, A, B, ab_dtype == NF4_AB_F32, c, W_merged,
+  hipError_t e = qn::launch_merge(K, N, r, v, A, B, ab_dtype, c, W_merged,
                                   static_cast<hipStream_t>(stream));
   return e == hipSuccess ? NF4_OK : NF4_EHIP;
 }
 
 int qlora_sgd_step(int64_t K, int64_t N, int64_t r, uint16_t* A, uint16_t* B, const float* dA, const float* dB,
                    float lr, float* A_master, float* B_master, void* stream) {
+  return qlora_sgd_step_dt(NF4_COMPUTE_BF16, K, N, r, A, B, dA, dB, lr, A_master, B_master, stream);
+}
+
+int qlora_sgd_step_dt(int param_dtype, int64_t K, int64_t N, int64_t r, uint16_t* A, uint16_t* B, const float* dA,
+                      const float* dB, float lr, float* A_master, float* B_master, void* stream) {
+  if (!dtype_ok(param_dtype)) return NF4_EINVAL;
   if (K < 1 || N < 1 || r < 1 || K * r >= kMaxOperandElems || r * N >= kMaxOperandElems) return NF4_EINVAL;
   if (A == nullptr || B == nullptr || dA == nullptr || dB == nullptr) return NF4_EINVAL;
   if ((A_master == nullptr) != (B_master == nullptr)) return NF4_EINVAL;
@@ -252,7 +277,8 @@ int qlora_sgd_step(int64_t K, int64_t N, int64_t r, uint16_t* A, uint16_t* B, co
       (reinterpret_cast<uintptr_t>(dA) & 3u) || (reinterpret_cast<uintptr_t>(dB) & 3u) ||
       (reinterpret_cast<uintptr_t>(A_master) & 3u) || (reinterpret_cast<uintptr_t>(B_master) & 3u))
     return NF4_EINVAL;
-  hipError_t e = qn::launch_sgd(K, N, r, A, B, dA, dB, lr, A_master, B_master, static_cast<hipStream_t>(stream));
+  hipError_t e =
+      qn::launch_sgd(K, N, r, A, B, dA, dB, lr, A_master, B_master, static_cast<hipStream_t>(stream), param_dtype);
   return e == hipSuccess ? NF4_OK : NF4_EHIP;
 }
 

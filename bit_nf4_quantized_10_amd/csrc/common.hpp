@@ -109,12 +109,51 @@ constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 1
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// The 16 reconstructions RNE_bf16(fl32(C[j] * ahat)) of one block, written
-// as 32 bytes (entry j at byte 2j) to 16-byte aligned LDS.
+// ---- the two 16-bit compute types of the layer ([P2] §20: BF16, or FP16
+// where BF16 is not wanted).  Each tag gives the MFMA operand vector, the
+// 16x16x32 and 32x32x16 MFMAs with fp32 accumulation, the fp32 -> 16-bit
+// round-to-nearest-even packing of two values, and the widening to fp32.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+struct Bf16 {
+  typedef bf16x8 v8;
+  static constexpr int kDtype = 0;
+  __device__ static __forceinline__ uint32_t pack2(float lo, float hi) { return pack_bf16x2(lo, hi); }
+  __device__ static __forceinline__ float widen(uint32_t bits16) { return bf16_bits_to_f32(bits16); }
+  __device__ static __forceinline__ f32x4 mfma16(const v8& a, const v8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x16 mfma32(const v8& a, const v8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+struct F16 {
+  typedef f16x8 v8;
+  static constexpr int kDtype = 1;
+  __device__ static __forceinline__ uint32_t pack2(float lo, float hi) {
+    f16x2 v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static __forceinline__ float widen(uint32_t bits16) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
+  }
+  __device__ static __forceinline__ f32x4 mfma16(const v8& a, const v8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ f32x16 mfma32(const v8& a, const v8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// The 16 reconstructions RNE_T(fl32(C[j] * ahat)) of one block, written as
+// 32 bytes (entry j at byte 2j) to 16-byte aligned LDS.
+template <class T = Bf16>
 __device__ __forceinline__ void write_block_table(uint16_t* tab, float ahat) {
   uint32_t w[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) w[j] = pack_bf16x2(__fmul_rn(kNF4[2 * j], ahat), __fmul_rn(kNF4[2 * j + 1], ahat));
+  for (int j = 0; j < 8; ++j) w[j] = T::pack2(__fmul_rn(kNF4[2 * j], ahat), __fmul_rn(kNF4[2 * j + 1], ahat));
   reinterpret_cast<uint4*>(tab)[0] = make_uint4(w[0], w[1], w[2], w[3]);
   reinterpret_cast<uint4*>(tab)[1] = make_uint4(w[4], w[5], w[6], w[7]);
 }

@@ -118,7 +118,7 @@ __device__ __forceinline__ uint4 ld128s(Rsrc r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-template <bool kForward, bool kKTail>
+template <class T, bool kForward, bool kKTail>
 struct Big {
   const BigArgs& a;
   char* smem;
@@ -225,7 +225,7 @@ struct Big {
     const int64_t krow = kForward ? s * kBK + tab_row : c0 + tab_row;
     float ahat = single ? R.s2 : __fadd_rn(__fmul_rn(q2t()[R.q + 128], R.s2), off);
     if (krow >= a.K) ahat = 0.0f;   // rows past K decode to zero
-    write_block_table(tabs(b) + (kForward ? (tab_row * 4 + tab_blk) : tab_row) * 16, ahat);
+    write_block_table<T>(tabs(b) + (kForward ? (tab_row * 4 + tab_blk) : tab_row) * 16, ahat);
   }
 
   // Split code words into byte-wise doubled nibbles: ix[2c] holds 2*code of
@@ -279,7 +279,7 @@ struct Big {
   // each 4 activation x 4 weight fragments (32 rows x 16 values; lane l holds
   // row l%32, values 8*(l/32)..+7) and 16 v_mfma_f32_32x32x16_bf16.
   struct Frags {
-    bf16x8 a[4], w[4];
+    typename T::v8 a[4], w[4];
   };
   __device__ void load_frags(int b, int ks, Frags& F) const {
     const int r32 = lane & 31, h = lane >> 5, wm = wave >> 1, wn = wave & 1;
@@ -287,16 +287,16 @@ struct Big {
     const char* Bt = sB(b);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      F.a[i] = *reinterpret_cast<const bf16x8*>(A + lds_off(wm * 128 + 32 * i + r32, 2 * ks + h));
+      F.a[i] = *reinterpret_cast<const typename T::v8*>(A + lds_off(wm * 128 + 32 * i + r32, 2 * ks + h));
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      F.w[j] = *reinterpret_cast<const bf16x8*>(Bt + lds_off(wn * 128 + 32 * j + r32, 2 * ks + h));
+      F.w[j] = *reinterpret_cast<const typename T::v8*>(Bt + lds_off(wn * 128 + 32 * j + r32, 2 * ks + h));
   }
   __device__ static void mma(const Frags& F, f32x16 (&acc)[4][4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(F.w[j], F.a[i], acc[i][j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = T::mfma32(F.w[j], F.a[i], acc[i][j]);
   }
   __device__ void compute(int b, f32x16 (&acc)[4][4]) const {
     Frags F;
@@ -323,7 +323,7 @@ constexpr int kRingLds = kSlots * 2 * kRTile;    // 160 KB
 
 __device__ __forceinline__ int roff(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
 
-template <bool kForward, bool kKTail>
+template <class T, bool kForward, bool kKTail>
 struct Dense {
   const BigArgs& a;
   char* smem;
@@ -388,14 +388,14 @@ struct Dense {
   }
 
   struct Frags {
-    bf16x8 a[4], w[4];
+    typename T::v8 a[4], w[4];
   };
   __device__ void load_frags(int b, int ks, Frags& F) const {
     const char* base = slot(b);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) F.a[i] = *reinterpret_cast<const bf16x8*>(base + foffA[ks][i]);
+    for (int i = 0; i < 4; ++i) F.a[i] = *reinterpret_cast<const typename T::v8*>(base + foffA[ks][i]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) F.w[j] = *reinterpret_cast<const bf16x8*>(base + foffW[ks][j]);
+    for (int j = 0; j < 4; ++j) F.w[j] = *reinterpret_cast<const typename T::v8*>(base + foffW[ks][j]);
   }
 
   // 16 MFMAs from Fc; in their shadow, the 8 fragment reads of substep ksn
@@ -409,14 +409,14 @@ struct Dense {
     for (int g = 0; g < 4; ++g) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        acc[g][u] = mfma32x32x16(Fc.w[u], Fc.a[g], acc[g][u]);
+        acc[g][u] = T::mfma32(Fc.w[u], Fc.a[g], acc[g][u]);
         __builtin_amdgcn_sched_barrier(0);
         if (g < 2) {
           const int q = 4 * g + u;
           if ((q & 1) == 0)
-            Fn.a[q >> 1] = *reinterpret_cast<const bf16x8*>(base + foffA[ksn][q >> 1]);
+            Fn.a[q >> 1] = *reinterpret_cast<const typename T::v8*>(base + foffA[ksn][q >> 1]);
           else
-            Fn.w[q >> 1] = *reinterpret_cast<const bf16x8*>(base + foffW[ksn][q >> 1]);
+            Fn.w[q >> 1] = *reinterpret_cast<const typename T::v8*>(base + foffW[ksn][q >> 1]);
           __builtin_amdgcn_sched_barrier(0);
         }
         if (u == 1) {
@@ -435,14 +435,14 @@ struct Dense {
       Frags F;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        F.a[i] = *reinterpret_cast<const bf16x8*>(sA(0) + lds_off(wm * 128 + 32 * i + r32, 2 * ks + h));
+        F.a[i] = *reinterpret_cast<const typename T::v8*>(sA(0) + lds_off(wm * 128 + 32 * i + r32, 2 * ks + h));
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        F.w[j] = *reinterpret_cast<const bf16x8*>(sB(0) + lds_off(wn * 128 + 32 * j + r32, 2 * ks + h));
+        F.w[j] = *reinterpret_cast<const typename T::v8*>(sB(0) + lds_off(wn * 128 + 32 * j + r32, 2 * ks + h));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(F.w[j], F.a[i], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = T::mfma32(F.w[j], F.a[i], acc[i][j]);
     }
   }
 };
@@ -454,7 +454,7 @@ struct Dense {
 // row, 16-byte chunk q of row R at q ^ (R & 31)) so that every global store
 // writes whole 512-byte row segments.  Shared by the fused and dense kernels;
 // the main loop has released LDS when this starts.
-template <bool kForward, class Core>
+template <class T, bool kForward, class Core>
 __device__ __forceinline__ void finish(const Core& k, const BigArgs& a, f32x16 (&acc)[4][4]) {
   const int lane = k.lane, t = k.t;
   const int64_t cols = kForward ? a.N : a.K;
@@ -495,8 +495,8 @@ __device__ __forceinline__ void finish(const Core& k, const BigArgs& a, f32x16 (
         for (int jj = 0; jj < 4; ++jj) {
           const int q = wn * 16 + 4 * j + jj;
           uint2 v;
-          v.x = pack_bf16x2(acc[i][j][4 * jj], acc[i][j][4 * jj + 1]);
-          v.y = pack_bf16x2(acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]);
+          v.x = T::pack2(acc[i][j][4 * jj], acc[i][j][4 * jj + 1]);
+          v.y = T::pack2(acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]);
           *reinterpret_cast<uint2*>(st + R * 512 + ((q ^ r32) << 4) + 8 * h) = v;
         }
     }
@@ -515,10 +515,10 @@ __device__ __forceinline__ void finish(const Core& k, const BigArgs& a, f32x16 (
   }
 }
 
-template <bool kForward, bool kKTail>
+template <class T, bool kForward, bool kKTail>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void qlora_big_kernel(BigArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  Big<kForward, kKTail> k(a, smem);
+  Big<T, kForward, kKTail> k(a, smem);
   {
     float* q2t = reinterpret_cast<float*>(smem + kOffQ);
     q2t[k.t] = q2_value(k.t - 128);
@@ -560,14 +560,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     k.split_codes(cur, ix);
     // MFMAs of stage s, with the fragments of substep ks+1 and two decode
     // parts of stage s+1 issued in the shadow of substep ks.
-    typename Big<kForward, kKTail>::Frags F0, F1;
+    typename Big<T, kForward, kKTail>::Frags F0, F1;
     k.load_frags(b, 0, F0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (ks < 3) k.load_frags(b, ks + 1, F1);
       k.decode_part(ix, b ^ 1, 2 * ks);
       k.decode_part(ix, b ^ 1, 2 * ks + 1);
-      Big<kForward, kKTail>::mma(F0, acc);
+      Big<T, kForward, kKTail>::mma(F0, acc);
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
@@ -582,13 +582,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     cur = nxt;
   }
 
-  finish<kForward>(k, a, acc);
+  finish<T, kForward>(k, a, acc);
 }
 
-template <bool kForward, bool kKTail>
+template <class T, bool kForward, bool kKTail>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void qlora_dense_kernel(BigArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  Dense<kForward, kKTail> k(a, smem);
+  Dense<T, kForward, kKTail> k(a, smem);
   const int64_t nst = (k.red + kRK - 1) / kRK;
   f32x16 acc[4][4];
 #pragma unroll
@@ -609,7 +609,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   for (int g = 0; g < 4; ++g) k.copy_one(S - 1, S - 1, 0, g);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(8 * (S - 2) + 4, 15));
   __builtin_amdgcn_s_barrier();
-  typename Dense<kForward, kKTail>::Frags F0, F1;
+  typename Dense<T, kForward, kKTail>::Frags F0, F1;
   k.load_frags(0, 0, F0);
   int b = 0;
   for (int64_t s = 0; s < nst; ++s) {
@@ -624,92 +624,98 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  finish<kForward>(k, a, acc);
+  finish<T, kForward>(k, a, acc);
 }
 
-template <bool kForward, bool kKTail>
+template <class T, bool kForward, bool kKTail>
 hipError_t launch_big_t(const BigArgs& a, hipStream_t stream, const Timer& tm) {
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_big_kernel<kForward, kKTail>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_big_kernel<T, kForward, kKTail>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
     configured = true;
   }
   const int64_t cols = kForward ? a.N : a.K;
   dim3 grid(static_cast<unsigned>((cols + kBN - 1) / kBN), static_cast<unsigned>((a.M + kBM - 1) / kBM), 1);
-  hipExtLaunchKernelGGL((qlora_big_kernel<kForward, kKTail>), grid, dim3(kThreads), kLdsBytes, stream, tm.start(),
+  hipExtLaunchKernelGGL((qlora_big_kernel<T, kForward, kKTail>), grid, dim3(kThreads), kLdsBytes, stream, tm.start(),
                         tm.end(), 0, a);
   return hipGetLastError();
 }
 
 template <bool kForward>
-hipError_t launch_big(const BigArgs& a, hipStream_t stream, const Timer& tm) {
+hipError_t launch_big(const BigArgs& a, hipStream_t stream, const Timer& tm, int dtype) {
   const int64_t red = kForward ? a.K : a.N;
-  return (red % kBK) ? launch_big_t<kForward, true>(a, stream, tm) : launch_big_t<kForward, false>(a, stream, tm);
+  if (dtype == F16::kDtype)
+    return (red % kBK) ? launch_big_t<F16, kForward, true>(a, stream, tm) : launch_big_t<F16, kForward, false>(a, stream, tm);
+  return (red % kBK) ? launch_big_t<Bf16, kForward, true>(a, stream, tm) : launch_big_t<Bf16, kForward, false>(a, stream, tm);
 }
 
-template <bool kForward, bool kKTail>
+template <class T, bool kForward, bool kKTail>
 hipError_t launch_dense_t(const BigArgs& a, hipStream_t stream, const Timer& tm) {
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_dense_kernel<kForward, kKTail>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_dense_kernel<T, kForward, kKTail>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kRingLds);
     if (e != hipSuccess) return e;
     configured = true;
   }
   const int64_t cols = kForward ? a.N : a.K;
   dim3 grid(static_cast<unsigned>((cols + kBN - 1) / kBN), static_cast<unsigned>((a.M + kBM - 1) / kBM), 1);
-  hipExtLaunchKernelGGL((qlora_dense_kernel<kForward, kKTail>), grid, dim3(kThreads), kRingLds, stream, tm.start(),
+  hipExtLaunchKernelGGL((qlora_dense_kernel<T, kForward, kKTail>), grid, dim3(kThreads), kRingLds, stream, tm.start(),
                         tm.end(), 0, a);
   return hipGetLastError();
 }
 
 template <bool kForward>
-hipError_t launch_dense(const BigArgs& a, hipStream_t stream, const Timer& tm) {
+hipError_t launch_dense(const BigArgs& a, hipStream_t stream, const Timer& tm, int dtype) {
   const int64_t red = kForward ? a.K : a.N;
-  return (red % kRK) ? launch_dense_t<kForward, true>(a, stream, tm) : launch_dense_t<kForward, false>(a, stream, tm);
+  if (dtype == F16::kDtype)
+    return (red % kRK) ? launch_dense_t<F16, kForward, true>(a, stream, tm)
+                       : launch_dense_t<F16, kForward, false>(a, stream, tm);
+  return (red % kRK) ? launch_dense_t<Bf16, kForward, true>(a, stream, tm)
+                     : launch_dense_t<Bf16, kForward, false>(a, stream, tm);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const uint16_t* WhatT,
-                            const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream) {
+                            const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype) {
   BigArgs a{X, K, NF4View{}, Z, cBt, Y, M, K, N, r, WhatT};
   const Timer t(QK_FWD_GEMM, stream, true);
-  return launch_dense<true>(a, stream, t);
+  return launch_dense<true>(a, stream, t, dtype);
 }
 
 hipError_t launch_fwd_dense_grouped(int64_t M, int64_t K, int64_t Ntot, int64_t r, const uint16_t* X,
                                     const uint16_t* WhatT, const uint16_t* Zcat, int g, const int64_t* gend,
-                                    const uint16_t* cBt, uint16_t* Y, hipStream_t stream) {
+                                    const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype) {
   BigArgs a{X, K, NF4View{}, Zcat, cBt, Y, M, K, Ntot, r, WhatT};
   a.ext_a_ld = g * r;
   a.ngroups = g - 1;
   for (int i = 0; i + 1 < g; ++i) a.gend[i] = gend[i];
   const Timer t(QK_FWD_GEMM, stream, true);
-  return launch_dense<true>(a, stream, t);
+  return launch_dense<true>(a, stream, t, dtype);
 }
 
 hipError_t launch_dx_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* What,
-                           const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream) {
+                           const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream, int dtype) {
   BigArgs a{G, N, NF4View{}, dZ, A, dX, M, K, N, r, What};
   const Timer t(QK_BWD_DX, stream, true);
-  return launch_dense<false>(a, stream, t);
+  return launch_dense<false>(a, stream, t, dtype);
 }
 
 hipError_t launch_fwd_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W,
-                          const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream) {
+                          const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype) {
   BigArgs a{X, K, W, Z, cBt, Y, M, K, N, r, nullptr};
   const Timer t(QK_FWD_GEMM, stream, true);
-  return launch_big<true>(a, stream, t);
+  return launch_big<true>(a, stream, t, dtype);
 }
 
 hipError_t launch_dx_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, NF4View W,
-                         const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream) {
+                         const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream, int dtype) {
   BigArgs a{G, N, W, dZ, A, dX, M, K, N, r, nullptr};
   const Timer t(QK_BWD_DX, stream, true);
-  return launch_big<false>(a, stream, t);
+  return launch_big<false>(a, stream, t, dtype);
 }
 
 }  // namespace qn

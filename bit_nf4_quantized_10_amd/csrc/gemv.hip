@@ -83,6 +83,7 @@ __device__ __forceinline__ uint32_t nib(uint32_t w, int t) { return (w >> (8 * (
 // MFMA as the 16-row operand; lane (q, g) accumulates columns j0 + 8q .. +7.
 // The four waves are added in LDS in a fixed order: (w0 + w2) + (w1 + w3).
 // zpart[split][m][j], fp32.  red: 16 KB of LDS.
+template <class T>
 __device__ void gemv_zpart(const uint16_t* __restrict__ X, int64_t M, int64_t K, int64_t rpw,
                            const uint16_t* __restrict__ A, int64_t r, float* __restrict__ zpart, int64_t split,
                            float* red) {
@@ -106,7 +107,7 @@ __device__ void gemv_zpart(const uint16_t* __restrict__ X, int64_t M, int64_t K,
       transpose8x8_bf16(rows8, cols8);
 #pragma unroll
       for (int tc = 0; tc < 8; ++tc)
-        acc[tc] = mfma16x16x32(__builtin_bit_cast(bf16x8, xv), __builtin_bit_cast(bf16x8, cols8[tc]), acc[tc]);
+        acc[tc] = T::mfma16(__builtin_bit_cast(typename T::v8, xv), __builtin_bit_cast(typename T::v8, cols8[tc]), acc[tc]);
     }
     // lane holds Z[m = 4g + e][j + tc]
     __syncthreads();
@@ -161,6 +162,7 @@ struct GvStep {
 // step to its LDS ring, then decodes the current step by table lookups, so no
 // per-weight multiply or conversion is needed; column t of the lane feeds the
 // MFMA of tile t.  part[split][m][n] = sum of the 4 waves (fixed order).
+template <class T>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemv_kernel(const uint16_t* __restrict__ X, int64_t M, NF4View W, int64_t K,
                                                    int64_t N, int64_t rpw, int64_t slabs, float* __restrict__ part,
                                                    const uint16_t* __restrict__ A, int64_t r,
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t splits = (K + kGvWaves * rpw - 1) / (kGvWaves * rpw);
   if (blockIdx.x >= slabs * splits) {
     // the last `splits` workgroups: Z partials over the same row ranges
-    gemv_zpart(X, M, K, rpw, A, r, zpart, blockIdx.x - slabs * splits, reinterpret_cast<float*>(tabs));
+    gemv_zpart<T>(X, M, K, rpw, A, r, zpart, blockIdx.x - slabs * splits, reinterpret_cast<float*>(tabs));
     return;
   }
   q2t[t] = q2_value(t - 128);
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     char* tb = my_tabs + buf * kGvTabBytes + gv_row(lane >> 1) + 64 * (lane & 1);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      write_block_table(reinterpret_cast<uint16_t*>(tb + 32 * u),
+      write_block_table<T>(reinterpret_cast<uint16_t*>(tb + 32 * u),
                         single ? S.s2[u] : __fadd_rn(__fmul_rn(q2t[S.q[u] + 128], S.s2[u]), off));
   };
 
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         od[i][1] = (R[u].w[i].y << 1) & 0x1e1e1e1eu;
       }
       const uint32_t tbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tb));
-      const bf16x8 xf = __builtin_bit_cast(bf16x8, R[u].x);
+      const typename T::v8 xf = __builtin_bit_cast(typename T::v8, R[u].x);
 #pragma unroll
       for (int tile = 0; tile < 16; ++tile) {
         const int h = tile >> 3, col = tile & 7;
@@ -276,7 +278,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           const uint32_t hi = lds_u16(a1 + (2 * p + 1) * 128);
           fw[p] = perm(hi, lo, 0x05040100u);
         }
-        acc[tile] = mfma16x16x32(xf, __builtin_bit_cast(bf16x8, make_uint4(fw[0], fw[1], fw[2], fw[3])), acc[tile]);
+        acc[tile] = T::mfma16(xf, __builtin_bit_cast(typename T::v8, make_uint4(fw[0], fw[1], fw[2], fw[3])), acc[tile]);
       }
       if (ks + 32 < rpw) build(R[(u + 1) % kGvDepth], buf ^ 1);
       load(R[u], ks + 32 * kGvDepth);   // past the k-range: masked, reads zeros
@@ -330,6 +332,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // computes it; only row 4g+e is kept).  Z = RNE_bf16(sum_s zpart[s]) in a
 // fixed order; workgroup (0, 0) writes it.  The split loops request 8
 // partials at a time before adding them in order.
+template <class T>
 __global__ __launch_bounds__(64) void gemv_finish_kernel(const float* __restrict__ part, int splits, int64_t M,
                                                          int64_t N, const float* __restrict__ zpart,
                                                          uint16_t* __restrict__ Z, const uint16_t* __restrict__ B,
@@ -373,14 +376,14 @@ __global__ __launch_bounds__(64) void gemv_finish_kernel(const float* __restrict
     }
     uint4 zv = make_uint4(0, 0, 0, 0);
     if (zok) {
-      zv = make_uint4(pack_bf16x2(zs[0], zs[1]), pack_bf16x2(zs[2], zs[3]), pack_bf16x2(zs[4], zs[5]),
-                      pack_bf16x2(zs[6], zs[7]));
+      zv = make_uint4(T::pack2(zs[0], zs[1]), T::pack2(zs[2], zs[3]), T::pack2(zs[4], zs[5]),
+                      T::pack2(zs[6], zs[7]));
       if (blockIdx.x == 0 && e == 0) *reinterpret_cast<uint4*>(Z + q * r + jb) = zv;
     }
     transpose8x8_bf16(rows8, cols8);
 #pragma unroll
     for (int tc = 0; tc < 8; ++tc)
-      accl[tc] = mfma16x16x32(__builtin_bit_cast(bf16x8, zv), __builtin_bit_cast(bf16x8, cols8[tc]), accl[tc]);
+      accl[tc] = T::mfma16(__builtin_bit_cast(typename T::v8, zv), __builtin_bit_cast(typename T::v8, cols8[tc]), accl[tc]);
   }
   const int64_t m = 4 * g + e;
   if (m >= M || !n_ok) return;
@@ -405,10 +408,10 @@ __global__ __launch_bounds__(64) void gemv_finish_kernel(const float* __restrict
     }
   }
   uint4 o;
-  o.x = pack_bf16x2(v[0] + c * accl[0][e], v[1] + c * accl[1][e]);
-  o.y = pack_bf16x2(v[2] + c * accl[2][e], v[3] + c * accl[3][e]);
-  o.z = pack_bf16x2(v[4] + c * accl[4][e], v[5] + c * accl[5][e]);
-  o.w = pack_bf16x2(v[6] + c * accl[6][e], v[7] + c * accl[7][e]);
+  o.x = T::pack2(v[0] + c * accl[0][e], v[1] + c * accl[1][e]);
+  o.y = T::pack2(v[2] + c * accl[2][e], v[3] + c * accl[3][e]);
+  o.z = T::pack2(v[4] + c * accl[4][e], v[5] + c * accl[5][e]);
+  o.w = T::pack2(v[6] + c * accl[6][e], v[7] + c * accl[7][e]);
   *reinterpret_cast<uint4*>(Y + m * N + n) = o;
 }
 
@@ -429,17 +432,17 @@ void plan_gemv(int64_t M, int64_t K, int64_t N, int64_t r, SkinnyPlan* p_) {
 
 hipError_t launch_gemv(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W, const uint16_t* A,
                        const uint16_t* B, float c, uint16_t* Y, uint16_t* Z, const SkinnyPlan& p, void* part_ws,
-                       hipStream_t stream) {
+                       hipStream_t stream, int dtype) {
   const int64_t slabs = cdiv(N, kGvCols);
   float* part = static_cast<float*>(part_ws);
   float* zpart = reinterpret_cast<float*>(static_cast<char*>(part_ws) + p.gv_part);
   Timer tm(QK_FWD_GEMV, stream);
-  hipLaunchKernelGGL(gemv_kernel, dim3(static_cast<unsigned>((slabs + 1) * p.gv_splits)), dim3(kGvWaves * 64), 0,
+  hipLaunchKernelGGL(dtype == kDtypeF16 ? gemv_kernel<F16> : gemv_kernel<Bf16>, dim3(static_cast<unsigned>((slabs + 1) * p.gv_splits)), dim3(kGvWaves * 64), 0,
                      stream, X, M, W, K, N, p.gv_rows_per_wave, slabs, part, A, r, zpart);
   tm.stop();
   Timer te(QK_REDUCE, stream);
   const unsigned phases = static_cast<unsigned>(M < 4 ? M : 4);   // rows 4g + e, e < phases
-  hipLaunchKernelGGL(gemv_finish_kernel, dim3(static_cast<unsigned>(cdiv(N, 128)), phases), dim3(64), 0, stream,
+  hipLaunchKernelGGL(dtype == kDtypeF16 ? gemv_finish_kernel<F16> : gemv_finish_kernel<Bf16>, dim3(static_cast<unsigned>(cdiv(N, 128)), phases), dim3(64), 0, stream,
                      static_cast<const float*>(part), static_cast<int>(p.gv_splits), M, N,
                      static_cast<const float*>(zpart), Z, B, r, c, Y);
   te.stop();

@@ -28,6 +28,11 @@ class Timer {
   void* packet_stop_;
 };
 
+// The layer's 16-bit compute type: 0 = bf16, 1 = fp16 (the kDtype of the
+// Bf16 / F16 tags); activations, adapters, outputs and the dequantized weight use it.
+constexpr int kDtypeBf16 = 0;
+constexpr int kDtypeF16 = 1;
+
 // Most member linears in one grouped call (e.g. q, k, v or gate, up).
 constexpr int kMaxGroupMembers = 8;
 
@@ -53,12 +58,14 @@ hipError_t launch_quantize(const float* W, int64_t P, uint8_t* codes, int8_t* qa
 hipError_t launch_dequantize(NF4View W, int64_t P, void* out, int out_dtype, int32_t* status, hipStream_t stream,
                              int64_t ncols = 0, int64_t out_ld = 0);
 
-// W' = fl32(ŵ + c A B) (fp64 accumulation; A, B fp32 when f32_ab, else bf16).
-hipError_t launch_merge(int64_t K, int64_t N, int64_t r, NF4View W, const void* A, const void* B, bool f32_ab,
+// W' = fl32(ŵ + c A B) (fp64 accumulation; A, B of element type ab_dtype,
+// one of NF4_AB_BF16 / NF4_AB_F32 / NF4_AB_F16).
+hipError_t launch_merge(int64_t K, int64_t N, int64_t r, NF4View W, const void* A, const void* B, int ab_dtype,
                         float c, float* out, hipStream_t stream);
-// One SGD step on A (K x r) and B (r x N), optionally through fp32 masters.
+// One SGD step on A (K x r) and B (r x N) of the 16-bit type dtype,
+// optionally through fp32 masters.
 hipError_t launch_sgd(int64_t K, int64_t N, int64_t r, uint16_t* A, uint16_t* B, const float* dA, const float* dB,
-                      float lr, float* A_master, float* B_master, hipStream_t stream);
+                      float lr, float* A_master, float* B_master, hipStream_t stream, int dtype = 0);
 
 // Grouped linears sharing X (see layer.hip).
 int64_t grouped_fwd_workspace_bytes(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r);
@@ -88,7 +95,8 @@ SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N, int64_t r);
 // (N x r), the forward's LoRA extension operand.
 hipError_t launch_lora_down(int64_t M, int64_t K, int64_t r, const uint16_t* X, const uint16_t* A, uint16_t* Z,
                             const SkinnyPlan& p, void* at_ws, void* part_ws, hipStream_t stream, int64_t N = 0,
-                            const uint16_t* B = nullptr, float c = 1.0f, uint16_t* cbt = nullptr, int64_t rb = 0);
+                            const uint16_t* B = nullptr, float c = 1.0f, uint16_t* cbt = nullptr, int64_t rb = 0,
+                            int dtype = 0);
 
 // Split plans of a group of g linears sharing X (column counts Ns[i], rank r
 // each); zp covers Z = X A over all g r columns.
@@ -100,54 +108,55 @@ struct GroupPlan {
 GroupPlan plan_grouped(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r);
 hipError_t launch_dz_grouped(int64_t M, int g, const int64_t* Ns, int64_t Ntot, int64_t r, const uint16_t* G,
                              const uint16_t* B, float c, uint16_t* dZ, const GroupPlan& gp, void* part_ws,
-                             hipStream_t stream);
+                             hipStream_t stream, int dtype = 0);
 hipError_t launch_colsums_grouped(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t Ntot, int64_t r,
                                   const uint16_t* X, const uint16_t* G, const uint16_t* Z, const uint16_t* dZ, float c,
                                   float* dA, float* dB, const GroupPlan& gp, void* da_ws, void* db_ws,
-                                  hipStream_t stream);
+                                  hipStream_t stream, int dtype = 0);
 // Small-M forward (M <= 16) in two launches: the split-K partials of X Ŵ and
 // of Z = X A (extra workgroups of the same launch), then their fixed-order
 // sums, Z (written out) and Y = X Ŵ + c Z B.  part_ws: gv_part + gv_zpart.
 hipError_t launch_gemv(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W, const uint16_t* A,
                        const uint16_t* B, float c, uint16_t* Y, uint16_t* Z, const SkinnyPlan& p, void* part_ws,
-                       hipStream_t stream);
+                       hipStream_t stream, int dtype = 0);
 hipError_t launch_dz(int64_t M, int64_t N, int64_t r, const uint16_t* G, const uint16_t* B, float c, uint16_t* dZ,
-                     const SkinnyPlan& p, void* part_ws, hipStream_t stream);
+                     const SkinnyPlan& p, void* part_ws, hipStream_t stream, int dtype = 0);
 hipError_t launch_colsums(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const uint16_t* G,
                           const uint16_t* Z, const uint16_t* dZ, float c, float* dA, float* dB, const SkinnyPlan& p,
-                          void* da_ws, void* db_ws, hipStream_t stream);
+                          void* da_ws, void* db_ws, hipStream_t stream, int dtype = 0);
 
 hipError_t launch_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W,
                       const uint16_t* A, const uint16_t* B, float c, uint16_t* Y, uint16_t* Z,
-                      void* ws, hipStream_t stream);
+                      void* ws, hipStream_t stream, int dtype = 0);
 
 hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G,
                       const uint16_t* X, const uint16_t* Z, NF4View W, const uint16_t* A,
                       const uint16_t* B, float c, uint16_t* dX, float* dA, float* dB, void* ws,
-                      hipStream_t stream);
+                      hipStream_t stream, int dtype = 0);
 
 // cBt: RNE_bf16(c B)ᵀ, N x r
 hipError_t launch_fwd_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W,
-                          const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream);
+                          const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype = 0);
 
 hipError_t launch_dx_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, NF4View W,
-                         const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream);
+                         const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream, int dtype = 0);
 
 hipError_t launch_fwd_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const uint16_t* WhatT,
-                            const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream);
+                            const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype = 0);
 // Forward over g members' concatenated columns (Ntot in all, member i ending
 // at column gend[i], every member a multiple of 256 columns): Zcat is M x g r,
 // member i's Z in columns i r .. +r; WhatT and cBt are the members' Ŵᵀ and
 // (c B)ᵀ stacked row-wise (Ntot x K and Ntot x r).
 hipError_t launch_fwd_dense_grouped(int64_t M, int64_t K, int64_t Ntot, int64_t r, const uint16_t* X,
                                     const uint16_t* WhatT, const uint16_t* Zcat, int g, const int64_t* gend,
-                                    const uint16_t* cBt, uint16_t* Y, hipStream_t stream);
+                                    const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype = 0);
 hipError_t launch_dx_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* What,
-                           const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream);
+                           const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream, int dtype = 0);
 
-// Dequantize a K x N weight to bf16, either as stored (K x N) or transposed (N x K).
+// Dequantize a K x N weight to the 16-bit compute type (dtype), either as
+// stored (K x N) or transposed (N x K).
 // out_ld: row stride of the untransposed output (0: N).
 hipError_t launch_dequant_bf16(NF4View W, int64_t K, int64_t N, bool transposed, uint16_t* out, hipStream_t stream,
-                               int64_t out_ld = 0);
+                               int64_t out_ld = 0, int dtype = 0);
 
 }  // namespace qn

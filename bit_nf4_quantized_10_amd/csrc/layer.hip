@@ -40,26 +40,27 @@ int64_t bwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r) {
 }
 
 hipError_t launch_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W, const uint16_t* A,
-                      const uint16_t* B, float c, uint16_t* Y, uint16_t* Z, void* ws, hipStream_t stream) {
+                      const uint16_t* B, float c, uint16_t* Y, uint16_t* Z, void* ws, hipStream_t stream,
+                      int dtype) {
   const SkinnyPlan p = plan_skinny(M, K, N, r);
   char* base = static_cast<char*>(ws);
   char* after_z = base + p.at_bytes + p.z_part;
   hipError_t e;
-  if (M <= 16) return launch_gemv(M, K, N, r, X, W, A, B, c, Y, Z, p, base, stream);
+  if (M <= 16) return launch_gemv(M, K, N, r, X, W, A, B, c, Y, Z, p, base, stream, dtype);
   uint16_t* cbt = reinterpret_cast<uint16_t*>(after_z);
-  if ((e = launch_lora_down(M, K, r, X, A, Z, p, base, base + p.at_bytes, stream, N, B, c, cbt)) != hipSuccess)
+  if ((e = launch_lora_down(M, K, r, X, A, Z, p, base, base + p.at_bytes, stream, N, B, c, cbt, 0, dtype)) != hipSuccess)
     return e;
   if (use_dense(M)) {
     uint16_t* wt = reinterpret_cast<uint16_t*>(after_z + cbt_bytes(M, N, r));
-    if ((e = launch_dequant_bf16(W, K, N, true, wt, stream)) != hipSuccess) return e;
-    return launch_fwd_dense(M, K, N, r, X, wt, Z, cbt, Y, stream);
+    if ((e = launch_dequant_bf16(W, K, N, true, wt, stream, 0, dtype)) != hipSuccess) return e;
+    return launch_fwd_dense(M, K, N, r, X, wt, Z, cbt, Y, stream, dtype);
   }
-  return launch_fwd_big(M, K, N, r, X, W, Z, cbt, Y, stream);
+  return launch_fwd_big(M, K, N, r, X, W, Z, cbt, Y, stream, dtype);
 }
 
 hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* X,
                       const uint16_t* Z, NF4View W, const uint16_t* A, const uint16_t* B, float c, uint16_t* dX,
-                      float* dA, float* dB, void* ws, hipStream_t stream) {
+                      float* dA, float* dB, void* ws, hipStream_t stream, int dtype) {
   const SkinnyPlan p = plan_skinny(M, K, N, r);
   char* base = static_cast<char*>(ws);
   void* dz_part = base;
@@ -67,16 +68,16 @@ hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
   void* da_part = base + p.dz_part + align256(M * r * 2);
   void* db_part = static_cast<char*>(da_part) + p.da_part;
   hipError_t e;
-  if ((e = launch_dz(M, N, r, G, B, c, dz16, p, dz_part, stream)) != hipSuccess) return e;
-  if ((e = launch_colsums(M, K, N, r, X, G, Z, dz16, c, dA, dB, p, da_part, db_part, stream)) != hipSuccess) return e;
+  if ((e = launch_dz(M, N, r, G, B, c, dz16, p, dz_part, stream, dtype)) != hipSuccess) return e;
+  if ((e = launch_colsums(M, K, N, r, X, G, Z, dz16, c, dA, dB, p, da_part, db_part, stream, dtype)) != hipSuccess) return e;
   if (dX == nullptr) return hipGetLastError();
   if (use_dense(M)) {
     uint16_t* wd = reinterpret_cast<uint16_t*>(static_cast<char*>(db_part) + p.db_part);
-    if ((e = launch_dequant_bf16(W, K, N, false, wd, stream)) != hipSuccess)
+    if ((e = launch_dequant_bf16(W, K, N, false, wd, stream, 0, dtype)) != hipSuccess)
       return e;
-    return launch_dx_dense(M, K, N, r, G, wd, dz16, A, dX, stream);
+    return launch_dx_dense(M, K, N, r, G, wd, dz16, A, dX, stream, dtype);
   }
-  return launch_dx_big(M, K, N, r, G, W, dz16, A, dX, stream);
+  return launch_dx_big(M, K, N, r, G, W, dz16, A, dX, stream, dtype);
 }
 
 // ------------------------------------------------------------ grouped linears

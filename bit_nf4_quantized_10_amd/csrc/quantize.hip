@@ -20,6 +20,8 @@
 // the linear 8-bit code, decides the second-level codes.
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -362,7 +364,7 @@ struct DqTile {
 
 // sshift: word index -> index of its scale (11: one per 256 blocks of 8
 // words; 3: one per block, for a state without a second level).
-template <int U>
+template <int U, bool kSingle>
 __device__ __forceinline__ void dq_load(DqTile<U>& t, int64_t tile, int64_t words, Rsrc rc, Rsrc rq, Rsrc rs,
                                         int sshift) {
 #pragma unroll
@@ -370,19 +372,20 @@ __device__ __forceinline__ void dq_load(DqTile<U>& t, int64_t tile, int64_t word
     const int64_t wi = tile * (kQuantThreads * U) + threadIdx.x + static_cast<int64_t>(u) * kQuantThreads;
     const bool in = wi < words;
     t.wd[u] = ld_b32(rc, in ? static_cast<uint32_t>(wi * 4) : kMasked);
-    t.q[u] = ld_i8(rq, in ? static_cast<uint32_t>(wi >> 3) : kMasked);
+    t.q[u] = kSingle ? 0 : ld_i8(rq, in ? static_cast<uint32_t>(wi >> 3) : kMasked);
     t.s2[u] = ld_f32(rs, in ? static_cast<uint32_t>((wi >> sshift) * 4) : kMasked);
   }
 }
 
-template <bool kBf16>
+// O: float (fp32 output) or the 16-bit tag (Bf16 / F16) of the output.
+template <class O>
 __device__ __forceinline__ void dq_store(void* out, int64_t e0, const float v[8]) {
-  if (kBf16) {
+  if constexpr (!std::is_same<O, float>::value) {
     uint4 pk;
-    pk.x = pack_bf16x2(v[0], v[1]);
-    pk.y = pack_bf16x2(v[2], v[3]);
-    pk.z = pack_bf16x2(v[4], v[5]);
-    pk.w = pack_bf16x2(v[6], v[7]);
+    pk.x = O::pack2(v[0], v[1]);
+    pk.y = O::pack2(v[2], v[3]);
+    pk.z = O::pack2(v[4], v[5]);
+    pk.w = O::pack2(v[6], v[7]);
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + e0) = pk;
   } else {
     float* o = static_cast<float*>(out) + e0;
@@ -394,28 +397,28 @@ __device__ __forceinline__ void dq_store(void* out, int64_t e0, const float v[8]
 // ncols = 0: the output is the flat P-element tensor; else the weight is
 // K x ncols and lands in columns 0 .. ncols-1 of an output with row stride
 // out_ld (ncols a multiple of 8, so a word never straddles two rows).
-template <int U, bool kBf16>
+template <int U, class O, bool kSingle, bool kStrided>
 __device__ __forceinline__ void dq_decode(const DqTile<U>& t, int64_t tile, int64_t words, const float* s_lut,
-                                          const float* s_q2, float off, bool single, void* out, uint32_t ncols,
+                                          const float* s_q2, float off, void* out, uint32_t ncols,
                                           int64_t out_ld) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t wi = tile * (kQuantThreads * U) + threadIdx.x + static_cast<int64_t>(u) * kQuantThreads;
     if (wi < words) {
-      const float ahat = single ? t.s2[u] : __fadd_rn(__fmul_rn(s_q2[t.q[u] + kLevels2], t.s2[u]), off);
+      const float ahat = kSingle ? t.s2[u] : __fadd_rn(__fmul_rn(s_q2[t.q[u] + kLevels2], t.s2[u]), off);
       float v[8];
       decode8(t.wd[u], ahat, s_lut, v);
       int64_t dst = wi * 8;
-      if (ncols != 0) {
+      if (kStrided) {
         const uint32_t e0 = static_cast<uint32_t>(wi * 8), k = e0 / ncols;
         dst = static_cast<int64_t>(k) * out_ld + (e0 - k * ncols);
       }
-      dq_store<kBf16>(out, dst, v);
+      dq_store<O>(out, dst, v);
     }
   }
 }
 
-template <int U, bool kBf16>
+template <int U, class O, bool kSingle, bool kStrided>
 __global__ __launch_bounds__(kQuantThreads) void nf4_dequant_kernel(NF4View W, int64_t P, void* __restrict__ out,
                                                                     int32_t* __restrict__ status, uint32_t ncols,
                                                                     int64_t out_ld) {
@@ -426,7 +429,7 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_dequant_kernel(NF4View W, i
   const int64_t code_bytes = (P + 1) / 2;
   const int64_t words = P >> 3;   // whole words
   const uint8_t* __restrict__ codes = W.codes;
-  const bool single = W.absmax != nullptr;   // no second level: â = absmax[block]
+  constexpr bool single = kSingle;   // no second level: â = absmax[block]
   const Rsrc rc = make_rsrc(codes, words * 4);
   const Rsrc rq = make_rsrc(W.qabsmax, single ? 0 : n1);
   const Rsrc rs = single ? make_rsrc(W.absmax, n1 * 4) : make_rsrc(W.absmax2, ((n1 + kBlock2 - 1) / kBlock2) * 4);
@@ -434,7 +437,7 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_dequant_kernel(NF4View W, i
   const int64_t tiles = (words + kQuantThreads * U - 1) / (kQuantThreads * U);
   int64_t tile = blockIdx.x;
   DqTile<U> cur;
-  dq_load(cur, tile, words, rc, rq, rs, sshift);
+  dq_load<U, kSingle>(cur, tile, words, rc, rq, rs, sshift);
   if (tid < 16) s_lut[tid] = kNF4[tid];
   if (tid <= 2 * kLevels2) s_q2[tid] = q2_value(tid - kLevels2);
   const float off = single ? 0.0f : W.offset[0];
@@ -451,18 +454,18 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_dequant_kernel(NF4View W, i
     for (int i = 0; i < 8; ++i) {
       const int64_t e = words * 8 + i;
       if (e >= P) break;
-      if (kBf16) static_cast<uint16_t*>(out)[e] = static_cast<uint16_t>(pack_bf16x2(v[i], 0.0f) & 0xffffu);
+      if constexpr (!std::is_same<O, float>::value) static_cast<uint16_t*>(out)[e] = static_cast<uint16_t>(O::pack2(v[i], 0.0f) & 0xffffu);
       else static_cast<float*>(out)[e] = v[i];
     }
   }
   // two register tiles in turn, so no copy waits on loads still in flight
   DqTile<U> nxt;
   for (; tile < tiles; tile += 2 * static_cast<int64_t>(gridDim.x)) {
-    dq_load(nxt, tile + gridDim.x, words, rc, rq, rs, sshift);
-    dq_decode<U, kBf16>(cur, tile, words, s_lut, s_q2, off, single, out, ncols, out_ld);
+    dq_load<U, kSingle>(nxt, tile + gridDim.x, words, rc, rq, rs, sshift);
+    dq_decode<U, O, kSingle, kStrided>(cur, tile, words, s_lut, s_q2, off, out, ncols, out_ld);
     if (tile + gridDim.x >= tiles) break;
-    dq_load(cur, tile + 2 * static_cast<int64_t>(gridDim.x), words, rc, rq, rs, sshift);
-    dq_decode<U, kBf16>(nxt, tile + gridDim.x, words, s_lut, s_q2, off, single, out, ncols, out_ld);
+    dq_load<U, kSingle>(cur, tile + 2 * static_cast<int64_t>(gridDim.x), words, rc, rq, rs, sshift);
+    dq_decode<U, O, kSingle, kStrided>(nxt, tile + gridDim.x, words, s_lut, s_q2, off, out, ncols, out_ld);
   }
 }
 
@@ -472,6 +475,7 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_dequant_kernel(NF4View W, i
 // bf16 writes (along k) are row-contiguous.
 constexpr int kTPad = 66;  // bf16 per LDS row (64 k + 2): 132-byte rows
 
+template <class T>
 __global__ __launch_bounds__(256) void nf4_dequant_t_kernel(NF4View W, int64_t K, int64_t N,
                                                             uint16_t* __restrict__ out) {
   __shared__ float s_lut[16];
@@ -499,7 +503,7 @@ __global__ __launch_bounds__(256) void nf4_dequant_t_kernel(NF4View W, int64_t K
       float v[8];
       decode8(w[c], ahat, s_lut, v);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) tile[(32 * part + 8 * c + e) * kTPad + kk] = static_cast<uint16_t>(pack_bf16x2(v[e], 0.0f));
+      for (int e = 0; e < 8; ++e) tile[(32 * part + 8 * c + e) * kTPad + kk] = static_cast<uint16_t>(T::pack2(v[e], 0.0f));
     }
   }
   __syncthreads();
@@ -547,29 +551,49 @@ hipError_t launch_quantize(const float* W, int64_t P, uint8_t* codes, int8_t* qa
   return hipGetLastError();
 }
 
-hipError_t launch_dequantize(NF4View W, int64_t P, void* out, int out_dtype, int32_t* status, hipStream_t stream,
-                             int64_t ncols, int64_t out_ld) {
+template <class O>
+hipError_t dequant_launch_t(NF4View W, int64_t P, void* out, int32_t* status, hipStream_t stream, int64_t ncols,
+                            int64_t out_ld) {
   constexpr int U = QN_DQ_U;
   const int64_t tiles = (P / 8 + kQuantThreads * U - 1) / (kQuantThreads * U);
   const int64_t blocks = tiles < 1 ? 1 : (tiles < QN_DQ_GRID ? tiles : QN_DQ_GRID);
   const Timer t(QK_DEQUANT, stream, true);
-  if (out_dtype == NF4_OUT_BF16)
-    hipExtLaunchKernelGGL((nf4_dequant_kernel<U, true>), dim3(static_cast<unsigned>(blocks)), dim3(kQuantThreads),
-                          0, stream, t.start(), t.end(), 0, W, P, out, status, static_cast<uint32_t>(ncols), out_ld);
-  else
-    hipExtLaunchKernelGGL((nf4_dequant_kernel<U, false>), dim3(static_cast<unsigned>(blocks)), dim3(kQuantThreads),
-                          0, stream, t.start(), t.end(), 0, W, P, out, status, static_cast<uint32_t>(ncols), out_ld);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kQuantThreads);
+  const uint32_t nc = static_cast<uint32_t>(ncols);
+  if (W.absmax != nullptr) {
+    if (ncols != 0)
+      hipExtLaunchKernelGGL((nf4_dequant_kernel<U, O, true, true>), grid, block, 0, stream, t.start(), t.end(), 0, W,
+                            P, out, status, nc, out_ld);
+    else
+      hipExtLaunchKernelGGL((nf4_dequant_kernel<U, O, true, false>), grid, block, 0, stream, t.start(), t.end(), 0, W,
+                            P, out, status, nc, out_ld);
+  } else {
+    if (ncols != 0)
+      hipExtLaunchKernelGGL((nf4_dequant_kernel<U, O, false, true>), grid, block, 0, stream, t.start(), t.end(), 0, W,
+                            P, out, status, nc, out_ld);
+    else
+      hipExtLaunchKernelGGL((nf4_dequant_kernel<U, O, false, false>), grid, block, 0, stream, t.start(), t.end(), 0,
+                            W, P, out, status, nc, out_ld);
+  }
   return hipGetLastError();
 }
 
+hipError_t launch_dequantize(NF4View W, int64_t P, void* out, int out_dtype, int32_t* status, hipStream_t stream,
+                             int64_t ncols, int64_t out_ld) {
+  if (out_dtype == NF4_OUT_BF16) return dequant_launch_t<Bf16>(W, P, out, status, stream, ncols, out_ld);
+  if (out_dtype == NF4_OUT_F16) return dequant_launch_t<F16>(W, P, out, status, stream, ncols, out_ld);
+  return dequant_launch_t<float>(W, P, out, status, stream, ncols, out_ld);
+}
+
 hipError_t launch_dequant_bf16(NF4View W, int64_t K, int64_t N, bool transposed, uint16_t* out, hipStream_t stream,
-                               int64_t out_ld) {
+                               int64_t out_ld, int dtype) {
   if (!transposed)
-    return launch_dequantize(W, K * N, out, NF4_OUT_BF16, nullptr, stream, out_ld != 0 && out_ld != N ? N : 0,
-                             out_ld);
+    return launch_dequantize(W, K * N, out, dtype == kDtypeF16 ? NF4_OUT_F16 : NF4_OUT_BF16, nullptr, stream,
+                             out_ld != 0 && out_ld != N ? N : 0, out_ld);
   Timer t(QK_DEQUANT_BF16, stream);
   dim3 grid(static_cast<unsigned>((N + 127) / 128), static_cast<unsigned>((K + 63) / 64));
-  hipLaunchKernelGGL(nf4_dequant_t_kernel, grid, dim3(256), 0, stream, W, K, N, out);
+  hipLaunchKernelGGL(dtype == kDtypeF16 ? nf4_dequant_t_kernel<F16> : nf4_dequant_t_kernel<Bf16>, grid, dim3(256), 0,
+                     stream, W, K, N, out);
   t.stop();
   return hipGetLastError();
 }

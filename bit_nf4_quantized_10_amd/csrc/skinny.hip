@@ -30,6 +30,14 @@ __device__ __forceinline__ uint16_t bf16_of(float x) {
   return static_cast<uint16_t>(pack_bf16x2(x, 0.0f) & 0xffffu);
 }
 
+// RNE to the layer's 16-bit type (f16: fp16, else bf16) and back to fp32.
+__device__ __forceinline__ uint16_t half_of(float x, int f16) {
+  return static_cast<uint16_t>((f16 ? F16::pack2(x, 0.0f) : Bf16::pack2(x, 0.0f)) & 0xffffu);
+}
+__device__ __forceinline__ float widen_of(uint32_t bits16, int f16) {
+  return f16 ? F16::widen(bits16) : Bf16::widen(bits16);
+}
+
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
@@ -45,6 +53,7 @@ struct TJob {
   int64_t rows, cols;
   float scale;
   int64_t bx, nblk;   // 32-column tiles per tile row, tiles in this job
+  int f16;            // elements are fp16 (else bf16)
 };
 
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(TJob j0, TJob j1) {
@@ -57,7 +66,7 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(TJob j0, TJob j1) {
   for (int i = ty; i < 32; i += 8) {
     const int64_t r = r0 + i, c = c0 + tx;
     uint16_t v = (r < j.rows && c < j.cols) ? j.src[r * j.cols + c] : 0;
-    if (j.scale != 1.0f) v = bf16_of(j.scale * bf16_bits_to_f32(v));
+    if (j.scale != 1.0f) v = half_of(j.scale * widen_of(v, j.f16), j.f16);
     tile[i][tx] = v;
   }
   __syncthreads();
@@ -67,9 +76,9 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(TJob j0, TJob j1) {
   }
 }
 
-TJob tjob(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols, float scale) {
+TJob tjob(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols, float scale, int dtype = kDtypeBf16) {
   const int64_t bx = cdiv(cols, 32);
-  return TJob{src, dst, rows, cols, scale, bx, bx * cdiv(rows, 32)};
+  return TJob{src, dst, rows, cols, scale, bx, bx * cdiv(rows, 32), dtype == kDtypeF16 ? 1 : 0};
 }
 
 // ------------------------------------------------------------ row sums
@@ -99,6 +108,7 @@ struct RsArgs {
 
 __device__ __forceinline__ int rs_off(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
 
+template <class T>
 __global__ __launch_bounds__(256) void rowsum_kernel(RsArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int t = threadIdx.x, lane = t & 63, q = lane & 15, g = lane >> 4;
@@ -154,11 +164,11 @@ __global__ __launch_bounds__(256) void rowsum_kernel(RsArgs a) {
     b = b == S - 1 ? 0 : b + 1;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const bf16x8 af = *reinterpret_cast<const bf16x8*>(slot + rs_off(16 * wave + q, 4 * st + g));
+      const typename T::v8 af = *reinterpret_cast<const typename T::v8*>(slot + rs_off(16 * wave + q, 4 * st + g));
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bf16x8 wf = *reinterpret_cast<const bf16x8*>(slot + 8192 + rs_off(16 * u + q, 4 * st + g));
-        acc[u] = mfma16x16x32(af, wf, acc[u]);
+        const typename T::v8 wf = *reinterpret_cast<const typename T::v8*>(slot + 8192 + rs_off(16 * u + q, 4 * st + g));
+        acc[u] = T::mfma16(af, wf, acc[u]);
       }
     }
   }
@@ -210,14 +220,16 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int cs_off(int row, int chunk) { return row * 128 + ((chunk ^ (((row >> 1) & 1) << 2)) << 4); }
 
-__device__ __forceinline__ bf16x8 tr_read2(const char* p0, const char* p1) {
+template <class T>
+__device__ __forceinline__ typename T::v8 tr_read2(const char* p0, const char* p1) {
   typedef __attribute__((address_space(3))) v4i16* lp;
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(p0));
   const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(p1));
   const v4i16 both[2] = {lo, hi};
-  return __builtin_bit_cast(bf16x8, both);
+  return __builtin_bit_cast(typename T::v8, both);
 }
 
+template <class T>
 __global__ __launch_bounds__(256) void colsum_kernel(CsJob j0, CsJob j1, int64_t M) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const bool second = blockIdx.x >= j0.nblk;
@@ -288,17 +300,17 @@ __global__ __launch_bounds__(256) void colsum_kernel(CsJob j0, CsJob j1, int64_t
       __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
     }
     const char* slot = ring + b * kCsSlot;
-    bf16x8 fa[2], fv[2];
+    typename T::v8 fa[2], fv[2];
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti) {
-      fa[ti] = tr_read2(slot + toff[ti][0], slot + toff[ti][1]);
-      fv[ti] = tr_read2(slot + 2048 + toff[ti][0], slot + 2048 + toff[ti][1]);
+      fa[ti] = tr_read2<T>(slot + toff[ti][0], slot + toff[ti][1]);
+      fv[ti] = tr_read2<T>(slot + 2048 + toff[ti][0], slot + 2048 + toff[ti][1]);
     }
     // D[j][c]: each lane holds column c = 32 ci + lane%32 and j = 32 vj + 8jj + 4(lane/32) + e
 #pragma unroll
     for (int vj = 0; vj < 2; ++vj)
 #pragma unroll
-      for (int ci = 0; ci < 2; ++ci) acc[vj][ci] = mfma32x32x16(fv[vj], fa[ci], acc[vj][ci]);
+      for (int ci = 0; ci < 2; ++ci) acc[vj][ci] = T::mfma32(fv[vj], fa[ci], acc[vj][ci]);
   }
   __builtin_amdgcn_s_waitcnt(0);
   // each wave's 64 x 64 block, [c][j] fp32, into the start of its own ring
@@ -342,6 +354,7 @@ struct RdJob {
   uint16_t* out_bf16;
   int64_t nblk;
   int64_t out_ld;   // row stride of the output (cols, or rows when transposed, for a dense result)
+  int f16;          // the 16-bit output is fp16 (else bf16)
 };
 
 __global__ __launch_bounds__(256) void reduce_kernel(RdJob j0, RdJob j1) {
@@ -363,7 +376,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(RdJob j0, RdJob j1) {
     s *= J.scale;
     const int64_t o = J.transpose ? (i % J.cols) * J.out_ld + i / J.cols : (i / J.cols) * J.out_ld + i % J.cols;
     if (J.out_f32) J.out_f32[o] = s;
-    if (J.out_bf16) J.out_bf16[o] = bf16_of(s);
+    if (J.out_bf16) J.out_bf16[o] = half_of(s, J.f16);
   }
 }
 
@@ -376,10 +389,11 @@ void split_plan(int64_t tiles, int64_t red, int64_t target, int64_t quantum, int
 }
 
 RdJob rdjob(const float* part, int64_t splits, int64_t rows, int64_t cols, float scale, bool transpose, float* out_f32,
-            uint16_t* out_bf16) {
+            uint16_t* out_bf16, int dtype = kDtypeBf16) {
   int64_t blocks = cdiv(rows * cols, 256);
   if (blocks > 2048) blocks = 2048;
-  return RdJob{part, splits, rows, cols, scale, transpose ? 1 : 0, out_f32, out_bf16, blocks, transpose ? rows : cols};
+  return RdJob{part, splits, rows, cols, scale, transpose ? 1 : 0, out_f32, out_bf16, blocks, transpose ? rows : cols,
+               dtype == kDtypeF16 ? 1 : 0};
 }
 
 hipError_t launch_reduce(const RdJob& ja, const RdJob* jb, hipStream_t stream) {
@@ -392,19 +406,43 @@ hipError_t launch_reduce(const RdJob& ja, const RdJob* jb, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_rowsum(const uint16_t* act, const uint16_t* wt, int64_t M, int64_t r, int64_t red, int64_t splits,
-                         int64_t per, float* part, hipStream_t stream, int64_t act_ld = 0, int64_t wt_ld = 0) {
+template <class T>
+hipError_t rowsum_launch_t(const RsArgs& a, int64_t splits, hipStream_t stream) {
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rowsum_kernel),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rowsum_kernel<T>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kRsLds);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  const RsArgs a{act, wt, M, r, red, per, cdiv(M, 64), cdiv(r, 64), part, act_ld ? act_ld : red, wt_ld ? wt_ld : red};
-  hipLaunchKernelGGL(rowsum_kernel, dim3(static_cast<unsigned>(a.row_blocks * a.j_chunks * splits)), dim3(256), kRsLds,
-                     stream, a);
+  hipLaunchKernelGGL(rowsum_kernel<T>, dim3(static_cast<unsigned>(a.row_blocks * a.j_chunks * splits)), dim3(256),
+                     kRsLds, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_rowsum(const uint16_t* act, const uint16_t* wt, int64_t M, int64_t r, int64_t red, int64_t splits,
+                         int64_t per, float* part, hipStream_t stream, int64_t act_ld = 0, int64_t wt_ld = 0,
+                         int dtype = kDtypeBf16) {
+  const RsArgs a{act, wt, M, r, red, per, cdiv(M, 64), cdiv(r, 64), part, act_ld ? act_ld : red, wt_ld ? wt_ld : red};
+  return dtype == kDtypeF16 ? rowsum_launch_t<F16>(a, splits, stream) : rowsum_launch_t<Bf16>(a, splits, stream);
+}
+
+template <class T>
+hipError_t colsum_launch_t(const CsJob& ja, const CsJob& jb, int64_t M, hipStream_t stream) {
+  static bool configured = false;
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&colsum_kernel<T>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kCsLds);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  hipLaunchKernelGGL(colsum_kernel<T>, dim3(static_cast<unsigned>(ja.nblk + jb.nblk)), dim3(256), kCsLds, stream, ja,
+                     jb, M);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum(const CsJob& ja, const CsJob& jb, int64_t M, hipStream_t stream, int dtype) {
+  return dtype == kDtypeF16 ? colsum_launch_t<F16>(ja, jb, M, stream) : colsum_launch_t<Bf16>(ja, jb, M, stream);
 }
 
 }  // namespace
@@ -438,53 +476,45 @@ SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N, int64_t r) {
 
 hipError_t launch_lora_down(int64_t M, int64_t K, int64_t r, const uint16_t* X, const uint16_t* A, uint16_t* Z,
                             const SkinnyPlan& p, void* at_ws, void* part_ws, hipStream_t stream, int64_t N,
-                            const uint16_t* B, float c, uint16_t* cbt, int64_t rb) {
+                            const uint16_t* B, float c, uint16_t* cbt, int64_t rb, int dtype) {
   uint16_t* At = static_cast<uint16_t*>(at_ws);
-  const TJob ja = tjob(A, At, K, r, 1.0f);
-  TJob jb = cbt != nullptr ? tjob(B, cbt, rb ? rb : r, N, c) : ja;
+  const TJob ja = tjob(A, At, K, r, 1.0f, dtype);
+  TJob jb = cbt != nullptr ? tjob(B, cbt, rb ? rb : r, N, c, dtype) : ja;
   if (cbt == nullptr) jb.nblk = 0;
   hipLaunchKernelGGL(transpose_bf16_kernel, dim3(static_cast<unsigned>(ja.nblk + jb.nblk)), dim3(256), 0, stream, ja,
                      jb);
   float* part = static_cast<float*>(part_ws);
   Timer tm(QK_LORA_DOWN, stream);
-  hipError_t e = launch_rowsum(X, At, M, r, K, p.z_splits, p.z_per, part, stream);
+  hipError_t e = launch_rowsum(X, At, M, r, K, p.z_splits, p.z_per, part, stream, 0, 0, dtype);
   tm.stop();
   if (e != hipSuccess) return e;
-  const RdJob jz = rdjob(part, p.z_splits, M, r, 1.0f, false, nullptr, Z);
+  const RdJob jz = rdjob(part, p.z_splits, M, r, 1.0f, false, nullptr, Z, dtype);
   return launch_reduce(jz, nullptr, stream);
 }
 
 hipError_t launch_dz(int64_t M, int64_t N, int64_t r, const uint16_t* G, const uint16_t* B, float c, uint16_t* dZ,
-                     const SkinnyPlan& p, void* part_ws, hipStream_t stream) {
+                     const SkinnyPlan& p, void* part_ws, hipStream_t stream, int dtype) {
   float* part = static_cast<float*>(part_ws);
   Timer tm(QK_BWD_DZ, stream);
-  hipError_t e = launch_rowsum(G, B, M, r, N, p.dz_splits, p.dz_per, part, stream);
+  hipError_t e = launch_rowsum(G, B, M, r, N, p.dz_splits, p.dz_per, part, stream, 0, 0, dtype);
   tm.stop();
   if (e != hipSuccess) return e;
-  const RdJob jz = rdjob(part, p.dz_splits, M, r, c, false, nullptr, dZ);
+  const RdJob jz = rdjob(part, p.dz_splits, M, r, c, false, nullptr, dZ, dtype);
   return launch_reduce(jz, nullptr, stream);
 }
 
 // dA = Xᵀ dZ (K x r) and dB = c Zᵀ G (r x N).
 hipError_t launch_colsums(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const uint16_t* G,
                           const uint16_t* Z, const uint16_t* dZ, float c, float* dA, float* dB, const SkinnyPlan& p,
-                          void* da_ws, void* db_ws, hipStream_t stream) {
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&colsum_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kCsLds);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+                          void* da_ws, void* db_ws, hipStream_t stream, int dtype) {
   const int64_t jc = cdiv(r, 64);
   CsJob ja{X, K, K, dZ, static_cast<float*>(da_ws), cdiv(K, 64), jc, p.da_per, 0, r, r};
   CsJob jb{G, N, N, Z, static_cast<float*>(db_ws), cdiv(N, 64), jc, p.db_per, 0, r, r};
   ja.nblk = ja.col_blocks * jc * p.da_splits;
   jb.nblk = jb.col_blocks * jc * p.db_splits;
   Timer tm(QK_BWD_COLSUM, stream);
-  hipLaunchKernelGGL(colsum_kernel, dim3(static_cast<unsigned>(ja.nblk + jb.nblk)), dim3(256), kCsLds, stream, ja, jb, M);
+  hipError_t e = launch_colsum(ja, jb, M, stream, dtype);
   tm.stop();
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const RdJob ra = rdjob(static_cast<float*>(da_ws), p.da_splits, K, r, 1.0f, false, dA, nullptr);
   const RdJob rb = rdjob(static_cast<float*>(db_ws), p.db_splits, N, r, c, true, dB, nullptr);
@@ -527,15 +557,16 @@ GroupPlan plan_grouped(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r
 // and B (row stride Ntot), reduced into column block i of dZ (row stride g r).
 hipError_t launch_dz_grouped(int64_t M, int g, const int64_t* Ns, int64_t Ntot, int64_t r, const uint16_t* G,
                              const uint16_t* B, float c, uint16_t* dZ, const GroupPlan& gp, void* part_ws,
-                             hipStream_t stream) {
+                             hipStream_t stream, int dtype) {
   float* part = static_cast<float*>(part_ws);
   int64_t off = 0;
   for (int i = 0; i < g; ++i) {
     Timer tm(QK_BWD_DZ, stream);
-    hipError_t e = launch_rowsum(G + off, B + off, M, r, Ns[i], gp.dz_splits[i], gp.dz_per[i], part, stream, Ntot, Ntot);
+    hipError_t e =
+        launch_rowsum(G + off, B + off, M, r, Ns[i], gp.dz_splits[i], gp.dz_per[i], part, stream, Ntot, Ntot, dtype);
     tm.stop();
     if (e != hipSuccess) return e;
-    RdJob jz = rdjob(part, gp.dz_splits[i], M, r, c, false, nullptr, dZ + i * r);
+    RdJob jz = rdjob(part, gp.dz_splits[i], M, r, c, false, nullptr, dZ + i * r, dtype);
     jz.out_ld = g * r;
     if ((e = launch_reduce(jz, nullptr, stream)) != hipSuccess) return e;
     off += Ns[i];
@@ -548,14 +579,7 @@ hipError_t launch_dz_grouped(int64_t M, int g, const int64_t* Ns, int64_t Ntot, 
 hipError_t launch_colsums_grouped(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t Ntot, int64_t r,
                                   const uint16_t* X, const uint16_t* G, const uint16_t* Z, const uint16_t* dZ, float c,
                                   float* dA, float* dB, const GroupPlan& gp, void* da_ws, void* db_ws,
-                                  hipStream_t stream) {
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&colsum_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kCsLds);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+                                  hipStream_t stream, int dtype) {
   const int64_t rt = g * r;
   CsJob jobs[kMaxGroupMembers + 1];
   RdJob rds[kMaxGroupMembers + 1];
@@ -574,10 +598,8 @@ hipError_t launch_colsums_grouped(int64_t M, int64_t K, int g, const int64_t* Ns
     CsJob second = j + 1 <= g ? jobs[j + 1] : jobs[j];
     if (j + 1 > g) second.nblk = 0;
     Timer tm(QK_BWD_COLSUM, stream);
-    hipLaunchKernelGGL(colsum_kernel, dim3(static_cast<unsigned>(jobs[j].nblk + second.nblk)), dim3(256), kCsLds,
-                       stream, jobs[j], second, M);
+    hipError_t e = launch_colsum(jobs[j], second, M, stream, dtype);
     tm.stop();
-    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   for (int j = 0; j <= g; j += 2) {

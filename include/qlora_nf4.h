@@ -45,9 +45,14 @@ extern "C" {
 #define NF4_EPADDING    4  /* status bit: odd length whose pad nibble is not code 7 */
 #define NF4_EHIP        8  /* a HIP runtime call or kernel launch failed */
 
+/* 16-bit compute types of the layer (see qlora_linear_fwd_dt). */
+#define NF4_COMPUTE_BF16 0
+#define NF4_COMPUTE_F16  1
+
 /* Output dtypes of nf4_dequantize. */
 #define NF4_OUT_F32   0
 #define NF4_OUT_BF16  1
+#define NF4_OUT_F16   2   /* round-to-nearest-even fp16 (overflow gives inf) */
 
 /* Fixed format constants: 64 weights per first-level block, 256 first-level
  * scales per second-level block, second-level codes q in [-127, 127] standing
@@ -144,6 +149,7 @@ int qlora_linear_bwd(int64_t M, int64_t K, int64_t N, int64_t r,
 /* Element types of the adapter matrices passed to qlora_merge. */
 #define NF4_AB_BF16 0
 #define NF4_AB_F32  1
+#define NF4_AB_F16  2
 
 /* Merge the adapter into the frozen base for re-export (page section
  * "Merge 后还是不是训练时的函数": the trained function is Ŵ + cAB, merged in
@@ -154,7 +160,7 @@ int qlora_linear_bwd(int64_t M, int64_t K, int64_t N, int64_t r,
  * sum accumulated in fp64 for t = 0 .. r-1 in order, c * sum and the addition
  * in fp64, and one rounding to fp32.  A: K x r, B: r x N, row-major, of
  * element type ab_dtype (NF4_AB_BF16 or NF4_AB_F32, e.g. fp32 master copies),
- * aligned to their element size; W_merged: K x N fp32, 16-byte aligned,
+ * (NF4_AB_F16: fp16) aligned to their element size; W_merged: K x N fp32, 16-byte aligned,
  * caller-owned.  Requirements: K, N, r >= 1, r <= 65536, W->numel == K*N,
  * K*N, K*r and r*N below 2^29.  Any N is allowed (blocks run over the flat
  * index).  NF4_EINVAL otherwise.  The state is only read. */
@@ -172,6 +178,11 @@ int qlora_merge(int64_t K, int64_t N, int64_t r, const nf4_state_t* W, const voi
  * NF4_EINVAL otherwise. */
 int qlora_sgd_step(int64_t K, int64_t N, int64_t r, uint16_t* A, uint16_t* B, const float* dA, const float* dB,
                    float lr, float* A_master, float* B_master, void* stream);
+/* The same step for parameters of the 16-bit type param_dtype
+ * (NF4_COMPUTE_BF16 or NF4_COMPUTE_F16). */
+int qlora_sgd_step_dt(int param_dtype, int64_t K, int64_t N, int64_t r, uint16_t* A, uint16_t* B,
+                      const float* dA, const float* dB, float lr, float* A_master, float* B_master,
+                      void* stream);
 
 /* Grouped linears sharing one input (e.g. the q, k, v projections, or gate
  * and up: adapters on several projections of one layer, page
@@ -199,6 +210,20 @@ int qlora_grouped_bwd(int64_t M, int64_t K, int g, const int64_t* N, int64_t r, 
                       const uint16_t* X, const uint16_t* Z, const nf4_state_t* W, const uint16_t* A,
                       const uint16_t* B, float c, uint16_t* dX, float* dA, float* dB,
                       void* workspace, int64_t workspace_bytes, void* stream);
+
+/* The 16-bit compute type of the layer ([P2] §20: BF16 where supported,
+ * else FP16).  The _dt entry points take it as their first argument; X, A,
+ * B, G, Y, Z and dX are then of that type (uint16_t bit patterns), the
+ * dequantized weight is RNE_T(ŵ) (fp16: overflow past 65504 gives inf), and
+ * every product accumulates in fp32.  qlora_linear_fwd / _bwd are the
+ * NF4_COMPUTE_BF16 case; requirements and results are otherwise the same. */
+int qlora_linear_fwd_dt(int compute_dtype, int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X,
+                        const nf4_state_t* W, const uint16_t* A, const uint16_t* B, float c, uint16_t* Y,
+                        uint16_t* Z, void* workspace, int64_t workspace_bytes, void* stream);
+int qlora_linear_bwd_dt(int compute_dtype, int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G,
+                        const uint16_t* X, const uint16_t* Z, const nf4_state_t* W, const uint16_t* A,
+                        const uint16_t* B, float c, uint16_t* dX, float* dA, float* dB, void* workspace,
+                        int64_t workspace_bytes, void* stream);
 
 /* Synchronise `stream`, then copy the device status word to *host_value.
  * Returns NF4_EHIP if the copy fails, else NF4_OK. */

@@ -61,6 +61,15 @@ def weight(K: int, N: int, seed: int, outliers: bool, std: float = 0.02) -> np.n
     return w.reshape(K, N)
 
 
+def f16_normal(shape, std: float, seed: int):
+    """Returns (bits uint16, values fp32) of an fp16 N(0, std) tensor (the
+    fp32 draw rounded to fp16 by numpy, nearest even)."""
+    n = int(np.prod(shape))
+    x = (_rng(seed).standard_normal(n) * std).astype(np.float32)
+    h = x.astype(np.float16).reshape(shape)
+    return h.view(np.uint16), h.astype(np.float32)
+
+
 def bf16_normal(shape, std: float, seed: int):
     """Returns (bits uint16, values fp32) of a bf16 N(0, std) tensor."""
     n = int(np.prod(shape))

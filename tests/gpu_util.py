@@ -26,7 +26,7 @@ def dev_bf16(bits):
 
 def host(t) -> np.ndarray:
     import torch
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         return t.float().cpu().numpy()
     return t.cpu().numpy()
 
