@@ -342,6 +342,34 @@ def bench_components(torch, qn, si, dev, sets, outs, qws, status):
                                  "how": "fwd + bwd of q, k, v (3 x 4096 x 4096, r = 64, M = 4096): one grouped "
                                         "call each way vs three single-linear calls each way, cache flushed"}
     del gws, sws, Yg, Zg, dXg, dAg, dBg, Ag, Bg, Gg
+    # mid-size batches (17 <= M < 512: the weight is decoded inside the GEMM)
+    mid = {}
+    for Mm in (128, 256):
+        Xm, Gm = sets[0]["X"][:Mm].contiguous(), sets[0]["G"][:Mm].contiguous()
+        fwm, bwm = qn.qlora_workspace_bytes(Mm, Kg, Ng, rg)
+        wsm = torch.empty(max(fwm, bwm), dtype=torch.uint8, device=dev)
+        Ym = torch.empty(Mm, Ng, dtype=torch.bfloat16, device=dev)
+        Zm = torch.empty(Mm, rg, dtype=torch.bfloat16, device=dev)
+        dXm = torch.empty(Mm, Kg, dtype=torch.bfloat16, device=dev)
+        dAm = torch.empty(Kg, rg, dtype=torch.float32, device=dev)
+        dBm = torch.empty(rg, Ng, dtype=torch.float32, device=dev)
+
+        def stepm(i):
+            qn.qlora_linear_fwd(Xm, gst[i % 3], sets[0]["A"], sets[0]["B"], cg, Kg, Ng, Ym, Zm, wsm)
+            qn.qlora_linear_bwd(Gm, Xm, Zm, gst[i % 3], sets[0]["A"], sets[0]["B"], cg, Kg, Ng, True, dXm, dAm,
+                                dBm, wsm)
+
+        stepm(0)
+        mms = _time_calls(torch, stepm, 6, flush)
+        fwk = _time_kernel(qn, torch, "fwd_gemm", stepm, 6, flush)
+        mfl = sum(layer_flops(Mm, Kg, Ng, rg))
+        wbytes = (Kg * Ng) // 2 + (Kg * Ng) // 64   # packed codes + second-level codes, read by each GEMM
+        mid[f"M{Mm}"] = {"ms": round(mms, 4), "TFLOPs": round(mfl / (mms * 1e-3) / 1e12, 1),
+                         "fwd_gemm_ms": round(fwk, 4),
+                         "fwd_gemm_TFLOPs": round((2 * Mm * Kg * Ng + 2 * Mm * rg * Ng) / (fwk * 1e-3) / 1e12, 1),
+                         "fwd_gemm_weight_GBps": round(wbytes / (fwk * 1e-3) / 1e9, 1)}
+        del wsm, Ym, Zm, dXm, dAm, dBm
+    res["mid_m_attn7b"] = mid
     # the same layer step in the fp16 compute type (fp16 MFMA, fp16 Ŵ)
     Xh, Ah, Bh, Gh = (sets[0][k].to(torch.float16) for k in ("X", "A", "B", "G"))
     fws16, bws16 = qn.qlora_workspace_bytes(Mg, Kg, Ng, rg)

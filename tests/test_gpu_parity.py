@@ -424,3 +424,48 @@ def test_full_size_decode65b_gemv(M):
     e = rel_err(host(Y)[:, cols], Yr)
     say(f"GEMV M={M} err={e:.2e}")
     assert e <= TOL and rel_err(host(Z), Zr) <= TOL
+
+
+@pytest.mark.parametrize("M", [8, 130, 600])   # dequant-GEMV, fused kernel, dequantize-then-GEMM
+def test_layer_in_hip_graph_replays_bit_exact(M):
+    """Every launch of a call goes on the caller's stream and nothing is
+    allocated or synchronised inside, so forward + backward can be captured
+    in a HIP graph; each replay (with eager work and synchronisations in
+    between) must reproduce the eager outputs bit for bit."""
+    import torch
+    K, N, r = 512, 768, 16
+    case = _layer_case(M, K, N, r, 0.5, seed=40 + M)
+    say(f"layer captured in a HIP graph, M={M}")
+    state, status = _quantize(case["W"])
+    assert status == 0
+    X, A, B, G = (dev_bf16(case[k]) for k in ("Xb", "Ab", "Bb", "Gb"))
+    fw, bw = qn.qlora_workspace_bytes(M, K, N, r)
+    fws = torch.empty(max(fw, 256), dtype=torch.uint8, device="cuda")
+    bws = torch.empty(max(bw, 256), dtype=torch.uint8, device="cuda")
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty(M, r, dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    dA = torch.empty(K, r, dtype=torch.float32, device="cuda")
+    dB = torch.empty(r, N, dtype=torch.float32, device="cuda")
+
+    def step():
+        qn.qlora_linear_fwd(X, state, A, B, 0.5, K, N, Y, Z, fws)
+        qn.qlora_linear_bwd(G, X, Z, state, A, B, 0.5, K, N, True, dX, dA, dB, bws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                      # eager reference (also configures the kernels)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref = [host(t).tobytes() for t in (Y, Z, dX, dA, dB)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (Y, Z, dX, dA, dB):
+            t.zero_()               # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert [host(t).tobytes() for t in (Y, Z, dX, dA, dB)] == ref, f"replay {rep}"
