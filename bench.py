@@ -342,9 +342,12 @@ def bench_components(torch, qn, si, dev, sets, outs, qws, status):
                                  "how": "fwd + bwd of q, k, v (3 x 4096 x 4096, r = 64, M = 4096): one grouped "
                                         "call each way vs three single-linear calls each way, cache flushed"}
     del gws, sws, Yg, Zg, dXg, dAg, dBg, Ag, Bg, Gg
-    # mid-size batches (17 <= M < 512: the weight is decoded inside the GEMM)
+    # mid-size batches (17 <= M < 512: the weight is decoded inside the GEMM,
+    # whose reduction is split across workgroups when its output has too few
+    # tiles for the device; fwd_gemm_ms is the GEMM launch alone, without the
+    # fixed-order sum of its partials)
     mid = {}
-    for Mm in (128, 256):
+    for Mm in (64, 128, 256, 384):
         Xm, Gm = sets[0]["X"][:Mm].contiguous(), sets[0]["G"][:Mm].contiguous()
         fwm, bwm = qn.qlora_workspace_bytes(Mm, Kg, Ng, rg)
         wsm = torch.empty(max(fwm, bwm), dtype=torch.uint8, device=dev)

@@ -46,6 +46,8 @@ namespace qn {
 
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kBM = 256;
 constexpr int kBN = 256;
 constexpr int kBK = 64;
@@ -78,7 +80,25 @@ struct BigArgs {
   int64_t ext_a_ld;
   int ngroups;
   int64_t gend[kMaxGroupMembers];
+  // Split-K (part non-null): workgroup z reduces elements [z k_per,
+  // (z+1) k_per) and writes its fp32 tile to part + z M cols (row-major);
+  // only z = 0 adds the LoRA extension.  The sum over z in order then gives
+  // the output.
+  float* part;
+  int64_t k_per;
 };
+
+// Reduction stages [beg, end) of this workgroup.
+template <bool kSplit>
+__device__ __forceinline__ void stage_range(const BigArgs& a, int64_t red, int64_t step, int64_t& beg, int64_t& end) {
+  const int64_t all = (red + step - 1) / step;
+  beg = 0;
+  end = all;
+  if (kSplit) {
+    beg = static_cast<int64_t>(blockIdx.z) * (a.k_per / step);
+    end = beg + a.k_per / step < all ? beg + a.k_per / step : all;
+  }
+}
 
 #ifndef QN_TILE_GROUP
 #define QN_TILE_GROUP 4
@@ -454,7 +474,7 @@ struct Dense {
 // row, 16-byte chunk q of row R at q ^ (R & 31)) so that every global store
 // writes whole 512-byte row segments.  Shared by the fused and dense kernels;
 // the main loop has released LDS when this starts.
-template <class T, bool kForward, class Core>
+template <class T, bool kForward, bool kSplit, class Core>
 __device__ __forceinline__ void finish(const Core& k, const BigArgs& a, f32x16 (&acc)[4][4]) {
   const int lane = k.lane, t = k.t;
   const int64_t cols = kForward ? a.N : a.K;
@@ -464,7 +484,8 @@ __device__ __forceinline__ void finish(const Core& k, const BigArgs& a, f32x16 (
     for (int i = 0; i < a.ngroups; ++i) zoff += k.c0 >= a.gend[i] ? a.r : 0;
   const Rsrc re = make_rsrc(a.ext_a + zoff, (a.M * lda - zoff) * 2);
   const Rsrc rb = make_rsrc(a.ext_b, cols * a.r * 2);
-  for (int64_t j0 = 0; j0 < a.r; j0 += kBK) {
+  const int64_t r_ext = (!kSplit || blockIdx.z == 0) ? a.r : 0;
+  for (int64_t j0 = 0; j0 < r_ext; j0 += kBK) {
     const int c = t & 7;
     const int64_t j = j0 + 8 * c;
 #pragma unroll
@@ -483,6 +504,29 @@ __device__ __forceinline__ void finish(const Core& k, const BigArgs& a, f32x16 (
 
   // Lane l holds, for tile (i, j), output row 32i + l%32 and, for each jj,
   // the 4 columns 32j + 8jj + 4(l/32) .. +3.
+  if constexpr (kSplit) {
+    // split-K: the fp32 tile, 16 bytes per buffer store; rows past M and
+    // columns past cols (cols % 8 == 0) are masked.
+    const int r32 = lane & 31, h = lane >> 5, wm = k.wave >> 1, wn = k.wave & 1;
+    const Rsrc rp = make_rsrc(a.part + (static_cast<int64_t>(blockIdx.z) * a.M + k.m0) * cols + k.c0,
+                              ((a.M - k.m0) * cols - k.c0) * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + 32 * i + r32;
+      const bool row_ok = k.m0 + row < a.M;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int col = wn * 128 + 32 * j + 8 * jj + 4 * h;
+          const uint32_t voff =
+              (row_ok && k.c0 + col < cols) ? static_cast<uint32_t>((row * cols + col) * 4) : kMasked;
+          const f32x4 v = {acc[i][j][4 * jj], acc[i][j][4 * jj + 1], acc[i][j][4 * jj + 2], acc[i][j][4 * jj + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rp, voff, 0, 0);
+        }
+    }
+    return;
+  }
   char* st = k.sA(0);
   {
     const int r32 = lane & 31, h = lane >> 5, wm = k.wave >> 1, wn = k.wave & 1;
@@ -515,7 +559,7 @@ __device__ __forceinline__ void finish(const Core& k, const BigArgs& a, f32x16 (
   }
 }
 
-template <class T, bool kForward, bool kKTail>
+template <class T, bool kForward, bool kKTail, bool kSplit>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void qlora_big_kernel(BigArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   Big<T, kForward, kKTail> k(a, smem);
@@ -523,7 +567,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     float* q2t = reinterpret_cast<float*>(smem + kOffQ);
     q2t[k.t] = q2_value(k.t - 128);
   }
-  const int64_t nst = (k.red + kBK - 1) / kBK;
+  int64_t s_beg, s_end;
+  stage_range<kSplit>(a, k.red, kBK, s_beg, s_end);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -533,13 +578,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // prologue: stage 0 into buffer 0, stage 1 weights into registers
+  // prologue: the first stage into buffer 0, the next one's weights into registers
   WRegs cur, nxt;
-  k.copy_act(0, 0);
-  k.load_w(cur, 0);
-  k.load_w(nxt, 1);
+  k.copy_act(s_beg, 0);
+  k.load_w(cur, s_beg);
+  k.load_w(nxt, s_beg + 1);
   __syncthreads();                 // q2t staged
-  k.build_table(cur, 0, 0);
+  k.build_table(cur, s_beg, 0);
   {
     uint32_t ix[16];
     k.split_codes(cur, ix);
@@ -550,9 +595,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   __syncthreads();
   cur = nxt;
 
-  for (int64_t s = 0; s < nst; ++s) {
-    const int b = static_cast<int>(s & 1);
-    // (stage s+1 and s+2 accesses past the end are masked or never read)
+  for (int64_t s = s_beg; s < s_end; ++s) {
+    const int b = static_cast<int>((s - s_beg) & 1);
+    // (stage s+1 and s+2 accesses past the range are masked or never read)
     k.copy_act(s + 1, b ^ 1);
     k.load_w(nxt, s + 2);
     k.build_table(cur, s + 1, b ^ 1);
@@ -582,14 +627,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     cur = nxt;
   }
 
-  finish<T, kForward>(k, a, acc);
+  finish<T, kForward, kSplit>(k, a, acc);
 }
 
-template <class T, bool kForward, bool kKTail>
+template <class T, bool kForward, bool kKTail, bool kSplit>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void qlora_dense_kernel(BigArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   Dense<T, kForward, kKTail> k(a, smem);
-  const int64_t nst = (k.red + kRK - 1) / kRK;
+  int64_t s_beg, s_end;
+  stage_range<kSplit>(a, k.red, kRK, s_beg, s_end);
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -602,17 +648,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // issued in two halves between B(x-S+1) and B(x-S+2), into slot x % S,
   // which B(x-S+1) released.  Each wave then has (S-2) later stages (8
   // copies each) outstanding when it waits for stage x.  Copies of stages
-  // past the end read zeros or land in slots that are never read.
+  // past the end read zeros or land in slots that are never read.  (Stages
+  // and slots count from the first stage of this workgroup's range.)
   constexpr int S = kSlots;
-  for (int x = 0; x < S - 1; ++x) k.copy_stage(x, x);
+  for (int x = 0; x < S - 1; ++x) k.copy_stage(s_beg + x, x);
 #pragma unroll
-  for (int g = 0; g < 4; ++g) k.copy_one(S - 1, S - 1, 0, g);
+  for (int g = 0; g < 4; ++g) k.copy_one(s_beg + S - 1, S - 1, 0, g);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(8 * (S - 2) + 4, 15));
   __builtin_amdgcn_s_barrier();
   typename Dense<T, kForward, kKTail>::Frags F0, F1;
   k.load_frags(0, 0, F0);
   int b = 0;
-  for (int64_t s = 0; s < nst; ++s) {
+  for (int64_t s = s_beg; s < s_end; ++s) {
     const int bp = b == 0 ? S - 1 : b - 1;   // slot of stage s + S - 1
     const int bn = b == S - 1 ? 0 : b + 1;   // slot of stage s + 1
     k.half_step(F0, F1, b, 1, s + S - 1, bp, 1, acc);
@@ -624,66 +671,153 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  finish<T, kForward>(k, a, acc);
+  finish<T, kForward, kSplit>(k, a, acc);
 }
 
-template <class T, bool kForward, bool kKTail>
+template <class T, bool kForward, bool kKTail, bool kSplit>
 hipError_t launch_big_t(const BigArgs& a, hipStream_t stream, const Timer& tm) {
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_big_kernel<T, kForward, kKTail>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_big_kernel<T, kForward, kKTail, kSplit>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  const int64_t cols = kForward ? a.N : a.K;
-  dim3 grid(static_cast<unsigned>((cols + kBN - 1) / kBN), static_cast<unsigned>((a.M + kBM - 1) / kBM), 1);
-  hipExtLaunchKernelGGL((qlora_big_kernel<T, kForward, kKTail>), grid, dim3(kThreads), kLdsBytes, stream, tm.start(),
-                        tm.end(), 0, a);
+  const int64_t cols = kForward ? a.N : a.K, red = kForward ? a.K : a.N;
+  const unsigned zs = kSplit ? static_cast<unsigned>((red + a.k_per - 1) / a.k_per) : 1u;
+  dim3 grid(static_cast<unsigned>((cols + kBN - 1) / kBN), static_cast<unsigned>((a.M + kBM - 1) / kBM), zs);
+  hipExtLaunchKernelGGL((qlora_big_kernel<T, kForward, kKTail, kSplit>), grid, dim3(kThreads), kLdsBytes, stream,
+                        tm.start(), tm.end(), 0, a);
   return hipGetLastError();
 }
 
-template <bool kForward>
-hipError_t launch_big(const BigArgs& a, hipStream_t stream, const Timer& tm, int dtype) {
-  const int64_t red = kForward ? a.K : a.N;
-  if (dtype == F16::kDtype)
-    return (red % kBK) ? launch_big_t<F16, kForward, true>(a, stream, tm) : launch_big_t<F16, kForward, false>(a, stream, tm);
-  return (red % kBK) ? launch_big_t<Bf16, kForward, true>(a, stream, tm) : launch_big_t<Bf16, kForward, false>(a, stream, tm);
-}
-
-template <class T, bool kForward, bool kKTail>
+template <class T, bool kForward, bool kKTail, bool kSplit>
 hipError_t launch_dense_t(const BigArgs& a, hipStream_t stream, const Timer& tm) {
   static bool configured = false;
   if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_dense_kernel<T, kForward, kKTail>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_dense_kernel<T, kForward, kKTail, kSplit>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kRingLds);
     if (e != hipSuccess) return e;
     configured = true;
   }
-  const int64_t cols = kForward ? a.N : a.K;
-  dim3 grid(static_cast<unsigned>((cols + kBN - 1) / kBN), static_cast<unsigned>((a.M + kBM - 1) / kBM), 1);
-  hipExtLaunchKernelGGL((qlora_dense_kernel<T, kForward, kKTail>), grid, dim3(kThreads), kRingLds, stream, tm.start(),
-                        tm.end(), 0, a);
+  const int64_t cols = kForward ? a.N : a.K, red = kForward ? a.K : a.N;
+  const unsigned zs = kSplit ? static_cast<unsigned>((red + a.k_per - 1) / a.k_per) : 1u;
+  dim3 grid(static_cast<unsigned>((cols + kBN - 1) / kBN), static_cast<unsigned>((a.M + kBM - 1) / kBM), zs);
+  hipExtLaunchKernelGGL((qlora_dense_kernel<T, kForward, kKTail, kSplit>), grid, dim3(kThreads), kRingLds, stream,
+                        tm.start(), tm.end(), 0, a);
   return hipGetLastError();
 }
 
-template <bool kForward>
-hipError_t launch_dense(const BigArgs& a, hipStream_t stream, const Timer& tm, int dtype) {
-  const int64_t red = kForward ? a.K : a.N;
-  if (dtype == F16::kDtype)
-    return (red % kRK) ? launch_dense_t<F16, kForward, true>(a, stream, tm)
-                       : launch_dense_t<F16, kForward, false>(a, stream, tm);
-  return (red % kRK) ? launch_dense_t<Bf16, kForward, true>(a, stream, tm)
-                     : launch_dense_t<Bf16, kForward, false>(a, stream, tm);
+// Instantiation by compute type, reduction tail and split.
+template <bool kForward, bool kDense, class T, bool kKTail>
+hipError_t launch_gemm_s(const BigArgs& a, hipStream_t stream, const Timer& tm) {
+  if (kDense)
+    return a.part != nullptr ? launch_dense_t<T, kForward, kKTail, true>(a, stream, tm)
+                             : launch_dense_t<T, kForward, kKTail, false>(a, stream, tm);
+  return a.part != nullptr ? launch_big_t<T, kForward, kKTail, true>(a, stream, tm)
+                           : launch_big_t<T, kForward, kKTail, false>(a, stream, tm);
 }
+template <bool kForward, bool kDense, class T>
+hipError_t launch_gemm_t(const BigArgs& a, hipStream_t stream, const Timer& tm) {
+  const int64_t red = kForward ? a.K : a.N;
+  return (red % (kDense ? kRK : kBK)) ? launch_gemm_s<kForward, kDense, T, true>(a, stream, tm)
+                                      : launch_gemm_s<kForward, kDense, T, false>(a, stream, tm);
+}
+template <bool kForward, bool kDense>
+hipError_t launch_gemm(const BigArgs& a, hipStream_t stream, const Timer& tm, int dtype) {
+  return dtype == F16::kDtype ? launch_gemm_t<kForward, kDense, F16>(a, stream, tm)
+                              : launch_gemm_t<kForward, kDense, Bf16>(a, stream, tm);
+}
+
+// out = the 16-bit rounding of sum_z part[z] (z in order, fp32), 8 elements
+// per thread and step; count % 8 == 0.
+template <class T>
+__global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part, int64_t splits, int64_t count,
+                                                        uint16_t* __restrict__ out) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256 * 8;
+  for (int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8; i < count; i += stride) {
+    f32x4 lo = *reinterpret_cast<const f32x4*>(part + i);
+    f32x4 hi = *reinterpret_cast<const f32x4*>(part + i + 4);
+#pragma unroll 4
+    for (int64_t z = 1; z < splits; ++z) {
+      const float* p = part + z * count + i;
+      lo += *reinterpret_cast<const f32x4*>(p);
+      hi += *reinterpret_cast<const f32x4*>(p + 4);
+    }
+    *reinterpret_cast<uint4*>(out + i) =
+        make_uint4(T::pack2(lo[0], lo[1]), T::pack2(lo[2], lo[3]), T::pack2(hi[0], hi[1]), T::pack2(hi[2], hi[3]));
+  }
+}
+
+// Attach the split plan of an M x cols output over a reduction of red to a
+// (part_ws null: no split).
+void attach_split(BigArgs& a, int64_t cols, int64_t red, void* part_ws) {
+  const SplitPlan sp = plan_split(a.M, cols, red);
+  if (part_ws == nullptr || sp.splits < 2) return;
+  a.part = static_cast<float*>(part_ws);
+  a.k_per = sp.k_per;
+}
+
+// After a split GEMM: the fixed-order sum into the 16-bit output.
+hipError_t split_sum(const BigArgs& a, int64_t cols, hipStream_t stream, int dtype) {
+  if (a.part == nullptr) return hipGetLastError();
+  const int64_t red = cols == a.N ? a.K : a.N;
+  const int64_t splits = (red + a.k_per - 1) / a.k_per, count = a.M * cols;
+  int64_t blocks = (count / 8 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  Timer tm(QK_REDUCE, stream);
+  if (dtype == F16::kDtype)
+    hipLaunchKernelGGL(split_sum_kernel<F16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a.part,
+                       splits, count, a.out);
+  else
+    hipLaunchKernelGGL(split_sum_kernel<Bf16>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, a.part,
+                       splits, count, a.out);
+  tm.stop();
+  return hipGetLastError();
+}
+
+#ifndef QN_SPLIT_TARGET
+#define QN_SPLIT_TARGET 256
+#endif
+#ifndef QN_SPLIT_MIN_STAGES
+#define QN_SPLIT_MIN_STAGES 4
+#endif
+#ifndef QN_SPLIT_BUDGET_MB
+#define QN_SPLIT_BUDGET_MB 32
+#endif
 
 }  // namespace
 
+// One 256 x 256 tile per workgroup and one workgroup per CU: with fewer
+// tiles than about 256 the reduction is split so that splits x tiles stays
+// within 256 workgroups, each split at least QN_SPLIT_MIN_STAGES 64-element
+// stages long, and the fp32 partials (written once, read once) within
+// QN_SPLIT_BUDGET_MB: past that their traffic costs more than the idle CUs.
+SplitPlan plan_split(int64_t M, int64_t cols, int64_t red) {
+  const int64_t tiles = ((M + kBM - 1) / kBM) * ((cols + kBN - 1) / kBN);
+  int64_t s = QN_SPLIT_TARGET / tiles;
+  const int64_t max_s = red / (kBK * QN_SPLIT_MIN_STAGES);
+  const int64_t budget_s = (static_cast<int64_t>(QN_SPLIT_BUDGET_MB) << 20) / (M * cols * 4);
+  if (s > max_s) s = max_s;
+  if (s > budget_s) s = budget_s;
+  if (s < 2) return SplitPlan{1, red, 0};
+  const int64_t per = ((red + s - 1) / s + kBK - 1) / kBK * kBK;
+  const int64_t splits = (red + per - 1) / per;
+  if (splits < 2) return SplitPlan{1, red, 0};
+  return SplitPlan{splits, per, (splits * M * cols * 4 + 255) / 256 * 256};
+}
+
 hipError_t launch_fwd_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const uint16_t* WhatT,
-                            const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype) {
+                            const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype,
+                            void* split_ws) {
   BigArgs a{X, K, NF4View{}, Z, cBt, Y, M, K, N, r, WhatT};
-  const Timer t(QK_FWD_GEMM, stream, true);
-  return launch_dense<true>(a, stream, t, dtype);
+  attach_split(a, N, K, split_ws);
+  hipError_t e;
+  {
+    const Timer t(QK_FWD_GEMM, stream, true);
+    if ((e = launch_gemm<true, true>(a, stream, t, dtype)) != hipSuccess) return e;
+  }
+  return split_sum(a, N, stream, dtype);
 }
 
 hipError_t launch_fwd_dense_grouped(int64_t M, int64_t K, int64_t Ntot, int64_t r, const uint16_t* X,
@@ -694,28 +828,46 @@ hipError_t launch_fwd_dense_grouped(int64_t M, int64_t K, int64_t Ntot, int64_t 
   a.ngroups = g - 1;
   for (int i = 0; i + 1 < g; ++i) a.gend[i] = gend[i];
   const Timer t(QK_FWD_GEMM, stream, true);
-  return launch_dense<true>(a, stream, t, dtype);
+  return launch_gemm<true, true>(a, stream, t, dtype);
 }
 
 hipError_t launch_dx_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* What,
-                           const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream, int dtype) {
+                           const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream, int dtype,
+                           void* split_ws) {
   BigArgs a{G, N, NF4View{}, dZ, A, dX, M, K, N, r, What};
-  const Timer t(QK_BWD_DX, stream, true);
-  return launch_dense<false>(a, stream, t, dtype);
+  attach_split(a, K, N, split_ws);
+  hipError_t e;
+  {
+    const Timer t(QK_BWD_DX, stream, true);
+    if ((e = launch_gemm<false, true>(a, stream, t, dtype)) != hipSuccess) return e;
+  }
+  return split_sum(a, K, stream, dtype);
 }
 
 hipError_t launch_fwd_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W,
-                          const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype) {
+                          const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype,
+                          void* split_ws) {
   BigArgs a{X, K, W, Z, cBt, Y, M, K, N, r, nullptr};
-  const Timer t(QK_FWD_GEMM, stream, true);
-  return launch_big<true>(a, stream, t, dtype);
+  attach_split(a, N, K, split_ws);
+  hipError_t e;
+  {
+    const Timer t(QK_FWD_GEMM, stream, true);
+    if ((e = launch_gemm<true, false>(a, stream, t, dtype)) != hipSuccess) return e;
+  }
+  return split_sum(a, N, stream, dtype);
 }
 
 hipError_t launch_dx_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, NF4View W,
-                         const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream, int dtype) {
+                         const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream, int dtype,
+                         void* split_ws) {
   BigArgs a{G, N, W, dZ, A, dX, M, K, N, r, nullptr};
-  const Timer t(QK_BWD_DX, stream, true);
-  return launch_big<false>(a, stream, t, dtype);
+  attach_split(a, K, N, split_ws);
+  hipError_t e;
+  {
+    const Timer t(QK_BWD_DX, stream, true);
+    if ((e = launch_gemm<false, false>(a, stream, t, dtype)) != hipSuccess) return e;
+  }
+  return split_sum(a, K, stream, dtype);
 }
 
 }  // namespace qn

@@ -134,15 +134,28 @@ hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
                       const uint16_t* B, float c, uint16_t* dX, float* dA, float* dB, void* ws,
                       hipStream_t stream, int dtype = 0);
 
+// Split-K plan of the 256 x 256-tile GEMMs for an M x cols output reduced
+// over red: splits (1: none), elements per split, fp32 partial bytes.
+struct SplitPlan {
+  int64_t splits, k_per, part_bytes;
+};
+SplitPlan plan_split(int64_t M, int64_t cols, int64_t red);
+
+// The GEMMs below split their reduction per plan_split when split_ws (at
+// least part_bytes, 16-byte aligned) is given, then sum the partials in
+// split order into the 16-bit output (a second launch).
 // cBt: RNE_bf16(c B)ᵀ, N x r
 hipError_t launch_fwd_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W,
-                          const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype = 0);
+                          const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype = 0,
+                          void* split_ws = nullptr);
 
 hipError_t launch_dx_big(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, NF4View W,
-                         const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream, int dtype = 0);
+                         const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream, int dtype = 0,
+                         void* split_ws = nullptr);
 
 hipError_t launch_fwd_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const uint16_t* WhatT,
-                            const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype = 0);
+                            const uint16_t* Z, const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype = 0,
+                            void* split_ws = nullptr);
 // Forward over g members' concatenated columns (Ntot in all, member i ending
 // at column gend[i], every member a multiple of 256 columns): Zcat is M x g r,
 // member i's Z in columns i r .. +r; WhatT and cBt are the members' Ŵᵀ and
@@ -151,7 +164,8 @@ hipError_t launch_fwd_dense_grouped(int64_t M, int64_t K, int64_t Ntot, int64_t 
                                     const uint16_t* WhatT, const uint16_t* Zcat, int g, const int64_t* gend,
                                     const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype = 0);
 hipError_t launch_dx_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* What,
-                           const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream, int dtype = 0);
+                           const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream, int dtype = 0,
+                           void* split_ws = nullptr);
 
 // Dequantize a K x N weight to the 16-bit compute type (dtype), either as
 // stored (K x N) or transposed (N x K).

@@ -8,6 +8,8 @@
 //                      M >= 512: Ŵᵀ dequantized to bf16, dense GEMM.
 //   backward: dZ = c G Bᵀ; dA = Xᵀ dZ; dB = c Zᵀ G; dX = G Ŵᵀ + dZ Aᵀ
 //             (M >= 512: Ŵ dequantized to bf16 first, dense GEMM).
+// Either GEMM splits its reduction when its output has too few 256 x 256
+// tiles to occupy the device (plan_split), with a fixed-order sum after.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -31,12 +33,13 @@ int64_t cbt_bytes(int64_t M, int64_t N, int64_t r) { return M > 16 ? align256(N 
 int64_t fwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r) {
   const SkinnyPlan p = plan_skinny(M, K, N, r);
   if (M <= 16) return p.gv_part + p.gv_zpart;
-  return p.at_bytes + p.z_part + cbt_bytes(M, N, r) + dense_bytes(M, K, N);
+  return p.at_bytes + p.z_part + cbt_bytes(M, N, r) + dense_bytes(M, K, N) + plan_split(M, N, K).part_bytes;
 }
 
 int64_t bwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r) {
   const SkinnyPlan p = plan_skinny(M, K, N, r);
-  return p.dz_part + align256(M * r * 2) + p.da_part + p.db_part + dense_bytes(M, K, N);
+  return p.dz_part + align256(M * r * 2) + p.da_part + p.db_part + dense_bytes(M, K, N) +
+         plan_split(M, K, N).part_bytes;
 }
 
 hipError_t launch_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W, const uint16_t* A,
@@ -48,14 +51,15 @@ hipError_t launch_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
   hipError_t e;
   if (M <= 16) return launch_gemv(M, K, N, r, X, W, A, B, c, Y, Z, p, base, stream, dtype);
   uint16_t* cbt = reinterpret_cast<uint16_t*>(after_z);
+  uint16_t* wt = reinterpret_cast<uint16_t*>(after_z + cbt_bytes(M, N, r));
+  void* split_ws = reinterpret_cast<char*>(wt) + dense_bytes(M, K, N);
   if ((e = launch_lora_down(M, K, r, X, A, Z, p, base, base + p.at_bytes, stream, N, B, c, cbt, 0, dtype)) != hipSuccess)
     return e;
   if (use_dense(M)) {
-    uint16_t* wt = reinterpret_cast<uint16_t*>(after_z + cbt_bytes(M, N, r));
     if ((e = launch_dequant_bf16(W, K, N, true, wt, stream, 0, dtype)) != hipSuccess) return e;
-    return launch_fwd_dense(M, K, N, r, X, wt, Z, cbt, Y, stream, dtype);
+    return launch_fwd_dense(M, K, N, r, X, wt, Z, cbt, Y, stream, dtype, split_ws);
   }
-  return launch_fwd_big(M, K, N, r, X, W, Z, cbt, Y, stream, dtype);
+  return launch_fwd_big(M, K, N, r, X, W, Z, cbt, Y, stream, dtype, split_ws);
 }
 
 hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* X,
@@ -71,13 +75,14 @@ hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
   if ((e = launch_dz(M, N, r, G, B, c, dz16, p, dz_part, stream, dtype)) != hipSuccess) return e;
   if ((e = launch_colsums(M, K, N, r, X, G, Z, dz16, c, dA, dB, p, da_part, db_part, stream, dtype)) != hipSuccess) return e;
   if (dX == nullptr) return hipGetLastError();
+  uint16_t* wd = reinterpret_cast<uint16_t*>(static_cast<char*>(db_part) + p.db_part);
+  void* split_ws = reinterpret_cast<char*>(wd) + dense_bytes(M, K, N);
   if (use_dense(M)) {
-    uint16_t* wd = reinterpret_cast<uint16_t*>(static_cast<char*>(db_part) + p.db_part);
     if ((e = launch_dequant_bf16(W, K, N, false, wd, stream, 0, dtype)) != hipSuccess)
       return e;
-    return launch_dx_dense(M, K, N, r, G, wd, dz16, A, dX, stream, dtype);
+    return launch_dx_dense(M, K, N, r, G, wd, dz16, A, dX, stream, dtype, split_ws);
   }
-  return launch_dx_big(M, K, N, r, G, W, dz16, A, dX, stream, dtype);
+  return launch_dx_big(M, K, N, r, G, W, dz16, A, dX, stream, dtype, split_ws);
 }
 
 // ------------------------------------------------------------ grouped linears

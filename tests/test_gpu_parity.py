@@ -212,6 +212,9 @@ LAYER_SHAPES = [
     (1024, 512, 768, 64, 0.25),  # dequantize-then-GEMM path, two row tiles x three column tiles
     (520, 64, 128, 8, 1.0),      # dense path with fewer reduction stages than LDS ring slots
     (512, 4104, 192, 16, 0.5),   # dense path, long reduction with a ragged last stage
+    # reductions split across workgroups (too few output tiles for the device):
+    (130, 2088, 320, 24, 0.25),  # fused forward in 7 splits, the last one ragged; dX unsplit
+    (200, 1032, 1600, 16, 0.5),  # fused forward in 4 splits (ragged last), fused dX in 5
 ]
 
 
@@ -261,7 +264,8 @@ def _integer_case(M, K, N, r, seed):
     return dict(W=W, X=X, A=A, B=B, G=G, Xb=bits(X), Ab=bits(A), Bb=bits(B), Gb=bits(G), c=0.5)
 
 
-@pytest.mark.parametrize("M,K,N,r", [(16, 256, 256, 8), (96, 320, 384, 16), (520, 256, 320, 16)])
+@pytest.mark.parametrize("M,K,N,r", [(16, 256, 256, 8), (96, 320, 384, 16), (520, 256, 320, 16),
+                                     (96, 1024, 384, 16), (300, 640, 1280, 16), (700, 1024, 512, 16)])
 def test_layer_exact_integer_case_bit_exact(M, K, N, r):
     say(f"exact-integer layer M={M} K={K} N={N} r={r}")
     case = _integer_case(M, K, N, r, seed=M + N)

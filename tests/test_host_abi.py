@@ -64,6 +64,18 @@ def test_layer_workspace_sizes_are_positive():
         assert f >= 0 and b > 0 and f % 256 == 0 and b % 256 == 0
 
 
+def test_mid_size_workspace_holds_split_partials():
+    # too few 256 x 256 output tiles to occupy the device: the GEMMs split
+    # their reduction and the workspace holds at least two fp32 partial
+    # copies of the output (Y for the forward, dX for the backward)
+    M, K, N, r = 256, 4096, 4096, 64
+    f, b = qn.qlora_workspace_bytes(M, K, N, r)
+    assert f >= 2 * M * N * 4 and b >= 2 * M * K * 4
+    # a full device of tiles: no partials (the forward needs far less)
+    f_big, _ = qn.qlora_workspace_bytes(4096, K, N, r)
+    assert f_big < 4096 * N * 4
+
+
 def test_entry_points_reject_bad_arguments_before_launch():
     L = qn.lib()
     st = qn._State(64, 0x1000, 0x2000, 0x3000, 0x4000)
