@@ -31,10 +31,13 @@
 // chunks are masked, so tails add exact zeros.
 //
 // qlora_dense_kernel (M >= 512) reads a weight dequantized beforehand to bf16
-// (bit-identical to the fused decode) and streams both operands through a
-// five-slot LDS ring (see Dense below).
+// (bit-identical to the fused decode) and streams both operands through two
+// LDS slots of 64-element stages, whole cache lines per copy (see Dense).
 //
-// Every global load is a raw buffer load, so masked lanes need no branches.
+// Every global load is a raw buffer load, so masked lanes need no branches:
+// a lane whose row, column or reduction index lies outside its operand
+// (tails, and the prefetches that run past the last stage) gets a per-lane
+// offset past the buffer's size, whatever the scalar stage offset added.
 // The MFMA is issued as D = Ŵ-fragment x activation-fragment, so each lane
 // holds 4 consecutive output columns of one output row.
 #include <hip/hip_ext.h>
@@ -210,7 +213,7 @@ struct Big {
     const uint32_t soff = static_cast<uint32_t>(k0 * 2);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t v = (!kKTail || k0 < act_lim[j]) ? act_voff[j] : kMasked;
+      const uint32_t v = k0 < act_lim[j] ? act_voff[j] : kMasked;
       char* dst = sA(b) + (wave * 64 + 8 * j) * 128;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r_act, (lds_ptr_t)(dst), 16, v, soff, 0, 0);
     }
@@ -222,19 +225,23 @@ struct Big {
     if (kForward) {
       const uint32_t soff = static_cast<uint32_t>((k0 * a.N) >> 1);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) R.w[i] = ld32s(r_codes, w_voff[i], soff);
-      R.q = static_cast<int>(static_cast<int8_t>(
-          __builtin_amdgcn_raw_buffer_load_b8(r_q, q_voff, static_cast<uint32_t>((k0 * a.N) >> 6), 0)));
+      for (int i = 0; i < 8; ++i) {
+        const bool ok = kKTail ? k0 + 8 * (t >> 5) + i < a.K : k0 < a.K;
+        R.w[i] = ld32s(r_codes, ok ? w_voff[i] : kMasked, soff);
+      }
+      R.q = static_cast<int>(static_cast<int8_t>(__builtin_amdgcn_raw_buffer_load_b8(
+          r_q, k0 + tab_row < a.K ? q_voff : kMasked, static_cast<uint32_t>((k0 * a.N) >> 6), 0)));
       const int64_t e = tab_e0 + k0 * a.N;
       R.s2 = ld_f32(r_s2, tab_ok ? static_cast<uint32_t>((e >> s_shift) * 4) : kMasked);
     } else {
       const uint32_t soff = static_cast<uint32_t>(k0 >> 1);
-      const uint4 lo = ld128s(r_codes, w_voff[0], soff);
-      const uint4 hi = ld128s(r_codes, w_voff[0], soff + 16);
+      const uint32_t wv = k0 < a.N ? w_voff[0] : kMasked;
+      const uint4 lo = ld128s(r_codes, wv, soff);
+      const uint4 hi = ld128s(r_codes, wv, soff + 16);
       R.w[0] = lo.x; R.w[1] = lo.y; R.w[2] = lo.z; R.w[3] = lo.w;
       R.w[4] = hi.x; R.w[5] = hi.y; R.w[6] = hi.z; R.w[7] = hi.w;
       R.q = static_cast<int>(static_cast<int8_t>(
-          __builtin_amdgcn_raw_buffer_load_b8(r_q, q_voff, static_cast<uint32_t>(k0 >> 6), 0)));
+          __builtin_amdgcn_raw_buffer_load_b8(r_q, k0 < a.N ? q_voff : kMasked, static_cast<uint32_t>(k0 >> 6), 0)));
       const int64_t e = tab_e0 + k0;
       R.s2 = ld_f32(r_s2, tab_ok ? static_cast<uint32_t>((e >> s_shift) * 4) : kMasked);
     }
@@ -328,20 +335,20 @@ struct Big {
   }
 };
 
-// Dense core: both operands are bf16 matrices with the reduction contiguous
-// (activations M x red and the dequantized weight, rows x red).  The
-// reduction advances 32 elements per stage through a ring of kSlots LDS
-// slots (slot = 256 activation rows + 256 weight rows, 64 bytes each, the
-// four 16-byte chunks of row R at chunk ^ ((R >> 1) & 3)).  Copies are
-// buffer loads straight into LDS, issued three to four stages ahead and
-// spread one per four MFMAs, so the memory pipeline never backs up into the
-// MFMA issue stream; one barrier per stage.
-constexpr int kRK = 32;
-constexpr int kRTile = 256 * 64;                 // one operand of one slot
-constexpr int kSlots = 5;
-constexpr int kRingLds = kSlots * 2 * kRTile;    // 160 KB
-
-__device__ __forceinline__ int roff(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
+// Dense core: both operands are 16-bit matrices with the reduction
+// contiguous (activations M x red and the dequantized weight, rows x red).
+// 64-element stages alternate between two LDS slots; a slot holds 256
+// activation rows and 256 weight rows of 128 bytes in the fused kernel's
+// layout (chunk c of row R at c ^ ((R ^ R >> 3) & 7)).  Copies are buffer
+// loads straight into LDS, each instruction 8 rows x 128 bytes, i.e. whole
+// cache lines: issuing the same bytes as 16 half-line rows per instruction
+// cost about 10% more time.  Stage s+2's 16 copies per wave go out in the
+// last substep of stage s and the first of stage s+1, one per two MFMAs (in
+// bursts they fill the TA command FIFO and stall the MFMA stream); the one
+// barrier per stage sits before the last substep, whose fragments are
+// already in registers.
+constexpr int kDenseSlot = 2 * kTileBytes;
+constexpr int kDenseLds = 2 * kDenseSlot;   // 128 KB
 
 template <class T, bool kForward, bool kKTail>
 struct Dense {
@@ -350,9 +357,9 @@ struct Dense {
   int t, lane, wave;
   int64_t m0, c0, red;
   Rsrc r_act, r_w;
-  uint32_t act_voff[4], w_voff[4];   // copy j: row wave*64 + 16j + lane/4, chunk (lane&3)^((lane>>3)&3)
-  int lim[4];
-  int foffA[2][4], foffW[2][4];      // fragment offsets within a slot, per substep
+  uint32_t act_voff[8], w_voff[8];   // copy j: row wave*64 + 8j + lane/8, chunk (lane&7)^(lane>>3)^j
+  int lim[8];                        // reduction tail: copy j's chunk valid while k0 < lim[j]
+  int fA[4], fW[4];                  // fragment offsets within a slot at substep 0
 
   __device__ Dense(const BigArgs& args, char* s) : a(args), smem(s) {
     t = threadIdx.x;
@@ -363,10 +370,11 @@ struct Dense {
     const int64_t wrows = kForward ? a.N : a.K;
     r_act = make_rsrc(a.act, a.M * red * 2);
     r_w = make_rsrc(a.wdense, wrows * red * 2);
-    const int chunk = (lane & 3) ^ ((lane >> 3) & 3);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = wave * 64 + 16 * j + (lane >> 2);
+    for (int j = 0; j < 8; ++j) {
+      // row = wave*64 + 8j + lane/8, whose swizzle is (lane/8) ^ j
+      const int chunk = (lane & 7) ^ (lane >> 3) ^ j;
+      const int row = wave * 64 + 8 * j + (lane >> 3);
       const int64_t m = m0 + row, n = c0 + row;
       act_voff[j] = m < a.M ? static_cast<uint32_t>((m * red + 8 * chunk) * 2) : kMasked;
       w_voff[j] = n < wrows ? static_cast<uint32_t>((n * red + 8 * chunk) * 2) : kMasked;
@@ -374,91 +382,80 @@ struct Dense {
     }
     const int r32 = lane & 31, h = lane >> 5, wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        foffA[ks][i] = roff(wm * 128 + 32 * i + r32, 2 * ks + h);
-        foffW[ks][i] = kRTile + roff(wn * 128 + 32 * i + r32, 2 * ks + h);
-      }
+    for (int i = 0; i < 4; ++i) {
+      fA[i] = lds_off(wm * 128 + 32 * i + r32, h);
+      fW[i] = kTileBytes + lds_off(wn * 128 + 32 * i + r32, h);
+    }
   }
 
-  // 64-wide layout used by the LoRA extension after the main loop
+  // slot 0 in the fused kernel's names, for the LoRA extension after the loop
   __device__ char* sA(int) const { return smem; }
   __device__ char* sB(int) const { return smem + kTileBytes; }
-  __device__ char* slot(int b) const { return smem + b * 2 * kRTile; }
 
-  // Copy instruction g (0..3) of half `half` of stage s into slot b: the
-  // activation (even g) or weight (odd g) rows wave*64 + 16j .. +15,
-  // j = 2*half + g/2, 64 bytes each.  Past the reduction end it reads zeros.
-  __device__ void copy_one(int64_t s, int b, int half, int g) const {
-    const int64_t k0 = s * kRK;
+  // Copy q (0..15) of stage s into slot b: the activation (even q) or weight
+  // (odd q) rows wave*64 + 8(q/2) .. +7.  Past the reduction end: masked.
+  __device__ void copy_one(int64_t s, int b, int q) const {
+    const int64_t k0 = s * kBK;
     const uint32_t soff = static_cast<uint32_t>(k0 * 2);
-    const int j = 2 * half + (g >> 1);
-    const bool ok = !kKTail || k0 < lim[j];
-    char* dst = slot(b) + (wave * 64 + 16 * j) * 64;
-    if ((g & 1) == 0)
+    const int j = q >> 1;
+    const bool ok = kKTail ? k0 < lim[j] : k0 < red;
+    char* dst = smem + b * kDenseSlot + (q & 1) * kTileBytes + (wave * 64 + 8 * j) * 128;
+    if ((q & 1) == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r_act, (lds_ptr_t)(dst), 16, ok ? act_voff[j] : kMasked, soff, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr_t)(dst + kRTile), 16, ok ? w_voff[j] : kMasked, soff, 0,
-                                               0);
-  }
-  __device__ void copy_stage(int64_t s, int b) const {
-#pragma unroll
-    for (int g = 0; g < 8; ++g) copy_one(s, b, g >> 2, g & 3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr_t)(dst), 16, ok ? w_voff[j] : kMasked, soff, 0, 0);
   }
 
   struct Frags {
     typename T::v8 a[4], w[4];
   };
+  // Fragment q (activation q/2 for even q, weight q/2 for odd q) of
+  // substep ks of slot b: chunk 2ks + h of its row, i.e. the substep-0
+  // offset with bits 5-6 flipped by ks.
+  __device__ void read_one(int b, int ks, int q, Frags& F) const {
+    const char* base = smem + b * kDenseSlot;
+    if ((q & 1) == 0)
+      F.a[q >> 1] = *reinterpret_cast<const typename T::v8*>(base + (fA[q >> 1] ^ (ks << 5)));
+    else
+      F.w[q >> 1] = *reinterpret_cast<const typename T::v8*>(base + (fW[q >> 1] ^ (ks << 5)));
+  }
   __device__ void load_frags(int b, int ks, Frags& F) const {
-    const char* base = slot(b);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) F.a[i] = *reinterpret_cast<const typename T::v8*>(base + foffA[ks][i]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) F.w[j] = *reinterpret_cast<const typename T::v8*>(base + foffW[ks][j]);
+    for (int q = 0; q < 8; ++q) read_one(b, ks, q, F);
   }
 
-  // 16 MFMAs from Fc; in their shadow, the 8 fragment reads of substep ksn
-  // of slot bn into Fn (all within the first 8 MFMAs, so the last 8 cover
-  // their latency) and the 4 copies of half ch of stage cs into slot cb.
-  // The order is pinned with scheduling barriers.
-  __device__ void half_step(const Frags& Fc, Frags& Fn, int bn, int ksn, int64_t cs, int cb, int ch,
-                            f32x16 (&acc)[4][4]) const {
-    const char* base = slot(bn);
+  // 16 MFMAs from Fc; in their shadow the 8 reads of substep ksn of slot bn
+  // into Fn (within the first 8 MFMAs, so the last 8 cover their latency)
+  // and, when nc > 0, copies q0 .. q0+nc-1 of stage cs into slot cb, one
+  // per 16/nc MFMAs.  The order is pinned with scheduling barriers.
+  __device__ void sub_step(const Frags& Fc, Frags& Fn, int bn, int ksn, int64_t cs, int cb, int q0, int nc,
+                           f32x16 (&acc)[4][4]) const {
+    const int sp = 16 / (nc > 0 ? nc : 1);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
+        const int m = 4 * g + u;
         acc[g][u] = T::mfma32(Fc.w[u], Fc.a[g], acc[g][u]);
         __builtin_amdgcn_sched_barrier(0);
-        if (g < 2) {
-          const int q = 4 * g + u;
-          if ((q & 1) == 0)
-            Fn.a[q >> 1] = *reinterpret_cast<const typename T::v8*>(base + foffA[ksn][q >> 1]);
-          else
-            Fn.w[q >> 1] = *reinterpret_cast<const typename T::v8*>(base + foffW[ksn][q >> 1]);
+        if (m < 8) {
+          read_one(bn, ksn, m, Fn);
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (u == 1) {
-          copy_one(cs, cb, ch, g);
+        if (nc > 0 && m % sp == (sp > 1 ? 1 : 0)) {
+          copy_one(cs, cb, q0 + m / sp);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
   }
 
-  // One 64-element reduction step from the 64-wide layout at sA(0)/sB(0).
+  // One 64-element reduction step from slot 0 (the LoRA extension).
   __device__ void compute(int, f32x16 (&acc)[4][4]) const {
-    const int r32 = lane & 31, h = lane >> 5, wm = wave >> 1, wn = wave & 1;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       Frags F;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        F.a[i] = *reinterpret_cast<const typename T::v8*>(sA(0) + lds_off(wm * 128 + 32 * i + r32, 2 * ks + h));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        F.w[j] = *reinterpret_cast<const typename T::v8*>(sB(0) + lds_off(wn * 128 + 32 * j + r32, 2 * ks + h));
+      load_frags(0, ks, F);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -635,7 +632,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   extern __shared__ __attribute__((aligned(16))) char smem[];
   Dense<T, kForward, kKTail> k(a, smem);
   int64_t s_beg, s_end;
-  stage_range<kSplit>(a, k.red, kRK, s_beg, s_end);
+  stage_range<kSplit>(a, k.red, kBK, s_beg, s_end);
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -643,31 +640,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  // Barrier B(x) (in the middle of stage x-1) says: every wave has finished
-  // reading slot (x-1) % S and stage x has landed.  Stage x's 8 copies are
-  // issued in two halves between B(x-S+1) and B(x-S+2), into slot x % S,
-  // which B(x-S+1) released.  Each wave then has (S-2) later stages (8
-  // copies each) outstanding when it waits for stage x.  Copies of stages
-  // past the end read zeros or land in slots that are never read.  (Stages
-  // and slots count from the first stage of this workgroup's range.)
-  constexpr int S = kSlots;
-  for (int x = 0; x < S - 1; ++x) k.copy_stage(s_beg + x, x);
+  // Stage s (counted from the first of this workgroup's range) lives in
+  // slot s & 1.  The barrier of stage s, before its last substep, says:
+  // every wave has read all of slot s & 1 (its last substep's fragments are
+  // in registers) and stage s+1 has landed in the other slot.  Stage s+2's
+  // copies into slot s & 1 follow it.  Copies past the end are masked or
+  // land in a slot that is never read.
 #pragma unroll
-  for (int g = 0; g < 4; ++g) k.copy_one(s_beg + S - 1, S - 1, 0, g);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(8 * (S - 2) + 4, 15));
+  for (int q = 0; q < 16; ++q) k.copy_one(s_beg, 0, q);
+  __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
   typename Dense<T, kForward, kKTail>::Frags F0, F1;
   k.load_frags(0, 0, F0);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) k.copy_one(s_beg + 1, 1, q);
   int b = 0;
   for (int64_t s = s_beg; s < s_end; ++s) {
-    const int bp = b == 0 ? S - 1 : b - 1;   // slot of stage s + S - 1
-    const int bn = b == S - 1 ? 0 : b + 1;   // slot of stage s + 1
-    k.half_step(F0, F1, b, 1, s + S - 1, bp, 1, acc);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(8 * (S - 2), 0));
+    k.sub_step(F0, F1, b, 1, s + 1, b ^ 1, 8, 8, acc);
+    k.sub_step(F1, F0, b, 2, 0, 0, 0, 0, acc);
+    k.sub_step(F0, F1, b, 3, 0, 0, 0, 0, acc);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    k.half_step(F1, F0, bn, 0, s + S, b, 0, acc);
-    b = bn;
+    k.sub_step(F1, F0, b ^ 1, 0, s + 2, b, 0, 8, acc);
+    b ^= 1;
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -696,14 +692,14 @@ hipError_t launch_dense_t(const BigArgs& a, hipStream_t stream, const Timer& tm)
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_dense_kernel<T, kForward, kKTail, kSplit>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kRingLds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kDenseLds);
     if (e != hipSuccess) return e;
     configured = true;
   }
   const int64_t cols = kForward ? a.N : a.K, red = kForward ? a.K : a.N;
   const unsigned zs = kSplit ? static_cast<unsigned>((red + a.k_per - 1) / a.k_per) : 1u;
   dim3 grid(static_cast<unsigned>((cols + kBN - 1) / kBN), static_cast<unsigned>((a.M + kBM - 1) / kBM), zs);
-  hipExtLaunchKernelGGL((qlora_dense_kernel<T, kForward, kKTail, kSplit>), grid, dim3(kThreads), kRingLds, stream,
+  hipExtLaunchKernelGGL((qlora_dense_kernel<T, kForward, kKTail, kSplit>), grid, dim3(kThreads), kDenseLds, stream,
                         tm.start(), tm.end(), 0, a);
   return hipGetLastError();
 }
@@ -720,8 +716,8 @@ hipError_t launch_gemm_s(const BigArgs& a, hipStream_t stream, const Timer& tm) 
 template <bool kForward, bool kDense, class T>
 hipError_t launch_gemm_t(const BigArgs& a, hipStream_t stream, const Timer& tm) {
   const int64_t red = kForward ? a.K : a.N;
-  return (red % (kDense ? kRK : kBK)) ? launch_gemm_s<kForward, kDense, T, true>(a, stream, tm)
-                                      : launch_gemm_s<kForward, kDense, T, false>(a, stream, tm);
+  return (red % kBK) ? launch_gemm_s<kForward, kDense, T, true>(a, stream, tm)
+                     : launch_gemm_s<kForward, kDense, T, false>(a, stream, tm);
 }
 template <bool kForward, bool kDense>
 hipError_t launch_gemm(const BigArgs& a, hipStream_t stream, const Timer& tm, int dtype) {
