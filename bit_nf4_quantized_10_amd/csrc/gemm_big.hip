@@ -360,6 +360,10 @@ struct Dense {
   uint32_t act_voff[8], w_voff[8];   // copy j: row wave*64 + 8j + lane/8, chunk (lane&7)^(lane>>3)^j
   int lim[8];                        // reduction tail: copy j's chunk valid while k0 < lim[j]
   int fA[4], fW[4];                  // fragment offsets within a slot at substep 0
+  // Stages: n_main of the product (from s_beg), then the LoRA extension's
+  // ceil(r_ext / 64) over (Z, (c B)ᵀ) or (dZ, A), copied like the others.
+  int64_t s_beg, n_main, r_ext, lda, cols;
+  Rsrc r_ea, r_eb;
 
   __device__ Dense(const BigArgs& args, char* s) : a(args), smem(s) {
     t = threadIdx.x;
@@ -386,24 +390,55 @@ struct Dense {
       fA[i] = lds_off(wm * 128 + 32 * i + r32, h);
       fW[i] = kTileBytes + lds_off(wn * 128 + 32 * i + r32, h);
     }
+    cols = wrows;
+    lda = a.ext_a_ld ? a.ext_a_ld : a.r;
+    int64_t zoff = 0;   // grouped forward: this tile's member's block of Z columns
+    if (kForward)
+      for (int i = 0; i < a.ngroups; ++i) zoff += c0 >= a.gend[i] ? a.r : 0;
+    r_ea = make_rsrc(a.ext_a + zoff, (a.M * lda - zoff) * 2);
+    r_eb = make_rsrc(a.ext_b, cols * a.r * 2);
+  }
+  // this workgroup's stages (with_ext: it also adds the LoRA extension)
+  __device__ int64_t set_stages(int64_t beg, int64_t end, bool with_ext) {
+    s_beg = beg;
+    n_main = end - beg;
+    r_ext = with_ext ? a.r : 0;
+    return n_main + (r_ext + kBK - 1) / kBK;
   }
 
   // slot 0 in the fused kernel's names, for the LoRA extension after the loop
   __device__ char* sA(int) const { return smem; }
   __device__ char* sB(int) const { return smem + kTileBytes; }
 
-  // Copy q (0..15) of stage s into slot b: the activation (even q) or weight
-  // (odd q) rows wave*64 + 8(q/2) .. +7.  Past the reduction end: masked.
-  __device__ void copy_one(int64_t s, int b, int q) const {
-    const int64_t k0 = s * kBK;
-    const uint32_t soff = static_cast<uint32_t>(k0 * 2);
+  // Copy q (0..15) of stage u (counted from s_beg) into slot b: the
+  // activation (even q) or weight (odd q) rows wave*64 + 8(q/2) .. +7.
+  // Past the reduction end and the extension: masked.  kMix: u may be an
+  // extension stage (else u < n_main, known to the caller).
+  template <bool kMix>
+  __device__ void copy_one(int64_t u, int b, int q) const {
     const int j = q >> 1;
-    const bool ok = kKTail ? k0 < lim[j] : k0 < red;
     char* dst = smem + b * kDenseSlot + (q & 1) * kTileBytes + (wave * 64 + 8 * j) * 128;
-    if ((q & 1) == 0)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_act, (lds_ptr_t)(dst), 16, ok ? act_voff[j] : kMasked, soff, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr_t)(dst), 16, ok ? w_voff[j] : kMasked, soff, 0, 0);
+    if (!kMix || u < n_main) {
+      const int64_t k0 = (s_beg + u) * kBK;
+      const uint32_t soff = static_cast<uint32_t>(k0 * 2);
+      const bool ok = kKTail ? k0 < lim[j] : k0 < red;
+      if ((q & 1) == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_act, (lds_ptr_t)(dst), 16, ok ? act_voff[j] : kMasked, soff, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, (lds_ptr_t)(dst), 16, ok ? w_voff[j] : kMasked, soff, 0, 0);
+    } else {
+      const int row = wave * 64 + 8 * j + (lane >> 3);
+      const int64_t e = (u - n_main) * kBK + 8 * ((lane & 7) ^ (lane >> 3) ^ j);
+      if ((q & 1) == 0) {
+        const int64_t m = m0 + row;
+        const uint32_t v = (m < a.M && e < r_ext) ? static_cast<uint32_t>((m * lda + e) * 2) : kMasked;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_ea, (lds_ptr_t)(dst), 16, v, 0, 0, 0);
+      } else {
+        const int64_t n = c0 + row;
+        const uint32_t v = (n < cols && e < r_ext) ? static_cast<uint32_t>((n * a.r + e) * 2) : kMasked;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r_eb, (lds_ptr_t)(dst), 16, v, 0, 0, 0);
+      }
+    }
   }
 
   struct Frags {
@@ -428,6 +463,7 @@ struct Dense {
   // into Fn (within the first 8 MFMAs, so the last 8 cover their latency)
   // and, when nc > 0, copies q0 .. q0+nc-1 of stage cs into slot cb, one
   // per 16/nc MFMAs.  The order is pinned with scheduling barriers.
+  template <bool kMix>
   __device__ void sub_step(const Frags& Fc, Frags& Fn, int bn, int ksn, int64_t cs, int cb, int q0, int nc,
                            f32x16 (&acc)[4][4]) const {
     const int sp = 16 / (nc > 0 ? nc : 1);
@@ -443,25 +479,28 @@ struct Dense {
           __builtin_amdgcn_sched_barrier(0);
         }
         if (nc > 0 && m % sp == (sp > 1 ? 1 : 0)) {
-          copy_one(cs, cb, q0 + m / sp);
+          copy_one<kMix>(cs, cb, q0 + m / sp);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
   }
 
-  // One 64-element reduction step from slot 0 (the LoRA extension).
-  __device__ void compute(int, f32x16 (&acc)[4][4]) const {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      Frags F;
-      load_frags(0, ks, F);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = T::mfma32(F.w[j], F.a[i], acc[i][j]);
-    }
+  // Stage u from slot b, with the next stages' fragment reads and copies
+  // in its shadow (see qlora_dense_kernel).
+  template <bool kMix>
+  __device__ void stage(int64_t u, int b, Frags& F0, Frags& F1, f32x16 (&acc)[4][4]) const {
+    sub_step<kMix>(F0, F1, b, 1, u + 1, b ^ 1, 8, 8, acc);
+    sub_step<kMix>(F1, F0, b, 2, 0, 0, 0, 0, acc);
+    sub_step<kMix>(F0, F1, b, 3, 0, 0, 0, 0, acc);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    sub_step<kMix>(F1, F0, b ^ 1, 0, u + 2, b, 0, 8, acc);
   }
+
+  // finish() is called without the extension (it ran as the last stages).
+  __device__ void compute(int, f32x16 (&)[4][4]) const {}
 };
 
 // LoRA extension: r more reduction steps over (Z, (c B)ᵀ) in the forward or
@@ -471,7 +510,7 @@ struct Dense {
 // row, 16-byte chunk q of row R at q ^ (R & 31)) so that every global store
 // writes whole 512-byte row segments.  Shared by the fused and dense kernels;
 // the main loop has released LDS when this starts.
-template <class T, bool kForward, bool kSplit, class Core>
+template <class T, bool kForward, bool kSplit, bool kExt, class Core>
 __device__ __forceinline__ void finish(const Core& k, const BigArgs& a, f32x16 (&acc)[4][4]) {
   const int lane = k.lane, t = k.t;
   const int64_t cols = kForward ? a.N : a.K;
@@ -481,7 +520,7 @@ __device__ __forceinline__ void finish(const Core& k, const BigArgs& a, f32x16 (
     for (int i = 0; i < a.ngroups; ++i) zoff += k.c0 >= a.gend[i] ? a.r : 0;
   const Rsrc re = make_rsrc(a.ext_a + zoff, (a.M * lda - zoff) * 2);
   const Rsrc rb = make_rsrc(a.ext_b, cols * a.r * 2);
-  const int64_t r_ext = (!kSplit || blockIdx.z == 0) ? a.r : 0;
+  const int64_t r_ext = kExt && (!kSplit || blockIdx.z == 0) ? a.r : 0;
   for (int64_t j0 = 0; j0 < r_ext; j0 += kBK) {
     const int c = t & 7;
     const int64_t j = j0 + 8 * c;
@@ -624,7 +663,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     cur = nxt;
   }
 
-  finish<T, kForward, kSplit>(k, a, acc);
+  finish<T, kForward, kSplit, true>(k, a, acc);
 }
 
 template <class T, bool kForward, bool kKTail, bool kSplit>
@@ -640,34 +679,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  // Stage s (counted from the first of this workgroup's range) lives in
-  // slot s & 1.  The barrier of stage s, before its last substep, says:
-  // every wave has read all of slot s & 1 (its last substep's fragments are
-  // in registers) and stage s+1 has landed in the other slot.  Stage s+2's
-  // copies into slot s & 1 follow it.  Copies past the end are masked or
-  // land in a slot that is never read.
+  // Stage u (counted from the first of this workgroup's range; the LoRA
+  // extension's stages follow the product's) lives in slot u & 1.  The
+  // barrier of stage u, before its last substep, says: every wave has read
+  // all of slot u & 1 (its last substep's fragments are in registers) and
+  // stage u+1 has landed in the other slot.  Stage u+2's copies into slot
+  // u & 1 follow it.  Copies past the end are masked or land in a slot that
+  // is never read.
+  const int64_t total = k.set_stages(s_beg, s_end, !kSplit || blockIdx.z == 0);
 #pragma unroll
-  for (int q = 0; q < 16; ++q) k.copy_one(s_beg, 0, q);
+  for (int q = 0; q < 16; ++q) k.template copy_one<true>(0, 0, q);
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_s_barrier();
   typename Dense<T, kForward, kKTail>::Frags F0, F1;
   k.load_frags(0, 0, F0);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) k.copy_one(s_beg + 1, 1, q);
+  for (int q = 0; q < 8; ++q) k.template copy_one<true>(1, 1, q);
   int b = 0;
-  for (int64_t s = s_beg; s < s_end; ++s) {
-    k.sub_step(F0, F1, b, 1, s + 1, b ^ 1, 8, 8, acc);
-    k.sub_step(F1, F0, b, 2, 0, 0, 0, 0, acc);
-    k.sub_step(F0, F1, b, 3, 0, 0, 0, 0, acc);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    k.sub_step(F1, F0, b ^ 1, 0, s + 2, b, 0, 8, acc);
-    b ^= 1;
-  }
+  int64_t u = 0;
+  // stages whose copies (of u+1 and u+2) are all of the product, then the rest
+  for (; u + 2 < k.n_main; ++u, b ^= 1) k.template stage<false>(u, b, F0, F1, acc);
+  for (; u < total; ++u, b ^= 1) k.template stage<true>(u, b, F0, F1, acc);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  finish<T, kForward, kSplit>(k, a, acc);
+  finish<T, kForward, kSplit, false>(k, a, acc);
 }
 
 template <class T, bool kForward, bool kKTail, bool kSplit>
