@@ -342,10 +342,11 @@ def bench_components(torch, qn, si, dev, sets, outs, qws, status):
                                  "how": "fwd + bwd of q, k, v (3 x 4096 x 4096, r = 64, M = 4096): one grouped "
                                         "call each way vs three single-linear calls each way, cache flushed"}
     del gws, sws, Yg, Zg, dXg, dAg, dBg, Ag, Bg, Gg
-    # mid-size batches (17 <= M < 512: the weight is decoded inside the GEMM,
-    # whose reduction is split across workgroups when its output has too few
-    # tiles for the device; fwd_gemm_ms is the GEMM launch alone, without the
-    # fixed-order sum of its partials)
+    # mid-size batches: M = 64 and 128 decode the weight inside the GEMM, 256
+    # and 384 dequantize it first; both GEMMs split their reduction across
+    # workgroups when the output has too few tiles for the device
+    # (fwd_gemm_ms is the GEMM launch alone, without the fixed-order sum of
+    # its partials)
     mid = {}
     for Mm in (64, 128, 256, 384):
         Xm, Gm = sets[0]["X"][:Mm].contiguous(), sets[0]["G"][:Mm].contiguous()

@@ -8,7 +8,7 @@
 // term is r more reduction steps over (Z, (c B)ᵀ) or (dZ, A) after the main
 // loop; the bf16 tile is then stored through LDS as whole rows.
 //
-// qlora_big_kernel (17 <= M < 512) decodes the packed weight inside its
+// qlora_big_kernel (17 <= M < 192) decodes the packed weight inside its
 // reduction loop.  Per 64-element stage the workgroup
 //   - copies the activation tile of stage s+1 from global memory straight into
 //     LDS (buffer loads with the LDS destination, no registers involved);
@@ -30,7 +30,7 @@
 // Rows at or past K get an all-zero table and the matching activation
 // chunks are masked, so tails add exact zeros.
 //
-// qlora_dense_kernel (M >= 512) reads a weight dequantized beforehand to bf16
+// qlora_dense_kernel (M >= 192) reads a weight dequantized beforehand to bf16
 // (bit-identical to the fused decode) and streams both operands through two
 // LDS slots of 64-element stages, whole cache lines per copy (see Dense).
 //
@@ -853,13 +853,18 @@ hipError_t launch_fwd_dense(int64_t M, int64_t K, int64_t N, int64_t r, const ui
 
 hipError_t launch_fwd_dense_grouped(int64_t M, int64_t K, int64_t Ntot, int64_t r, const uint16_t* X,
                                     const uint16_t* WhatT, const uint16_t* Zcat, int g, const int64_t* gend,
-                                    const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype) {
+                                    const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype, void* split_ws) {
   BigArgs a{X, K, NF4View{}, Zcat, cBt, Y, M, K, Ntot, r, WhatT};
   a.ext_a_ld = g * r;
   a.ngroups = g - 1;
   for (int i = 0; i + 1 < g; ++i) a.gend[i] = gend[i];
-  const Timer t(QK_FWD_GEMM, stream, true);
-  return launch_gemm<true, true>(a, stream, t, dtype);
+  attach_split(a, Ntot, K, split_ws);
+  hipError_t e;
+  {
+    const Timer t(QK_FWD_GEMM, stream, true);
+    if ((e = launch_gemm<true, true>(a, stream, t, dtype)) != hipSuccess) return e;
+  }
+  return split_sum(a, Ntot, stream, dtype);
 }
 
 hipError_t launch_dx_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* What,

@@ -162,7 +162,8 @@ hipError_t launch_fwd_dense(int64_t M, int64_t K, int64_t N, int64_t r, const ui
 // (c B)ᵀ stacked row-wise (Ntot x K and Ntot x r).
 hipError_t launch_fwd_dense_grouped(int64_t M, int64_t K, int64_t Ntot, int64_t r, const uint16_t* X,
                                     const uint16_t* WhatT, const uint16_t* Zcat, int g, const int64_t* gend,
-                                    const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype = 0);
+                                    const uint16_t* cBt, uint16_t* Y, hipStream_t stream, int dtype = 0,
+                                    void* split_ws = nullptr);
 hipError_t launch_dx_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* G, const uint16_t* What,
                            const uint16_t* dZ, const uint16_t* A, uint16_t* dX, hipStream_t stream, int dtype = 0,
                            void* split_ws = nullptr);

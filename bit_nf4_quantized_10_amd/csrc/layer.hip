@@ -4,10 +4,10 @@
 //                      launch), then their sums and c Z B;
 //             else   : Aᵀ and (c B)ᵀ in bf16 (one launch); Z = X A (split
 //                      rows/K, fixed-order reduce); then
-//                      M < 512: fused dequant-GEMM with the LoRA extension;
-//                      M >= 512: Ŵᵀ dequantized to bf16, dense GEMM.
+//                      M < 192: fused dequant-GEMM with the LoRA extension;
+//                      M >= 192: Ŵᵀ dequantized to bf16, dense GEMM.
 //   backward: dZ = c G Bᵀ; dA = Xᵀ dZ; dB = c Zᵀ G; dX = G Ŵᵀ + dZ Aᵀ
-//             (M >= 512: Ŵ dequantized to bf16 first, dense GEMM).
+//             (M >= 192: Ŵ dequantized to bf16 first, dense GEMM).
 // Either GEMM splits its reduction when its output has too few 256 x 256
 // tiles to occupy the device (plan_split), with a fixed-order sum after.
 #include "common.hpp"
@@ -21,8 +21,13 @@ int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 // From this many tokens on, the weight is dequantized once to bf16 and the
 // product runs as a dense bf16 GEMM; below, the fused kernel decodes the
 // packed codes inside its k-loop (each weight tile is then decoded by fewer
-// row-tiles, so the one-off decode pass does not pay for itself).
-constexpr int64_t kDenseMinM = 512;
+// row-tiles, so the one-off decode pass does not pay for itself).  Both
+// give bit-identical outputs; with split reductions, the measured layer
+// step (4096 x 4096, r = 64) crosses over between M = 176 and 192.
+#ifndef QN_DENSE_MIN_M
+#define QN_DENSE_MIN_M 192
+#endif
+constexpr int64_t kDenseMinM = QN_DENSE_MIN_M;
 bool use_dense(int64_t M) { return M >= kDenseMinM; }
 int64_t dense_bytes(int64_t M, int64_t K, int64_t N) { return use_dense(M) ? align256(K * N * 2) : 0; }
 }  // namespace
@@ -95,14 +100,16 @@ int64_t grouped_fwd_workspace_bytes(int64_t M, int64_t K, int g, const int64_t* 
   const GroupPlan gp = plan_grouped(M, K, g, Ns, r);
   int64_t Ntot = 0;
   for (int i = 0; i < g; ++i) Ntot += Ns[i];
-  return gp.zp.at_bytes + gp.zp.z_part + align256(Ntot * r * 2) + align256(Ntot * K * 2);
+  return gp.zp.at_bytes + gp.zp.z_part + align256(Ntot * r * 2) + align256(Ntot * K * 2) +
+         plan_split(M, Ntot, K).part_bytes;
 }
 
 int64_t grouped_bwd_workspace_bytes(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r) {
   const GroupPlan gp = plan_grouped(M, K, g, Ns, r);
   int64_t Ntot = 0;
   for (int i = 0; i < g; ++i) Ntot += Ns[i];
-  return gp.dz_part + align256(M * g * r * 2) + gp.da_part + gp.db_part_total + align256(K * Ntot * 2);
+  return gp.dz_part + align256(M * g * r * 2) + gp.da_part + gp.db_part_total + align256(K * Ntot * 2) +
+         plan_split(M, K, Ntot).part_bytes;
 }
 
 hipError_t launch_grouped_fwd(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r, const uint16_t* X,
@@ -124,7 +131,8 @@ hipError_t launch_grouped_fwd(int64_t M, int64_t K, int g, const int64_t* Ns, in
     off += Ns[i];
     gend[i] = off;
   }
-  return launch_fwd_dense_grouped(M, K, Ntot, r, X, wt, Z, g, gend, cbt, Y, stream);
+  return launch_fwd_dense_grouped(M, K, Ntot, r, X, wt, Z, g, gend, cbt, Y, stream, kDtypeBf16,
+                                  reinterpret_cast<char*>(wt) + align256(Ntot * K * 2));
 }
 
 hipError_t launch_grouped_bwd(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r, const uint16_t* G,
@@ -150,7 +158,8 @@ hipError_t launch_grouped_bwd(int64_t M, int64_t K, int g, const int64_t* Ns, in
     if ((e = launch_dequant_bf16(W[i], K, Ns[i], false, wd + off, stream, Ntot)) != hipSuccess) return e;
     off += Ns[i];
   }
-  return launch_dx_dense(M, K, Ntot, g * r, G, wd, dz16, A, dX, stream);
+  return launch_dx_dense(M, K, Ntot, g * r, G, wd, dz16, A, dX, stream, kDtypeBf16,
+                         reinterpret_cast<char*>(wd) + align256(K * Ntot * 2));
 }
 
 }  // namespace qn

@@ -126,7 +126,7 @@ int qlora_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r,
  * below 2^29 elements (every bf16 operand under 1 GiB, so that 32-bit
  * buffer offsets suffice), all pointers 16-byte aligned, workspace >= fwd_bytes.  The
  * state is only read.  M <= 16 runs the memory-bound dequant-GEMV kernels;
- * M >= 512 dequantizes Ŵ to bf16 in the workspace and runs a dense GEMM. */
+ * M >= 192 dequantizes Ŵ to bf16 in the workspace and runs a dense GEMM. */
 int qlora_linear_fwd(int64_t M, int64_t K, int64_t N, int64_t r,
                      const uint16_t* X, const nf4_state_t* W,
                      const uint16_t* A, const uint16_t* B, float c,
@@ -240,7 +240,7 @@ int nf4_status_read(const int32_t* status, int32_t* host_value, void* stream);
 #define QK_BWD_DZ       7   /* dZ = c G Bᵀ partials                     */
 #define QK_BWD_DX       8   /* dX = G Ŵᵀ + dZ Aᵀ                        */
 #define QK_BWD_COLSUM   9   /* dA = Xᵀ dZ and dB = c Zᵀ G partials      */
-#define QK_DEQUANT_BF16 10  /* Ŵ (or Ŵᵀ) to bf16 for the M >= 512 GEMMs */
+#define QK_DEQUANT_BF16 10  /* Ŵ (or Ŵᵀ) to bf16 for the M >= 192 GEMMs */
 #define QK_REDUCE       11  /* fixed-order split reductions             */
 #define QK_MERGE        12  /* adapter merge W' = fl32(ŵ + cAB)          */
 #define QK_SGD          13  /* adapter SGD step                          */

@@ -67,7 +67,7 @@ def _run(case, K, N):
 
 @pytest.mark.parametrize("M,K,N,r,c", [(16, 256, 256, 8, 2.0), (1, 512, 192, 16, 0.5), (130, 264, 320, 24, 0.25),
                                        (600, 264, 320, 24, 0.5), (1024, 512, 768, 64, 0.25),
-                                       (200, 1032, 1600, 16, 0.5)])
+                                       (150, 1032, 1600, 16, 0.5), (200, 1032, 1600, 16, 0.5)])
 def test_f16_layer_matches_oracle(M, K, N, r, c):
     say(f"fp16 layer M={M} K={K} N={N} r={r}")
     case = _f16_case(M, K, N, r, c, seed=M + 5 * N)

@@ -71,7 +71,8 @@ def _run(case, K, Ns, need_dx=True):
 
 
 @pytest.mark.parametrize("M,K,Ns,r,c", [(600, 264, [256, 512, 256], 16, 0.5), (16, 256, [256, 256], 8, 2.0),
-                                         (1000, 512, [512, 256, 768], 24, 0.25)])
+                                         (1000, 512, [512, 256, 768], 24, 0.25),
+                                         (64, 1032, [256, 512], 16, 0.5)])   # both GEMMs split, ragged K
 def test_grouped_matches_oracle(M, K, Ns, r, c):
     say(f"grouped M={M} K={K} Ns={Ns} r={r}")
     case = _group_case(M, K, Ns, r, c, seed=M + K + len(Ns))

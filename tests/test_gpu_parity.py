@@ -208,13 +208,14 @@ LAYER_SHAPES = [
     (17, 256, 256, 8, 2.0),      # large-M path, ragged M
     (130, 264, 320, 24, 0.25),   # ragged M, K % 32 != 0, N % 128 != 0, r % 32 != 0
     (256, 512, 512, 64, 0.25),
-    (600, 264, 320, 24, 0.5),    # dequantize-then-GEMM path (M >= 512), ragged everywhere
+    (600, 264, 320, 24, 0.5),    # dequantize-then-GEMM path (M >= 192), ragged everywhere
     (1024, 512, 768, 64, 0.25),  # dequantize-then-GEMM path, two row tiles x three column tiles
     (520, 64, 128, 8, 1.0),      # dense path with fewer reduction stages than LDS ring slots
     (512, 4104, 192, 16, 0.5),   # dense path, long reduction with a ragged last stage
     # reductions split across workgroups (too few output tiles for the device):
     (130, 2088, 320, 24, 0.25),  # fused forward in 7 splits, the last one ragged; dX unsplit
-    (200, 1032, 1600, 16, 0.5),  # fused forward in 4 splits (ragged last), fused dX in 5
+    (150, 1032, 1600, 16, 0.5),  # fused forward in 4 splits (ragged last), fused dX in 6
+    (200, 1032, 1600, 16, 0.5),  # the same through the dense kernel (4 and 6 splits)
 ]
 
 
@@ -265,7 +266,8 @@ def _integer_case(M, K, N, r, seed):
 
 
 @pytest.mark.parametrize("M,K,N,r", [(16, 256, 256, 8), (96, 320, 384, 16), (520, 256, 320, 16),
-                                     (96, 1024, 384, 16), (300, 640, 1280, 16), (700, 1024, 512, 16)])
+                                     (96, 1024, 384, 16), (120, 512, 1280, 16), (300, 640, 1280, 16),
+                                     (700, 1024, 512, 16)])
 def test_layer_exact_integer_case_bit_exact(M, K, N, r):
     say(f"exact-integer layer M={M} K={K} N={N} r={r}")
     case = _integer_case(M, K, N, r, seed=M + N)

@@ -83,7 +83,7 @@ def _run(case, M, K, N, r):
 
 
 @pytest.mark.parametrize("M,K,N,r,c", [(16, 256, 256, 8, 2.0), (1, 512, 192, 16, 0.5), (130, 264, 320, 24, 0.25),
-                                       (600, 264, 320, 24, 0.5)])
+                                       (150, 1032, 1600, 16, 0.5), (600, 264, 320, 24, 0.5)])
 def test_single_level_layer_matches_oracle(M, K, N, r, c):
     say(f"single-level layer M={M} K={K} N={N} r={r}")
     case = _layer_case(M, K, N, r, c, seed=M * 3 + N)
