@@ -590,7 +590,10 @@ __device__ __forceinline__ void finish(const Core& k, const BigArgs& a, f32x16 (
       const int R = k.wave * 64 + 2 * u + (lane >> 5);
       const int64_t m = k.m0 + R;
       const uint4 v = *reinterpret_cast<const uint4*>(st + R * 512 + ((q ^ (R & 31)) << 4));
-      if (m < a.M && n < cols) *reinterpret_cast<uint4*>(a.out + m * cols + n) = v;
+      // non-temporal: the output streams out during the epilogue instead of
+      // waiting, dirty in L2, for the end-of-kernel release (1-2 us per launch)
+      if (m < a.M && n < cols)
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(a.out + m * cols + n));
     }
   }
 }
