@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "side_jobs.hpp"
+
 namespace qn {
 
 // Optional per-kernel event timer (see qlora_timer_enable).  Construct right
@@ -91,12 +93,16 @@ struct SkinnyPlan {
 void plan_gemv(int64_t M, int64_t K, int64_t N, int64_t r, SkinnyPlan* p);
 SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N, int64_t r);
 
-// Z = X A; with cbt != nullptr the same launch also writes cbt = RNE_bf16(c B)ᵀ
-// (N x r), the forward's LoRA extension operand.
+// The transposes Z = X A needs (Aᵀ into At) and, with cbt != nullptr, the
+// forward's LoRA extension operand cbt = RNE_16(c B)ᵀ (N x r).
+void lora_transposes(int64_t K, int64_t r, const uint16_t* A, uint16_t* At, int64_t N, const uint16_t* B, float c,
+                     uint16_t* cbt, int64_t rb, int dtype, TJob out[2]);
+// Z = X A: the transposes above (one launch, unless pre_transposed: another
+// launch already ran them), then the split partials and their sum.
 hipError_t launch_lora_down(int64_t M, int64_t K, int64_t r, const uint16_t* X, const uint16_t* A, uint16_t* Z,
                             const SkinnyPlan& p, void* at_ws, void* part_ws, hipStream_t stream, int64_t N = 0,
                             const uint16_t* B = nullptr, float c = 1.0f, uint16_t* cbt = nullptr, int64_t rb = 0,
-                            int dtype = 0);
+                            int dtype = 0, bool pre_transposed = false);
 
 // Split plans of a group of g linears sharing X (column counts Ns[i], rank r
 // each); zp covers Z = X A over all g r columns.
@@ -119,8 +125,10 @@ hipError_t launch_colsums_grouped(int64_t M, int64_t K, int g, const int64_t* Ns
 hipError_t launch_gemv(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W, const uint16_t* A,
                        const uint16_t* B, float c, uint16_t* Y, uint16_t* Z, const SkinnyPlan& p, void* part_ws,
                        hipStream_t stream, int dtype = 0);
+// dZ = c G Bᵀ: split partials, then their sum (with defer != nullptr that sum
+// is not launched but returned, for the caller to run in a later launch).
 hipError_t launch_dz(int64_t M, int64_t N, int64_t r, const uint16_t* G, const uint16_t* B, float c, uint16_t* dZ,
-                     const SkinnyPlan& p, void* part_ws, hipStream_t stream, int dtype = 0);
+                     const SkinnyPlan& p, void* part_ws, hipStream_t stream, int dtype = 0, RdJob* defer = nullptr);
 hipError_t launch_colsums(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const uint16_t* G,
                           const uint16_t* Z, const uint16_t* dZ, float c, float* dA, float* dB, const SkinnyPlan& p,
                           void* da_ws, void* db_ws, hipStream_t stream, int dtype = 0);
@@ -171,7 +179,11 @@ hipError_t launch_dx_dense(int64_t M, int64_t K, int64_t N, int64_t r, const uin
 // Dequantize a K x N weight to the 16-bit compute type (dtype), either as
 // stored (K x N) or transposed (N x K).
 // out_ld: row stride of the untransposed output (0: N).
+// Side jobs run as extra workgroups of the same launch: side_t (two
+// transposes, transposed output only), side_r (one split sum, untransposed
+// output only).
 hipError_t launch_dequant_bf16(NF4View W, int64_t K, int64_t N, bool transposed, uint16_t* out, hipStream_t stream,
-                               int64_t out_ld = 0, int dtype = 0);
+                               int64_t out_ld = 0, int dtype = 0, const TJob* side_t = nullptr,
+                               const RdJob* side_r = nullptr);
 
 }  // namespace qn

@@ -2,12 +2,14 @@
 // sequence of the forward and backward passes.
 //   forward : M <= 16: dequant-GEMV and Z = X A split-K partials (one
 //                      launch), then their sums and c Z B;
-//             else   : Aᵀ and (c B)ᵀ in bf16 (one launch); Z = X A (split
-//                      rows/K, fixed-order reduce); then
-//                      M < 192: fused dequant-GEMM with the LoRA extension;
-//                      M >= 192: Ŵᵀ dequantized to bf16, dense GEMM.
+//             M < 192: Aᵀ and (c B)ᵀ in bf16 (one launch); Z = X A (split
+//                      rows/K, fixed-order reduce); fused dequant-GEMM with
+//                      the LoRA extension;
+//             else   : Ŵᵀ dequantized to bf16 with Aᵀ and (c B)ᵀ in the same
+//                      launch; Z = X A; dense GEMM.
 //   backward: dZ = c G Bᵀ; dA = Xᵀ dZ; dB = c Zᵀ G; dX = G Ŵᵀ + dZ Aᵀ
-//             (M >= 192: Ŵ dequantized to bf16 first, dense GEMM).
+//             (M >= 192: Ŵ dequantized to bf16, with dZ's split sum in the
+//             same launch, before dA and dB; then a dense GEMM).
 // Either GEMM splits its reduction when its output has too few 256 x 256
 // tiles to occupy the device (plan_split), with a fixed-order sum after.
 #include "common.hpp"
@@ -58,12 +60,19 @@ hipError_t launch_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
   uint16_t* cbt = reinterpret_cast<uint16_t*>(after_z);
   uint16_t* wt = reinterpret_cast<uint16_t*>(after_z + cbt_bytes(M, N, r));
   void* split_ws = reinterpret_cast<char*>(wt) + dense_bytes(M, K, N);
-  if ((e = launch_lora_down(M, K, r, X, A, Z, p, base, base + p.at_bytes, stream, N, B, c, cbt, 0, dtype)) != hipSuccess)
-    return e;
+  uint16_t* at = reinterpret_cast<uint16_t*>(base);
   if (use_dense(M)) {
-    if ((e = launch_dequant_bf16(W, K, N, true, wt, stream, 0, dtype)) != hipSuccess) return e;
+    // Aᵀ and (c B)ᵀ ride along in the launch that dequantizes Ŵᵀ
+    TJob tj[2];
+    lora_transposes(K, r, A, at, N, B, c, cbt, 0, dtype, tj);
+    if ((e = launch_dequant_bf16(W, K, N, true, wt, stream, 0, dtype, tj)) != hipSuccess) return e;
+    if ((e = launch_lora_down(M, K, r, X, A, Z, p, base, base + p.at_bytes, stream, N, B, c, cbt, 0, dtype, true)) !=
+        hipSuccess)
+      return e;
     return launch_fwd_dense(M, K, N, r, X, wt, Z, cbt, Y, stream, dtype, split_ws);
   }
+  if ((e = launch_lora_down(M, K, r, X, A, Z, p, base, base + p.at_bytes, stream, N, B, c, cbt, 0, dtype)) != hipSuccess)
+    return e;
   return launch_fwd_big(M, K, N, r, X, W, Z, cbt, Y, stream, dtype, split_ws);
 }
 
@@ -76,17 +85,21 @@ hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
   uint16_t* dz16 = reinterpret_cast<uint16_t*>(base + p.dz_part);
   void* da_part = base + p.dz_part + align256(M * r * 2);
   void* db_part = static_cast<char*>(da_part) + p.da_part;
-  hipError_t e;
-  if ((e = launch_dz(M, N, r, G, B, c, dz16, p, dz_part, stream, dtype)) != hipSuccess) return e;
-  if ((e = launch_colsums(M, K, N, r, X, G, Z, dz16, c, dA, dB, p, da_part, db_part, stream, dtype)) != hipSuccess) return e;
-  if (dX == nullptr) return hipGetLastError();
   uint16_t* wd = reinterpret_cast<uint16_t*>(static_cast<char*>(db_part) + p.db_part);
   void* split_ws = reinterpret_cast<char*>(wd) + dense_bytes(M, K, N);
-  if (use_dense(M)) {
-    if ((e = launch_dequant_bf16(W, K, N, false, wd, stream, 0, dtype)) != hipSuccess)
+  hipError_t e;
+  if (dX != nullptr && use_dense(M)) {
+    // the fixed-order sum of dZ rides along in the launch that dequantizes Ŵ
+    RdJob jz;
+    if ((e = launch_dz(M, N, r, G, B, c, dz16, p, dz_part, stream, dtype, &jz)) != hipSuccess) return e;
+    if ((e = launch_dequant_bf16(W, K, N, false, wd, stream, 0, dtype, nullptr, &jz)) != hipSuccess) return e;
+    if ((e = launch_colsums(M, K, N, r, X, G, Z, dz16, c, dA, dB, p, da_part, db_part, stream, dtype)) != hipSuccess)
       return e;
     return launch_dx_dense(M, K, N, r, G, wd, dz16, A, dX, stream, dtype, split_ws);
   }
+  if ((e = launch_dz(M, N, r, G, B, c, dz16, p, dz_part, stream, dtype)) != hipSuccess) return e;
+  if ((e = launch_colsums(M, K, N, r, X, G, Z, dz16, c, dA, dB, p, da_part, db_part, stream, dtype)) != hipSuccess) return e;
+  if (dX == nullptr) return hipGetLastError();
   return launch_dx_big(M, K, N, r, G, W, dz16, A, dX, stream, dtype, split_ws);
 }
 

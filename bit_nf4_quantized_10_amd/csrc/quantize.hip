@@ -24,6 +24,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "side_jobs.hpp"
 
 namespace qn {
 
@@ -418,10 +419,15 @@ __device__ __forceinline__ void dq_decode(const DqTile<U>& t, int64_t tile, int6
   }
 }
 
+// Workgroups dq_blocks and up run the side job (a split sum) instead.
 template <int U, class O, bool kSingle, bool kStrided>
 __global__ __launch_bounds__(kQuantThreads) void nf4_dequant_kernel(NF4View W, int64_t P, void* __restrict__ out,
                                                                     int32_t* __restrict__ status, uint32_t ncols,
-                                                                    int64_t out_ld) {
+                                                                    int64_t out_ld, int64_t dq_blocks, RdJob side) {
+  if (blockIdx.x >= dq_blocks) {
+    reduce_block(side, blockIdx.x - dq_blocks);
+    return;
+  }
   __shared__ float s_lut[16];
   __shared__ float s_q2[2 * kLevels2 + 2];
   const int tid = threadIdx.x;
@@ -460,12 +466,12 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_dequant_kernel(NF4View W, i
   }
   // two register tiles in turn, so no copy waits on loads still in flight
   DqTile<U> nxt;
-  for (; tile < tiles; tile += 2 * static_cast<int64_t>(gridDim.x)) {
-    dq_load<U, kSingle>(nxt, tile + gridDim.x, words, rc, rq, rs, sshift);
+  for (; tile < tiles; tile += 2 * dq_blocks) {
+    dq_load<U, kSingle>(nxt, tile + dq_blocks, words, rc, rq, rs, sshift);
     dq_decode<U, O, kSingle, kStrided>(cur, tile, words, s_lut, s_q2, off, out, ncols, out_ld);
-    if (tile + gridDim.x >= tiles) break;
-    dq_load<U, kSingle>(cur, tile + 2 * static_cast<int64_t>(gridDim.x), words, rc, rq, rs, sshift);
-    dq_decode<U, O, kSingle, kStrided>(nxt, tile + gridDim.x, words, s_lut, s_q2, off, out, ncols, out_ld);
+    if (tile + dq_blocks >= tiles) break;
+    dq_load<U, kSingle>(cur, tile + 2 * dq_blocks, words, rc, rq, rs, sshift);
+    dq_decode<U, O, kSingle, kStrided>(nxt, tile + dq_blocks, words, s_lut, s_q2, off, out, ncols, out_ld);
   }
 }
 
@@ -475,11 +481,21 @@ __global__ __launch_bounds__(kQuantThreads) void nf4_dequant_kernel(NF4View W, i
 // bf16 writes (along k) are row-contiguous.
 constexpr int kTPad = 66;  // bf16 per LDS row (64 k + 2): 132-byte rows
 
+// Tile rows blockIdx.y >= ceil(K / 64) run the side jobs (two transposes)
+// instead, one 32 x 32 tile per workgroup.
 template <class T>
 __global__ __launch_bounds__(256) void nf4_dequant_t_kernel(NF4View W, int64_t K, int64_t N,
-                                                            uint16_t* __restrict__ out) {
+                                                            uint16_t* __restrict__ out, TJob t0, TJob t1) {
   __shared__ float s_lut[16];
   __shared__ __attribute__((aligned(16))) uint16_t tile[128 * kTPad];
+  const int64_t ky = (K + 63) / 64;
+  if (blockIdx.y >= ky) {
+    const int64_t id = (static_cast<int64_t>(blockIdx.y) - ky) * gridDim.x + blockIdx.x;
+    uint16_t(*tt)[33] = reinterpret_cast<uint16_t(*)[33]>(tile);
+    if (id < t0.nblk) transpose_block(t0, id, tt);
+    else if (id - t0.nblk < t1.nblk) transpose_block(t1, id - t0.nblk, tt);
+    return;
+  }
   const int t = threadIdx.x;
   if (t < 16) s_lut[t] = kNF4[t];
   __syncthreads();
@@ -553,47 +569,61 @@ hipError_t launch_quantize(const float* W, int64_t P, uint8_t* codes, int8_t* qa
 
 template <class O>
 hipError_t dequant_launch_t(NF4View W, int64_t P, void* out, int32_t* status, hipStream_t stream, int64_t ncols,
-                            int64_t out_ld) {
+                            int64_t out_ld, const RdJob* side) {
   constexpr int U = QN_DQ_U;
   const int64_t tiles = (P / 8 + kQuantThreads * U - 1) / (kQuantThreads * U);
   const int64_t blocks = tiles < 1 ? 1 : (tiles < QN_DQ_GRID ? tiles : QN_DQ_GRID);
+  RdJob sj{};
+  if (side != nullptr) sj = *side;
   const Timer t(QK_DEQUANT, stream, true);
-  const dim3 grid(static_cast<unsigned>(blocks)), block(kQuantThreads);
+  const dim3 grid(static_cast<unsigned>(blocks + sj.nblk)), block(kQuantThreads);
   const uint32_t nc = static_cast<uint32_t>(ncols);
   if (W.absmax != nullptr) {
     if (ncols != 0)
       hipExtLaunchKernelGGL((nf4_dequant_kernel<U, O, true, true>), grid, block, 0, stream, t.start(), t.end(), 0, W,
-                            P, out, status, nc, out_ld);
+                            P, out, status, nc, out_ld, blocks, sj);
     else
       hipExtLaunchKernelGGL((nf4_dequant_kernel<U, O, true, false>), grid, block, 0, stream, t.start(), t.end(), 0, W,
-                            P, out, status, nc, out_ld);
+                            P, out, status, nc, out_ld, blocks, sj);
   } else {
     if (ncols != 0)
       hipExtLaunchKernelGGL((nf4_dequant_kernel<U, O, false, true>), grid, block, 0, stream, t.start(), t.end(), 0, W,
-                            P, out, status, nc, out_ld);
+                            P, out, status, nc, out_ld, blocks, sj);
     else
       hipExtLaunchKernelGGL((nf4_dequant_kernel<U, O, false, false>), grid, block, 0, stream, t.start(), t.end(), 0,
-                            W, P, out, status, nc, out_ld);
+                            W, P, out, status, nc, out_ld, blocks, sj);
   }
   return hipGetLastError();
 }
 
+static hipError_t dequantize_with(NF4View W, int64_t P, void* out, int out_dtype, int32_t* status, hipStream_t stream,
+                           int64_t ncols, int64_t out_ld, const RdJob* side) {
+  if (out_dtype == NF4_OUT_BF16) return dequant_launch_t<Bf16>(W, P, out, status, stream, ncols, out_ld, side);
+  if (out_dtype == NF4_OUT_F16) return dequant_launch_t<F16>(W, P, out, status, stream, ncols, out_ld, side);
+  return dequant_launch_t<float>(W, P, out, status, stream, ncols, out_ld, side);
+}
+
 hipError_t launch_dequantize(NF4View W, int64_t P, void* out, int out_dtype, int32_t* status, hipStream_t stream,
                              int64_t ncols, int64_t out_ld) {
-  if (out_dtype == NF4_OUT_BF16) return dequant_launch_t<Bf16>(W, P, out, status, stream, ncols, out_ld);
-  if (out_dtype == NF4_OUT_F16) return dequant_launch_t<F16>(W, P, out, status, stream, ncols, out_ld);
-  return dequant_launch_t<float>(W, P, out, status, stream, ncols, out_ld);
+  return dequantize_with(W, P, out, out_dtype, status, stream, ncols, out_ld, nullptr);
 }
 
 hipError_t launch_dequant_bf16(NF4View W, int64_t K, int64_t N, bool transposed, uint16_t* out, hipStream_t stream,
-                               int64_t out_ld, int dtype) {
+                               int64_t out_ld, int dtype, const TJob* side_t, const RdJob* side_r) {
   if (!transposed)
-    return launch_dequantize(W, K * N, out, dtype == kDtypeF16 ? NF4_OUT_F16 : NF4_OUT_BF16, nullptr, stream,
-                             out_ld != 0 && out_ld != N ? N : 0, out_ld);
+    return dequantize_with(W, K * N, out, dtype == kDtypeF16 ? NF4_OUT_F16 : NF4_OUT_BF16, nullptr, stream,
+                           out_ld != 0 && out_ld != N ? N : 0, out_ld, side_r);
+  TJob t0{}, t1{};
+  if (side_t != nullptr) {
+    t0 = side_t[0];
+    t1 = side_t[1];
+  }
+  const int64_t gx = (N + 127) / 128, ky = (K + 63) / 64;
+  const int64_t side_rows = (t0.nblk + t1.nblk + gx - 1) / gx;
   Timer t(QK_DEQUANT_BF16, stream);
-  dim3 grid(static_cast<unsigned>((N + 127) / 128), static_cast<unsigned>((K + 63) / 64));
+  dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(ky + side_rows));
   hipLaunchKernelGGL(dtype == kDtypeF16 ? nf4_dequant_t_kernel<F16> : nf4_dequant_t_kernel<Bf16>, grid, dim3(256), 0,
-                     stream, W, K, N, out);
+                     stream, W, K, N, out, t0, t1);
   t.stop();
   return hipGetLastError();
 }

@@ -18,6 +18,7 @@
 // Every reduction is in a fixed order, so results are run-to-run identical.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "side_jobs.hpp"
 
 namespace qn {
 
@@ -26,59 +27,20 @@ namespace {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
-__device__ __forceinline__ uint16_t bf16_of(float x) {
-  return static_cast<uint16_t>(pack_bf16x2(x, 0.0f) & 0xffffu);
-}
-
-// RNE to the layer's 16-bit type (f16: fp16, else bf16) and back to fp32.
-__device__ __forceinline__ uint16_t half_of(float x, int f16) {
-  return static_cast<uint16_t>((f16 ? F16::pack2(x, 0.0f) : Bf16::pack2(x, 0.0f)) & 0xffffu);
-}
-__device__ __forceinline__ float widen_of(uint32_t bits16, int f16) {
-  return f16 ? F16::widen(bits16) : Bf16::widen(bits16);
-}
-
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
 // ------------------------------------------------------------ transpose
-// dst[c][r] = RNE_bf16(scale * src[r][c]) for a rows x cols bf16 matrix
-// (32 x 32 LDS tiles; scale 1 copies the bits).  One launch serves two such
-// jobs: Aᵀ for the rank-r products and, in the forward, the LoRA extension
-// operand (c B)ᵀ, rounded once to bf16.
-struct TJob {
-  const uint16_t* src;
-  uint16_t* dst;
-  int64_t rows, cols;
-  float scale;
-  int64_t bx, nblk;   // 32-column tiles per tile row, tiles in this job
-  int f16;            // elements are fp16 (else bf16)
-};
-
+// Two TJobs per launch (side_jobs.hpp): Aᵀ and, in the forward, (c B)ᵀ.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(TJob j0, TJob j1) {
   __shared__ uint16_t tile[32][33];
   const bool second = blockIdx.x >= j0.nblk;
-  const TJob j = second ? j1 : j0;
-  const int64_t b = second ? blockIdx.x - j0.nblk : blockIdx.x;
-  const int64_t r0 = (b / j.bx) * 32, c0 = (b % j.bx) * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  for (int i = ty; i < 32; i += 8) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    uint16_t v = (r < j.rows && c < j.cols) ? j.src[r * j.cols + c] : 0;
-    if (j.scale != 1.0f) v = half_of(j.scale * widen_of(v, j.f16), j.f16);
-    tile[i][tx] = v;
-  }
-  __syncthreads();
-  for (int i = ty; i < 32; i += 8) {
-    const int64_t c = c0 + i, r = r0 + tx;
-    if (c < j.cols && r < j.rows) j.dst[c * j.rows + r] = tile[tx][i];
-  }
+  transpose_block(second ? j1 : j0, second ? blockIdx.x - j0.nblk : blockIdx.x, tile);
 }
 
 TJob tjob(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols, float scale, int dtype = kDtypeBf16) {
-  const int64_t bx = cdiv(cols, 32);
-  return TJob{src, dst, rows, cols, scale, bx, bx * cdiv(rows, 32), dtype == kDtypeF16 ? 1 : 0};
+  return make_tjob(src, dst, rows, cols, scale, dtype == kDtypeF16 ? 1 : 0);
 }
 
 // ------------------------------------------------------------ row sums
@@ -343,41 +305,10 @@ __global__ __launch_bounds__(256) void colsum_kernel(CsJob j0, CsJob j1, int64_t
   }
 }
 
-// out = scale * sum_s part[s] in split order, optionally transposed from
-// [rows][cols] to [cols][rows]; fp32 and/or bf16 outputs.  Two jobs per launch.
-struct RdJob {
-  const float* part;
-  int64_t splits, rows, cols;
-  float scale;
-  int transpose;
-  float* out_f32;
-  uint16_t* out_bf16;
-  int64_t nblk;
-  int64_t out_ld;   // row stride of the output (cols, or rows when transposed, for a dense result)
-  int f16;          // the 16-bit output is fp16 (else bf16)
-};
-
+// Two RdJobs per launch (side_jobs.hpp).
 __global__ __launch_bounds__(256) void reduce_kernel(RdJob j0, RdJob j1) {
   const bool second = blockIdx.x >= j0.nblk;
-  const RdJob& J = second ? j1 : j0;
-  const int64_t blk = second ? blockIdx.x - j0.nblk : blockIdx.x;
-  const int64_t count = J.rows * J.cols;
-  for (int64_t i = blk * 256 + threadIdx.x; i < count; i += J.nblk * 256) {
-    float s = 0.0f;
-    int64_t k = 0;
-    for (; k + 8 <= J.splits; k += 8) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = J.part[(k + u) * count + i];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) s += v[u];
-    }
-    for (; k < J.splits; ++k) s += J.part[k * count + i];
-    s *= J.scale;
-    const int64_t o = J.transpose ? (i % J.cols) * J.out_ld + i / J.cols : (i / J.cols) * J.out_ld + i % J.cols;
-    if (J.out_f32) J.out_f32[o] = s;
-    if (J.out_bf16) J.out_bf16[o] = half_of(s, J.f16);
-  }
+  reduce_block(second ? j1 : j0, second ? blockIdx.x - j0.nblk : blockIdx.x);
 }
 
 void split_plan(int64_t tiles, int64_t red, int64_t target, int64_t quantum, int64_t* splits, int64_t* per) {
@@ -390,10 +321,7 @@ void split_plan(int64_t tiles, int64_t red, int64_t target, int64_t quantum, int
 
 RdJob rdjob(const float* part, int64_t splits, int64_t rows, int64_t cols, float scale, bool transpose, float* out_f32,
             uint16_t* out_bf16, int dtype = kDtypeBf16) {
-  int64_t blocks = cdiv(rows * cols, 256);
-  if (blocks > 2048) blocks = 2048;
-  return RdJob{part, splits, rows, cols, scale, transpose ? 1 : 0, out_f32, out_bf16, blocks, transpose ? rows : cols,
-               dtype == kDtypeF16 ? 1 : 0};
+  return make_rdjob(part, splits, rows, cols, scale, transpose, out_f32, out_bf16, dtype == kDtypeF16 ? 1 : 0);
 }
 
 hipError_t launch_reduce(const RdJob& ja, const RdJob* jb, hipStream_t stream) {
@@ -474,15 +402,23 @@ SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N, int64_t r) {
   return p;
 }
 
+void lora_transposes(int64_t K, int64_t r, const uint16_t* A, uint16_t* At, int64_t N, const uint16_t* B, float c,
+                     uint16_t* cbt, int64_t rb, int dtype, TJob out[2]) {
+  out[0] = tjob(A, At, K, r, 1.0f, dtype);
+  out[1] = cbt != nullptr ? tjob(B, cbt, rb ? rb : r, N, c, dtype) : out[0];
+  if (cbt == nullptr) out[1].nblk = 0;
+}
+
 hipError_t launch_lora_down(int64_t M, int64_t K, int64_t r, const uint16_t* X, const uint16_t* A, uint16_t* Z,
                             const SkinnyPlan& p, void* at_ws, void* part_ws, hipStream_t stream, int64_t N,
-                            const uint16_t* B, float c, uint16_t* cbt, int64_t rb, int dtype) {
+                            const uint16_t* B, float c, uint16_t* cbt, int64_t rb, int dtype, bool pre_transposed) {
   uint16_t* At = static_cast<uint16_t*>(at_ws);
-  const TJob ja = tjob(A, At, K, r, 1.0f, dtype);
-  TJob jb = cbt != nullptr ? tjob(B, cbt, rb ? rb : r, N, c, dtype) : ja;
-  if (cbt == nullptr) jb.nblk = 0;
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(static_cast<unsigned>(ja.nblk + jb.nblk)), dim3(256), 0, stream, ja,
-                     jb);
+  if (!pre_transposed) {
+    TJob tj[2];
+    lora_transposes(K, r, A, At, N, B, c, cbt, rb, dtype, tj);
+    hipLaunchKernelGGL(transpose_bf16_kernel, dim3(static_cast<unsigned>(tj[0].nblk + tj[1].nblk)), dim3(256), 0,
+                       stream, tj[0], tj[1]);
+  }
   float* part = static_cast<float*>(part_ws);
   Timer tm(QK_LORA_DOWN, stream);
   hipError_t e = launch_rowsum(X, At, M, r, K, p.z_splits, p.z_per, part, stream, 0, 0, dtype);
@@ -493,13 +429,17 @@ hipError_t launch_lora_down(int64_t M, int64_t K, int64_t r, const uint16_t* X, 
 }
 
 hipError_t launch_dz(int64_t M, int64_t N, int64_t r, const uint16_t* G, const uint16_t* B, float c, uint16_t* dZ,
-                     const SkinnyPlan& p, void* part_ws, hipStream_t stream, int dtype) {
+                     const SkinnyPlan& p, void* part_ws, hipStream_t stream, int dtype, RdJob* defer) {
   float* part = static_cast<float*>(part_ws);
   Timer tm(QK_BWD_DZ, stream);
   hipError_t e = launch_rowsum(G, B, M, r, N, p.dz_splits, p.dz_per, part, stream, 0, 0, dtype);
   tm.stop();
   if (e != hipSuccess) return e;
   const RdJob jz = rdjob(part, p.dz_splits, M, r, c, false, nullptr, dZ, dtype);
+  if (defer != nullptr) {
+    *defer = jz;
+    return hipSuccess;
+  }
   return launch_reduce(jz, nullptr, stream);
 }
 
