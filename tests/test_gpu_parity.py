@@ -237,10 +237,11 @@ def test_layer_fwd_bwd_matches_oracle(M, K, N, r, c):
     assert rel_err(lora, c * Zr @ case["B"]) <= 0.1
 
 
-def test_layer_bwd_without_dx():
-    M, K, N, r = 64, 256, 128, 16
+@pytest.mark.parametrize("M", [64, 256])   # fused path; two-pass path (dZ's sum then runs on its own)
+def test_layer_bwd_without_dx(M):
+    K, N, r = 256, 128, 16
     case = _layer_case(M, K, N, r, 0.5, seed=5)
-    say("layer bwd with dX skipped")
+    say(f"layer bwd with dX skipped, M={M}")
     _, _, _, dX, dA, dB = _run_layer(case, M, K, N, r, need_dx=False)
     assert dX is None
     W_hat = o.dequantize(o.quantize(case["W"]), "bf16").reshape(K, N)
