@@ -108,13 +108,13 @@ hipError_t launch_lora_down(int64_t M, int64_t K, int64_t r, const uint16_t* X, 
 // each); zp covers Z = X A over all g r columns.
 struct GroupPlan {
   SkinnyPlan zp;
-  int64_t dz_splits[kMaxGroupMembers], dz_per[kMaxGroupMembers], dz_part;
+  int64_t dz_splits[kMaxGroupMembers], dz_per[kMaxGroupMembers], dz_part, dz_off[kMaxGroupMembers];
   int64_t cs_splits, cs_per, da_part, db_part_total, db_off[kMaxGroupMembers];
 };
 GroupPlan plan_grouped(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r);
 hipError_t launch_dz_grouped(int64_t M, int g, const int64_t* Ns, int64_t Ntot, int64_t r, const uint16_t* G,
                              const uint16_t* B, float c, uint16_t* dZ, const GroupPlan& gp, void* part_ws,
-                             hipStream_t stream, int dtype = 0);
+                             hipStream_t stream, int dtype = 0, RdJob* defer = nullptr);
 hipError_t launch_colsums_grouped(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t Ntot, int64_t r,
                                   const uint16_t* X, const uint16_t* G, const uint16_t* Z, const uint16_t* dZ, float c,
                                   float* dA, float* dB, const GroupPlan& gp, void* da_ws, void* db_ws,

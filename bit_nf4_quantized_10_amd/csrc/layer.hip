@@ -108,7 +108,10 @@ hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
 // A, dA: K x g r; B, dB: r x Ntot; Z: M x g r).  Every member is
 // dequantized to bf16 into one stacked weight and the product runs as one
 // dense GEMM over all Ntot columns (forward) or over all Ntot reduction
-// columns (dX), with one Z = X A over all g r columns.
+// columns (dX), with one Z = X A over all g r columns.  The transposes ride
+// in the first member's dequantize launch, each member's dZ sum in its own
+// dequantize launch, and dA with every member's dB is one column-sum launch
+// (up to three members).
 int64_t grouped_fwd_workspace_bytes(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r) {
   const GroupPlan gp = plan_grouped(M, K, g, Ns, r);
   int64_t Ntot = 0;
@@ -135,15 +138,22 @@ hipError_t launch_grouped_fwd(int64_t M, int64_t K, int g, const int64_t* Ns, in
   char* zpart = base + gp.zp.at_bytes;
   uint16_t* cbt = reinterpret_cast<uint16_t*>(zpart + gp.zp.z_part);
   uint16_t* wt = reinterpret_cast<uint16_t*>(zpart + gp.zp.z_part + align256(Ntot * r * 2));
-  hipError_t e = launch_lora_down(M, K, g * r, X, A, Z, gp.zp, base, zpart, stream, Ntot, B, c, cbt, r);
-  if (e != hipSuccess) return e;
+  // Aᵀ and (c B)ᵀ of all members ride along in the first member's dequantize launch
+  TJob tj[2];
+  lora_transposes(K, g * r, A, reinterpret_cast<uint16_t*>(base), Ntot, B, c, cbt, r, kDtypeBf16, tj);
+  hipError_t e;
   int64_t gend[kMaxGroupMembers];
   int64_t off = 0;
   for (int i = 0; i < g; ++i) {
-    if ((e = launch_dequant_bf16(W[i], K, Ns[i], true, wt + off * K, stream)) != hipSuccess) return e;
+    if ((e = launch_dequant_bf16(W[i], K, Ns[i], true, wt + off * K, stream, 0, kDtypeBf16, i == 0 ? tj : nullptr)) !=
+        hipSuccess)
+      return e;
     off += Ns[i];
     gend[i] = off;
   }
+  if ((e = launch_lora_down(M, K, g * r, X, A, Z, gp.zp, base, zpart, stream, Ntot, B, c, cbt, r, kDtypeBf16, true)) !=
+      hipSuccess)
+    return e;
   return launch_fwd_dense_grouped(M, K, Ntot, r, X, wt, Z, g, gend, cbt, Y, stream, kDtypeBf16,
                                   reinterpret_cast<char*>(wt) + align256(Ntot * K * 2));
 }
@@ -160,17 +170,24 @@ hipError_t launch_grouped_bwd(int64_t M, int64_t K, int g, const int64_t* Ns, in
   char* da_ws = base + gp.dz_part + align256(M * g * r * 2);
   char* db_ws = da_ws + gp.da_part;
   uint16_t* wd = reinterpret_cast<uint16_t*>(db_ws + gp.db_part_total);
-  hipError_t e = launch_dz_grouped(M, g, Ns, Ntot, r, G, B, c, dz16, gp, base, stream);
+  // with dX wanted, member i's dZ sum rides along in member i's dequantize launch
+  RdJob jz[kMaxGroupMembers];
+  hipError_t e = launch_dz_grouped(M, g, Ns, Ntot, r, G, B, c, dz16, gp, base, stream, kDtypeBf16,
+                                   dX != nullptr ? jz : nullptr);
   if (e != hipSuccess) return e;
+  if (dX != nullptr) {
+    int64_t off = 0;
+    for (int i = 0; i < g; ++i) {
+      if ((e = launch_dequant_bf16(W[i], K, Ns[i], false, wd + off, stream, Ntot, kDtypeBf16, nullptr, &jz[i])) !=
+          hipSuccess)
+        return e;
+      off += Ns[i];
+    }
+  }
   if ((e = launch_colsums_grouped(M, K, g, Ns, Ntot, r, X, G, Z, dz16, c, dA, dB, gp, da_ws, db_ws, stream)) !=
       hipSuccess)
     return e;
   if (dX == nullptr) return hipGetLastError();
-  int64_t off = 0;
-  for (int i = 0; i < g; ++i) {
-    if ((e = launch_dequant_bf16(W[i], K, Ns[i], false, wd + off, stream, Ntot)) != hipSuccess) return e;
-    off += Ns[i];
-  }
   return launch_dx_dense(M, K, Ntot, g * r, G, wd, dz16, A, dX, stream, kDtypeBf16,
                          reinterpret_cast<char*>(wd) + align256(K * Ntot * 2));
 }

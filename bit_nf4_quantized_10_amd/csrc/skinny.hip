@@ -191,12 +191,23 @@ __device__ __forceinline__ typename T::v8 tr_read2(const char* p0, const char* p
   return __builtin_bit_cast(typename T::v8, both);
 }
 
+// Up to kCsJobs jobs per launch, their workgroups one after another.
+constexpr int kCsJobs = 4;
+struct CsJobs {
+  CsJob j[kCsJobs];
+};
+
 template <class T>
-__global__ __launch_bounds__(256) void colsum_kernel(CsJob j0, CsJob j1, int64_t M) {
+__global__ __launch_bounds__(256) void colsum_kernel(CsJobs jobs, int64_t M) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const bool second = blockIdx.x >= j0.nblk;
-  const CsJob& J = second ? j1 : j0;
-  const int64_t blk = second ? blockIdx.x - j0.nblk : blockIdx.x;
+  int64_t blk = blockIdx.x;
+  CsJob J = jobs.j[0];
+#pragma unroll
+  for (int i = 1; i < kCsJobs; ++i)
+    if (blk >= J.nblk) {
+      blk -= J.nblk;
+      J = jobs.j[i];
+    }
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t cb = blk % J.col_blocks, rest = blk / J.col_blocks;
@@ -356,7 +367,7 @@ hipError_t launch_rowsum(const uint16_t* act, const uint16_t* wt, int64_t M, int
 }
 
 template <class T>
-hipError_t colsum_launch_t(const CsJob& ja, const CsJob& jb, int64_t M, hipStream_t stream) {
+hipError_t colsum_launch_t(const CsJobs& jobs, int64_t M, hipStream_t stream) {
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&colsum_kernel<T>),
@@ -364,13 +375,17 @@ hipError_t colsum_launch_t(const CsJob& ja, const CsJob& jb, int64_t M, hipStrea
     if (e != hipSuccess) return e;
     configured = true;
   }
-  hipLaunchKernelGGL(colsum_kernel<T>, dim3(static_cast<unsigned>(ja.nblk + jb.nblk)), dim3(256), kCsLds, stream, ja,
-                     jb, M);
+  int64_t blocks = 0;
+  for (int i = 0; i < kCsJobs; ++i) blocks += jobs.j[i].nblk;
+  hipLaunchKernelGGL(colsum_kernel<T>, dim3(static_cast<unsigned>(blocks)), dim3(256), kCsLds, stream, jobs, M);
   return hipGetLastError();
 }
 
-hipError_t launch_colsum(const CsJob& ja, const CsJob& jb, int64_t M, hipStream_t stream, int dtype) {
-  return dtype == kDtypeF16 ? colsum_launch_t<F16>(ja, jb, M, stream) : colsum_launch_t<Bf16>(ja, jb, M, stream);
+// jobs[0 .. n-1] (n <= kCsJobs) in one launch.
+hipError_t launch_colsum(const CsJob* jobs, int n, int64_t M, hipStream_t stream, int dtype) {
+  CsJobs js{};
+  for (int i = 0; i < n; ++i) js.j[i] = jobs[i];
+  return dtype == kDtypeF16 ? colsum_launch_t<F16>(js, M, stream) : colsum_launch_t<Bf16>(js, M, stream);
 }
 
 }  // namespace
@@ -452,8 +467,9 @@ hipError_t launch_colsums(int64_t M, int64_t K, int64_t N, int64_t r, const uint
   CsJob jb{G, N, N, Z, static_cast<float*>(db_ws), cdiv(N, 64), jc, p.db_per, 0, r, r};
   ja.nblk = ja.col_blocks * jc * p.da_splits;
   jb.nblk = jb.col_blocks * jc * p.db_splits;
+  const CsJob both[2] = {ja, jb};
   Timer tm(QK_BWD_COLSUM, stream);
-  hipError_t e = launch_colsum(ja, jb, M, stream, dtype);
+  hipError_t e = launch_colsum(both, 2, M, stream, dtype);
   tm.stop();
   if (e != hipSuccess) return e;
   const RdJob ra = rdjob(static_cast<float*>(da_ws), p.da_splits, K, r, 1.0f, false, dA, nullptr);
@@ -480,9 +496,12 @@ GroupPlan plan_grouped(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r
     const SkinnyPlan pi = plan_skinny(M, K, Ns[i], r);
     gp.dz_splits[i] = pi.dz_splits;
     gp.dz_per[i] = pi.dz_per;
-    gp.dz_part = gp.dz_part > pi.dz_part ? gp.dz_part : pi.dz_part;
+    gp.dz_off[i] = gp.dz_part;   // every member's partials kept until its sum runs
+    gp.dz_part += pi.dz_part;
     cs_tiles += cdiv(Ns[i], 64) * cdiv(r, 64);
   }
+  // the jobs run kCsJobs to a launch (all of them for up to three members)
+  // (the jobs run kCsJobs to a launch: all of them for up to three members)
   split_plan(cs_tiles, M, QN_CS_WGS, 64, &gp.cs_splits, &gp.cs_per);
   gp.da_part = round_up(gp.cs_splits * K * rt * 4, 256);
   gp.db_part_total = 0;
@@ -495,12 +514,13 @@ GroupPlan plan_grouped(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r
 
 // dZ_i = c G_i B_iᵀ for every member: a row-sum over member i's columns of G
 // and B (row stride Ntot), reduced into column block i of dZ (row stride g r).
+// With defer != nullptr the g sums are not launched but returned there.
 hipError_t launch_dz_grouped(int64_t M, int g, const int64_t* Ns, int64_t Ntot, int64_t r, const uint16_t* G,
                              const uint16_t* B, float c, uint16_t* dZ, const GroupPlan& gp, void* part_ws,
-                             hipStream_t stream, int dtype) {
-  float* part = static_cast<float*>(part_ws);
+                             hipStream_t stream, int dtype, RdJob* defer) {
   int64_t off = 0;
   for (int i = 0; i < g; ++i) {
+    float* part = reinterpret_cast<float*>(static_cast<char*>(part_ws) + gp.dz_off[i]);
     Timer tm(QK_BWD_DZ, stream);
     hipError_t e =
         launch_rowsum(G + off, B + off, M, r, Ns[i], gp.dz_splits[i], gp.dz_per[i], part, stream, Ntot, Ntot, dtype);
@@ -508,7 +528,8 @@ hipError_t launch_dz_grouped(int64_t M, int g, const int64_t* Ns, int64_t Ntot, 
     if (e != hipSuccess) return e;
     RdJob jz = rdjob(part, gp.dz_splits[i], M, r, c, false, nullptr, dZ + i * r, dtype);
     jz.out_ld = g * r;
-    if ((e = launch_reduce(jz, nullptr, stream)) != hipSuccess) return e;
+    if (defer != nullptr) defer[i] = jz;
+    else if ((e = launch_reduce(jz, nullptr, stream)) != hipSuccess) return e;
     off += Ns[i];
   }
   return hipSuccess;
@@ -534,11 +555,10 @@ hipError_t launch_colsums_grouped(int64_t M, int64_t K, int g, const int64_t* Ns
     off += Ns[i];
   }
   for (int j = 0; j <= g; ++j) jobs[j].nblk = jobs[j].col_blocks * jobs[j].j_chunks * gp.cs_splits;
-  for (int j = 0; j <= g; j += 2) {
-    CsJob second = j + 1 <= g ? jobs[j + 1] : jobs[j];
-    if (j + 1 > g) second.nblk = 0;
+  for (int j = 0; j <= g; j += kCsJobs) {
+    const int n = g + 1 - j < kCsJobs ? g + 1 - j : kCsJobs;
     Timer tm(QK_BWD_COLSUM, stream);
-    hipError_t e = launch_colsum(jobs[j], second, M, stream, dtype);
+    hipError_t e = launch_colsum(jobs + j, n, M, stream, dtype);
     tm.stop();
     if (e != hipSuccess) return e;
   }
