@@ -81,8 +81,8 @@ def main():
                     help="also run one plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not supported "
-              "(see DESIGN.md for how the path would shard)", file=sys.stderr)
+        print("bench.py: the layer is measured on exactly one GPU; multi-GPU runs are not supported "
+              "(a sharded layer splits N across GPUs and all-reduces dX and dZ in the backward)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -109,7 +109,7 @@ constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 1
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// ---- the two 16-bit compute types of the layer ([P2] §20: BF16, or FP16
+// ---- the two 16-bit compute types of the layer (page "SFT（四）：QLoRA的4-bit量化与LoRA微调原理" §20: BF16, or FP16
 // where BF16 is not wanted).  Each tag gives the MFMA operand vector, the
 // 16x16x32 and 32x32x16 MFMAs with fp32 accumulation, the fp32 -> 16-bit
 // round-to-nearest-even packing of two values, and the widening to fp32.

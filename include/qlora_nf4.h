@@ -211,7 +211,7 @@ int qlora_grouped_bwd(int64_t M, int64_t K, int g, const int64_t* N, int64_t r, 
                       const uint16_t* B, float c, uint16_t* dX, float* dA, float* dB,
                       void* workspace, int64_t workspace_bytes, void* stream);
 
-/* The 16-bit compute type of the layer ([P2] §20: BF16 where supported,
+/* The 16-bit compute type of the layer (page "SFT（四）：QLoRA的4-bit量化与LoRA微调原理" §20: BF16 where supported,
  * else FP16).  The _dt entry points take it as their first argument; X, A,
  * B, G, Y, Z and dX are then of that type (uint16_t bit patterns), the
  * dequantized weight is RNE_T(ŵ) (fp16: overflow past 65504 gives inf), and

@@ -38,7 +38,7 @@ Pages cited (by title and section):
 [P3] "精读笔记 · QLoRA: Efficient Finetuning of Quantized LLMs", §3.0 (store
      NF4, compute in BF16) and §3.2 (double-quantization accounting).
 
-Readings where the pages leave a step open (the same list is in the design doc):
+Readings where the pages leave a step open:
   R1  W is K x N row-major; blocks of 64 run over the flat index k*N + n.
   R2  The mean of the first-level absmax values is summed in float64 as a fixed
       tree: each group of 256 by stride-halving (pairs i, i+128, then i, i+64,
