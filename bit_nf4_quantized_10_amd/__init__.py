@@ -322,9 +322,10 @@ def qlora_workspace_bytes(M: int, K: int, N: int, r: int) -> tuple[int, int]:
 
 
 def qlora_linear_fwd(X, state: NF4State, A, B, c: float, K: int, N: int, Y=None, Z=None,
-                     workspace=None, stream=None):
+                     workspace=None, stream=None, return_z: bool = True):
     """Y = X Ŵ + c (X A) B.  X: M x K, A: K x r, B: r x N, all bf16 or all fp16
-    (the compute type).  Returns (Y, Z)."""
+    (the compute type).  Returns (Y, Z); with return_z=False and no Z given,
+    Z stays in the workspace and (Y, None) is returned."""
     import torch
     M, r = X.shape[0], A.shape[1]
     dt = _compute_dtype(X)
@@ -332,26 +333,28 @@ def qlora_linear_fwd(X, state: NF4State, A, B, c: float, K: int, N: int, Y=None,
         _require_cuda(t, n, dt)
     if Y is None:
         Y = torch.empty(M, N, dtype=dt, device=X.device)
-    if Z is None:
+    if Z is None and return_z:
         Z = torch.empty(M, r, dtype=dt, device=X.device)
     if workspace is None:
         workspace = torch.empty(max(qlora_workspace_bytes(M, K, N, r)[0], 256), dtype=torch.uint8,
                                 device=X.device)
     st = state.c_struct()
     _check(lib().qlora_linear_fwd_dt(_COMPUTE[dt], M, K, N, r, X.data_ptr(), ctypes.byref(st), A.data_ptr(),
-                                     B.data_ptr(), float(c), Y.data_ptr(), Z.data_ptr(), workspace.data_ptr(),
+                                     B.data_ptr(), float(c), Y.data_ptr(), _ptr(Z), workspace.data_ptr(),
                                      workspace.numel(), _stream(stream)), "qlora_linear_fwd_dt")
     return Y, Z
 
 
 def qlora_linear_bwd(G, X, Z, state: NF4State, A, B, c: float, K: int, N: int, need_dx: bool = True,
                      dX=None, dA=None, dB=None, workspace=None, stream=None):
-    """dZ = c G Bᵀ, dA = Xᵀ dZ, dB = c Zᵀ G, dX = G Ŵᵀ + dZ Aᵀ.  Returns (dX, dA, dB)."""
+    """dZ = c G Bᵀ, dA = Xᵀ dZ, dB = c Zᵀ G, dX = G Ŵᵀ + dZ Aᵀ.  Returns (dX, dA, dB).
+    Z = None recomputes Z = X A in the workspace."""
     import torch
     M, r = X.shape[0], A.shape[1]
     dt = _compute_dtype(X)
     for t, n in ((G, "G"), (X, "X"), (Z, "Z"), (A, "A"), (B, "B")):
-        _require_cuda(t, n, dt)
+        if t is not None or n != "Z":
+            _require_cuda(t, n, dt)
     if need_dx and dX is None:
         dX = torch.empty(M, K, dtype=dt, device=X.device)
     if dA is None:
@@ -362,7 +365,7 @@ def qlora_linear_bwd(G, X, Z, state: NF4State, A, B, c: float, K: int, N: int, n
         workspace = torch.empty(max(qlora_workspace_bytes(M, K, N, r)[1], 256), dtype=torch.uint8,
                                 device=X.device)
     st = state.c_struct()
-    _check(lib().qlora_linear_bwd_dt(_COMPUTE[dt], M, K, N, r, G.data_ptr(), X.data_ptr(), Z.data_ptr(),
+    _check(lib().qlora_linear_bwd_dt(_COMPUTE[dt], M, K, N, r, G.data_ptr(), X.data_ptr(), _ptr(Z),
                                      ctypes.byref(st), A.data_ptr(), B.data_ptr(), float(c),
                                      _ptr(dX if need_dx else None), dA.data_ptr(), dB.data_ptr(),
                                      workspace.data_ptr(), workspace.numel(), _stream(stream)), "qlora_linear_bwd_dt")

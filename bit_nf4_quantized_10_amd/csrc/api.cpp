@@ -143,8 +143,8 @@ int qlora_linear_fwd_dt(int compute_dtype, int64_t M, int64_t K, int64_t N, int6
                      const uint16_t* A, const uint16_t* B, float c, uint16_t* Y, uint16_t* Z, void* workspace,
                      int64_t workspace_bytes, void* stream) {
   if (!dtype_ok(compute_dtype) || !layer_shape_ok(M, K, N, r) || !state_ok(W) || W->numel != K * N) return NF4_EINVAL;
-  if (!X || !A || !B || !Y || !Z || !workspace) return NF4_EINVAL;
-  if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y) || !aligned16(Z) ||
+  if (!X || !A || !B || !Y || !workspace) return NF4_EINVAL;   // Z may be NULL
+  if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y) || (Z && !aligned16(Z)) ||
       !aligned16(W->codes) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return NF4_EINVAL;
   if (workspace_bytes < qn::fwd_workspace_bytes(M, K, N, r)) return NF4_EINVAL;
@@ -166,8 +166,8 @@ int qlora_linear_bwd_dt(int compute_dtype, int64_t M, int64_t K, int64_t N, int6
                      uint16_t* dX, float* dA, float* dB, void* workspace, int64_t workspace_bytes,
                      void* stream) {
   if (!dtype_ok(compute_dtype) || !layer_shape_ok(M, K, N, r) || !state_ok(W) || W->numel != K * N) return NF4_EINVAL;
-  if (!G || !X || !Z || !A || !B || !dA || !dB || !workspace) return NF4_EINVAL;
-  if (!aligned16(G) || !aligned16(X) || !aligned16(Z) || !aligned16(A) || !aligned16(B) || !aligned16(dA) ||
+  if (!G || !X || !A || !B || !dA || !dB || !workspace) return NF4_EINVAL;   // Z may be NULL
+  if (!aligned16(G) || !aligned16(X) || (Z && !aligned16(Z)) || !aligned16(A) || !aligned16(B) || !aligned16(dA) ||
       !aligned16(dB) || (dX && !aligned16(dX)) || !aligned16(W->codes) ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return NF4_EINVAL;

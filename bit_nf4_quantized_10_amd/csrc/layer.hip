@@ -37,16 +37,28 @@ int64_t dense_bytes(int64_t M, int64_t K, int64_t N) { return use_dense(M) ? ali
 // (c B)ᵀ in bf16 for the GEMM kernels' LoRA extension
 int64_t cbt_bytes(int64_t M, int64_t N, int64_t r) { return M > 16 ? align256(N * r * 2) : 0; }
 
-int64_t fwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r) {
+// Workspace layouts: the kernels' scratch, then a Z buffer for calls that do
+// not pass Z (the forward computes Z there; the backward recomputes it there
+// from X and A, with its own Aᵀ and split partials in front of it).
+int64_t fwd_core_bytes(int64_t M, int64_t K, int64_t N, int64_t r) {
   const SkinnyPlan p = plan_skinny(M, K, N, r);
   if (M <= 16) return p.gv_part + p.gv_zpart;
   return p.at_bytes + p.z_part + cbt_bytes(M, N, r) + dense_bytes(M, K, N) + plan_split(M, N, K).part_bytes;
 }
 
-int64_t bwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r) {
+int64_t bwd_core_bytes(int64_t M, int64_t K, int64_t N, int64_t r) {
   const SkinnyPlan p = plan_skinny(M, K, N, r);
   return p.dz_part + align256(M * r * 2) + p.da_part + p.db_part + dense_bytes(M, K, N) +
          plan_split(M, K, N).part_bytes;
+}
+
+int64_t fwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r) {
+  return fwd_core_bytes(M, K, N, r) + align256(M * r * 2);
+}
+
+int64_t bwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r) {
+  const SkinnyPlan p = plan_skinny(M, K, N, r);
+  return bwd_core_bytes(M, K, N, r) + p.at_bytes + p.z_part + align256(M * r * 2);
 }
 
 hipError_t launch_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W, const uint16_t* A,
@@ -55,6 +67,7 @@ hipError_t launch_fwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
   const SkinnyPlan p = plan_skinny(M, K, N, r);
   char* base = static_cast<char*>(ws);
   char* after_z = base + p.at_bytes + p.z_part;
+  if (Z == nullptr) Z = reinterpret_cast<uint16_t*>(base + fwd_core_bytes(M, K, N, r));
   hipError_t e;
   if (M <= 16) return launch_gemv(M, K, N, r, X, W, A, B, c, Y, Z, p, base, stream, dtype);
   uint16_t* cbt = reinterpret_cast<uint16_t*>(after_z);
@@ -88,6 +101,15 @@ hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
   uint16_t* wd = reinterpret_cast<uint16_t*>(static_cast<char*>(db_part) + p.db_part);
   void* split_ws = reinterpret_cast<char*>(wd) + dense_bytes(M, K, N);
   hipError_t e;
+  if (Z == nullptr) {
+    // recompute Z = X A (for M > 16 the forward's own kernels, so the same bits)
+    char* zr = base + bwd_core_bytes(M, K, N, r);
+    uint16_t* zbuf = reinterpret_cast<uint16_t*>(zr + p.at_bytes + p.z_part);
+    if ((e = launch_lora_down(M, K, r, X, A, zbuf, p, zr, zr + p.at_bytes, stream, 0, nullptr, 1.0f, nullptr, 0,
+                              dtype)) != hipSuccess)
+      return e;
+    Z = zbuf;
+  }
   if (dX != nullptr && use_dense(M)) {
     // the fixed-order sum of dZ rides along in the launch that dequantizes Ŵ
     RdJob jz;

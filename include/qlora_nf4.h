@@ -121,7 +121,8 @@ int qlora_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r,
  * X: M x K bf16, W: state of the K x N weight (W->numel == K*N), A: K x r
  * bf16, B: r x N bf16, c = alpha / r.  Ŵ is exactly the bf16 weight that
  * nf4_dequantize(W, NF4_OUT_BF16) returns.  Z is written for the backward
- * pass.  Requirements: M, K, N, r >= 1, N % 64 == 0, K % 8 == 0, r % 8 == 0,
+ * pass; with Z = NULL it is computed in the workspace and not returned.
+ * Requirements: M, K, N, r >= 1, N % 64 == 0, K % 8 == 0, r % 8 == 0,
  * r <= 256, M <= 2^20, K, N <= 2^24, each of M*K, M*N, K*N, K*r and r*N
  * below 2^29 elements (every bf16 operand under 1 GiB, so that 32-bit
  * buffer offsets suffice), all pointers 16-byte aligned, workspace >= fwd_bytes.  The
@@ -137,7 +138,9 @@ int qlora_linear_fwd(int64_t M, int64_t K, int64_t N, int64_t r,
  * "冻结权重为什么仍然需要输入梯度"):
  *   dZ = c G Bᵀ,  dA = Xᵀ dZ (K x r fp32),  dB = c Zᵀ G (r x N fp32),
  *   dX = G Ŵᵀ + dZ Aᵀ (M x K bf16; skipped when dX is NULL).
- * Z is the forward's Z.  The frozen state receives no gradient and is only
+ * Z is the forward's Z, or NULL: then Z = X A is recomputed in the
+ * workspace (one more read of X; for M > 16 with the forward's own kernels,
+ * so the same bits).  The frozen state receives no gradient and is only
  * read.  Same requirements as the forward; workspace >= bwd_bytes.  dA and
  * dB are computed with deterministic (fixed-order) split reductions. */
 int qlora_linear_bwd(int64_t M, int64_t K, int64_t N, int64_t r,

@@ -249,6 +249,32 @@ def test_layer_bwd_without_dx(M):
     assert rel_err(host(dA), dAr) <= TOL and rel_err(host(dB), dBr) <= TOL
 
 
+@pytest.mark.parametrize("M", [8, 130, 600])   # dequant-GEMV, fused kernel, dequantize-then-GEMM
+def test_layer_without_z(M):
+    """Z is optional: a forward without Z gives the same Y, and a backward
+    without Z recomputes it (for M > 16 with the forward's own kernels, so
+    every output is the same bits)."""
+    K, N, r, c = 512, 768, 16, 0.5
+    case = _layer_case(M, K, N, r, c, seed=60 + M)
+    say(f"layer without Z, M={M}")
+    state, status = _quantize(case["W"])
+    assert status == 0
+    X, A, B, G = (dev_bf16(case[k]) for k in ("Xb", "Ab", "Bb", "Gb"))
+    Y1, Z1 = qn.qlora_linear_fwd(X, state, A, B, c, K, N)
+    Y2, Z2 = qn.qlora_linear_fwd(X, state, A, B, c, K, N, return_z=False)
+    assert Z2 is None
+    assert host(Y1).tobytes() == host(Y2).tobytes()
+    g1 = qn.qlora_linear_bwd(G, X, Z1, state, A, B, c, K, N)
+    g2 = qn.qlora_linear_bwd(G, X, None, state, A, B, c, K, N)
+    if M > 16:
+        for a, b in zip(g1, g2):
+            assert host(a).tobytes() == host(b).tobytes()
+    W_hat = o.dequantize(o.quantize(case["W"]), "bf16").reshape(K, N)
+    dXr, dAr, dBr, _ = o.layer_backward(case["G"], case["X"], W_hat, case["A"], case["B"], c)
+    for got, ref in zip(g2, (dXr, dAr, dBr)):
+        assert rel_err(host(got), ref) <= TOL
+
+
 def _integer_case(M, K, N, r, seed):
     """Every block holds +-2^e, so the double quantization is exact and every
     accumulation is an exact small-integer sum in fp32 (and bf16)."""

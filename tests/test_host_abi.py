@@ -107,6 +107,11 @@ def test_entry_points_reject_bad_arguments_before_launch():
         assert L.qlora_linear_fwd(4, 64, 64, 8, *small_ws) == qn.NF4_EINVAL
     assert L.qlora_linear_bwd(4, 64, 64, 8, 0x100, 0x100, 0x100, ctypes.byref(st2), 0x200, 0x300,
                               ctypes.c_float(1.0), None, None, 0x600, 0x10000, 1 << 30, None) == qn.NF4_EINVAL
+    # Z may be NULL (computed / recomputed in the workspace), but a given Z must be aligned
+    mis_z = (0x100, ctypes.byref(st2), 0x200, 0x300, ctypes.c_float(1.0), 0x400, 0x502, 0x10000, 1 << 30, None)
+    assert L.qlora_linear_fwd(4, 64, 64, 8, *mis_z) == qn.NF4_EINVAL
+    assert L.qlora_linear_bwd(4, 64, 64, 8, 0x100, 0x100, 0x502, ctypes.byref(st2), 0x200, 0x300,
+                              ctypes.c_float(1.0), None, 0x600, 0x700, 0x10000, 1 << 30, None) == qn.NF4_EINVAL
 
 
 def test_timer_ids_validated():
