@@ -417,10 +417,11 @@ def bench_components(torch, qn, si, dev, sets, outs, qws, status):
     return res
 
 
-def cpu_baseline(wl, reps=3):
+def cpu_baseline(wl, reps=9):
     """The oracle as it stands, on the host cores, on the full workload:
     quantize of the 4096 x 4096 weight, then forward and backward at all 4096
-    token rows (fp64 numpy); median of `reps` runs."""
+    token rows (fp64 numpy); median of `reps` runs (about 10-12 s of CPU work
+    in all)."""
     import synth_inputs as si
     from oracle import nf4_oracle as o
     try:
@@ -442,7 +443,8 @@ def cpu_baseline(wl, reps=3):
     fwd_f, bwd_f = layer_flops(M, K, N, r)
     return {"value": round((fwd_f + bwd_f) / step_s / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"full workload (quantize + fwd + bwd, M={M}), median of {reps} runs: {step_s:.2f} s per step"}
+            "sample": f"full workload (quantize + fwd + bwd, M={M}), median of {reps} runs "
+                      f"({sum(times):.1f} s of CPU work): {step_s:.2f} s per step"}
 
 
 if __name__ == "__main__":
