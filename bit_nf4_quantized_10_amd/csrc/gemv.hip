@@ -74,9 +74,6 @@ __device__ __forceinline__ void transpose8x8_bf16(const uint4 (&in)[8], uint4 (&
   }
 }
 
-// Nibble of column t (0..7) in a code word: byte t/2, high nibble for even t.
-__device__ __forceinline__ uint32_t nib(uint32_t w, int t) { return (w >> (8 * (t >> 1) + ((t & 1) ? 0 : 4))) & 15u; }
-
 // Split-K partial of Z = X A for M <= 16 over rows [split * 4 rpw, +4 rpw),
 // each wave over the rows its GEMV counterpart streams.  A is read row-major
 // (8 rows of 8 columns per lane, transposed in registers), X rows feed the

@@ -27,10 +27,6 @@ namespace {
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
-}
-
 // ------------------------------------------------------------ transpose
 // Two TJobs per launch (side_jobs.hpp): Aᵀ and, in the forward, (c B)ᵀ.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(TJob j0, TJob j1) {
