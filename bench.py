@@ -10,7 +10,8 @@ Infinity Cache cannot hold a step's inputs from the previous step.
 Also reported (not part of `value`): the roofline of the dominant kernel
 (timed live with HIP events on the launch stream), the memory-bound paths in
 GB/s (quantize, bf16 dequantize, small-M dequant-GEMV at M = 1/8/16 on the
-65B MLP shape), and the CPU oracle timed on a bounded sample.
+65B MLP shape), the 7B MLP set and a 65B block's seven linears (quantize all,
+then fwd+bwd of all), and the CPU oracle timed on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--copy-probe]
 """
@@ -165,6 +166,7 @@ def main():
                 "traffic": traffic, "kernel": dominant, "avg_ms": round(dom_avg, 4),
                 "launches": dom_n, "flops_per_launch": dflops}
 
+    print(f"bench: {args.steps} timed steps, {ms_step:.4f} ms each", file=sys.stderr, flush=True)
     components = {"kernel_avg_ms_warmup": {k: round(v, 4) for k, v in per_kernel.items()}}
     if not args.no_components:
         components.update(bench_components(torch, qn, si, dev, sets, outs, qws, status))
@@ -275,6 +277,7 @@ def bench_components(torch, qn, si, dev, sets, outs, qws, status):
                          "frac_hbm_call": round(gbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "GBps_kernel": round(gbytes / (kms * 1e-3) / 1e9, 1)}
     res["gemv_decode65b"] = gemv
+    print("bench: memory-bound paths measured", file=sys.stderr, flush=True)
     # what plain streaming reaches on this device, as context for the HBM fractions
     # (the fractions above are against the 8 TB/s specification)
     big = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -395,6 +398,10 @@ def bench_components(torch, qn, si, dev, sets, outs, qws, status):
                                 "how": "qlora_linear_fwd + _bwd in the fp16 compute type, 4096 x 4096, r = 64, "
                                        "M = 4096, cache flushed"}
     del Xh, Ah, Bh, Gh, ws16, Yh, Zh, dXh, dAh, dBh
+    # every linear of the 7B MLP set and of a 65B block, one pass each
+    for name in ("mlp7b_4096x11008", "block65b_m2048"):
+        res[name] = bench_workload_set(torch, qn, si, dev, name, flush)
+        print(f"bench: {name} measured", file=sys.stderr, flush=True)
     # the vendor library's plain bf16 GEMM of the same base shape on this
     # device (torch.matmul -> hipBLASLt), as context for the MFMA fraction
     Mv, Kv, Nv = 4096, 4096, 4096
@@ -415,6 +422,75 @@ def bench_components(torch, qn, si, dev, sets, outs, qws, status):
         "how": "torch.matmul of 4096x4096 by 4096x4096 bf16 (hipBLASLt), 20 back-to-back calls"}
     del xa, wb, yv
     return res
+
+
+def bench_workload_set(torch, qn, si, dev, name, flush, reps=3):
+    """All linears of a multi-matrix workload, each with its own weight and
+    inputs: nf4_quantize of every weight, then qlora_linear_fwd and _bwd of
+    every linear, one after another on one stream (inputs resident in HBM,
+    the Infinity Cache overwritten before each timed pass).  The layers'
+    TFLOP/s count the fwd+bwd flops only; the quantize is timed on its own
+    as well, against its algorithmic bytes."""
+    bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+    mats, ws_bytes, qws_bytes = [], 256, 256
+    for j in range(len(si.WORKLOADS[name]["shapes"])):
+        d = si.layer_inputs(name, matrix=j)
+        M, K, N, r = d["M"], d["K"], d["N"], d["r"]
+        m = {"M": M, "K": K, "N": N, "r": r, "c": d["c"], "W": torch.from_numpy(d["W"]).to(dev).reshape(-1),
+             "X": bf(d["X_bits"]), "A": bf(d["A_bits"]), "B": bf(d["B_bits"]), "G": bf(d["G_bits"]),
+             "state": qn.empty_state(K * N, dev),
+             "Y": torch.empty(M, N, dtype=torch.bfloat16, device=dev),
+             "Z": torch.empty(M, r, dtype=torch.bfloat16, device=dev),
+             "dX": torch.empty(M, K, dtype=torch.bfloat16, device=dev),
+             "dA": torch.empty(K, r, dtype=torch.float32, device=dev),
+             "dB": torch.empty(r, N, dtype=torch.float32, device=dev)}
+        del d
+        ws_bytes = max(ws_bytes, *qn.qlora_workspace_bytes(M, K, N, r))
+        qws_bytes = max(qws_bytes, qn.nf4_sizes(K * N)["quant_workspace_bytes"])
+        mats.append(m)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    qws = torch.empty(qws_bytes, dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def quant_all(i):
+        for m in mats:
+            qn.nf4_quantize(m["W"], m["state"], qws, status)
+
+    def layers_all(i):
+        for m in mats:
+            qn.qlora_linear_fwd(m["X"], m["state"], m["A"], m["B"], m["c"], m["K"], m["N"], m["Y"], m["Z"], ws)
+            qn.qlora_linear_bwd(m["G"], m["X"], m["Z"], m["state"], m["A"], m["B"], m["c"], m["K"], m["N"], True,
+                                m["dX"], m["dA"], m["dB"], ws)
+
+    def step(i):
+        quant_all(i)
+        layers_all(i)
+
+    step(0)
+    if qn.nf4_status_read(status) != 0:
+        raise RuntimeError(f"quantize reported a bad status on {name}")
+    sms = _time_calls(torch, step, reps, flush)
+    qms = _time_calls(torch, quant_all, reps, flush)
+    lms = _time_calls(torch, layers_all, reps, flush)
+    flops = sum(sum(layer_flops(m["M"], m["K"], m["N"], m["r"])) for m in mats)
+    qbytes = 0
+    for m in mats:
+        P = m["K"] * m["N"]
+        sz = qn.nf4_sizes(P)
+        qbytes += 4 * P + (P + 1) // 2 + sz["n1"] + 4 * sz["n2"] + 4
+    out = {"matrices_KxN": [[m["K"], m["N"]] for m in mats], "M": mats[0]["M"], "r": mats[0]["r"],
+           "step_ms": round(sms, 4), "step_TFLOPs": round(flops / (sms * 1e-3) / 1e12, 1),
+           "layers_ms": round(lms, 4), "layers_TFLOPs": round(flops / (lms * 1e-3) / 1e12, 1),
+           "layers_frac_bf16_peak": round(flops / (lms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "quantize_ms": round(qms, 4), "quantize_bytes": qbytes,
+           "quantize_GBps": round(qbytes / (qms * 1e-3) / 1e9, 1),
+           "quantize_frac_hbm": round(qbytes / (qms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "flops_fwd_bwd": flops,
+           "how": "nf4_quantize of every weight, then fwd + bwd of every linear, one stream, cache flushed; "
+                  f"mean of {reps} passes"}
+    del mats, ws, qws
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(wl, reps=9):
