@@ -179,6 +179,64 @@ def test_quantize_decode65b_sampled_bit_exact():
         np.testing.assert_array_equal(got_w, ow.weights_of_blocks(blocks, dt))
 
 
+def test_quantize_largest_accepted_size_sampled_bit_exact():
+    """The largest state the library accepts: 2^29 - 1 weights, an fp32 input
+    just under 2 GiB (32-bit buffer offsets).  The count is odd, so the last
+    block is partial (63 weights) and the last byte carries the pad code;
+    its n2 = 32768 second-level groups are the most the separate offset
+    kernel sums.  An all-zero block and an outlier block sit inside.  The
+    second-level fields are compared in full; the codes and both
+    dequantized outputs on sampled blocks, the partial last block included."""
+    import torch
+    P = (1 << 29) - 1
+    say(f"quantize at the largest accepted size, P = {P}")
+    rng = np.random.default_rng(29)
+    w = rng.standard_normal(P, dtype=np.float32)
+    w *= np.float32(0.02)
+    zb = 4_000_001                       # an all-zero block
+    w[zb * 64:(zb + 1) * 64] = 0.0
+    w[(zb + 1) * 64 + 5] = np.float32(3.0)   # an outlier in the next block
+    state, status = _quantize(w)
+    assert status == 0
+    a = o.first_level_absmax(w)
+    q, s2, off = o.double_quantize(a)
+    ahat = o.reconstruct_absmax(q, s2, off)
+    n1 = a.size
+    assert n1 == 1 << 23 and s2.size == 1 << 15
+    got = state_to_host(state)
+    np.testing.assert_array_equal(got["qabsmax"], q)
+    np.testing.assert_array_equal(got["absmax2"].view(np.uint32), s2.view(np.uint32))
+    assert np.float32(got["offset"]).view(np.uint32) == np.float32(off).view(np.uint32)
+    packed = got["codes_packed"]
+    assert packed.size == (P + 1) // 2
+    # whole blocks: sampled, with the zero and outlier blocks
+    blocks = np.unique(np.concatenate([rng.choice(n1 - 1, 3000, replace=False), [0, zb, zb + 1, n1 - 2]]))
+    vals = w[: (n1 - 1) * 64].reshape(-1, 64)[blocks]
+    codes = o.nf4_codes(vals.ravel(), a[blocks]).reshape(-1, 64)
+    assert np.all(codes[np.searchsorted(blocks, zb)] == 7)
+    exp = ((codes[:, 0::2] << 4) | codes[:, 1::2]).astype(np.uint8)
+    np.testing.assert_array_equal(packed[: (n1 - 1) * 32].reshape(-1, 32)[blocks], exp)
+    # the partial last block: 63 codes, then the pad code 7 in the low nibble
+    tail = w[(n1 - 1) * 64:]
+    assert tail.size == 63
+    tcodes = o.nf4_codes(tail, a[n1 - 1:])
+    texp, tlen = o.pack_nibbles(tcodes)
+    assert tlen == 63 and (packed[-1] & 15) == 7
+    np.testing.assert_array_equal(packed[(n1 - 1) * 32:], texp)
+    # both dequantized outputs on the same blocks and the tail
+    idx = torch.from_numpy((blocks[:, None] * 64 + np.arange(64)[None, :]).ravel()).cuda()
+    for dt in ("fp32", "bf16"):
+        full = qn.nf4_dequantize(state, dt)
+        assert full.numel() == P
+        got_w = host(full[idx].contiguous()).reshape(len(blocks), 64)
+        got_t = host(full[(n1 - 1) * 64:].contiguous())
+        del full
+        exp_w = o.reconstruct_weights(codes.ravel(), np.repeat(ahat[blocks], 64), dt).reshape(-1, 64)
+        exp_t = o.reconstruct_weights(tcodes, np.repeat(ahat[n1 - 1:], 63), dt)
+        np.testing.assert_array_equal(got_w, exp_w)
+        np.testing.assert_array_equal(got_t, exp_t)
+
+
 # -------------------------------------------------------------------- layer
 def _layer_case(M, K, N, r, c, seed):
     rng = np.random.default_rng(seed)
@@ -437,6 +495,61 @@ def test_full_size_mlp7b(matrix):
 @pytest.mark.parametrize("matrix", range(7))
 def test_full_size_block65b(matrix):
     _full_size_check("block65b_m2048", matrix=matrix, row_samples=32, col_groups=2)
+
+
+def test_layer_at_the_largest_accepted_operands():
+    """W, Y and G each just under 2^29 elements, the per-operand limit of
+    32-bit buffer offsets: M = 8192, K = 8192, N = 65472 (1023 blocks of 64,
+    so the last column tile of the forward is partial), r = 64, through
+    dequantize-then-GEMM both ways.  Y and dX on sampled columns (all rows),
+    Z, dA and dB in full."""
+    import torch
+    M, K, N, r, c = 8192, 8192, 65472, 64, 0.25
+    assert K * N < 1 << 29 and M * N < 1 << 29
+    say(f"layer at the largest operands M={M} K={K} N={N} r={r}")
+    rng = np.random.default_rng(31)
+
+    def bf(shape, std):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        x *= np.float32(std)
+        bits = si.to_bf16_bits(x).reshape(shape)
+        return bits, si.bf16_bits_to_f32(bits).reshape(shape)
+
+    W = rng.standard_normal((K, N), dtype=np.float32)
+    W *= np.float32(0.02)
+    state, status = _quantize(W)
+    assert status == 0
+    Xb, Xf = bf((M, K), 1.0)
+    Ab, Af = bf((K, r), 1.0 / r)
+    Bb, Bf = bf((r, N), 0.1)
+    Gb, Gf = bf((M, N), 1.0)
+    X, A, B, G = dev_bf16(Xb), dev_bf16(Ab), dev_bf16(Bb), dev_bf16(Gb)
+    del Xb, Ab, Bb, Gb
+    Y, Z = qn.qlora_linear_fwd(X, state, A, B, c, K, N)
+    dX, dA, dB = qn.qlora_linear_bwd(G, X, Z, state, A, B, c, K, N)
+    groups = np.array([0, 511, N // 64 - 1])
+    ks = np.array([0, 4097, K - 1])
+    Y_s = host(Y[:, torch.from_numpy(np.concatenate([np.arange(g * 64, g * 64 + 64) for g in groups])).cuda()])
+    dX_s = host(dX[:, torch.from_numpy(ks).cuda()])
+    Z_h, dA_h, dB_h = host(Z), host(dA), host(dB)
+    del Y, dX, G
+    ow = OracleWeight(W)
+    del W
+    X64, A64, B64 = Xf.astype(np.float64), Af.astype(np.float64), Bf.astype(np.float64)
+    Zr = X64 @ A64
+    cols, Wc = ow.columns(groups)
+    e_y = rel_err(Y_s, X64 @ Wc.astype(np.float64) + c * (Zr @ B64[:, cols]))
+    G64 = Gf.astype(np.float64)
+    del Gf
+    dZr = c * (G64 @ B64.T)
+    e_dx = rel_err(dX_s, G64 @ ow.rows(ks).astype(np.float64).T + dZr @ A64[ks].T)
+    e_db = rel_err(dB_h, c * (Zr.T @ G64))
+    del G64
+    e_da = rel_err(dA_h, X64.T @ dZr)
+    e_z = rel_err(Z_h, Zr)
+    say(f"errors Y={e_y:.2e} Z={e_z:.2e} dX={e_dx:.2e} dA={e_da:.2e} dB={e_db:.2e}")
+    for v in (e_y, e_z, e_dx, e_da, e_db):
+        assert v <= TOL
 
 
 @pytest.mark.parametrize("M", [1, 8, 16])
