@@ -499,14 +499,14 @@ def test_full_size_block65b(matrix):
 
 def test_layer_at_the_largest_accepted_operands():
     """W, Y and G each just under 2^29 elements, the per-operand limit of
-    32-bit buffer offsets: M = 8192, K = 8192, N = 65472 (1023 blocks of 64,
-    so the last column tile of the forward is partial), r = 64, through
-    dequantize-then-GEMM both ways.  Y and dX on sampled columns (all rows),
-    Z, dA and dB in full."""
+    32-bit buffer offsets: K = 8192, N = 65472 (1023 blocks of 64, so the
+    last column tile is partial), r = 64.  One quantized weight serves the
+    three layer paths: M = 16 (dequant-GEMV), M = 130 (decode inside the
+    GEMM) and M = 8192 (dequantize, then GEMM; Y and G at the limit too).
+    Y and dX on sampled columns (all rows), Z, dA and dB in full."""
     import torch
-    M, K, N, r, c = 8192, 8192, 65472, 64, 0.25
-    assert K * N < 1 << 29 and M * N < 1 << 29
-    say(f"layer at the largest operands M={M} K={K} N={N} r={r}")
+    K, N, r, c = 8192, 65472, 64, 0.25
+    assert K * N < 1 << 29 and 8192 * N < 1 << 29
     rng = np.random.default_rng(31)
 
     def bf(shape, std):
@@ -517,39 +517,46 @@ def test_layer_at_the_largest_accepted_operands():
 
     W = rng.standard_normal((K, N), dtype=np.float32)
     W *= np.float32(0.02)
+    say(f"layer at the largest operands: quantize K={K} N={N}")
     state, status = _quantize(W)
     assert status == 0
-    Xb, Xf = bf((M, K), 1.0)
-    Ab, Af = bf((K, r), 1.0 / r)
-    Bb, Bf = bf((r, N), 0.1)
-    Gb, Gf = bf((M, N), 1.0)
-    X, A, B, G = dev_bf16(Xb), dev_bf16(Ab), dev_bf16(Bb), dev_bf16(Gb)
-    del Xb, Ab, Bb, Gb
-    Y, Z = qn.qlora_linear_fwd(X, state, A, B, c, K, N)
-    dX, dA, dB = qn.qlora_linear_bwd(G, X, Z, state, A, B, c, K, N)
-    groups = np.array([0, 511, N // 64 - 1])
-    ks = np.array([0, 4097, K - 1])
-    Y_s = host(Y[:, torch.from_numpy(np.concatenate([np.arange(g * 64, g * 64 + 64) for g in groups])).cuda()])
-    dX_s = host(dX[:, torch.from_numpy(ks).cuda()])
-    Z_h, dA_h, dB_h = host(Z), host(dA), host(dB)
-    del Y, dX, G
     ow = OracleWeight(W)
     del W
-    X64, A64, B64 = Xf.astype(np.float64), Af.astype(np.float64), Bf.astype(np.float64)
-    Zr = X64 @ A64
+    groups = np.array([0, 511, N // 64 - 1])
+    ks = np.array([0, 4097, K - 1])
     cols, Wc = ow.columns(groups)
-    e_y = rel_err(Y_s, X64 @ Wc.astype(np.float64) + c * (Zr @ B64[:, cols]))
-    G64 = Gf.astype(np.float64)
-    del Gf
-    dZr = c * (G64 @ B64.T)
-    e_dx = rel_err(dX_s, G64 @ ow.rows(ks).astype(np.float64).T + dZr @ A64[ks].T)
-    e_db = rel_err(dB_h, c * (Zr.T @ G64))
-    del G64
-    e_da = rel_err(dA_h, X64.T @ dZr)
-    e_z = rel_err(Z_h, Zr)
-    say(f"errors Y={e_y:.2e} Z={e_z:.2e} dX={e_dx:.2e} dA={e_da:.2e} dB={e_db:.2e}")
-    for v in (e_y, e_z, e_dx, e_da, e_db):
-        assert v <= TOL
+    Wr = ow.rows(ks).astype(np.float64)
+    Ab, Af = bf((K, r), 1.0 / r)
+    Bb, Bf = bf((r, N), 0.1)
+    A, B = dev_bf16(Ab), dev_bf16(Bb)
+    A64, B64 = Af.astype(np.float64), Bf.astype(np.float64)
+    col_idx = torch.from_numpy(cols).cuda()
+    k_idx = torch.from_numpy(ks).cuda()
+    for M in (16, 130, 8192):
+        say(f"layer at the largest operands M={M} K={K} N={N} r={r}")
+        Xb, Xf = bf((M, K), 1.0)
+        Gb, Gf = bf((M, N), 1.0)
+        X, G = dev_bf16(Xb), dev_bf16(Gb)
+        del Xb, Gb
+        Y, Z = qn.qlora_linear_fwd(X, state, A, B, c, K, N)
+        dX, dA, dB = qn.qlora_linear_bwd(G, X, Z, state, A, B, c, K, N)
+        Y_s, dX_s = host(Y[:, col_idx]), host(dX[:, k_idx])
+        Z_h, dA_h, dB_h = host(Z), host(dA), host(dB)
+        del X, G, Y, Z, dX, dA, dB
+        X64 = Xf.astype(np.float64)
+        Zr = X64 @ A64
+        e_y = rel_err(Y_s, X64 @ Wc.astype(np.float64) + c * (Zr @ B64[:, cols]))
+        G64 = Gf.astype(np.float64)
+        del Gf
+        dZr = c * (G64 @ B64.T)
+        e_dx = rel_err(dX_s, G64 @ Wr.T + dZr @ A64[ks].T)
+        e_db = rel_err(dB_h, c * (Zr.T @ G64))
+        del G64
+        e_da = rel_err(dA_h, X64.T @ dZr)
+        e_z = rel_err(Z_h, Zr)
+        say(f"M={M} errors Y={e_y:.2e} Z={e_z:.2e} dX={e_dx:.2e} dA={e_da:.2e} dB={e_db:.2e}")
+        for v in (e_y, e_z, e_dx, e_da, e_db):
+            assert v <= TOL
 
 
 @pytest.mark.parametrize("M", [1, 8, 16])
