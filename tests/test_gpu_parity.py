@@ -295,6 +295,35 @@ def test_layer_fwd_bwd_matches_oracle(M, K, N, r, c):
     assert rel_err(lora, c * Zr @ case["B"]) <= 0.1
 
 
+def _random_layer_shapes(n, seed):
+    """Seeded shapes across the three layer paths (M <= 16, 17..191, >= 192),
+    ragged in every dimension within the layer's rules (K % 8 == 0,
+    N % 64 == 0, r % 8 == 0, r <= 256)."""
+    rng = np.random.default_rng(seed)
+    bands = [(1, 17), (17, 192), (192, 1300)]
+    shapes = []
+    for i in range(n):
+        lo, hi = bands[i % 3]
+        shapes.append((int(rng.integers(lo, hi)), 8 * int(rng.integers(8, 200)), 64 * int(rng.integers(1, 26)),
+                       8 * int(rng.integers(1, 33)), float(rng.choice([0.25, 0.5, 2.0]))))
+    return shapes
+
+
+@pytest.mark.parametrize("M,K,N,r,c", _random_layer_shapes(15, 2026))
+def test_layer_random_shapes_match_oracle(M, K, N, r, c):
+    say(f"layer fwd/bwd, random shape M={M} K={K} N={N} r={r}")
+    case = _layer_case(M, K, N, r, c, seed=M * 13 + N)
+    state, Y, Z, dX, dA, dB = _run_layer(case, M, K, N, r)
+    W_hat = o.dequantize(o.quantize(case["W"]), "bf16").reshape(K, N)
+    Yr, Zr = o.layer_forward(case["X"], W_hat, case["A"], case["B"], c)
+    dXr, dAr, dBr, _ = o.layer_backward(case["G"], case["X"], W_hat, case["A"], case["B"], c)
+    errs = {"Y": rel_err(host(Y), Yr), "Z": rel_err(host(Z), Zr), "dX": rel_err(host(dX), dXr),
+            "dA": rel_err(host(dA), dAr), "dB": rel_err(host(dB), dBr)}
+    say(f"errors {errs}")
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
+
+
 @pytest.mark.parametrize("M", [64, 256])   # fused path; two-pass path (dZ's sum then runs on its own)
 def test_layer_bwd_without_dx(M):
     K, N, r = 256, 128, 16
@@ -352,7 +381,9 @@ def _integer_case(M, K, N, r, seed):
 
 @pytest.mark.parametrize("M,K,N,r", [(16, 256, 256, 8), (96, 320, 384, 16), (520, 256, 320, 16),
                                      (96, 1024, 384, 16), (120, 512, 1280, 16), (300, 640, 1280, 16),
-                                     (700, 1024, 512, 16)])
+                                     (700, 1024, 512, 16),
+                                     # ranks above 64: several 64-wide column chunks of Z, dZ, dA, dB
+                                     (8, 256, 256, 256), (96, 320, 384, 256), (300, 640, 512, 136)])
 def test_layer_exact_integer_case_bit_exact(M, K, N, r):
     say(f"exact-integer layer M={M} K={K} N={N} r={r}")
     case = _integer_case(M, K, N, r, seed=M + N)
