@@ -92,7 +92,38 @@ def test_grouped_matches_oracle(M, K, Ns, r, c):
         off += N
 
 
-@pytest.mark.parametrize("M,K,Ns,r", [(96, 320, [256, 256, 512], 16), (520, 256, [256, 768], 8)])
+def _random_group_shapes(n, seed):
+    """Seeded grouped shapes: 1 to 8 members of 256 to 1280 columns, ranks
+    with g * r <= 256, M across the three layer paths, ragged K."""
+    rng = np.random.default_rng(seed)
+    bands = [(1, 17), (17, 192), (192, 900)]
+    shapes = []
+    for i in range(n):
+        g = int(rng.choice([1, 2, 4, 5, 8]))
+        lo, hi = bands[i % 3]
+        r = 8 * int(rng.integers(1, 256 // (8 * g) + 1))
+        Ns = [256 * int(x) for x in rng.integers(1, 6, size=g)]
+        shapes.append((int(rng.integers(lo, hi)), 8 * int(rng.integers(8, 160)), Ns, r,
+                       float(rng.choice([0.25, 0.5, 2.0]))))
+    return shapes
+
+
+@pytest.mark.parametrize("M,K,Ns,r,c", _random_group_shapes(9, 77))
+def test_grouped_random_shapes_match_oracle(M, K, Ns, r, c):
+    say(f"grouped, random shape M={M} K={K} Ns={Ns} r={r}")
+    case = _group_case(M, K, Ns, r, c, seed=M + 3 * K)
+    Y, Z, dX, dA, dB = _run(case, K, Ns)
+    Yr, Zr, dXr, dAr, dBr = _oracle(case, Ns, r)
+    errs = {"Y": rel_err(host(Y), Yr), "Z": rel_err(host(Z), Zr), "dX": rel_err(host(dX), dXr),
+            "dA": rel_err(host(dA), dAr), "dB": rel_err(host(dB), dBr)}
+    say(f"errors {errs}")
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
+
+
+@pytest.mark.parametrize("M,K,Ns,r", [(96, 320, [256, 256, 512], 16), (520, 256, [256, 768], 8),
+                                       # eight members: the column sums take two launches
+                                       (300, 256, [256, 512, 256, 256, 768, 256, 512, 256], 24)])
 def test_grouped_exact_integer_case_bit_exact(M, K, Ns, r):
     say(f"grouped exact-integer M={M} K={K} Ns={Ns} r={r}")
     case = _group_case(M, K, Ns, r, 0.5, seed=M + 3, integer=True)
