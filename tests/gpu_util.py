@@ -84,3 +84,17 @@ class OracleWeight:
             blocks = k * nb + np.arange(nb)
             out.append(self.weights_of_blocks(blocks).ravel())
         return np.stack(out)
+
+
+def random_layer_shapes(n, seed):
+    """Seeded shapes across the three layer paths (M <= 16, 17..191, >= 192),
+    ragged in every dimension within the layer's rules (K % 8 == 0,
+    N % 64 == 0, r % 8 == 0, r <= 256)."""
+    rng = np.random.default_rng(seed)
+    bands = [(1, 17), (17, 192), (192, 1300)]
+    shapes = []
+    for i in range(n):
+        lo, hi = bands[i % 3]
+        shapes.append((int(rng.integers(lo, hi)), 8 * int(rng.integers(8, 200)), 64 * int(rng.integers(1, 26)),
+                       8 * int(rng.integers(1, 33)), float(rng.choice([0.25, 0.5, 2.0]))))
+    return shapes

@@ -9,7 +9,7 @@ import pytest
 import bit_nf4_quantized_10_amd as qn
 import synth_inputs as si
 from oracle import nf4_oracle as o
-from tests.gpu_util import dev_f32, host, rel_err, say
+from tests.gpu_util import dev_f32, host, random_layer_shapes, rel_err, say
 from tests.test_gpu_parity import TOL, _integer_case, _special_tensors
 
 pytestmark = pytest.mark.gpu
@@ -67,7 +67,8 @@ def _run(case, K, N):
 
 @pytest.mark.parametrize("M,K,N,r,c", [(16, 256, 256, 8, 2.0), (1, 512, 192, 16, 0.5), (130, 264, 320, 24, 0.25),
                                        (600, 264, 320, 24, 0.5), (1024, 512, 768, 64, 0.25),
-                                       (150, 1032, 1600, 16, 0.5), (200, 1032, 1600, 16, 0.5)])
+                                       (150, 1032, 1600, 16, 0.5), (200, 1032, 1600, 16, 0.5)]
+                         + random_layer_shapes(6, 1616))
 def test_f16_layer_matches_oracle(M, K, N, r, c):
     say(f"fp16 layer M={M} K={K} N={N} r={r}")
     case = _f16_case(M, K, N, r, c, seed=M + 5 * N)

@@ -13,7 +13,7 @@ import pytest
 import bit_nf4_quantized_10_amd as qn
 import synth_inputs as si
 from oracle import nf4_oracle as o
-from tests.gpu_util import OracleWeight, dev_bf16, dev_f32, host, rel_err, say, state_to_host
+from tests.gpu_util import OracleWeight, dev_bf16, dev_f32, host, random_layer_shapes, rel_err, say, state_to_host
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
@@ -295,21 +295,7 @@ def test_layer_fwd_bwd_matches_oracle(M, K, N, r, c):
     assert rel_err(lora, c * Zr @ case["B"]) <= 0.1
 
 
-def _random_layer_shapes(n, seed):
-    """Seeded shapes across the three layer paths (M <= 16, 17..191, >= 192),
-    ragged in every dimension within the layer's rules (K % 8 == 0,
-    N % 64 == 0, r % 8 == 0, r <= 256)."""
-    rng = np.random.default_rng(seed)
-    bands = [(1, 17), (17, 192), (192, 1300)]
-    shapes = []
-    for i in range(n):
-        lo, hi = bands[i % 3]
-        shapes.append((int(rng.integers(lo, hi)), 8 * int(rng.integers(8, 200)), 64 * int(rng.integers(1, 26)),
-                       8 * int(rng.integers(1, 33)), float(rng.choice([0.25, 0.5, 2.0]))))
-    return shapes
-
-
-@pytest.mark.parametrize("M,K,N,r,c", _random_layer_shapes(15, 2026))
+@pytest.mark.parametrize("M,K,N,r,c", random_layer_shapes(15, 2026))
 def test_layer_random_shapes_match_oracle(M, K, N, r, c):
     say(f"layer fwd/bwd, random shape M={M} K={K} N={N} r={r}")
     case = _layer_case(M, K, N, r, c, seed=M * 13 + N)
