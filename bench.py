@@ -192,15 +192,24 @@ def main():
     print(json.dumps(line))
 
 
+def _flush_cache(flush):
+    """Leave the 256 MB Infinity Cache cold and clean: overwrite it with a
+    512 MB buffer, then read that buffer back, so that the timed call finds
+    none of its inputs cached and has no dirty lines of the flush itself to
+    write back (a write-only flush charges the next call with up to 256 MB
+    of write-backs)."""
+    flush.add_(1)
+    flush.sum()
+
+
 def _time_kernel(qn, torch, name, fn, reps, flush=None):
     """Average duration of kernel `name` over `reps` calls of fn, timed by the
-    library's HIP events on the launch stream; with `flush`, the 256 MB
-    Infinity Cache is overwritten before every call (outside the timed
-    kernel)."""
+    library's HIP events on the launch stream; with `flush`, the cache is
+    flushed before every call (outside the timed kernel)."""
     qn.qlora_timer_enable(name, True)
     for i in range(reps):
         if flush is not None:
-            flush.add_(1)
+            _flush_cache(flush)
         fn(i)
     torch.cuda.synchronize()
     ms, n = qn.qlora_timer_read(name)
@@ -213,7 +222,7 @@ def _time_calls(torch, fn, reps, flush):
     after a cache flush."""
     total = 0.0
     for i in range(reps):
-        flush.add_(1)
+        _flush_cache(flush)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         fn(i)
@@ -224,8 +233,9 @@ def _time_calls(torch, fn, reps, flush):
 
 
 def bench_components(torch, qn, si, dev, sets, outs, qws, status):
-    """The memory-bound paths, each call preceded by a write of a 512 MB buffer
-    so that no input or output is served from the Infinity Cache."""
+    """The memory-bound paths, each call preceded by a cache flush (a 512 MB
+    buffer written, then read) so that no input or output is served from the
+    Infinity Cache."""
     res = {}
     flush = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
     P = sets[0]["W"].numel()
@@ -252,14 +262,32 @@ def bench_components(torch, qn, si, dev, sets, outs, qws, status):
     K, N, r, c = d["K"], d["N"], d["r"], d["c"]
     Pg = K * N
     states = []
+    Wg = torch.from_numpy(d["W"]).to(dev).reshape(-1)
     for i in range(2):
-        W = torch.from_numpy(d["W"]).to(dev).reshape(-1)
-        st, _ = qn.nf4_quantize(W)
+        st, _ = qn.nf4_quantize(Wg)
         states.append(st)
-        del W
+    # quantize and bf16 dequantize at this size too (721 MB of fp32 in, 360 MB of bf16 out)
+    sg = qn.nf4_sizes(Pg)
+    qws_g = torch.empty(sg["quant_workspace_bytes"], dtype=torch.uint8, device=dev)
+    st_g = qn.empty_state(Pg, dev)
+    qfn_g = lambda i: qn.nf4_quantize(Wg, st_g, qws_g, status)
+    qfn_g(0)
+    qms_g = _time_calls(torch, qfn_g, 5, flush)
+    qbytes_g = 4 * Pg + (Pg + 1) // 2 + sg["n1"] + 4 * sg["n2"] + 4
+    res["quantize_decode65b"] = {"bytes": qbytes_g, "call_ms": round(qms_g, 4),
+                                 "GBps_call": round(qbytes_g / (qms_g * 1e-3) / 1e9, 1),
+                                 "frac_hbm_call": round(qbytes_g / (qms_g * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del Wg, qws_g, st_g
+    out_g = torch.empty(Pg, dtype=torch.bfloat16, device=dev)
+    dms_g = _time_kernel(qn, torch, "dequant",
+                         lambda i: qn.nf4_dequantize(states[i % 2], "bf16", out=out_g), 8, flush)
+    dbytes_g = (Pg + 1) // 2 + sg["n1"] + 4 * sg["n2"] + 4 + 2 * Pg
+    res["dequant_bf16_decode65b"] = {"bytes": dbytes_g, "ms": round(dms_g, 4),
+                                     "GBps": round(dbytes_g / (dms_g * 1e-3) / 1e9, 1),
+                                     "frac_hbm": round(dbytes_g / (dms_g * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del out_g
     bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
     A, B = bf(d["A_bits"]), bf(d["B_bits"])
-    sg = qn.nf4_sizes(Pg)
     gemv = {}
     for M in (1, 8, 16):
         X = bf(d["X_bits"][:M])
