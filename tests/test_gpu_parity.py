@@ -596,6 +596,69 @@ def test_full_size_decode65b_gemv(M):
     assert e <= TOL and rel_err(host(Z), Zr) <= TOL
 
 
+@pytest.mark.parametrize("M", [8, 600])   # dequant-GEMV; dequantize-then-GEMM
+def test_quantize_and_layer_step_in_hip_graph_replays_bit_exact(M):
+    """The whole step (quantize, dequantize to bf16 and fp32, forward,
+    backward) captured in one HIP graph with caller-owned buffers.  The weight
+    has 2056 second-level groups, so the quantize also runs its separate
+    offset kernel.  Every replay (state and outputs cleared eagerly before it)
+    must reproduce the eager bytes of every output."""
+    import torch
+    K, N, r = 2048, 16448, 16
+    rng = np.random.default_rng(90 + M)
+    W = dev_f32((rng.standard_normal((K, N)) * 0.02).astype(np.float32))
+    Xb, _ = si.bf16_normal((M, K), 1.0, 91)
+    Ab, _ = si.bf16_normal((K, r), 1.0 / r, 92)
+    Bb, _ = si.bf16_normal((r, N), 0.1, 93)
+    Gb, _ = si.bf16_normal((M, N), 1.0, 94)
+    X, A, B, G = dev_bf16(Xb), dev_bf16(Ab), dev_bf16(Bb), dev_bf16(Gb)
+    P = K * N
+    sz = qn.nf4_sizes(P)
+    assert sz["n2"] > 2048
+    say(f"quantize + layer step captured in a HIP graph, M={M} K={K} N={N}")
+    state = qn.empty_state(P, "cuda")
+    qws = torch.empty(sz["quant_workspace_bytes"], dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fw, bw = qn.qlora_workspace_bytes(M, K, N, r)
+    ws = torch.empty(max(fw, bw, 256), dtype=torch.uint8, device="cuda")
+    W16 = torch.empty(P, dtype=torch.bfloat16, device="cuda")
+    W32 = torch.empty(P, dtype=torch.float32, device="cuda")
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty(M, r, dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    dA = torch.empty(K, r, dtype=torch.float32, device="cuda")
+    dB = torch.empty(r, N, dtype=torch.float32, device="cuda")
+    outs = (state.codes, state.qabsmax, state.absmax2, state.offset, status, W16, W32, Y, Z, dX, dA, dB)
+
+    def step():
+        qn.nf4_quantize(W, state, qws, status)
+        qn.nf4_dequantize(state, "bf16", out=W16, status=status)
+        qn.nf4_dequantize(state, "fp32", out=W32, status=status)
+        qn.qlora_linear_fwd(X, state, A, B, 0.5, K, N, Y, Z, ws)
+        qn.qlora_linear_bwd(G, X, Z, state, A, B, 0.5, K, N, True, dX, dA, dB, ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                      # eager reference (also configures the kernels)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    raw = lambda t: t.contiguous().view(torch.uint8).cpu().numpy().tobytes()
+    ref = [raw(t) for t in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in outs:
+            t.zero_()               # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [raw(t) for t in outs]
+        assert got == ref, f"replay {rep}: " + ", ".join(str(i) for i, (a, b) in enumerate(zip(got, ref)) if a != b)
+
+
 @pytest.mark.parametrize("M", [8, 130, 600])   # dequant-GEMV, fused kernel, dequantize-then-GEMM
 def test_layer_in_hip_graph_replays_bit_exact(M):
     """Every launch of a call goes on the caller's stream and nothing is
