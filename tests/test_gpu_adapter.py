@@ -186,3 +186,65 @@ def test_training_step_lowers_the_loss():
     l1, _, _ = loss_and_grad()
     assert l1 < l0
     assert np.array_equal(host(st.codes), codes_before)
+
+
+@pytest.mark.parametrize("M", [8, 300])   # dequant-GEMV; dequantize-then-GEMM
+def test_training_step_in_hip_graph_replays_eager_steps(M):
+    """One training step (forward, backward, SGD on the adapter through fp32
+    masters, then the merge of the updated adapter) captured once in a HIP
+    graph.  Replaying it three times must reproduce three eager steps bit for
+    bit: the adapter changes in place, so every replay starts from the
+    previous one's result."""
+    import torch
+    K, N, r, c, lr = 512, 384, 16, 0.5, 0.05
+    say(f"training step captured in a HIP graph, M={M}")
+    rng = np.random.default_rng(300 + M)
+    state = _quantize((rng.standard_normal((K, N)) * 0.02).astype(np.float32))
+    Xb, _ = si.bf16_normal((M, K), 1.0, 301)
+    Gb, _ = si.bf16_normal((M, N), 1.0, 302)
+    A0, _, B0, _ = _adapter(K, N, r, "bf16", 303)
+    X, G = dev_bf16(Xb), dev_bf16(Gb)
+    A, B = A0.clone(), B0.clone()
+    Am, Bm = A0.float(), B0.float()
+    fw, bw = qn.qlora_workspace_bytes(M, K, N, r)
+    ws = torch.empty(max(fw, bw, 256), dtype=torch.uint8, device="cuda")
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty(M, r, dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    dA = torch.empty(K, r, dtype=torch.float32, device="cuda")
+    dB = torch.empty(r, N, dtype=torch.float32, device="cuda")
+    Wm = torch.empty(K * N, dtype=torch.float32, device="cuda")
+    tracked = (Y, Z, dX, dA, dB, A, B, Am, Bm, Wm)
+
+    def step():
+        qn.qlora_linear_fwd(X, state, A, B, c, K, N, Y, Z, ws)
+        qn.qlora_linear_bwd(G, X, Z, state, A, B, c, K, N, True, dX, dA, dB, ws)
+        qn.qlora_sgd_step(A, B, dA, dB, lr, Am, Bm)
+        qn.qlora_merge(state, A, B, c, K, N, out=Wm)
+
+    raw = lambda t: t.contiguous().view(torch.uint8).cpu().numpy().tobytes()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    eager = []
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            step()
+            s.synchronize()
+            eager.append([raw(t) for t in tracked])
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert eager[0] != eager[1]   # the adapter really moves
+    A.copy_(A0); B.copy_(B0); Am.copy_(A0.float()); Bm.copy_(B0.float())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (Y, Z, dX, dA, dB, Wm):
+            t.zero_()               # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [raw(t) for t in tracked]
+        assert got == eager[rep], f"replay {rep}: " + ", ".join(
+            str(i) for i, (a, b) in enumerate(zip(got, eager[rep])) if a != b)

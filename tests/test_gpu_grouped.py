@@ -184,3 +184,52 @@ def test_grouped_full_size_qkv_7b_sampled():
     assert rel_err(host(dA), Xf.T @ dZr) <= TOL
     dBr = np.hstack([c * (Zr[:, i * r:(i + 1) * r].T @ Gf[:, 4096 * i:4096 * (i + 1)]) for i in range(3)])
     assert rel_err(host(dB), dBr) <= TOL
+
+
+@pytest.mark.parametrize("M", [16, 600])
+def test_grouped_in_hip_graph_replays_bit_exact(M):
+    """Grouped forward + backward with caller-owned buffers captured in a HIP
+    graph; each replay (outputs cleared eagerly before it) reproduces the
+    eager bytes."""
+    import torch
+    K, Ns, r = 512, [256, 768, 512, 256, 512], 16
+    say(f"grouped step captured in a HIP graph, M={M} Ns={Ns}")
+    case = _group_case(M, K, Ns, r, 0.5, seed=500 + M)
+    states = []
+    for W in case["Ws"]:
+        st, status = qn.nf4_quantize(dev_f32(W))
+        assert qn.nf4_status_read(status) == 0
+        states.append(st)
+    X, A, B, G = (dev_bf16(case[k]) for k in ("Xb", "Ab", "Bb", "Gb"))
+    g, Ntot = len(Ns), sum(Ns)
+    fw, bw = qn.qlora_grouped_workspace_bytes(M, K, Ns, r)
+    ws = torch.empty(max(fw, bw, 256), dtype=torch.uint8, device="cuda")
+    Y = torch.empty(M, Ntot, dtype=torch.bfloat16, device="cuda")
+    Z = torch.empty(M, g * r, dtype=torch.bfloat16, device="cuda")
+    dX = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    dA = torch.empty(K, g * r, dtype=torch.float32, device="cuda")
+    dB = torch.empty(r, Ntot, dtype=torch.float32, device="cuda")
+    outs = (Y, Z, dX, dA, dB)
+
+    def step():
+        qn.qlora_grouped_fwd(X, states, A, B, 0.5, K, Ns, Y, Z, ws)
+        qn.qlora_grouped_bwd(G, X, Z, states, A, B, 0.5, K, Ns, True, dX, dA, dB, ws)
+
+    raw = lambda t: t.contiguous().view(torch.uint8).cpu().numpy().tobytes()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref = [raw(t) for t in outs]
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        step()
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        assert [raw(t) for t in outs] == ref, f"replay {rep}"
