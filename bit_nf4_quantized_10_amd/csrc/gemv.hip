@@ -414,11 +414,15 @@ __global__ __launch_bounds__(64) void gemv_finish_kernel(const float* __restrict
 
 }  // namespace
 
+#ifndef QN_GV_WAVES
+#define QN_GV_WAVES 1400
+#endif
+
 void plan_gemv(int64_t M, int64_t K, int64_t N, int64_t r, SkinnyPlan* p_) {
   SkinnyPlan& p = *p_;
   // 4 waves x rows_per_wave rows per workgroup, ~1400 waves in total
   const int64_t slabs = cdiv(N, kGvCols);
-  const int64_t groups = cdiv(1400, slabs * kGvWaves);
+  const int64_t groups = cdiv(QN_GV_WAVES, slabs * kGvWaves);
   int64_t rpw = round_up(cdiv(K, groups * kGvWaves), 32);
   if (rpw < 64) rpw = 64;
   p.gv_rows_per_wave = rpw;
