@@ -499,7 +499,14 @@ __global__ __launch_bounds__(256) void nf4_dequant_t_kernel(NF4View W, int64_t K
   const int t = threadIdx.x;
   if (t < 16) s_lut[t] = kNF4[t];
   __syncthreads();
-  const int64_t k0 = static_cast<int64_t>(blockIdx.y) * 64, n0 = static_cast<int64_t>(blockIdx.x) * 128;
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id.  Within each
+  // complete group of 16 ids, tiles 2m and 2m+1 (neighbours along n, whose
+  // 64-byte code rows share 128-byte lines) go to ids q and q + 8, i.e. to
+  // one XCD, so that its L2 serves the second half of every line.
+  const int64_t nx = gridDim.x, L = static_cast<int64_t>(blockIdx.y) * nx + blockIdx.x;
+  int64_t id = L;
+  if ((L | 15) < nx * ky) id = (L & ~static_cast<int64_t>(15)) + ((L & 7) << 1) + ((L >> 3) & 1);
+  const int64_t k0 = (id / nx) * 64, n0 = (id % nx) * 128;
   const bool single = W.absmax != nullptr;   // no second level: â = absmax[block]
   const float off = single ? 0.0f : W.offset[0];
   {
