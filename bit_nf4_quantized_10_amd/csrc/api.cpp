@@ -54,14 +54,16 @@ struct TimerSlot {
 std::mutex g_timer_mu;
 TimerSlot g_timers[QK_NUM_KERNELS];
 
+// Events a timer slot holds once enabled: enough for 4096 timed launches
+// between two reads.  They are created by qlora_timer_enable, never on the
+// launch path; a launch that finds the pool empty is simply not timed (it
+// is then not counted either, so the average stays right).
+constexpr size_t kTimerEvents = 8192;
+
 hipEvent_t take_event(TimerSlot& s) {
-  if (!s.pool.empty()) {
-    hipEvent_t e = s.pool.back();
-    s.pool.pop_back();
-    return e;
-  }
-  hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (s.pool.empty()) return nullptr;
+  hipEvent_t e = s.pool.back();
+  s.pool.pop_back();
   return e;
 }
 
@@ -74,8 +76,8 @@ Timer::Timer(int kernel_id, hipStream_t stream, bool packet)
   std::lock_guard<std::mutex> lk(g_timer_mu);
   TimerSlot& s = g_timers[id_];
   if (!s.enabled) return;
+  if (s.pool.size() < 2) return;
   hipEvent_t a = take_event(s), b = take_event(s);
-  if (a == nullptr || b == nullptr) return;
   s.pending.emplace_back(a, b);
   if (packet) {
     start_event_ = a;
@@ -186,8 +188,11 @@ int qlora_linear_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t*
                              workspace_bytes, stream);
 }
 
+// Each member's rank must itself be a multiple of 8: the kernels move Z,
+// (c B)ᵀ and the dB partials in 8-element chunks along the concatenated
+// rank axis, and a chunk must never straddle two members.
 static bool grouped_shape_ok(int64_t M, int64_t K, int g, const int64_t* N, int64_t r, int64_t* Ntot) {
-  if (g < 1 || g > qn::kMaxGroupMembers || N == nullptr || r < 1) return false;
+  if (g < 1 || g > qn::kMaxGroupMembers || N == nullptr || r < 8 || r % 8 != 0) return false;
   int64_t tot = 0;
   for (int i = 0; i < g; ++i) {
     if (N[i] < 256 || N[i] % 256 != 0 || N[i] > (int64_t(1) << 24)) return false;
@@ -293,7 +298,18 @@ int nf4_status_read(const int32_t* status, int32_t* host_value, void* stream) {
 int qlora_timer_enable(int kernel_id, int enable) {
   if (kernel_id < 0 || kernel_id >= QK_NUM_KERNELS) return NF4_EINVAL;
   std::lock_guard<std::mutex> lk(g_timer_mu);
-  g_timers[kernel_id].enabled = enable != 0;
+  TimerSlot& s = g_timers[kernel_id];
+  if (enable != 0) {
+    // the slot's events are created here, once; they stay with the slot
+    // (the library's only held state, and only once a timer was enabled)
+    const size_t have = s.pool.size() + 2 * s.pending.size();
+    for (size_t i = have; i < kTimerEvents; ++i) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return NF4_EHIP;
+      s.pool.push_back(e);
+    }
+  }
+  s.enabled = enable != 0;
   return NF4_OK;
 }
 

@@ -710,13 +710,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
 template <class T, bool kForward, bool kKTail, bool kSplit>
 hipError_t launch_big_t(const BigArgs& a, hipStream_t stream, const Timer& tm) {
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_big_kernel<T, kForward, kKTail, kSplit>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  // raised once per process; the initialisation of a function-local static
+  // is thread-safe, so concurrent first calls do not race
+  static const hipError_t lds_limit = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_big_kernel<T, kForward, kKTail, kSplit>),
+                                                          hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (lds_limit != hipSuccess) return lds_limit;
   const int64_t cols = kForward ? a.N : a.K, red = kForward ? a.K : a.N;
   const unsigned zs = kSplit ? static_cast<unsigned>((red + a.k_per - 1) / a.k_per) : 1u;
   dim3 grid(static_cast<unsigned>((cols + kBN - 1) / kBN), static_cast<unsigned>((a.M + kBM - 1) / kBM), zs);
@@ -727,13 +725,11 @@ hipError_t launch_big_t(const BigArgs& a, hipStream_t stream, const Timer& tm) {
 
 template <class T, bool kForward, bool kKTail, bool kSplit>
 hipError_t launch_dense_t(const BigArgs& a, hipStream_t stream, const Timer& tm) {
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_dense_kernel<T, kForward, kKTail, kSplit>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kDenseLds);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  // raised once per process; the initialisation of a function-local static
+  // is thread-safe, so concurrent first calls do not race
+  static const hipError_t lds_limit = hipFuncSetAttribute(reinterpret_cast<const void*>(&qlora_dense_kernel<T, kForward, kKTail, kSplit>),
+                                                          hipFuncAttributeMaxDynamicSharedMemorySize, kDenseLds);
+  if (lds_limit != hipSuccess) return lds_limit;
   const int64_t cols = kForward ? a.N : a.K, red = kForward ? a.K : a.N;
   const unsigned zs = kSplit ? static_cast<unsigned>((red + a.k_per - 1) / a.k_per) : 1u;
   dim3 grid(static_cast<unsigned>((cols + kBN - 1) / kBN), static_cast<unsigned>((a.M + kBM - 1) / kBM), zs);

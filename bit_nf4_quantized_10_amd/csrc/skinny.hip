@@ -343,13 +343,11 @@ hipError_t launch_reduce(const RdJob& ja, const RdJob* jb, hipStream_t stream) {
 
 template <class T>
 hipError_t rowsum_launch_t(const RsArgs& a, int64_t splits, hipStream_t stream) {
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&rowsum_kernel<T>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kRsLds);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  // raised once per process; the initialisation of a function-local static
+  // is thread-safe, so concurrent first calls do not race
+  static const hipError_t lds_limit = hipFuncSetAttribute(reinterpret_cast<const void*>(&rowsum_kernel<T>),
+                                                          hipFuncAttributeMaxDynamicSharedMemorySize, kRsLds);
+  if (lds_limit != hipSuccess) return lds_limit;
   hipLaunchKernelGGL(rowsum_kernel<T>, dim3(static_cast<unsigned>(a.row_blocks * a.j_chunks * splits)), dim3(256),
                      kRsLds, stream, a);
   return hipGetLastError();
@@ -364,13 +362,11 @@ hipError_t launch_rowsum(const uint16_t* act, const uint16_t* wt, int64_t M, int
 
 template <class T>
 hipError_t colsum_launch_t(const CsJobs& jobs, int64_t M, hipStream_t stream) {
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&colsum_kernel<T>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kCsLds);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  // raised once per process; the initialisation of a function-local static
+  // is thread-safe, so concurrent first calls do not race
+  static const hipError_t lds_limit = hipFuncSetAttribute(reinterpret_cast<const void*>(&colsum_kernel<T>),
+                                                          hipFuncAttributeMaxDynamicSharedMemorySize, kCsLds);
+  if (lds_limit != hipSuccess) return lds_limit;
   int64_t blocks = 0;
   for (int i = 0; i < kCsJobs; ++i) blocks += jobs.j[i].nblk;
   hipLaunchKernelGGL(colsum_kernel<T>, dim3(static_cast<unsigned>(blocks)), dim3(256), kCsLds, stream, jobs, M);

@@ -197,7 +197,8 @@ int qlora_sgd_step_dt(int param_dtype, int64_t K, int64_t N, int64_t r, uint16_t
  *   Y = [Y_1 .. Y_g] (M x Ntot, Ntot = sum N[i]),  Z = [Z_1 .. Z_g] (M x g r),
  *   A = [A_1 .. A_g] (K x g r),                   B = [B_1 .. B_g] (r x Ntot),
  * and Y_i = X Ŵ_i + c Z_i B_i, Z_i = X A_i, i.e. the layer above per member,
- * with X read once.  Every N[i] must be a multiple of 256; the concatenated
+ * with X read once.  Every N[i] must be a multiple of 256 and r a multiple
+ * of 8 (so no 8-element chunk of Z, A or B straddles two members); the concatenated
  * shape (M, K, Ntot, g r) must meet qlora_linear_fwd's requirements; W is a
  * host array of g states.  All members are dequantized to a bf16 workspace
  * and multiplied by one dense GEMM for any M.  Host only: */
@@ -253,7 +254,12 @@ int nf4_status_read(const int32_t* status, int32_t* host_value, void* stream);
  * stream around every launch of kernel `kernel_id`.  qlora_timer_read
  * waits for the recorded events, returns the summed elapsed milliseconds
  * and the launch count since the last read, and resets them.  Host-side
- * only; meant for benchmarks (it adds two event records per launch). */
+ * only; meant for benchmarks (it adds two event records per launch).
+ * qlora_timer_enable creates the slot's pool of 8192 events the first time
+ * (NF4_EHIP if that fails); the pool is the library's only held state and
+ * stays until the process ends.  Launches never create events: beyond 4096
+ * launches between two reads, further launches are neither timed nor
+ * counted. */
 int qlora_timer_enable(int kernel_id, int enable);
 int qlora_timer_read(int kernel_id, double* total_ms, int64_t* launches);
 

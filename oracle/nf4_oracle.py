@@ -68,6 +68,9 @@ Parity status of each function (see the tests under tests/):
   power-of-two rank-1 increments).  sgd_step: pinned by the P1 update of the
   worked layer example (a, b after one step; the loss falls).
   tree_offset: pinned by exactly-summable inputs and the fsum error bound.
+  reconstruct_absmax: pinned by exact rational arithmetic, both roundings of
+  R4 taken on the exact values, on offsets comparable to the decoded values
+  (a one-rounding or unrounded-table variant fails that pin).
   linear_absmax_table / linear_absmax_codes: pinned by the P2 §6 example,
   exact rational brute force and special cases.  The CHOICE of this codebook
   for the second level (R3) is a reading: "parity unpinned" by the pages for
@@ -155,33 +158,33 @@ def nf4_codes(w32: np.ndarray, a32: np.ndarray, chunk: int = 1 << 18) -> np.ndar
 
 
 def pack_nibbles(codes) -> tuple[np.ndarray, int]:
-    """Two codes per byte, the first in the high nibble; an odd count is padded
-    with code 7; the logical length is returned beside the payload
-    ([P1] "从 NF4 索引打包成字节")."""
-    codes = np.asarray(codes)
-    if codes.size and (codes.min() < 0 or codes.max() > 15):
-        raise ValueError("4-bit integer codes required")
-    length = int(codes.size)
-    c = codes.astype(np.uint8)
-    if length % 2:
-        c = np.append(c, np.uint8(7))
-    payload = ((c[0::2] << 4) | c[1::2]).astype(np.uint8)
-    return payload, length
+    """Byte stream of a code sequence ([P1] "从 NF4 索引打包成字节"): code
+    2i goes to the high nibble of byte i and code 2i+1 to its low nibble; a
+    sequence of odd length gets code 7 as its last low nibble.  Returns the
+    bytes and the number of codes they stand for."""
+    seq = np.asarray(codes).ravel()
+    n = int(seq.size)
+    if n and not (0 <= int(seq.min()) and int(seq.max()) <= 15):
+        raise ValueError(f"codes must lie in 0..15, got {int(seq.min())}..{int(seq.max())}")
+    even = np.full(n + (n & 1), 7, dtype=np.uint8)
+    even[:n] = seq
+    hi, lo = even[0::2], even[1::2]
+    return (hi * np.uint8(16) + lo).astype(np.uint8), n
 
 
 def unpack_nibbles(payload, length: int) -> np.ndarray:
-    """Inverse of pack_nibbles with the page's checks: payload size must be
-    (length+1)//2 and an odd length must end in pad code 7
-    ([P1] "从 NF4 索引打包成字节")."""
-    payload = np.asarray(payload, dtype=np.uint8).ravel()
-    if length < 0 or payload.size != (length + 1) // 2:
-        raise ValueError("payload and logical length disagree")
-    if length % 2 and (payload[-1] & 15) != 7:
-        raise ValueError("unexpected padding code")
-    codes = np.empty(payload.size * 2, dtype=np.uint8)
-    codes[0::2] = payload >> 4
-    codes[1::2] = payload & 15
-    return codes[:length]
+    """Code sequence of a byte stream, the inverse of pack_nibbles, with the
+    two checks the page makes when reading codes back: the stream holds
+    exactly ceil(length / 2) bytes, and the nibble after an odd-length
+    sequence is the pad code 7 ([P1] "从 NF4 索引打包成字节")."""
+    data = np.asarray(payload, dtype=np.uint8).ravel()
+    need = (length + 1) // 2
+    if length < 0 or data.size != need:
+        raise ValueError(f"{data.size} bytes cannot hold {length} codes (expected {need})")
+    if length & 1 and int(data[-1]) % 16 != 7:
+        raise ValueError(f"pad nibble is {int(data[-1]) % 16}, expected 7")
+    both = np.stack([data // 16, data % 16], axis=1).ravel()
+    return both[:length].astype(np.uint8)
 
 
 def _stride_halving(x: np.ndarray) -> np.ndarray:

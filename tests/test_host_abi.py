@@ -170,3 +170,23 @@ def test_grouped_entry_points_reject_bad_arguments():
     Ns = (i64 * 2)(256, 256)
     assert L.qlora_grouped_fwd(8, 256, 2, Ns, 8, 0x100, states, 0x200, 0x300, ctypes.c_float(1.0), 0x400, 0x500,
                                0x10000, 1 << 30, None) == qn.NF4_EINVAL
+
+
+@pytest.mark.parametrize("g,r", [(2, 4), (4, 2), (8, 1), (2, 12), (3, 20)])
+def test_grouped_member_rank_must_be_a_multiple_of_8(g, r):
+    """Per-member ranks that are not multiples of 8 are rejected by all three
+    grouped calls even when g r is: the kernels move the concatenated Z, A,
+    (c B)ᵀ and dB partials in 8-element chunks, which would then mix two
+    members."""
+    L = qn.lib()
+    i64 = ctypes.c_int64
+    K = 256
+    Ns = (i64 * g)(*([256] * g))
+    f, b = i64(), i64()
+    assert L.qlora_grouped_workspace_bytes(64, K, g, Ns, 8, ctypes.byref(f), ctypes.byref(b)) == qn.NF4_OK
+    assert L.qlora_grouped_workspace_bytes(64, K, g, Ns, r, ctypes.byref(f), ctypes.byref(b)) == qn.NF4_EINVAL
+    states = (qn._State * g)(*[qn._State(K * 256, 0x1000, 0x2000, 0x3000, 0x4000) for _ in range(g)])
+    assert L.qlora_grouped_fwd(64, K, g, Ns, r, 0x100, states, 0x200, 0x300, ctypes.c_float(1.0), 0x400, 0x500,
+                               0x10000, 1 << 30, None) == qn.NF4_EINVAL
+    assert L.qlora_grouped_bwd(64, K, g, Ns, r, 0x100, 0x100, 0x500, states, 0x200, 0x300, ctypes.c_float(1.0),
+                               None, 0x600, 0x700, 0x10000, 1 << 30, None) == qn.NF4_EINVAL

@@ -493,6 +493,52 @@ def test_double_quantize_error_bound(seed):
         assert abs(int(q[g * 256 + i])) == 127
 
 
+def _reconstruct_absmax_pin_holds(reconstruct, seed: int = 0) -> bool:
+    """The exact-rational pin of the scale reconstruction for a given
+    function: â = fl32(fl32(Q[q] s2) + offset), each rounding taken on the
+    exact rational value ([P1] "Double Quantization 压缩的是 Scale": decode
+    the second level, then add the offset back; reading R4).  The inputs mix
+    offsets of the size of the decoded values, so that one rounding instead
+    of two, or an unrounded table value, changes many results."""
+    rng = np.random.default_rng(100 + seed)
+    n1 = 256 * 6 + 17
+    q = rng.integers(-127, 128, n1).astype(np.int8)
+    s2 = (np.abs(rng.standard_normal(7)) * 0.05 + 1e-3).astype(np.float32)
+    table = o.linear_absmax_table(127)
+    for off in (np.float32(0.031), np.float32(-0.0173), np.float32(rng.uniform(0.001, 0.2))):
+        got = reconstruct(q, s2, off)
+        for i in range(n1):
+            prod = exact_round_f32(Fraction(float(table[int(q[i]) + 127])) * Fraction(float(s2[i // 256])))
+            if got[i] != exact_round_f32(Fraction(float(prod)) + Fraction(float(off))):
+                return False
+    return True
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_reconstruct_absmax_two_exact_roundings(seed):
+    assert _reconstruct_absmax_pin_holds(o.reconstruct_absmax, seed)
+
+
+def test_reconstruct_absmax_pin_catches_one_rounding():
+    """Plausible mistakes in the scale reconstruction fail the exact pin:
+    the whole expression in float64 rounded once (a fused multiply-add),
+    and the code value q/127 used unrounded."""
+    table = o.linear_absmax_table(127)
+
+    def one_rounding(q, s2, off):
+        qv = table[np.asarray(q, np.int64) + 127].astype(np.float64)
+        s = np.repeat(np.asarray(s2, np.float64), 256)[: qv.size]
+        return (qv * s + np.float64(off)).astype(np.float32)
+
+    def unrounded_code(q, s2, off):
+        qv = np.asarray(q, np.int64) / 127.0
+        s = np.repeat(np.asarray(s2, np.float64), 256)[: qv.size]
+        return ((qv * s).astype(np.float32) + np.float32(off)).astype(np.float32)
+
+    for bad in (one_rounding, unrounded_code):
+        assert not _reconstruct_absmax_pin_holds(bad), bad.__name__
+
+
 # ------------------------------------------------------------------ bf16 (R5)
 def test_bf16_round_matches_exact_rne():
     rng = np.random.default_rng(9)
@@ -586,6 +632,14 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     assert _merge_pins_hold(orig_merge)
     for bad in (merge_raw_w, merge_no_c, merge_flipped):
         assert not _merge_pins_hold(bad), bad.__name__
+    # 5. the scale reconstruction rounded once (float64, then one fl32)
+    def reconstruct_once(q, s2, off):
+        qv = o.linear_absmax_table(127)[np.asarray(q, np.int64) + 127].astype(np.float64)
+        s = np.repeat(np.asarray(s2, np.float64), 256)[: qv.size]
+        return (qv * s + np.float64(off)).astype(np.float32)
+
+    monkeypatch.setattr(o, "reconstruct_absmax", reconstruct_once)
+    assert not _reconstruct_absmax_pin_holds(o.reconstruct_absmax)
 
 
 def _merge_pins_hold(merge) -> bool:
