@@ -1,19 +1,22 @@
 """Benchmark of the QLoRA NF4 linear layer on one MI355X.
 
-One step = nf4_quantize(W) -> qlora_linear_fwd -> qlora_linear_bwd on the
-7B-attention-shaped projection (M = 4096 tokens, K = N = 4096, r = 64,
-alpha = 16), inputs resident in HBM.  `value` is the forward+backward
-algorithmic TFLOP/s of the whole step (the quantize time is inside the step,
-its flops are not counted).  Three input sets are rotated so that the 256 MB
-Infinity Cache cannot hold a step's inputs from the previous step.
+Headline workload: the seven linears of one 65B-shaped transformer block on
+one GPU (q, k, v, o 8192 x 8192; gate, up 8192 x 22016; down 22016 x 8192;
+809.5M weights), M = 2048 tokens, LoRA r = 64, alpha = 16.  One step =
+nf4_quantize of all seven fp32 weights, then qlora_linear_fwd and
+qlora_linear_bwd of every linear, one after another on one stream, inputs
+resident in HBM.  `value` is the forward+backward algorithmic TFLOP/s of the
+whole step (the quantize time is inside the step, its bytes are not counted).
 
-Also reported (not part of `value`): the roofline of the dominant kernel
-(timed live with HIP events on the launch stream), the memory-bound paths in
-GB/s (quantize, bf16 dequantize, small-M dequant-GEMV at M = 1/8/16 on the
-65B MLP shape), the 7B MLP set and a 65B block's seven linears (quantize all,
-then fwd+bwd of all), and the CPU oracle timed on a bounded sample.
+Also reported (not part of `value`): the roofline of the dominant kernel (the
+gate/up forward GEMM, timed live with HIP events on the launch stream, alone
+and together with every launch that feeds it), the 7B attention projection
+step, the memory-bound paths in GB/s against 8 TB/s and against the device's
+own read ceiling at the same size (quantize, bf16 dequantize, small-M
+dequant-GEMV at M = 1/8/16 on the 65B MLP shape), the 7B MLP set, and the CPU
+oracle timed on a bounded sample of the headline workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--copy-probe]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-components] [--copy-probe]
 """
 from __future__ import annotations
 
@@ -34,7 +37,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 FP64_PEAK_TFLOPS = 78.6      # MI355X fp64 vector (FMA counted as two flops)
 METRIC = "QLoRA linear fwd+bwd TFLOP/s and NF4 dequant-GEMV GB/s, % of roofline"
-KERNEL_SOURCES = {"fwd_gemm": "gemm_big.hip", "bwd_dx": "gemm_big.hip", "fwd_gemv": "skinny.hip",
+HEADLINE = "block65b_m2048"
+KERNEL_SOURCES = {"fwd_gemm": "gemm_big.hip", "bwd_dx": "gemm_big.hip", "fwd_gemv": "gemv.hip",
                   "quant_pass1": "quantize.hip", "dequant": "quantize.hip"}
 
 
@@ -57,10 +61,10 @@ def src_hash(fname):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_traffic(kernel):
-    """HBM bytes per launch from the committed PMC summary of this kernel, if
-    it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_attn7b_4096_pmc.md")
+def read_traffic(kernel, workload="attn7b_4096"):
+    """HBM bytes per launch from the committed PMC summary of this kernel at
+    this workload, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path, encoding="utf-8").read()
@@ -71,17 +75,60 @@ def read_traffic(kernel):
     return float(m_bytes.group(1))
 
 
+def build_workload(torch, qn, si, dev, name, keep_host=False):
+    """Device buffers of every linear of a multi-matrix workload (inputs,
+    states, outputs) and one workspace big enough for any of its calls."""
+    bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+    mats, ws_bytes, qws_bytes, host = [], 256, 256, []
+    for j in range(len(si.WORKLOADS[name]["shapes"])):
+        d = si.layer_inputs(name, matrix=j)
+        M, K, N, r = d["M"], d["K"], d["N"], d["r"]
+        m = {"M": M, "K": K, "N": N, "r": r, "c": d["c"], "W": torch.from_numpy(d["W"]).to(dev).reshape(-1),
+             "X": bf(d["X_bits"]), "A": bf(d["A_bits"]), "B": bf(d["B_bits"]), "G": bf(d["G_bits"]),
+             "state": qn.empty_state(K * N, dev),
+             "Y": torch.empty(M, N, dtype=torch.bfloat16, device=dev),
+             "Z": torch.empty(M, r, dtype=torch.bfloat16, device=dev),
+             "dX": torch.empty(M, K, dtype=torch.bfloat16, device=dev),
+             "dA": torch.empty(K, r, dtype=torch.float32, device=dev),
+             "dB": torch.empty(r, N, dtype=torch.float32, device=dev)}
+        if keep_host:
+            host.append(d)
+        del d
+        ws_bytes = max(ws_bytes, *qn.qlora_workspace_bytes(M, K, N, r))
+        qws_bytes = max(qws_bytes, qn.nf4_sizes(K * N)["quant_workspace_bytes"])
+        mats.append(m)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    qws = torch.empty(qws_bytes, dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    return mats, ws, qws, status, host
+
+
+def run_linear(qn, m, ws, timed=()):
+    """Forward then backward of one linear; the kernels named in `timed`
+    are timed (library timers) during this linear only."""
+    for k in timed:
+        qn.qlora_timer_enable(k, True)
+    qn.qlora_linear_fwd(m["X"], m["state"], m["A"], m["B"], m["c"], m["K"], m["N"], m["Y"], m["Z"], ws)
+    for k in timed:
+        qn.qlora_timer_enable(k, False)
+    qn.qlora_linear_bwd(m["G"], m["X"], m["Z"], m["state"], m["A"], m["B"], m["c"], m["K"], m["N"], True,
+                        m["dX"], m["dA"], m["dB"], ws)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # a step takes about 0.35 ms: 200 warm-up steps bring the clocks to their steady state
-    # (20 steps after 3 warm-up ones read about 10 % low), 1000 timed steps take about 0.35 s
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=200)
+    # a step takes about 7.5 ms: 30 warm-up steps bring the clocks to their steady
+    # state, 200 timed steps take about 1.5 s
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-components", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--memory-only", action="store_true",
+                    help="run only the memory-bound paths on the 65B MLP weight (for profiler runs); prints "
+                         "their figures instead of the benchmark line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: the layer is measured on exactly one GPU; multi-GPU runs are not supported "
@@ -95,38 +142,29 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-    wl = "attn7b_4096"
-    sets = []
-    for i in range(3):
-        d = si.layer_inputs(wl, matrix=0)   # same values, distinct buffers
-        bf = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
-        sets.append({"W": torch.from_numpy(d["W"]).to(dev).reshape(-1), "X": bf(d["X_bits"]),
-                     "A": bf(d["A_bits"]), "B": bf(d["B_bits"]), "G": bf(d["G_bits"])})
-    M, K, N, r, c = d["M"], d["K"], d["N"], d["r"], d["c"]
-    P = K * N
-    sizes = qn.nf4_sizes(P)
-    fwd_ws, bwd_ws = qn.qlora_workspace_bytes(M, K, N, r)
-    qws = torch.empty(sizes["quant_workspace_bytes"], dtype=torch.uint8, device=dev)
-    fws = torch.empty(max(fwd_ws, 256), dtype=torch.uint8, device=dev)
-    bws = torch.empty(max(bwd_ws, 256), dtype=torch.uint8, device=dev)
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
-    outs = []
-    for s in sets:
-        outs.append({"state": qn.empty_state(P, dev),
-                     "Y": torch.empty(M, N, dtype=torch.bfloat16, device=dev),
-                     "Z": torch.empty(M, r, dtype=torch.bfloat16, device=dev),
-                     "dX": torch.empty(M, K, dtype=torch.bfloat16, device=dev),
-                     "dA": torch.empty(K, r, dtype=torch.float32, device=dev),
-                     "dB": torch.empty(r, N, dtype=torch.float32, device=dev)})
+    if args.memory_only:
+        flush = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        res = bench_memory65b(torch, qn, si, dev, flush, status)
+        if args.copy_probe:
+            a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+            torch.empty_like(a).copy_(a)
+            torch.cuda.synchronize()
+        print(json.dumps({"memory_paths_decode65b": res}))
+        return
+    wl = HEADLINE
+    mats, ws, qws, status, host = build_workload(torch, qn, si, dev, wl, keep_host=not args.no_cpu)
+    names = ["q", "k", "v", "o", "gate", "up", "down"]
+    dominant_ids = (4, 5)   # gate and up: the forward GEMMs with the most flops per launch
+    print(f"bench: {wl} inputs resident", file=sys.stderr, flush=True)
 
-    def step(i):
-        s, o = sets[i % 3], outs[i % 3]
-        qn.nf4_quantize(s["W"], o["state"], qws, status)
-        qn.qlora_linear_fwd(s["X"], o["state"], s["A"], s["B"], c, K, N, o["Y"], o["Z"], fws)
-        qn.qlora_linear_bwd(s["G"], s["X"], o["Z"], o["state"], s["A"], s["B"], c, K, N, True,
-                            o["dX"], o["dA"], o["dB"], bws)
+    def step(i, timed=()):
+        for m in mats:
+            qn.nf4_quantize(m["W"], m["state"], qws, status)
+        for j, m in enumerate(mats):
+            run_linear(qn, m, ws, timed if j in dominant_ids else ())
 
-    # warmup, with every kernel timed once to find the dominant one
+    # warmup, with every kernel timed to give the per-kernel averages
     for k in qn.KERNEL_IDS:
         qn.qlora_timer_enable(k, True)
     for i in range(max(args.warmup, 1)):
@@ -137,41 +175,79 @@ def main():
         ms, n = qn.qlora_timer_read(k)
         qn.qlora_timer_enable(k, False)
         if n:
-            per_kernel[k] = ms / n
-    dominant = max(("fwd_gemm", "bwd_dx"), key=lambda k: per_kernel.get(k, 0.0))
+            per_kernel[k] = {"avg_ms": round(ms / n, 4), "launches_per_step": round(n / max(args.warmup, 1), 2)}
     if qn.nf4_status_read(status) != 0:
         raise RuntimeError("quantize reported a bad status")
 
-    # timed region
-    qn.qlora_timer_enable(dominant, True)
+    # timed region: the dominant GEMM (and the launches that feed it) timed
+    # live on the launch stream during the gate and up forwards
+    feeders = ("dequant_bf16", "lora_down", "reduce")
+    timed = ("fwd_gemm",) + feeders
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
-        step(i)
+        step(i, timed)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = ev0.elapsed_time(ev1) / args.steps
-    dom_ms, dom_n = qn.qlora_timer_read(dominant)
-    qn.qlora_timer_enable(dominant, False)
+    dom_ms, dom_n = qn.qlora_timer_read("fwd_gemm")
+    feed = {k: qn.qlora_timer_read(k) for k in feeders}
     dom_avg = dom_ms / max(dom_n, 1)
+    feed_ms = sum(v[0] for v in feed.values()) / max(dom_n, 1)
 
-    fwd_f, bwd_f = layer_flops(M, K, N, r)
-    value = (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
-    dflops = kernel_flops(dominant, M, K, N, r)
+    M, K, N, r = (mats[4][k] for k in ("M", "K", "N", "r"))
+    flops = sum(sum(layer_flops(m["M"], m["K"], m["N"], m["r"])) for m in mats)
+    fwd_f = sum(layer_flops(m["M"], m["K"], m["N"], m["r"])[0] for m in mats)
+    value = flops / (ms_step * 1e-3) / 1e12
+    dflops = kernel_flops("fwd_gemm", M, K, N, r)
     achieved = dflops / (dom_avg * 1e-3) / 1e12
-    traffic = read_traffic(dominant)
+    with_feed = dflops / ((dom_avg + feed_ms) * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic, "kernel": dominant, "avg_ms": round(dom_avg, 4),
-                "launches": dom_n, "flops_per_launch": dflops}
-
+                "traffic": read_traffic("fwd_gemm", "block65b_gate"),
+                "kernel": f"fwd_gemm (gate/up forward, M={M} K={K} N={N} r={r})",
+                "avg_ms": round(dom_avg, 4), "launches": dom_n, "flops_per_launch": dflops,
+                "feeders": {k: {"ms_per_launch_of_gemm": round(v[0] / max(dom_n, 1), 4), "launches": v[1]}
+                            for k, v in feed.items()},
+                "achieved_with_feeders": round(with_feed, 2),
+                "frac_with_feeders": round(with_feed / MFMA_BF16_PEAK_TFLOPS, 4)}
     print(f"bench: {args.steps} timed steps, {ms_step:.4f} ms each", file=sys.stderr, flush=True)
-    components = {"kernel_avg_ms_warmup": {k: round(v, 4) for k, v in per_kernel.items()}}
+
+    # the two halves of the step, each timed on its own
+    def part(fn, n=20):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    q_ms = part(lambda i: [qn.nf4_quantize(m["W"], m["state"], qws, status) for m in mats])
+    l_ms = part(lambda i: [run_linear(qn, m, ws) for m in mats])
+    qbytes = 0
+    for m in mats:
+        sz = qn.nf4_sizes(m["K"] * m["N"])
+        qbytes += 4 * m["K"] * m["N"] + (m["K"] * m["N"] + 1) // 2 + sz["n1"] + 4 * sz["n2"] + 4
+    components = {"kernel_avg_ms_warmup": per_kernel,
+                  "headline_parts": {"quantize_ms": round(q_ms, 4), "quantize_bytes": qbytes,
+                                     "quantize_GBps": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
+                                     "quantize_frac_hbm": round(qbytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                     "layers_ms": round(l_ms, 4),
+                                     "layers_TFLOPs": round(flops / (l_ms * 1e-3) / 1e12, 1),
+                                     "layers_frac_bf16_peak": round(flops / (l_ms * 1e-3) / 1e12
+                                                                    / MFMA_BF16_PEAK_TFLOPS, 4),
+                                     "how": "20 back-to-back passes of each half alone"}}
+    cpu = None if args.no_cpu else cpu_baseline(host, flops)
+    del host
     if not args.no_components:
-        components.update(bench_components(torch, qn, si, dev, sets, outs, qws, status))
+        del mats, ws, qws
+        torch.cuda.empty_cache()
+        components.update(bench_components(torch, qn, si, dev, args))
     if args.copy_probe:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
@@ -179,19 +255,80 @@ def main():
         torch.cuda.synchronize()
         components["copy_probe_bytes"] = {"read": a.numel() * 4, "write": a.numel() * 4}
 
-    cpu = None if args.no_cpu else cpu_baseline(wl)
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl, "M": M, "K": K, "N": N, "r": r, "alpha": 16.0,
-                   "step": "nf4_quantize + qlora_linear_fwd + qlora_linear_bwd",
-                   "flops_fwd": fwd_f, "flops_bwd": bwd_f, "input_sets_rotated": 3,
-                   "wall_s": round(wall, 3)},
+        "config": {"workload": wl, "linears": {n: list(kn) for n, kn in zip(names, mats_shapes())},
+                   "M": M, "r": r, "alpha": 16.0,
+                   "step": "nf4_quantize of all 7 weights, then qlora_linear_fwd + qlora_linear_bwd of each linear",
+                   "weights": sum(k * n for k, n in mats_shapes()),
+                   "flops_fwd": fwd_f, "flops_bwd": flops - fwd_f, "wall_s": round(wall, 3)},
         "roofline": roofline, "cpu_baseline": cpu, "components": components,
     }
     print(json.dumps(line))
+
+
+def mats_shapes():
+    import synth_inputs as si
+    return list(si.WORKLOADS[HEADLINE]["shapes"])
+
+
+def attn7b_step(torch, qn, si, dev, steps, warmup):
+    """The 7B attention-shaped projection (M = K = N = 4096, r = 64):
+    nf4_quantize + fwd + bwd, three input sets rotated so the Infinity Cache
+    cannot carry a step's inputs over; the forward GEMM timed live."""
+    stream = torch.cuda.current_stream()
+    bf = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+    sets = []
+    for i in range(3):
+        d = si.layer_inputs("attn7b_4096", matrix=0)   # same values, distinct buffers
+        sets.append({"W": torch.from_numpy(d["W"]).to(dev).reshape(-1), "X": bf(d["X_bits"]),
+                     "A": bf(d["A_bits"]), "B": bf(d["B_bits"]), "G": bf(d["G_bits"])})
+    M, K, N, r, c = d["M"], d["K"], d["N"], d["r"], d["c"]
+    P = K * N
+    sizes = qn.nf4_sizes(P)
+    fwd_ws, bwd_ws = qn.qlora_workspace_bytes(M, K, N, r)
+    qws = torch.empty(sizes["quant_workspace_bytes"], dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(fwd_ws, bwd_ws, 256), dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    outs = [{"state": qn.empty_state(P, dev), "Y": torch.empty(M, N, dtype=torch.bfloat16, device=dev),
+             "Z": torch.empty(M, r, dtype=torch.bfloat16, device=dev),
+             "dX": torch.empty(M, K, dtype=torch.bfloat16, device=dev),
+             "dA": torch.empty(K, r, dtype=torch.float32, device=dev),
+             "dB": torch.empty(r, N, dtype=torch.float32, device=dev)} for _ in sets]
+
+    def step(i):
+        s, o = sets[i % 3], outs[i % 3]
+        qn.nf4_quantize(s["W"], o["state"], qws, status)
+        qn.qlora_linear_fwd(s["X"], o["state"], s["A"], s["B"], c, K, N, o["Y"], o["Z"], ws)
+        qn.qlora_linear_bwd(s["G"], s["X"], o["Z"], o["state"], s["A"], s["B"], c, K, N, True,
+                            o["dX"], o["dA"], o["dB"], ws)
+
+    for i in range(warmup):
+        step(i)
+    qn.qlora_timer_enable("fwd_gemm", True)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    gms, gn = qn.qlora_timer_read("fwd_gemm")
+    qn.qlora_timer_enable("fwd_gemm", False)
+    ms_step = ev0.elapsed_time(ev1) / steps
+    fwd_f, bwd_f = layer_flops(M, K, N, r)
+    gflops = kernel_flops("fwd_gemm", M, K, N, r)
+    out = {"ms_per_step": round(ms_step, 4), "TFLOPs": round((fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12, 1),
+           "steps": steps, "warmup": warmup,
+           "fwd_gemm_ms": round(gms / max(gn, 1), 4),
+           "fwd_gemm_frac_bf16_peak": round(gflops / (gms / max(gn, 1) * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "fwd_gemm_traffic": read_traffic("fwd_gemm"),
+           "how": "nf4_quantize + qlora_linear_fwd + qlora_linear_bwd, M = K = N = 4096, r = 64, three input "
+                  "sets rotated"}
+    return out, sets, outs, qws, status
 
 
 def _flush_cache(flush):
@@ -234,31 +371,30 @@ def _time_calls(torch, fn, reps, flush):
     return total / reps
 
 
-def bench_components(torch, qn, si, dev, sets, outs, qws, status):
-    """The memory-bound paths, each call preceded by a cache flush (a 512 MB
-    buffer written, then read) so that no input or output is served from the
-    Infinity Cache."""
+def read_ceiling(torch, dev, nbytes, flush, reps=7):
+    """The device's own read ceiling at a given size: the plain streaming read
+    of libqlora_probe.so over a buffer of that size, from a clean cache;
+    best of several workgroup counts, median over reps."""
+    from bit_nf4_quantized_10_amd import probe
+    buf = torch.ones(nbytes // 16 * 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    best = None
+    for grid in (2048, 4096, 8192):
+        t = sorted(_time_calls(torch, lambda i: probe.read_probe(buf, sink, grid), 1, flush) for _ in range(reps))
+        ms = t[len(t) // 2]
+        if best is None or ms < best[0]:
+            best = (ms, grid)
+    del buf
+    return {"bytes": nbytes // 16 * 16, "ms": round(best[0], 4),
+            "GBps": round(nbytes / (best[0] * 1e-3) / 1e9, 1), "grid": best[1]}
+
+
+def bench_memory65b(torch, qn, si, dev, flush, status):
+    """The memory-bound paths on the 65B MLP weight (8192 x 22016): the whole
+    nf4_quantize call, the bf16 dequantize, and the small-M dequant-GEMV
+    forward at M = 1, 8, 16 (whole call and GEMV kernel), each call after a
+    cache flush; plus the device's read ceiling at the GEMV's size."""
     res = {}
-    flush = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
-    P = sets[0]["W"].numel()
-    n1, n2 = qn.nf4_sizes(P)["n1"], qn.nf4_sizes(P)["n2"]
-    # quantize: fp32 read, codes + int8 codes + fp32 scales written
-    qbytes = 4 * P + (P + 1) // 2 + n1 + 4 * n2 + 4
-    qfn = lambda i: qn.nf4_quantize(sets[i % 3]["W"], outs[i % 3]["state"], qws, status)
-    ms = _time_kernel(qn, torch, "quant_pass1", qfn, 10, flush)
-    full_ms = _time_calls(torch, qfn, 10, flush)
-    res["quantize_attn7b"] = {"bytes": qbytes, "pass1_ms": round(ms, 4), "call_ms": round(full_ms, 4),
-                              "GBps_call": round(qbytes / (full_ms * 1e-3) / 1e9, 1),
-                              "frac_hbm_call": round(qbytes / (full_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    # bf16 dequantize
-    dbytes = (P + 1) // 2 + n1 + 4 * n2 + 4 + 2 * P
-    outs_bf = [torch.empty(P, dtype=torch.bfloat16, device=dev) for _ in range(3)]
-    ms = _time_kernel(qn, torch, "dequant",
-                      lambda i: qn.nf4_dequantize(outs[i % 3]["state"], "bf16", out=outs_bf[i % 3]), 16, flush)
-    res["dequant_bf16_attn7b"] = {"bytes": dbytes, "ms": round(ms, 4),
-                                  "GBps": round(dbytes / (ms * 1e-3) / 1e9, 1),
-                                  "frac_hbm": round(dbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    del outs_bf
     # small-M dequant-GEMV on the 65B MLP shape
     d = si.layer_inputs("decode65b_8192x22016", M=16, with_grad=False)
     K, N, r, c = d["K"], d["N"], d["r"], d["c"]
@@ -306,19 +442,58 @@ def bench_components(torch, qn, si, dev, sets, outs, qws, status):
                          "GBps_call": round(gbytes / (call_ms * 1e-3) / 1e9, 1),
                          "frac_hbm_call": round(gbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "GBps_kernel": round(gbytes / (kms * 1e-3) / 1e9, 1)}
+    # the device's own read ceiling at the GEMV's size: the kernel is judged
+    # against it as well as against the 8 TB/s specification
+    ceil = read_ceiling(torch, dev, gemv["M16"]["bytes"], flush)
+    for v in gemv.values():
+        v["frac_read_ceiling_kernel"] = round(v["GBps_kernel"] / ceil["GBps"], 4)
+        v["frac_read_ceiling_call"] = round(v["GBps_call"] / ceil["GBps"], 4)
     res["gemv_decode65b"] = gemv
+    res["read_ceiling_gemv_size"] = ceil
+    return res
+
+
+def bench_components(torch, qn, si, dev, args):
+    """The 7B attention step, then the memory-bound paths (each call preceded
+    by a cache flush: a 512 MB buffer written, then read, so that no input or
+    output is served from the Infinity Cache), then other workloads."""
+    res = {}
+    attn, sets, outs, qws, status = attn7b_step(torch, qn, si, dev, steps=1000, warmup=200)
+    res["attn7b_4096"] = attn
+    print("bench: attn7b_4096 measured", file=sys.stderr, flush=True)
+    flush = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
+    P = sets[0]["W"].numel()
+    n1, n2 = qn.nf4_sizes(P)["n1"], qn.nf4_sizes(P)["n2"]
+    # quantize: fp32 read, codes + int8 codes + fp32 scales written
+    qbytes = 4 * P + (P + 1) // 2 + n1 + 4 * n2 + 4
+    qfn = lambda i: qn.nf4_quantize(sets[i % 3]["W"], outs[i % 3]["state"], qws, status)
+    ms = _time_kernel(qn, torch, "quant_pass1", qfn, 10, flush)
+    full_ms = _time_calls(torch, qfn, 10, flush)
+    res["quantize_attn7b"] = {"bytes": qbytes, "pass1_ms": round(ms, 4), "call_ms": round(full_ms, 4),
+                              "GBps_call": round(qbytes / (full_ms * 1e-3) / 1e9, 1),
+                              "frac_hbm_call": round(qbytes / (full_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    # bf16 dequantize
+    dbytes = (P + 1) // 2 + n1 + 4 * n2 + 4 + 2 * P
+    outs_bf = [torch.empty(P, dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    ms = _time_kernel(qn, torch, "dequant",
+                      lambda i: qn.nf4_dequantize(outs[i % 3]["state"], "bf16", out=outs_bf[i % 3]), 16, flush)
+    res["dequant_bf16_attn7b"] = {"bytes": dbytes, "ms": round(ms, 4),
+                                  "GBps": round(dbytes / (ms * 1e-3) / 1e9, 1),
+                                  "frac_hbm": round(dbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del outs_bf
+    res.update(bench_memory65b(torch, qn, si, dev, flush, status))
+    ceil = res["read_ceiling_gemv_size"]
     print("bench: memory-bound paths measured", file=sys.stderr, flush=True)
-    # what plain streaming reaches on this device, as context for the HBM fractions
-    # (the fractions above are against the 8 TB/s specification)
-    big = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    out = torch.empty_like(big)
-    rd = min(_time_calls(torch, lambda i: big.sum(), 3, flush) for _ in range(2))
+    out = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     wr = min(_time_calls(torch, lambda i: out.fill_(1.0), 3, flush) for _ in range(2))
     res["device_streaming_ceiling"] = {
-        "read_GBps": round(big.numel() * 4 / (rd * 1e-3) / 1e9, 1),
-        "write_GBps": round(big.numel() * 4 / (wr * 1e-3) / 1e9, 1),
-        "how": "torch sum / fill of a 1 GiB fp32 tensor, cache flushed before each call"}
-    del big, out
+        "read_at_gemv_size": ceil,
+        "read_1GiB": read_ceiling(torch, dev, 1 << 30, flush, reps=3),
+        "write_1GiB_GBps": round(out.numel() * 4 / (wr * 1e-3) / 1e9, 1),
+        "how": "reads: the plain streaming read of libqlora_probe.so (16-byte loads, four in flight per lane), "
+               "best of 2048/4096/8192 workgroups, median of 7 (3 at 1 GiB); write: torch fill of 1 GiB; "
+               "cache flushed before each call"}
+    del out
     # adapter merge for re-export at the bench workload's shape: fp64 FMA bound
     # (2 K N r flops), plus the re-quantize of the merged weight
     dm = si.layer_inputs("attn7b_4096", with_weight=False, with_grad=False)
@@ -428,10 +603,11 @@ def bench_components(torch, qn, si, dev, sets, outs, qws, status):
                                 "how": "qlora_linear_fwd + _bwd in the fp16 compute type, 4096 x 4096, r = 64, "
                                        "M = 4096, cache flushed"}
     del Xh, Ah, Bh, Gh, ws16, Yh, Zh, dXh, dAh, dBh
-    # every linear of the 7B MLP set and of a 65B block, one pass each
-    for name in ("mlp7b_4096x11008", "block65b_m2048"):
-        res[name] = bench_workload_set(torch, qn, si, dev, name, flush)
-        print(f"bench: {name} measured", file=sys.stderr, flush=True)
+    # every linear of the 7B MLP set, one pass each
+    del sets, outs
+    torch.cuda.empty_cache()
+    res["mlp7b_4096x11008"] = bench_workload_set(torch, qn, si, dev, "mlp7b_4096x11008", flush)
+    print("bench: mlp7b_4096x11008 measured", file=sys.stderr, flush=True)
     # the vendor library's plain bf16 GEMM of the same base shape on this
     # device (torch.matmul -> hipBLASLt), as context for the MFMA fraction
     Mv, Kv, Nv = 4096, 4096, 4096
@@ -461,26 +637,7 @@ def bench_workload_set(torch, qn, si, dev, name, flush, reps=3):
     the Infinity Cache overwritten before each timed pass).  The layers'
     TFLOP/s count the fwd+bwd flops only; the quantize is timed on its own
     as well, against its algorithmic bytes."""
-    bf = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
-    mats, ws_bytes, qws_bytes = [], 256, 256
-    for j in range(len(si.WORKLOADS[name]["shapes"])):
-        d = si.layer_inputs(name, matrix=j)
-        M, K, N, r = d["M"], d["K"], d["N"], d["r"]
-        m = {"M": M, "K": K, "N": N, "r": r, "c": d["c"], "W": torch.from_numpy(d["W"]).to(dev).reshape(-1),
-             "X": bf(d["X_bits"]), "A": bf(d["A_bits"]), "B": bf(d["B_bits"]), "G": bf(d["G_bits"]),
-             "state": qn.empty_state(K * N, dev),
-             "Y": torch.empty(M, N, dtype=torch.bfloat16, device=dev),
-             "Z": torch.empty(M, r, dtype=torch.bfloat16, device=dev),
-             "dX": torch.empty(M, K, dtype=torch.bfloat16, device=dev),
-             "dA": torch.empty(K, r, dtype=torch.float32, device=dev),
-             "dB": torch.empty(r, N, dtype=torch.float32, device=dev)}
-        del d
-        ws_bytes = max(ws_bytes, *qn.qlora_workspace_bytes(M, K, N, r))
-        qws_bytes = max(qws_bytes, qn.nf4_sizes(K * N)["quant_workspace_bytes"])
-        mats.append(m)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    qws = torch.empty(qws_bytes, dtype=torch.uint8, device=dev)
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    mats, ws, qws, status, _ = build_workload(torch, qn, si, dev, name)
 
     def quant_all(i):
         for m in mats:
@@ -523,34 +680,47 @@ def bench_workload_set(torch, qn, si, dev, name, flush, reps=3):
     return out
 
 
-def cpu_baseline(wl, reps=9):
-    """The oracle as it stands, on the host cores, on the full workload:
-    quantize of the 4096 x 4096 weight, then forward and backward at all 4096
-    token rows (fp64 numpy); median of `reps` runs (about 10-12 s of CPU work
-    in all)."""
-    import synth_inputs as si
+def cpu_baseline(host, flops_total, rows=128, reps=3):
+    """The oracle as it stands, on the host cores, on a bounded sample of the
+    headline step, scaled to the whole step:
+      - nf4_quantize's oracle on the q weight (8192 x 8192, 67.1M of the
+        block's 809.5M weights), time scaled by the weight count;
+      - the oracle's forward and backward of all seven linears on the first
+        `rows` of the 2048 token rows, time scaled by 2048 / rows.  The
+        layer products run on the bf16-rounded fp32 weights, which have the
+        shape and dtype of Ŵ (the values do not change the oracle's time).
+    Median of `reps` runs of each part."""
     from oracle import nf4_oracle as o
     try:
         from threadpoolctl import threadpool_info
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    d = si.layer_inputs(wl, matrix=0)
-    M, K, N, r, c = d["M"], d["K"], d["N"], d["r"], d["c"]
-    times = []
+    weights = sum(d["K"] * d["N"] for d in host)
+    d0 = host[0]
+    tq = []
     for _ in range(reps):
         t0 = time.perf_counter()
-        st = o.quantize(d["W"].ravel())
-        W_hat = o.dequantize(st, "bf16").reshape(K, N)
-        o.layer_forward(d["X"], W_hat, d["A"], d["B"], c)
-        o.layer_backward(d["G"], d["X"], W_hat, d["A"], d["B"], c)
-        times.append(time.perf_counter() - t0)
-    step_s = sorted(times)[len(times) // 2]
-    fwd_f, bwd_f = layer_flops(M, K, N, r)
-    return {"value": round((fwd_f + bwd_f) / step_s / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"full workload (quantize + fwd + bwd, M={M}), median of {reps} runs "
-                      f"({sum(times):.1f} s of CPU work): {step_s:.2f} s per step"}
+        o.quantize(d0["W"].ravel())
+        tq.append(time.perf_counter() - t0)
+    w_hat = [o.bf16_round(d["W"]) for d in host]
+    tl = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        for d, wh in zip(host, w_hat):
+            o.layer_forward(d["X"][:rows], wh, d["A"], d["B"], d["c"])
+            o.layer_backward(d["G"][:rows], d["X"][:rows], wh, d["A"], d["B"], d["c"])
+        tl.append(time.perf_counter() - t0)
+    q_s = sorted(tq)[reps // 2] * weights / d0["W"].size
+    l_s = sorted(tl)[reps // 2] * host[0]["M"] / rows
+    step_s = q_s + l_s
+    return {"value": round(flops_total / step_s / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "host_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"oracle quantize of the 8192x8192 q weight ({d0['W'].size / 1e6:.1f}M of {weights / 1e6:.1f}M "
+                      f"weights, {sorted(tq)[reps // 2]:.2f} s) and fwd+bwd of all 7 linears on {rows} of "
+                      f"{host[0]['M']} token rows ({sorted(tl)[reps // 2]:.2f} s), each the median of {reps} runs "
+                      f"({sum(tq) + sum(tl):.1f} s of CPU work), scaled to the whole step: {step_s:.1f} s per step; "
+                      f"cores = BLAS threads used, host_cores = CPUs the process may run on"}
 
 
 if __name__ == "__main__":

@@ -190,3 +190,18 @@ def test_grouped_member_rank_must_be_a_multiple_of_8(g, r):
                                0x10000, 1 << 30, None) == qn.NF4_EINVAL
     assert L.qlora_grouped_bwd(64, K, g, Ns, r, 0x100, 0x100, 0x500, states, 0x200, 0x300, ctypes.c_float(1.0),
                                None, 0x600, 0x700, 0x10000, 1 << 30, None) == qn.NF4_EINVAL
+
+
+def test_read_probe_library_exports_its_header_and_validates():
+    """libqlora_probe.so (the read-ceiling helper of the benchmark) exports
+    what include/qlora_read_probe.h declares and rejects bad arguments
+    before launching anything."""
+    from bit_nf4_quantized_10_amd import probe
+    text = open(os.path.join(ROOT, "include", "qlora_read_probe.h"), encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    declared = sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+    assert declared == sorted(probe.C_FUNCTIONS)
+    L = probe.lib()
+    for args in [(None, 1024, 256, 0x100, None), (0x100, 8, 256, 0x100, None), (0x100, 1000, 256, 0x100, None),
+                 (0x100, 1024, 0, 0x100, None), (0x108, 1024, 256, 0x100, None), (0x100, 1024, 256, None, None)]:
+        assert L.qlora_read_probe(*args) == 1, args
