@@ -52,6 +52,11 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m bit_nf4_quantized_10_amd.build_lib`")
+        # PyTorch brings its own HIP and HSA runtimes.  Loaded first, they
+        # satisfy this library's libamdhip64 dependency, so the process holds
+        # one HSA runtime; loaded the other way round, the process ends up
+        # with two, and the second cannot reach the GPU.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         i64, vp, i32p = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
         sp = ctypes.POINTER(_State)
