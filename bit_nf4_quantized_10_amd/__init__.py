@@ -27,8 +27,9 @@ C_FUNCTIONS = [
     "qlora_linear_fwd", "qlora_linear_bwd", "nf4_status_read", "qlora_timer_enable",
     "qlora_timer_read", "qlora_merge", "qlora_sgd_step", "qlora_grouped_workspace_bytes",
     "qlora_grouped_fwd", "qlora_grouped_bwd", "qlora_linear_fwd_dt", "qlora_linear_bwd_dt", "qlora_sgd_step_dt",
-    "nf4_error_string",
+    "qlora_linear_fwd_noalloc", "nf4_error_string",
 ]
+NF4_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 
 
 class NF4Error(RuntimeError):
@@ -81,6 +82,7 @@ def lib() -> ctypes.CDLL:
         L.qlora_linear_fwd_dt.argtypes = [ctypes.c_int] + L.qlora_linear_fwd.argtypes
         L.qlora_linear_bwd_dt.argtypes = [ctypes.c_int] + L.qlora_linear_bwd.argtypes
         L.qlora_sgd_step_dt.argtypes = [ctypes.c_int] + L.qlora_sgd_step.argtypes
+        L.qlora_linear_fwd_noalloc.argtypes = [i64, i64, i64, i64, vp, sp, vp, vp, ctypes.c_float, vp, vp, vp]
         L.nf4_error_string.argtypes = [ctypes.c_int]
         L.nf4_error_string.restype = ctypes.c_char_p
         for name in C_FUNCTIONS[:-1]:
@@ -347,6 +349,24 @@ def qlora_linear_fwd(X, state: NF4State, A, B, c: float, K: int, N: int, Y=None,
     _check(lib().qlora_linear_fwd_dt(_COMPUTE[dt], M, K, N, r, X.data_ptr(), ctypes.byref(st), A.data_ptr(),
                                      B.data_ptr(), float(c), Y.data_ptr(), _ptr(Z), workspace.data_ptr(),
                                      workspace.numel(), _stream(stream)), "qlora_linear_fwd_dt")
+    return Y, Z
+
+
+def qlora_linear_fwd_noalloc(X, state: NF4State, A, B, c: float, K: int, N: int, Y, Z=None, stream=None):
+    """qlora_linear_fwd (bf16) with the library's own device scratch instead
+    of a workspace: allocates nothing.  Y (and Z, if given) must be passed
+    in.  Shapes whose forward workspace exceeds NF4_NOALLOC_SCRATCH_BYTES
+    are rejected.  Returns (Y, Z)."""
+    import torch
+    M, r = X.shape[0], A.shape[1]
+    for t, n in ((X, "X"), (A, "A"), (B, "B"), (Y, "Y")):
+        _require_cuda(t, n, torch.bfloat16)
+    if Z is not None:
+        _require_cuda(Z, "Z", torch.bfloat16)
+    st = state.c_struct()
+    _check(lib().qlora_linear_fwd_noalloc(M, K, N, r, X.data_ptr(), ctypes.byref(st), A.data_ptr(), B.data_ptr(),
+                                          float(c), Y.data_ptr(), _ptr(Z), _stream(stream)),
+           "qlora_linear_fwd_noalloc")
     return Y, Z
 
 

@@ -67,6 +67,37 @@ hipEvent_t take_event(TimerSlot& s) {
   return e;
 }
 
+// ------------------------------------------------- no-allocation forward
+// Scratch of qlora_linear_fwd_noalloc: one file-scope device array, which
+// every GPU the library runs on holds (its own copy, at its own address)
+// until the process ends.  Host code never passes the array's name to a
+// kernel: that name is a host-side stand-in.  The device address comes from
+// hipGetSymbolAddress, once per device with that device current, and is
+// kept per device below.
+static __device__ __align__(256) char scratch[NF4_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the current device (looked up on the first call).
+hipError_t scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 namespace qn {
@@ -153,6 +184,21 @@ int qlora_linear_fwd_dt(int compute_dtype, int64_t M, int64_t K, int64_t N, int6
   const qn::NF4View v = view_of(W);
   hipError_t e =
       qn::launch_fwd(M, K, N, r, X, v, A, B, c, Y, Z, workspace, static_cast<hipStream_t>(stream), compute_dtype);
+  return e == hipSuccess ? NF4_OK : NF4_EHIP;
+}
+
+int qlora_linear_fwd_noalloc(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, const nf4_state_t* W,
+                             const uint16_t* A, const uint16_t* B, float c, uint16_t* Y, uint16_t* Z, void* stream) {
+  if (!layer_shape_ok(M, K, N, r) || !state_ok(W) || W->numel != K * N) return NF4_EINVAL;
+  if (!X || !A || !B || !Y) return NF4_EINVAL;
+  if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y) || (Z && !aligned16(Z))) return NF4_EINVAL;
+  if (qn::fwd_workspace_bytes(M, K, N, r) > NF4_NOALLOC_SCRATCH_BYTES) return NF4_EINVAL;
+  void* ws = nullptr;
+  if (scratch_of_current_device(&ws) != hipSuccess) return NF4_EHIP;
+  // the forward's kernels need no zeroed scratch: every region they read
+  // was written earlier in the same call
+  hipError_t e = qn::launch_fwd(M, K, N, r, X, view_of(W), A, B, c, Y, Z, ws, static_cast<hipStream_t>(stream),
+                                NF4_COMPUTE_BF16);
   return e == hipSuccess ? NF4_OK : NF4_EHIP;
 }
 

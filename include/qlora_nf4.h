@@ -134,6 +134,24 @@ int qlora_linear_fwd(int64_t M, int64_t K, int64_t N, int64_t r,
                      uint16_t* Y, uint16_t* Z,
                      void* workspace, int64_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): qlora_linear_fwd
+ * (bf16 compute) with its scratch taken from a device array of
+ * NF4_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on,
+ * instead of a workspace argument.  The call allocates nothing.  Shapes
+ * whose forward workspace (qlora_workspace_bytes' fwd_bytes) exceeds that
+ * size return NF4_EINVAL: in practice the small-M (dequant-GEMV) and
+ * fused-decode forwards, not the M >= 192 one, whose workspace holds the
+ * dequantized weight.  Z may be NULL (then it is computed in the scratch).
+ * The scratch keeps the last call's contents; calls that overlap on one GPU
+ * (two streams, or two host threads) race on it and must be serialised by
+ * the caller.  The stream must belong to the current device.  Results are
+ * bit-identical to qlora_linear_fwd's. */
+#define NF4_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+int qlora_linear_fwd_noalloc(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X,
+                             const nf4_state_t* W, const uint16_t* A, const uint16_t* B, float c,
+                             uint16_t* Y, uint16_t* Z, void* stream);
+
 /* Backward of the same linear given G = dL/dY (page section
  * "冻结权重为什么仍然需要输入梯度"):
  *   dZ = c G Bᵀ,  dA = Xᵀ dZ (K x r fp32),  dB = c Zᵀ G (r x N fp32),
