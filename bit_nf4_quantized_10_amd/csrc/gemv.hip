@@ -2,17 +2,21 @@
 // (page "QLoRA：冻结的 4-bit 权重怎样参与一次微调", section "量化基座与可训练支路怎样相加";
 // the decode is the one of section "Double Quantization 压缩的是 Scale").
 //
-// Workgroup (4 waves) = one 256-column slab; wave w covers a contiguous range
-// of 32-row steps.  Lane (q, g) owns columns n0 + 16q .. +15 and rows
-// 8g .. 8g+7 of each step.  Per step each wave writes the 128 block tables
-// (32 rows x 4 blocks, 16 bf16 RNE(fl32(C[j] * â)) each) of the step to its
-// own LDS area and decodes by table lookups: one byte-select add and one
-// 16-bit LDS read per weight, pairs packed with v_perm; column t of the lane
-// feeds the MFMA of tile t with the zero-padded 16-row activation block.
-// Three steps of code loads are in flight per wave (per-wave buffer
-// descriptors, so rows past the wave's range read as zeros and meet zero
-// activations).  The four waves are added in LDS in a fixed order; the
-// split-K partials and the LoRA term are added by gemv_finish_kernel.
+// Workgroup (4 waves) = two neighbouring 128-column strips x two row ranges;
+// each wave streams one strip over its own contiguous range of 32-row steps,
+// so the two waves of a row range read the two halves of every 128-byte line
+// at about the same time.  Lane (q, g) owns columns n0 + 8q .. +7 and rows
+// 8g .. 8g+7 of each step.  Per step a wave stages its codes in LDS (16-byte
+// loads of whole 64-byte row pieces), builds the step's 64 block tables
+// (32 rows x 2 blocks, 16 RNE(fl32(C[j] * â)) each; one per lane) and
+// decodes by table lookups: one byte-select add and one 16-bit LDS read per
+// weight, pairs packed with v_perm; column t of the lane feeds the MFMA of
+// tile t with the zero-padded 16-row activation block.  A lookup instruction
+// touches eight tables that together fill the 64 LDS banks once.  Three
+// steps of loads are in flight per wave (per-wave buffer descriptors, so rows
+// past the wave's range read as zeros and meet zero activations).  The two
+// row ranges of a strip are added in LDS in a fixed order; the split-K
+// partials and the LoRA term are added by gemv_finish_kernel.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,17 +32,20 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 }
 
 constexpr int kGvWaves = 4;
-constexpr int kGvCols = 256;    // columns per workgroup slab (16 per lane)
-// One wave's block tables for one 32-row step: row r (4 tables of 16 bf16,
-// 128 bytes) at byte r * 128 + 128 * (r / 8), so that the four rows 8g + c
-// (g = 0..3) that one lookup instruction touches fall on both halves of the
-// 64 LDS banks.
-constexpr int kGvTabBytes = 32 * 128 + 4 * 128;
+constexpr int kGvCols = 128;    // columns per workgroup strip (8 per lane)
+// Per wave, for one 32-row step: the 64 block tables (32 rows x 2 blocks, 16
+// bf16 each) and the step's codes (32 rows x 64 bytes).  The table of row
+// 8g + i, block b sits at byte (4i + g) * 64 + 32b, and code row 8g + i at
+// (4i + g) * 64, so the 64 lanes of one lookup (rows 8g + i, g < 4, both
+// blocks) or of one code read cover the 64 LDS banks once.
+constexpr int kGvTabBytes = 32 * 2 * 32;
+constexpr int kGvStageBytes = 32 * 64;
+constexpr int kGvWaveLds = kGvTabBytes + kGvStageBytes;
 #ifndef QN_GV_DEPTH
 #define QN_GV_DEPTH 3
 #endif
 constexpr int kGvDepth = QN_GV_DEPTH;   // 32-row steps of code loads in flight per wave
-__device__ __forceinline__ int gv_row(int r) { return r * 128 + 128 * (r >> 3); }
+__device__ __forceinline__ int gv_pos(int row) { return 4 * (row & 7) + (row >> 3); }   // row 8g + i -> 4i + g
 
 // base + byte b of w, one VALU instruction (SDWA byte select on the second operand)
 __device__ __forceinline__ uint32_t add_byte(uint32_t base, uint32_t w, int b) {
@@ -146,178 +153,166 @@ __device__ void gemv_zpart(const uint16_t* __restrict__ X, int64_t M, int64_t K,
 }
 
 struct GvStep {
-  uint2 w[8];   // code words of rows 8g..8g+7 (16 columns each)
-  uint4 x;      // activation fragment
-  int q[2];     // second-level codes of the two tables this lane builds
-  float s2[2];
+  uint4 c[2];   // 16 code bytes of one row per load (row order of the LDS stage)
+  uint4 x;      // activation fragment X[q][k + 8g .. k + 8g + 7]
+  int q;        // second-level code of the table this lane builds
+  float s2;
 };
 
-// Workgroup (4 waves) = one 256-column slab; wave w covers rows
+// Workgroup (4 waves) = one 128-column strip; wave w covers rows
 // [(split*4 + w) * rpw, +rpw) in steps of 32.  Lane (q, g): columns
-// n0 + 16q .. +15, rows 8g .. 8g+7 of each step.  Per step, each wave first
-// writes the 128 block tables (32 rows x 4 blocks, 16 bf16 each) of the NEXT
-// step to its LDS ring, then decodes the current step by table lookups, so no
-// per-weight multiply or conversion is needed; column t of the lane feeds the
-// MFMA of tile t.  part[split][m][n] = sum of the 4 waves (fixed order).
+// n0 + 8q .. +7, rows 8g .. 8g+7 of each step.  Per step a wave copies its
+// 2 KB of codes (two 16-byte loads per lane, whole 64-byte row pieces) into
+// its LDS stage, each lane builds one of the step's 64 block tables, and the
+// lane reads its eight 4-byte code words back in MFMA order.  Each weight is
+// one byte-select add and one 16-bit table lookup, pairs packed with v_perm;
+// column t of the lane feeds the MFMA of tile t.  part[split][m][n] = sum of
+// the 4 waves (fixed order).
 template <class T>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemv_kernel(const uint16_t* __restrict__ X, int64_t M, NF4View W, int64_t K,
-                                                   int64_t N, int64_t rpw, int64_t slabs, float* __restrict__ part,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void gemv_kernel(const uint16_t* __restrict__ X, int64_t M, NF4View W, int64_t K,
+                                                   int64_t N, int64_t rpw, int64_t pairs, float* __restrict__ part,
                                                    const uint16_t* __restrict__ A, int64_t r,
                                                    float* __restrict__ zpart) {
   __shared__ float q2t[256];
-  __shared__ __attribute__((aligned(16))) char tabs[kGvWaves * 2 * kGvTabBytes];
+  __shared__ __attribute__((aligned(16))) char lds[kGvWaves * kGvWaveLds];
   const int t = threadIdx.x, lane = t & 63, q = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int64_t splits = (K + kGvWaves * rpw - 1) / (kGvWaves * rpw);
-  if (blockIdx.x >= slabs * splits) {
+  const int64_t splits = (K + 2 * rpw - 1) / (2 * rpw);
+  const int64_t gv = pairs * splits;
+  if (blockIdx.x >= gv) {
     // the last `splits` workgroups: Z partials over the same row ranges
-    gemv_zpart<T>(X, M, K, rpw, A, r, zpart, blockIdx.x - slabs * splits, reinterpret_cast<float*>(tabs));
+    gemv_zpart<T>(X, M, K, rpw / 2, A, r, zpart, blockIdx.x - gv, reinterpret_cast<float*>(lds));
     return;
   }
   q2t[t] = q2_value(t - 128);
-  const int64_t slab = blockIdx.x % slabs, split = blockIdx.x / slabs;
-  const int64_t n0 = slab * kGvCols;
-  const int64_t kw0 = (split * kGvWaves + wave) * rpw;
+  // Workgroup ids are dealt to the 8 XCDs in turn.  Logical workgroup L
+  // (pair L % pairs of row range L / pairs) is placed so that each XCD runs a
+  // contiguous run of L: neighbouring pairs of one row range share an XCD,
+  // whose L2 then fetches the lines of int8 scale codes they share once.
+  const int64_t per = gv / 8, rem = gv % 8, xcd = blockIdx.x % 8;
+  const int64_t L = xcd * per + min(xcd, rem) + blockIdx.x / 8;
+  const int64_t split = L / pairs;
+  const int64_t n0 = (2 * (L % pairs) + (wave & 1)) * kGvCols;
+  const int64_t kw0 = (split * 2 + (wave >> 1)) * rpw;
   const int64_t kend = min(K, kw0 + rpw);   // this wave's rows; nothing past them is fetched
   const int64_t rows = kend > kw0 ? kend - kw0 : 0;
-  const int64_t P = K * N;
-  // descriptors over this wave's rows only: rows past kend read zeros, and the
-  // step advance is a scalar offset (N is a multiple of 64)
   const int64_t kb0 = kend > kw0 ? kw0 : 0;
+  // descriptors over this wave's rows only: rows past kend read zeros
   const Rsrc rc = make_rsrc(W.codes + kb0 * N / 2, rows * N / 2);
   // a state without a second level stores one fp32 scale per block: â = that
   const bool single = W.absmax != nullptr;
+  const int64_t P = K * N;
   const Rsrc rq = single ? make_rsrc(nullptr, 0) : make_rsrc(W.qabsmax + kb0 * N / 64, rows * N / 64);
   const Rsrc rs = single ? make_rsrc(W.absmax, ((P + 63) / 64) * 4) : make_rsrc(W.absmax2, ((P + 16383) / 16384) * 4);
   const int s_shift = single ? 6 : 14;
   const Rsrc rx = make_rsrc(X, M * K * 2);
   const float off = single ? 0.0f : W.offset[0];
-  const int64_t n = n0 + 16 * q;
-  const bool n_ok = n < N;
-  const int blk = q >> 2;
-  char* my_tabs = tabs + wave * 2 * kGvTabBytes;
-  uint32_t voff_w[8], voff_q[2];
+  char* tabs = lds + wave * kGvWaveLds;
+  char* stage = tabs + kGvTabBytes;
+
+  // code load j, lane l: stage position p = 16j + l/4 (row 8(p & 3) + p/4),
+  // bytes 16(l & 3) .. +15 of that row's 64-byte piece
+  uint32_t voff_c[2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) voff_w[i] = n_ok ? static_cast<uint32_t>(((8 * g + i) * N + n) >> 1) : kMasked;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int64_t nb = n0 + 64 * (2 * (lane & 1) + u);
-    voff_q[u] = nb < N ? static_cast<uint32_t>(((lane >> 1) * N + nb) >> 6) : kMasked;
+  for (int j = 0; j < 2; ++j) {
+    const int p = 16 * j + (lane >> 2), row = 8 * (p & 3) + (p >> 2);
+    const int64_t cb = n0 + 32 * (lane & 3);
+    voff_c[j] = cb < N ? static_cast<uint32_t>((row * N + cb) >> 1) : kMasked;
   }
+  // the table this lane builds: row trow, block tblk of the step
+  const int trow = lane >> 1, tblk = lane & 1;
+  const int64_t tcol = n0 + 64 * tblk;
+  const uint32_t voff_q = tcol < N ? static_cast<uint32_t>((trow * N + tcol) >> 6) : kMasked;
+  char* my_tab = tabs + gv_pos(trow) * 64 + 32 * tblk;
   const uint32_t voff_x = q < M ? static_cast<uint32_t>((q * K + kw0 + 8 * g) * 2) : kMasked;
 
   auto load = [&](GvStep& S, int64_t kk) {
+    // offsets past this wave's rows (or masked) are out of the descriptor: zeros
     const uint32_t sw = static_cast<uint32_t>((kk * N) >> 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      S.w[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, voff_w[i], sw, 0));
+    for (int j = 0; j < 2; ++j) S.c[j] = ld_b128(rc, voff_c[j] + sw);
     // zero activations past this wave's rows (their codes read as 0, a finite weight)
     S.x = ld_b128(rx, (kw0 + kk + 8 * g < kend) ? voff_x + static_cast<uint32_t>(kk * 2) : kMasked);
-    const uint32_t sq = static_cast<uint32_t>((kk * N) >> 6);
-    const uint32_t kt = static_cast<uint32_t>(kw0 + kk + (lane >> 1));
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      S.q[u] = static_cast<int>(static_cast<int8_t>(__builtin_amdgcn_raw_buffer_load_b8(rq, voff_q[u], sq, 0)));
-      const uint32_t nb = static_cast<uint32_t>(n0 + 64 * (2 * (lane & 1) + u));
-      const bool ok = kt < kend && nb < N;
-      S.s2[u] = ld_f32(rs, ok ? ((kt * static_cast<uint32_t>(N) + nb) >> s_shift) * 4 : kMasked);
-    }
-  };
-  auto build = [&](const GvStep& S, int buf) {
-    char* tb = my_tabs + buf * kGvTabBytes + gv_row(lane >> 1) + 64 * (lane & 1);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      write_block_table<T>(reinterpret_cast<uint16_t*>(tb + 32 * u),
-                        single ? S.s2[u] : __fadd_rn(__fmul_rn(q2t[S.q[u] + 128], S.s2[u]), off));
+    const int64_t kt = kw0 + kk + trow;
+    const bool ok = kt < kend && tcol < N;
+    S.q = ld_i8(rq, ok ? voff_q + static_cast<uint32_t>((kk * N) >> 6) : kMasked);
+    S.s2 = ld_f32(rs, ok ? static_cast<uint32_t>(((kt * N + tcol) >> s_shift) * 4) : kMasked);
   };
 
-  f32x4 acc[16];
+  f32x4 acc[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = f32x4{0, 0, 0, 0};
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0, 0, 0, 0};
   __syncthreads();  // q2t
   // kGvDepth steps of loads in flight per wave: set u holds step D j + u and
-  // is refilled with step D (j+1) + u as soon as it has been decoded.  Each
-  // wave's tables live in its own LDS ring, so no workgroup barrier is needed
+  // is refilled with step D (j+1) + u as soon as it has been staged.  Each
+  // wave's stage and tables are its own, so no workgroup barrier is needed
   // (LDS operations of one wave complete in order).
   GvStep R[kGvDepth];
 #pragma unroll
   for (int u = 0; u < kGvDepth; ++u) load(R[u], 32 * u);
-  build(R[0], 0);
+  // lookups of row 8g + i go to tbase + 256 i + 2 code
+  const uint32_t tbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tabs + g * 64 + 32 * (q >> 3)));
   for (int64_t kk = 0; kk < rpw; kk += 32 * kGvDepth) {
 #pragma unroll
     for (int u = 0; u < kGvDepth; ++u) {
       const int64_t ks = kk + 32 * u;
       if (ks >= rpw) break;
-      const int buf = static_cast<int>((ks >> 5) & 1);   // tables alternate per 32-row step
-      // table of row 8g + i (i < 8) for this lane's block: tb + 128 i
-      const char* tb = my_tabs + buf * kGvTabBytes + gv_row(8 * g) + 32 * blk;
-      // doubled codes: byte b of ev = 2 * code of column 2b, of od = 2 * code of
-      // column 2b + 1 (x word: columns 0..7, y word: columns 8..15)
-      uint32_t ev[8][2], od[8][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) *reinterpret_cast<uint4*>(stage + j * 1024 + lane * 16) = R[u].c[j];
+      write_block_table<T>(reinterpret_cast<uint16_t*>(my_tab),
+                           single ? R[u].s2 : __fadd_rn(__fmul_rn(q2t[R[u].q + 128], R[u].s2), off));
+      const typename T::v8 xf = __builtin_bit_cast(typename T::v8, R[u].x);
+      uint32_t w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = *reinterpret_cast<const uint32_t*>(stage + (4 * i + g) * 64 + 4 * q);
+      load(R[u], ks + 32 * kGvDepth);   // past the k-range: masked, reads zeros
+      // doubled codes: byte b of ev = 2 * code of column 2b, of od = 2 * code
+      // of column 2b + 1
+      uint32_t ev[8], od[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        ev[i][0] = (R[u].w[i].x >> 3) & 0x1e1e1e1eu;
-        od[i][0] = (R[u].w[i].x << 1) & 0x1e1e1e1eu;
-        ev[i][1] = (R[u].w[i].y >> 3) & 0x1e1e1e1eu;
-        od[i][1] = (R[u].w[i].y << 1) & 0x1e1e1e1eu;
+        ev[i] = (w[i] >> 3) & 0x1e1e1e1eu;
+        od[i] = (w[i] << 1) & 0x1e1e1e1eu;
       }
-      const uint32_t tbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tb));
-      const typename T::v8 xf = __builtin_bit_cast(typename T::v8, R[u].x);
 #pragma unroll
-      for (int tile = 0; tile < 16; ++tile) {
-        const int h = tile >> 3, col = tile & 7;
+      for (int tile = 0; tile < 8; ++tile) {
         uint32_t fw[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const uint32_t a0 = add_byte(tbase, (col & 1) ? od[2 * p][h] : ev[2 * p][h], col >> 1);
-          const uint32_t a1 = add_byte(tbase, (col & 1) ? od[2 * p + 1][h] : ev[2 * p + 1][h], col >> 1);
-          const uint32_t lo = lds_u16(a0 + 2 * p * 128);
-          const uint32_t hi = lds_u16(a1 + (2 * p + 1) * 128);
+          const uint32_t a0 = add_byte(tbase, (tile & 1) ? od[2 * p] : ev[2 * p], tile >> 1);
+          const uint32_t a1 = add_byte(tbase, (tile & 1) ? od[2 * p + 1] : ev[2 * p + 1], tile >> 1);
+          const uint32_t lo = lds_u16(a0 + 2 * p * 256);
+          const uint32_t hi = lds_u16(a1 + (2 * p + 1) * 256);
           fw[p] = perm(hi, lo, 0x05040100u);
         }
         acc[tile] = T::mfma16(xf, __builtin_bit_cast(typename T::v8, make_uint4(fw[0], fw[1], fw[2], fw[3])), acc[tile]);
       }
-      if (ks + 32 < rpw) build(R[(u + 1) % kGvDepth], buf ^ 1);
-      load(R[u], ks + 32 * kGvDepth);   // past the k-range: masked, reads zeros
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // lane holds Y[m = 4g+e][n + tile]; fixed-order sum: (w0 + w2) + (w1 + w3)
-  float* red = reinterpret_cast<float*>(tabs);   // 2 waves x 64 floats x 64 lanes = 32 KB
+  // lane holds Y[m = 4g+e][n0 + 8q + tile]; the two row ranges of a strip
+  // are added in a fixed order: wave w (w < 2) + wave w + 2
+  float* red = reinterpret_cast<float*>(lds);   // 2 waves x 32 floats x 64 lanes = 16 KB
   if (wave >= 2) {
 #pragma unroll
-    for (int tile = 0; tile < 16; ++tile)
+    for (int tile = 0; tile < 8; ++tile)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) red[((wave - 2) * 64 + tile * 4 + e) * 64 + lane] = acc[tile][e];
+      for (int e = 0; e < 4; ++e) red[((wave - 2) * 32 + tile * 4 + e) * 64 + lane] = acc[tile][e];
   }
   __syncthreads();
   if (wave < 2) {
-#pragma unroll
-    for (int tile = 0; tile < 16; ++tile)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[tile][e] += red[(wave * 64 + tile * 4 + e) * 64 + lane];
-  }
-  __syncthreads();
-  if (wave == 1) {
-#pragma unroll
-    for (int tile = 0; tile < 16; ++tile)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) red[(tile * 4 + e) * 64 + lane] = acc[tile][e];
-  }
-  __syncthreads();
-  if (wave == 0) {
     float* out = part + split * M * N;
+    const int64_t n = n0 + 8 * q;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int64_t m = 4 * g + e;
-      float v[16];
+      float v[8];
 #pragma unroll
-      for (int tile = 0; tile < 16; ++tile) v[tile] = acc[tile][e] + red[(tile * 4 + e) * 64 + lane];
-      if (m < M && n_ok) {
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-          *reinterpret_cast<float4*>(out + m * N + n + 4 * h) = make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
+      for (int tile = 0; tile < 8; ++tile) v[tile] = acc[tile][e] + red[(wave * 32 + tile * 4 + e) * 64 + lane];
+      if (m < M && n < N) {
+        *reinterpret_cast<float4*>(out + m * N + n) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(out + m * N + n + 4) = make_float4(v[4], v[5], v[6], v[7]);
       }
     }
   }
@@ -415,18 +410,19 @@ __global__ __launch_bounds__(64) void gemv_finish_kernel(const float* __restrict
 }  // namespace
 
 #ifndef QN_GV_WAVES
-#define QN_GV_WAVES 1400
+#define QN_GV_WAVES 2752
 #endif
 
 void plan_gemv(int64_t M, int64_t K, int64_t N, int64_t r, SkinnyPlan* p_) {
   SkinnyPlan& p = *p_;
-  // 4 waves x rows_per_wave rows per workgroup, ~1400 waves in total
-  const int64_t slabs = cdiv(N, kGvCols);
-  const int64_t groups = cdiv(QN_GV_WAVES, slabs * kGvWaves);
-  int64_t rpw = round_up(cdiv(K, groups * kGvWaves), 32);
-  if (rpw < 64) rpw = 64;
+  // workgroup = 2 strips x 2 row ranges of rows_per_wave rows, about
+  // QN_GV_WAVES waves in total; rows_per_wave is a multiple of 64 so that the Z
+  // workgroups' four waves split a row range in 32-row steps
+  const int64_t pairs = cdiv(N, 2 * kGvCols);
+  const int64_t groups = cdiv(QN_GV_WAVES, pairs * kGvWaves);
+  int64_t rpw = round_up(cdiv(K, groups * 2), 64);
   p.gv_rows_per_wave = rpw;
-  p.gv_splits = cdiv(K, rpw * kGvWaves);
+  p.gv_splits = cdiv(K, 2 * rpw);
   p.gv_part = round_up(p.gv_splits * M * N * 4, 256);
   p.gv_zpart = round_up(p.gv_splits * M * r * 4, 256);
 }
@@ -434,12 +430,12 @@ void plan_gemv(int64_t M, int64_t K, int64_t N, int64_t r, SkinnyPlan* p_) {
 hipError_t launch_gemv(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t* X, NF4View W, const uint16_t* A,
                        const uint16_t* B, float c, uint16_t* Y, uint16_t* Z, const SkinnyPlan& p, void* part_ws,
                        hipStream_t stream, int dtype) {
-  const int64_t slabs = cdiv(N, kGvCols);
+  const int64_t pairs = cdiv(N, 2 * kGvCols);
   float* part = static_cast<float*>(part_ws);
   float* zpart = reinterpret_cast<float*>(static_cast<char*>(part_ws) + p.gv_part);
   Timer tm(QK_FWD_GEMV, stream);
-  hipLaunchKernelGGL(dtype == kDtypeF16 ? gemv_kernel<F16> : gemv_kernel<Bf16>, dim3(static_cast<unsigned>((slabs + 1) * p.gv_splits)), dim3(kGvWaves * 64), 0,
-                     stream, X, M, W, K, N, p.gv_rows_per_wave, slabs, part, A, r, zpart);
+  hipLaunchKernelGGL(dtype == kDtypeF16 ? gemv_kernel<F16> : gemv_kernel<Bf16>, dim3(static_cast<unsigned>((pairs + 1) * p.gv_splits)), dim3(kGvWaves * 64), 0,
+                     stream, X, M, W, K, N, p.gv_rows_per_wave, pairs, part, A, r, zpart);
   tm.stop();
   Timer te(QK_REDUCE, stream);
   const unsigned phases = static_cast<unsigned>(M < 4 ? M : 4);   // rows 4g + e, e < phases
