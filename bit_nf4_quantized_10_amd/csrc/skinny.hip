@@ -169,9 +169,13 @@ struct CsJob {
   const uint16_t* act;   // M x cols, leading dimension ld
   int64_t ld, cols;
   const uint16_t* v;     // M x r, leading dimension v_ld
-  float* part;           // [splits][cols][r]
+  float* part;           // [splits][cols][r]; with `transposed`, the final r x cols result
   int64_t col_blocks, j_chunks, per_split, nblk;
   int64_t r, v_ld;
+  // a job with one split may write its final result: scale * sum, stored
+  // r x cols (row j, column c) instead of as a partial
+  int transposed = 0;
+  float scale = 1.0f;
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -282,6 +286,34 @@ __global__ __launch_bounds__(256) void colsum_kernel(CsJobs jobs, int64_t M) {
       for (int ci = 0; ci < 2; ++ci) acc[vj][ci] = T::mfma32(fv[vj], fa[ci], acc[vj][ci]);
   }
   __builtin_amdgcn_s_waitcnt(0);
+  if (J.transposed) {
+    // each wave's block as [j][c] (rows of 72 floats: the two half-waves'
+    // stores fall on different banks), then the fixed-order wave sum, scaled,
+    // stored along the columns
+    constexpr int kLd = 72;
+    float* mine = reinterpret_cast<float*>(ring);
+    const int h = lane >> 5, cl = lane & 31;
+#pragma unroll
+    for (int vj = 0; vj < 2; ++vj)
+#pragma unroll
+      for (int ci = 0; ci < 2; ++ci)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mine[(32 * vj + 8 * jj + 4 * h + e) * kLd + 32 * ci + cl] = acc[vj][ci][4 * jj + e];
+    __syncthreads();
+    const int j = t >> 2, cq = 16 * (t & 3);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = cq + 4 * u;
+      f32x4 s4 = *reinterpret_cast<const f32x4*>(smem + (j * kLd + c) * 4);
+#pragma unroll
+      for (int w = 1; w < 4; ++w) s4 += *reinterpret_cast<const f32x4*>(smem + w * (kCsSlots * kCsSlot) + (j * kLd + c) * 4);
+      s4 *= J.scale;
+      if (c0 + c < J.cols && jb + j < r) *reinterpret_cast<f32x4*>(J.part + (jb + j) * J.cols + c0 + c) = s4;
+    }
+    return;
+  }
   // each wave's 64 x 64 block, [c][j] fp32, into the start of its own ring
   {
     float* mine = reinterpret_cast<float*>(ring);
@@ -459,11 +491,20 @@ hipError_t launch_colsums(int64_t M, int64_t K, int64_t N, int64_t r, const uint
   CsJob jb{G, N, N, Z, static_cast<float*>(db_ws), cdiv(N, 64), jc, p.db_per, 0, r, r};
   ja.nblk = ja.col_blocks * jc * p.da_splits;
   jb.nblk = jb.col_blocks * jc * p.db_splits;
+  // with one token split the sums are final: dA is written in place, dB
+  // scaled and transposed, and no reduce launch follows
+  const bool direct = p.da_splits == 1 && p.db_splits == 1;
+  if (direct) {
+    ja.part = dA;
+    jb.part = dB;
+    jb.transposed = 1;
+    jb.scale = c;
+  }
   const CsJob both[2] = {ja, jb};
   Timer tm(QK_BWD_COLSUM, stream);
   hipError_t e = launch_colsum(both, 2, M, stream, dtype);
   tm.stop();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || direct) return e;
   const RdJob ra = rdjob(static_cast<float*>(da_ws), p.da_splits, K, r, 1.0f, false, dA, nullptr);
   const RdJob rb = rdjob(static_cast<float*>(db_ws), p.db_splits, N, r, c, true, dB, nullptr);
   return launch_reduce(ra, &rb, stream);
