@@ -17,6 +17,7 @@ dequant-GEMV at M = 1/8/16 on the 65B MLP shape), the 7B MLP set, and the CPU
 oracle timed on a bounded sample of the headline workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-components] [--copy-probe]
+       python bench.py --memory-only | --attn7b-only [--copy-probe]   (profiler runs)
 """
 from __future__ import annotations
 
@@ -126,6 +127,9 @@ def main():
     ap.add_argument("--no-components", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--attn7b-only", action="store_true",
+                    help="run only the 7B attention step (M = K = N = 4096) for --steps steps after --warmup steps "
+                         "(for profiler runs); prints its figures instead of the benchmark line")
     ap.add_argument("--memory-only", action="store_true",
                     help="run only the memory-bound paths on the 65B MLP weight (for profiler runs); prints "
                          "their figures instead of the benchmark line")
@@ -142,6 +146,14 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
+    if args.attn7b_only:
+        attn = attn7b_step(torch, qn, si, dev, steps=args.steps, warmup=args.warmup)[0]
+        if args.copy_probe:
+            a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+            torch.empty_like(a).copy_(a)
+            torch.cuda.synchronize()
+        print(json.dumps({"attn7b_4096": attn}))
+        return
     if args.memory_only:
         flush = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
         status = torch.zeros(1, dtype=torch.int32, device=dev)

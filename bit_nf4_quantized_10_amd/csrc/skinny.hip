@@ -7,14 +7,10 @@
 //     along the reduction, so MFMA fragments are loaded straight from global
 //     memory (A is transposed once, r x K, so that it is too).
 //   dA = Xᵀ dZ (K x r), dB = c Zᵀ G (r x N): "column sums" over the M tokens;
-//     both operands are strided along the reduction, so 32-token tiles are
-//     transposed through LDS.
-//   The small-M forward (M <= 16): each wave streams a 128-column slab of the
-//     packed weight over a k-range with 8 code words per lane per 32 rows,
-//     transposes the nibbles in registers and feeds 8 MFMAs whose A operand is
-//     the (zero-padded) 16-row activation block; the four waves of a workgroup
-//     cover consecutive k-ranges and are summed in LDS in a fixed order; the
-//     split-K partials and the LoRA term c Z B are added by a final kernel.
+//     both operands are strided along the reduction, so 16-token steps are
+//     transposed by LDS reads.  With a single token split the column sums
+//     write dA and dB themselves; otherwise a reduce kernel adds the splits.
+// (The small-M dequant-GEMV is in gemv.hip.)
 // Every reduction is in a fixed order, so results are run-to-run identical.
 #include "common.hpp"
 #include "kernels.hpp"
