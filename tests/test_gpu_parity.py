@@ -295,6 +295,38 @@ def test_layer_fwd_bwd_matches_oracle(M, K, N, r, c):
     assert rel_err(lora, c * Zr @ case["B"]) <= 0.1
 
 
+# Small-M (dequant-GEMV) shapes at the edges of its launch: fewer rows than one
+# 32-row step, K not a multiple of 32 or 64, an odd number of 128-column strips
+# (the second strip of the last workgroup empty or half empty), a single strip,
+# and several row-range pairs with a ragged last one.
+GEMV_EDGE_SHAPES = [
+    (1, 8, 64, 8, 0.5),
+    (3, 72, 320, 8, 2.0),
+    (16, 1000, 448, 16, 0.25),
+    (5, 136, 64, 24, 1.0),
+    (12, 2056, 576, 32, 0.5),
+    (16, 4104, 1088, 64, 0.25),
+]
+
+
+@pytest.mark.parametrize("M,K,N,r,c", GEMV_EDGE_SHAPES)
+def test_gemv_edge_shapes_match_oracle(M, K, N, r, c):
+    say(f"dequant-GEMV edge shape M={M} K={K} N={N} r={r}")
+    case = _layer_case(M, K, N, r, c, seed=M * 31 + K + N)
+    state, Y, Z, dX, dA, dB = _run_layer(case, M, K, N, r)
+    W_hat = o.dequantize(o.quantize(case["W"]), "bf16").reshape(K, N)
+    Yr, Zr = o.layer_forward(case["X"], W_hat, case["A"], case["B"], c)
+    dXr, dAr, dBr, _ = o.layer_backward(case["G"], case["X"], W_hat, case["A"], case["B"], c)
+    errs = {"Y": rel_err(host(Y), Yr), "Z": rel_err(host(Z), Zr), "dX": rel_err(host(dX), dXr),
+            "dA": rel_err(host(dA), dAr), "dB": rel_err(host(dB), dBr)}
+    say(f"errors {errs}")
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
+    # every column, including those of a half-empty last strip, is compared on its own
+    col = np.abs(host(Y).astype(np.float64) - Yr).max(axis=0) / np.abs(Yr).max()
+    assert col.max() <= TOL, int(col.argmax())
+
+
 @pytest.mark.parametrize("M,K,N,r,c", random_layer_shapes(15, 2026))
 def test_layer_random_shapes_match_oracle(M, K, N, r, c):
     say(f"layer fwd/bwd, random shape M={M} K={K} N={N} r={r}")
