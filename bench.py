@@ -620,25 +620,31 @@ def bench_components(torch, qn, si, dev, args):
     torch.cuda.empty_cache()
     res["mlp7b_4096x11008"] = bench_workload_set(torch, qn, si, dev, "mlp7b_4096x11008", flush)
     print("bench: mlp7b_4096x11008 measured", file=sys.stderr, flush=True)
-    # the vendor library's plain bf16 GEMM of the same base shape on this
-    # device (torch.matmul -> hipBLASLt), as context for the MFMA fraction
-    Mv, Kv, Nv = 4096, 4096, 4096
-    xa = torch.randn(Mv, Kv, device=dev).to(torch.bfloat16)
-    wb = torch.randn(Kv, Nv, device=dev).to(torch.bfloat16)
-    yv = torch.empty(Mv, Nv, dtype=torch.bfloat16, device=dev)
-    for _ in range(3):
-        torch.matmul(xa, wb, out=yv)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(20):
-        torch.matmul(xa, wb, out=yv)
-    e1.record()
-    torch.cuda.synchronize()
-    vms = e0.elapsed_time(e1) / 20
-    res["vendor_gemm_bf16_4096"] = {
-        "ms": round(vms, 4), "TFLOPs": round(2 * Mv * Kv * Nv / (vms * 1e-3) / 1e12, 1),
-        "how": "torch.matmul of 4096x4096 by 4096x4096 bf16 (hipBLASLt), 20 back-to-back calls"}
-    del xa, wb, yv
+    # the vendor library's plain bf16 GEMM on this device (torch.matmul ->
+    # hipBLASLt), as context for the MFMA fraction: the 4096^3 base shape and
+    # the four distinct GEMM shapes of the 65B block, the weight operand stored
+    # N x K as the forward's dequantized weight is (both operands contiguous
+    # along the reduction)
+    vendor = {}
+    for (Mv, Kv, Nv) in ((4096, 4096, 4096), (2048, 8192, 8192), (2048, 8192, 22016), (2048, 22016, 8192)):
+        xa = torch.randn(Mv, Kv, device=dev).to(torch.bfloat16)
+        wb = torch.randn(Nv, Kv, device=dev).to(torch.bfloat16)
+        yv = torch.empty(Mv, Nv, dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            torch.matmul(xa, wb.t(), out=yv)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            torch.matmul(xa, wb.t(), out=yv)
+        e1.record()
+        torch.cuda.synchronize()
+        vms = e0.elapsed_time(e1) / 20
+        vendor[f"{Mv}x{Kv}x{Nv}"] = {"ms": round(vms, 4),
+                                     "TFLOPs": round(2 * Mv * Kv * Nv / (vms * 1e-3) / 1e12, 1)}
+        del xa, wb, yv
+    vendor["how"] = ("torch.matmul of M x K by (N x K)ᵀ bf16 (hipBLASLt), random normal operands, "
+                     "20 back-to-back calls per shape, keyed MxKxN")
+    res["vendor_gemm_bf16"] = vendor
     return res
 
 
