@@ -27,7 +27,7 @@ C_FUNCTIONS = [
     "qlora_linear_fwd", "qlora_linear_bwd", "nf4_status_read", "qlora_timer_enable",
     "qlora_timer_read", "qlora_merge", "qlora_sgd_step", "qlora_grouped_workspace_bytes",
     "qlora_grouped_fwd", "qlora_grouped_bwd", "qlora_linear_fwd_dt", "qlora_linear_bwd_dt", "qlora_sgd_step_dt",
-    "qlora_linear_fwd_noalloc", "nf4_error_string",
+    "qlora_linear_fwd_noalloc", "qlora_grouped_fwd_dt", "qlora_grouped_bwd_dt", "nf4_error_string",
 ]
 NF4_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 
@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.qlora_linear_bwd_dt.argtypes = [ctypes.c_int] + L.qlora_linear_bwd.argtypes
         L.qlora_sgd_step_dt.argtypes = [ctypes.c_int] + L.qlora_sgd_step.argtypes
         L.qlora_linear_fwd_noalloc.argtypes = [i64, i64, i64, i64, vp, sp, vp, vp, ctypes.c_float, vp, vp, vp]
+        L.qlora_grouped_fwd_dt.argtypes = [ctypes.c_int] + L.qlora_grouped_fwd.argtypes
+        L.qlora_grouped_bwd_dt.argtypes = [ctypes.c_int] + L.qlora_grouped_bwd.argtypes
         L.nf4_error_string.argtypes = [ctypes.c_int]
         L.nf4_error_string.restype = ctypes.c_char_p
         for name in C_FUNCTIONS[:-1]:
@@ -205,39 +207,48 @@ def qlora_grouped_workspace_bytes(M: int, K: int, Ns, r: int) -> tuple[int, int]
 
 def qlora_grouped_fwd(X, states, A, B, c: float, K: int, Ns, Y=None, Z=None, workspace=None, stream=None):
     """Members sharing X, side by side: A = [A_i] (K x g r), B = [B_i] (r x sum N),
-    returns (Y = [Y_i] (M x sum N), Z = [Z_i] (M x g r))."""
+    returns (Y = [Y_i] (M x sum N), Z = [Z_i] (M x g r)).  The compute type is
+    X's dtype (bf16 or fp16); A, B, Y and Z share it."""
     import torch
     g, Narr, Sarr = _group_args(states, Ns)
     M = X.shape[0]
     r = A.shape[1] // g
     Ntot = sum(Ns)
+    dt = _compute_dtype(X)
     for t, n in ((X, "X"), (A, "A"), (B, "B")):
-        _require_cuda(t, n, torch.bfloat16)
+        _require_cuda(t, n, dt)
     if Y is None:
-        Y = torch.empty(M, Ntot, dtype=torch.bfloat16, device=X.device)
+        Y = torch.empty(M, Ntot, dtype=dt, device=X.device)
     if Z is None:
-        Z = torch.empty(M, g * r, dtype=torch.bfloat16, device=X.device)
+        Z = torch.empty(M, g * r, dtype=dt, device=X.device)
+    _require_cuda(Y, "Y", dt)
+    _require_cuda(Z, "Z", dt)
     if workspace is None:
         workspace = torch.empty(max(qlora_grouped_workspace_bytes(M, K, Ns, r)[0], 256), dtype=torch.uint8,
                                 device=X.device)
-    _check(lib().qlora_grouped_fwd(M, K, g, Narr, r, X.data_ptr(), Sarr, A.data_ptr(), B.data_ptr(),
-                                   ctypes.c_float(c), Y.data_ptr(), Z.data_ptr(), workspace.data_ptr(),
-                                   workspace.numel(), _stream(stream)), "qlora_grouped_fwd")
+    _check(lib().qlora_grouped_fwd_dt(_COMPUTE[dt], M, K, g, Narr, r, X.data_ptr(), Sarr, A.data_ptr(),
+                                      B.data_ptr(), ctypes.c_float(c), Y.data_ptr(), Z.data_ptr(),
+                                      workspace.data_ptr(), workspace.numel(), _stream(stream)),
+           "qlora_grouped_fwd_dt")
     return Y, Z
 
 
 def qlora_grouped_bwd(G, X, Z, states, A, B, c: float, K: int, Ns, need_dx: bool = True, dX=None, dA=None,
                       dB=None, workspace=None, stream=None):
-    """Returns (dX or None, dA = [dA_i] (K x g r fp32), dB = [dB_i] (r x sum N fp32))."""
+    """Returns (dX or None, dA = [dA_i] (K x g r fp32), dB = [dB_i] (r x sum N fp32)).
+    The compute type is X's dtype (bf16 or fp16); G, Z, A, B and dX share it."""
     import torch
     g, Narr, Sarr = _group_args(states, Ns)
     M = X.shape[0]
     r = A.shape[1] // g
     Ntot = sum(Ns)
+    dt = _compute_dtype(X)
     for t, n in ((G, "G"), (X, "X"), (Z, "Z"), (A, "A"), (B, "B")):
-        _require_cuda(t, n, torch.bfloat16)
+        _require_cuda(t, n, dt)
     if need_dx and dX is None:
-        dX = torch.empty(M, K, dtype=torch.bfloat16, device=X.device)
+        dX = torch.empty(M, K, dtype=dt, device=X.device)
+    if need_dx:
+        _require_cuda(dX, "dX", dt)
     if dA is None:
         dA = torch.empty(K, g * r, dtype=torch.float32, device=X.device)
     if dB is None:
@@ -245,10 +256,11 @@ def qlora_grouped_bwd(G, X, Z, states, A, B, c: float, K: int, Ns, need_dx: bool
     if workspace is None:
         workspace = torch.empty(max(qlora_grouped_workspace_bytes(M, K, Ns, r)[1], 256), dtype=torch.uint8,
                                 device=X.device)
-    _check(lib().qlora_grouped_bwd(M, K, g, Narr, r, G.data_ptr(), X.data_ptr(), Z.data_ptr(), Sarr,
-                                   A.data_ptr(), B.data_ptr(), ctypes.c_float(c),
-                                   dX.data_ptr() if need_dx else None, dA.data_ptr(), dB.data_ptr(),
-                                   workspace.data_ptr(), workspace.numel(), _stream(stream)), "qlora_grouped_bwd")
+    _check(lib().qlora_grouped_bwd_dt(_COMPUTE[dt], M, K, g, Narr, r, G.data_ptr(), X.data_ptr(), Z.data_ptr(),
+                                      Sarr, A.data_ptr(), B.data_ptr(), ctypes.c_float(c),
+                                      dX.data_ptr() if need_dx else None, dA.data_ptr(), dB.data_ptr(),
+                                      workspace.data_ptr(), workspace.numel(), _stream(stream)),
+           "qlora_grouped_bwd_dt")
     return (dX if need_dx else None), dA, dB
 
 

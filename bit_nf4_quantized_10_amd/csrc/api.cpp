@@ -266,11 +266,12 @@ int qlora_grouped_workspace_bytes(int64_t M, int64_t K, int g, const int64_t* N,
   return NF4_OK;
 }
 
-int qlora_grouped_fwd(int64_t M, int64_t K, int g, const int64_t* N, int64_t r, const uint16_t* X,
-                      const nf4_state_t* W, const uint16_t* A, const uint16_t* B, float c, uint16_t* Y, uint16_t* Z,
-                      void* workspace, int64_t workspace_bytes, void* stream) {
+int qlora_grouped_fwd_dt(int compute_dtype, int64_t M, int64_t K, int g, const int64_t* N, int64_t r,
+                         const uint16_t* X, const nf4_state_t* W, const uint16_t* A, const uint16_t* B, float c,
+                         uint16_t* Y, uint16_t* Z, void* workspace, int64_t workspace_bytes, void* stream) {
   int64_t Ntot;
   qn::NF4View views[qn::kMaxGroupMembers];
+  if (!dtype_ok(compute_dtype)) return NF4_EINVAL;
   if (!grouped_shape_ok(M, K, g, N, r, &Ntot) || !grouped_states_ok(W, g, K, N, views)) return NF4_EINVAL;
   if (!X || !A || !B || !Y || !Z || !workspace) return NF4_EINVAL;
   if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y) || !aligned16(Z) ||
@@ -278,15 +279,24 @@ int qlora_grouped_fwd(int64_t M, int64_t K, int g, const int64_t* N, int64_t r, 
     return NF4_EINVAL;
   if (workspace_bytes < qn::grouped_fwd_workspace_bytes(M, K, g, N, r)) return NF4_EINVAL;
   hipError_t e = qn::launch_grouped_fwd(M, K, g, N, r, X, views, A, B, c, Y, Z, workspace,
-                                        static_cast<hipStream_t>(stream));
+                                        static_cast<hipStream_t>(stream), compute_dtype);
   return e == hipSuccess ? NF4_OK : NF4_EHIP;
 }
 
-int qlora_grouped_bwd(int64_t M, int64_t K, int g, const int64_t* N, int64_t r, const uint16_t* G, const uint16_t* X,
-                      const uint16_t* Z, const nf4_state_t* W, const uint16_t* A, const uint16_t* B, float c,
-                      uint16_t* dX, float* dA, float* dB, void* workspace, int64_t workspace_bytes, void* stream) {
+int qlora_grouped_fwd(int64_t M, int64_t K, int g, const int64_t* N, int64_t r, const uint16_t* X,
+                      const nf4_state_t* W, const uint16_t* A, const uint16_t* B, float c, uint16_t* Y, uint16_t* Z,
+                      void* workspace, int64_t workspace_bytes, void* stream) {
+  return qlora_grouped_fwd_dt(NF4_COMPUTE_BF16, M, K, g, N, r, X, W, A, B, c, Y, Z, workspace, workspace_bytes,
+                              stream);
+}
+
+int qlora_grouped_bwd_dt(int compute_dtype, int64_t M, int64_t K, int g, const int64_t* N, int64_t r,
+                         const uint16_t* G, const uint16_t* X, const uint16_t* Z, const nf4_state_t* W,
+                         const uint16_t* A, const uint16_t* B, float c, uint16_t* dX, float* dA, float* dB,
+                         void* workspace, int64_t workspace_bytes, void* stream) {
   int64_t Ntot;
   qn::NF4View views[qn::kMaxGroupMembers];
+  if (!dtype_ok(compute_dtype)) return NF4_EINVAL;
   if (!grouped_shape_ok(M, K, g, N, r, &Ntot) || !grouped_states_ok(W, g, K, N, views)) return NF4_EINVAL;
   if (!G || !X || !Z || !A || !B || !dA || !dB || !workspace) return NF4_EINVAL;
   if (!aligned16(G) || !aligned16(X) || !aligned16(Z) || !aligned16(A) || !aligned16(B) || !aligned16(dA) ||
@@ -294,8 +304,15 @@ int qlora_grouped_bwd(int64_t M, int64_t K, int g, const int64_t* N, int64_t r, 
     return NF4_EINVAL;
   if (workspace_bytes < qn::grouped_bwd_workspace_bytes(M, K, g, N, r)) return NF4_EINVAL;
   hipError_t e = qn::launch_grouped_bwd(M, K, g, N, r, G, X, Z, views, A, B, c, dX, dA, dB, workspace,
-                                        static_cast<hipStream_t>(stream));
+                                        static_cast<hipStream_t>(stream), compute_dtype);
   return e == hipSuccess ? NF4_OK : NF4_EHIP;
+}
+
+int qlora_grouped_bwd(int64_t M, int64_t K, int g, const int64_t* N, int64_t r, const uint16_t* G, const uint16_t* X,
+                      const uint16_t* Z, const nf4_state_t* W, const uint16_t* A, const uint16_t* B, float c,
+                      uint16_t* dX, float* dA, float* dB, void* workspace, int64_t workspace_bytes, void* stream) {
+  return qlora_grouped_bwd_dt(NF4_COMPUTE_BF16, M, K, g, N, r, G, X, Z, W, A, B, c, dX, dA, dB, workspace,
+                              workspace_bytes, stream);
 }
 
 int qlora_merge(int64_t K, int64_t N, int64_t r, const nf4_state_t* W, const void* A, const void* B, int ab_dtype,

@@ -74,11 +74,11 @@ int64_t grouped_fwd_workspace_bytes(int64_t M, int64_t K, int g, const int64_t* 
 int64_t grouped_bwd_workspace_bytes(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r);
 hipError_t launch_grouped_fwd(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r, const uint16_t* X,
                               const NF4View* W, const uint16_t* A, const uint16_t* B, float c, uint16_t* Y,
-                              uint16_t* Z, void* ws, hipStream_t stream);
+                              uint16_t* Z, void* ws, hipStream_t stream, int dtype = kDtypeBf16);
 hipError_t launch_grouped_bwd(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r, const uint16_t* G,
                               const uint16_t* X, const uint16_t* Z, const NF4View* W, const uint16_t* A,
                               const uint16_t* B, float c, uint16_t* dX, float* dA, float* dB, void* ws,
-                              hipStream_t stream);
+                              hipStream_t stream, int dtype = kDtypeBf16);
 
 // Workspace needs (bytes) of the layer kernels; the C ABI adds them up.
 int64_t fwd_workspace_bytes(int64_t M, int64_t K, int64_t N, int64_t r);

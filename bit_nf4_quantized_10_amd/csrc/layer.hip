@@ -128,7 +128,7 @@ hipError_t launch_bwd(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_t
 // ------------------------------------------------------------ grouped linears
 // g members sharing X with their outputs side by side (Y, G: M x Ntot;
 // A, dA: K x g r; B, dB: r x Ntot; Z: M x g r).  Every member is
-// dequantized to bf16 into one stacked weight and the product runs as one
+// dequantized to the compute type (bf16 or fp16) into one stacked weight and the product runs as one
 // dense GEMM over all Ntot columns (forward) or over all Ntot reduction
 // columns (dX), with one Z = X A over all g r columns.  The transposes ride
 // in the first member's dequantize launch, each member's dZ sum in its own
@@ -152,7 +152,7 @@ int64_t grouped_bwd_workspace_bytes(int64_t M, int64_t K, int g, const int64_t* 
 
 hipError_t launch_grouped_fwd(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r, const uint16_t* X,
                               const NF4View* W, const uint16_t* A, const uint16_t* B, float c, uint16_t* Y,
-                              uint16_t* Z, void* ws, hipStream_t stream) {
+                              uint16_t* Z, void* ws, hipStream_t stream, int dtype) {
   const GroupPlan gp = plan_grouped(M, K, g, Ns, r);
   int64_t Ntot = 0;
   for (int i = 0; i < g; ++i) Ntot += Ns[i];
@@ -162,28 +162,28 @@ hipError_t launch_grouped_fwd(int64_t M, int64_t K, int g, const int64_t* Ns, in
   uint16_t* wt = reinterpret_cast<uint16_t*>(zpart + gp.zp.z_part + align256(Ntot * r * 2));
   // Aᵀ and (c B)ᵀ of all members ride along in the first member's dequantize launch
   TJob tj[2];
-  lora_transposes(K, g * r, A, reinterpret_cast<uint16_t*>(base), Ntot, B, c, cbt, r, kDtypeBf16, tj);
+  lora_transposes(K, g * r, A, reinterpret_cast<uint16_t*>(base), Ntot, B, c, cbt, r, dtype, tj);
   hipError_t e;
   int64_t gend[kMaxGroupMembers];
   int64_t off = 0;
   for (int i = 0; i < g; ++i) {
-    if ((e = launch_dequant_bf16(W[i], K, Ns[i], true, wt + off * K, stream, 0, kDtypeBf16, i == 0 ? tj : nullptr)) !=
+    if ((e = launch_dequant_bf16(W[i], K, Ns[i], true, wt + off * K, stream, 0, dtype, i == 0 ? tj : nullptr)) !=
         hipSuccess)
       return e;
     off += Ns[i];
     gend[i] = off;
   }
-  if ((e = launch_lora_down(M, K, g * r, X, A, Z, gp.zp, base, zpart, stream, Ntot, B, c, cbt, r, kDtypeBf16, true)) !=
+  if ((e = launch_lora_down(M, K, g * r, X, A, Z, gp.zp, base, zpart, stream, Ntot, B, c, cbt, r, dtype, true)) !=
       hipSuccess)
     return e;
-  return launch_fwd_dense_grouped(M, K, Ntot, r, X, wt, Z, g, gend, cbt, Y, stream, kDtypeBf16,
+  return launch_fwd_dense_grouped(M, K, Ntot, r, X, wt, Z, g, gend, cbt, Y, stream, dtype,
                                   reinterpret_cast<char*>(wt) + align256(Ntot * K * 2));
 }
 
 hipError_t launch_grouped_bwd(int64_t M, int64_t K, int g, const int64_t* Ns, int64_t r, const uint16_t* G,
                               const uint16_t* X, const uint16_t* Z, const NF4View* W, const uint16_t* A,
                               const uint16_t* B, float c, uint16_t* dX, float* dA, float* dB, void* ws,
-                              hipStream_t stream) {
+                              hipStream_t stream, int dtype) {
   const GroupPlan gp = plan_grouped(M, K, g, Ns, r);
   int64_t Ntot = 0;
   for (int i = 0; i < g; ++i) Ntot += Ns[i];
@@ -194,23 +194,23 @@ hipError_t launch_grouped_bwd(int64_t M, int64_t K, int g, const int64_t* Ns, in
   uint16_t* wd = reinterpret_cast<uint16_t*>(db_ws + gp.db_part_total);
   // with dX wanted, member i's dZ sum rides along in member i's dequantize launch
   RdJob jz[kMaxGroupMembers];
-  hipError_t e = launch_dz_grouped(M, g, Ns, Ntot, r, G, B, c, dz16, gp, base, stream, kDtypeBf16,
+  hipError_t e = launch_dz_grouped(M, g, Ns, Ntot, r, G, B, c, dz16, gp, base, stream, dtype,
                                    dX != nullptr ? jz : nullptr);
   if (e != hipSuccess) return e;
   if (dX != nullptr) {
     int64_t off = 0;
     for (int i = 0; i < g; ++i) {
-      if ((e = launch_dequant_bf16(W[i], K, Ns[i], false, wd + off, stream, Ntot, kDtypeBf16, nullptr, &jz[i])) !=
+      if ((e = launch_dequant_bf16(W[i], K, Ns[i], false, wd + off, stream, Ntot, dtype, nullptr, &jz[i])) !=
           hipSuccess)
         return e;
       off += Ns[i];
     }
   }
-  if ((e = launch_colsums_grouped(M, K, g, Ns, Ntot, r, X, G, Z, dz16, c, dA, dB, gp, da_ws, db_ws, stream)) !=
+  if ((e = launch_colsums_grouped(M, K, g, Ns, Ntot, r, X, G, Z, dz16, c, dA, dB, gp, da_ws, db_ws, stream, dtype)) !=
       hipSuccess)
     return e;
   if (dX == nullptr) return hipGetLastError();
-  return launch_dx_dense(M, K, Ntot, g * r, G, wd, dz16, A, dX, stream, kDtypeBf16,
+  return launch_dx_dense(M, K, Ntot, g * r, G, wd, dz16, A, dX, stream, dtype,
                          reinterpret_cast<char*>(wd) + align256(K * Ntot * 2));
 }
 

@@ -218,8 +218,9 @@ int qlora_sgd_step_dt(int param_dtype, int64_t K, int64_t N, int64_t r, uint16_t
  * with X read once.  Every N[i] must be a multiple of 256 and r a multiple
  * of 8 (so no 8-element chunk of Z, A or B straddles two members); the concatenated
  * shape (M, K, Ntot, g r) must meet qlora_linear_fwd's requirements; W is a
- * host array of g states.  All members are dequantized to a bf16 workspace
- * and multiplied by one dense GEMM for any M.  Host only: */
+ * host array of g states.  All members are dequantized to a 16-bit workspace
+ * and multiplied by one dense GEMM for any M (fp16: qlora_grouped_fwd_dt
+ * below).  Host only: */
 int qlora_grouped_workspace_bytes(int64_t M, int64_t K, int g, const int64_t* N, int64_t r,
                                   int64_t* fwd_bytes, int64_t* bwd_bytes);
 int qlora_grouped_fwd(int64_t M, int64_t K, int g, const int64_t* N, int64_t r, const uint16_t* X,
@@ -246,6 +247,18 @@ int qlora_linear_bwd_dt(int compute_dtype, int64_t M, int64_t K, int64_t N, int6
                         const uint16_t* X, const uint16_t* Z, const nf4_state_t* W, const uint16_t* A,
                         const uint16_t* B, float c, uint16_t* dX, float* dA, float* dB, void* workspace,
                         int64_t workspace_bytes, void* stream);
+/* The grouped calls (qlora_grouped_fwd / _bwd above) in the compute type
+ * compute_dtype (page "SFT（四）：QLoRA的4-bit量化与LoRA微调原理" §20): X, A, B, G, Y, Z and dX
+ * of that type, the stacked weight RNE_T(ŵ), dA and dB fp32, fp32
+ * accumulation.  qlora_grouped_fwd / _bwd are the NF4_COMPUTE_BF16 case;
+ * requirements, errors and results are otherwise the same. */
+int qlora_grouped_fwd_dt(int compute_dtype, int64_t M, int64_t K, int g, const int64_t* N, int64_t r,
+                         const uint16_t* X, const nf4_state_t* W, const uint16_t* A, const uint16_t* B, float c,
+                         uint16_t* Y, uint16_t* Z, void* workspace, int64_t workspace_bytes, void* stream);
+int qlora_grouped_bwd_dt(int compute_dtype, int64_t M, int64_t K, int g, const int64_t* N, int64_t r,
+                         const uint16_t* G, const uint16_t* X, const uint16_t* Z, const nf4_state_t* W,
+                         const uint16_t* A, const uint16_t* B, float c, uint16_t* dX, float* dA, float* dB,
+                         void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Synchronise `stream`, then copy the device status word to *host_value.
  * Returns NF4_EHIP if the copy fails, else NF4_OK. */

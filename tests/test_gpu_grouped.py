@@ -43,12 +43,13 @@ def _group_case(M, K, Ns, r, c, seed, integer=False):
     return dict(Ws=Ws, X=X, A=A, B=B, G=G, Xb=Xb, Ab=Ab, Bb=Bb, Gb=Gb, c=c)
 
 
-def _oracle(case, Ns, r):
-    """Member by member with the oracle's layer: outputs side by side, dX summed."""
+def _oracle(case, Ns, r, wdt="bf16"):
+    """Member by member with the oracle's layer: outputs side by side, dX summed.
+    wdt: the 16-bit type of the dequantized weight ("bf16" or "f16")."""
     Ys, Zs, dAs, dBs, dX = [], [], [], [], 0.0
     off = 0
     for i, N in enumerate(Ns):
-        W_hat = o.dequantize(o.quantize(case["Ws"][i]), "bf16").reshape(-1, N)
+        W_hat = o.dequantize(o.quantize(case["Ws"][i]), wdt).reshape(-1, N)
         A_i, B_i = case["A"][:, i * r:(i + 1) * r], case["B"][:, off:off + N]
         Y, Z = o.layer_forward(case["X"], W_hat, A_i, B_i, case["c"])
         dX_i, dA_i, dB_i, _ = o.layer_backward(case["G"][:, off:off + N], case["X"], W_hat, A_i, B_i, case["c"])
@@ -58,13 +59,19 @@ def _oracle(case, Ns, r):
     return np.hstack(Ys), np.hstack(Zs), dX, np.hstack(dAs), np.hstack(dBs)
 
 
-def _run(case, K, Ns, need_dx=True):
+def _dev_f16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(torch.float16).cuda()
+
+
+def _run(case, K, Ns, need_dx=True, f16=False):
     states = []
     for W in case["Ws"]:
         st, status = qn.nf4_quantize(dev_f32(W))
         assert qn.nf4_status_read(status) == 0
         states.append(st)
-    X, A, B, G = (dev_bf16(case[k]) for k in ("Xb", "Ab", "Bb", "Gb"))
+    dev = _dev_f16 if f16 else dev_bf16
+    X, A, B, G = (dev(case[k]) for k in ("Xb", "Ab", "Bb", "Gb"))
     Y, Z = qn.qlora_grouped_fwd(X, states, A, B, case["c"], K, Ns)
     dX, dA, dB = qn.qlora_grouped_bwd(G, X, Z, states, A, B, case["c"], K, Ns, need_dx=need_dx)
     return Y, Z, dX, dA, dB
@@ -133,6 +140,52 @@ def test_grouped_exact_integer_case_bit_exact(M, K, Ns, r):
         r32 = o.bf16_round(ref.astype(np.float32))
         assert np.array_equal(r32, ref.astype(np.float32)), f"{name} not bf16-exact by construction"
         np.testing.assert_array_equal(host(got), r32, err_msg=name)
+    np.testing.assert_array_equal(host(dA), dAr.astype(np.float32))
+    np.testing.assert_array_equal(host(dB), dBr.astype(np.float32))
+
+
+def _f16_group_case(M, K, Ns, r, c, seed):
+    rng = np.random.default_rng(seed)
+    g, Ntot = len(Ns), sum(Ns)
+    Ws = [(rng.standard_normal((K, N)) * 0.02).astype(np.float32) for N in Ns]
+    mk = lambda shape, std: si.f16_normal(shape, std, int(rng.integers(1 << 30)))
+    Xb, X = mk((M, K), 1.0)
+    Ab, A = mk((K, g * r), 1.0 / r)
+    Bb, B = mk((r, Ntot), 0.1)
+    Gb, G = mk((M, Ntot), 1.0)
+    return dict(Ws=Ws, X=X, A=A, B=B, G=G, Xb=Xb, Ab=Ab, Bb=Bb, Gb=Gb, c=c)
+
+
+@pytest.mark.parametrize("M,K,Ns,r,c", [(600, 264, [256, 512, 256], 16, 0.5), (16, 256, [256, 256], 8, 2.0),
+                                         (64, 1032, [256, 512], 16, 0.5)] + _random_group_shapes(3, 91))
+def test_grouped_f16_matches_oracle(M, K, Ns, r, c):
+    """The grouped calls in the fp16 compute type (qlora_grouped_fwd_dt /
+    _bwd_dt): every member against the oracle with its fp16 weight."""
+    import torch
+    say(f"grouped fp16 M={M} K={K} Ns={Ns} r={r}")
+    case = _f16_group_case(M, K, Ns, r, c, seed=M + 7 * K + len(Ns))
+    Y, Z, dX, dA, dB = _run(case, K, Ns, f16=True)
+    assert Y.dtype == torch.float16 and Z.dtype == torch.float16 and dX.dtype == torch.float16
+    Yr, Zr, dXr, dAr, dBr = _oracle(case, Ns, r, "f16")
+    errs = {"Y": rel_err(host(Y), Yr), "Z": rel_err(host(Z), Zr), "dX": rel_err(host(dX), dXr),
+            "dA": rel_err(host(dA), dAr), "dB": rel_err(host(dB), dBr)}
+    say(f"errors {errs}")
+    for k, v in errs.items():
+        assert v <= TOL, (k, v)
+
+
+@pytest.mark.parametrize("M,K,Ns,r", [(96, 320, [256, 256, 512], 16), (520, 256, [256, 768], 8)])
+def test_grouped_f16_exact_integer_case_bit_exact(M, K, Ns, r):
+    say(f"grouped fp16 exact-integer M={M} K={K} Ns={Ns} r={r}")
+    case = _group_case(M, K, Ns, r, 0.5, seed=M + 11, integer=True)
+    for k in ("X", "A", "B", "G"):
+        case[k + "b"] = case[k].astype(np.float16).view(np.uint16)
+    Y, Z, dX, dA, dB = _run(case, K, Ns, f16=True)
+    Yr, Zr, dXr, dAr, dBr = _oracle(case, Ns, r, "f16")
+    for got, ref, name in ((Y, Yr, "Y"), (Z, Zr, "Z"), (dX, dXr, "dX")):
+        r16 = o.f16_round(ref.astype(np.float32))
+        assert np.array_equal(r16, ref.astype(np.float32)), f"{name} not fp16-exact by construction"
+        np.testing.assert_array_equal(host(got), r16, err_msg=name)
     np.testing.assert_array_equal(host(dA), dAr.astype(np.float32))
     np.testing.assert_array_equal(host(dB), dBr.astype(np.float32))
 

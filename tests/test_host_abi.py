@@ -172,6 +172,21 @@ def test_grouped_entry_points_reject_bad_arguments():
                                0x10000, 1 << 30, None) == qn.NF4_EINVAL
 
 
+def test_grouped_dt_entry_points_reject_unknown_compute_type():
+    """qlora_grouped_fwd_dt / _bwd_dt take NF4_COMPUTE_BF16 or NF4_COMPUTE_F16
+    only; anything else is rejected before any launch."""
+    L = qn.lib()
+    i64 = ctypes.c_int64
+    Ns = (i64 * 2)(256, 256)
+    states = (qn._State * 2)(*[qn._State(256 * 256, 0x1000, 0x2000, 0x3000, 0x4000) for _ in range(2)])
+    for dt in (-1, 2, 7):
+        assert L.qlora_grouped_fwd_dt(dt, 8, 256, 2, Ns, 8, 0x100, states, 0x200, 0x300, ctypes.c_float(1.0),
+                                      0x400, 0x500, 0x10000, 1 << 30, None) == qn.NF4_EINVAL
+        assert L.qlora_grouped_bwd_dt(dt, 8, 256, 2, Ns, 8, 0x100, 0x100, 0x500, states, 0x200, 0x300,
+                                      ctypes.c_float(1.0), None, 0x600, 0x700, 0x10000, 1 << 30,
+                                      None) == qn.NF4_EINVAL
+
+
 @pytest.mark.parametrize("g,r", [(2, 4), (4, 2), (8, 1), (2, 12), (3, 20)])
 def test_grouped_member_rank_must_be_a_multiple_of_8(g, r):
     """Per-member ranks that are not multiples of 8 are rejected by all three
