@@ -318,86 +318,124 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   }
 }
 
-// Y = sum_s part[s] + c Z B for M <= 16: one wave per 128 columns and row
-// phase e (blockIdx.y); lane (q, g) owns columns n0+8q..+7 and row 4g+e.
-// The LoRA product runs on MFMA with B transposed in registers (every phase
-// computes it; only row 4g+e is kept).  Z = RNE_bf16(sum_s zpart[s]) in a
-// fixed order; workgroup (0, 0) writes it.  The split loops request 8
-// partials at a time before adding them in order.
-template <class T>
-__global__ __launch_bounds__(64) void gemv_finish_kernel(const float* __restrict__ part, int splits, int64_t M,
-                                                         int64_t N, const float* __restrict__ zpart,
-                                                         uint16_t* __restrict__ Z, const uint16_t* __restrict__ B,
-                                                         int64_t r, float c, uint16_t* __restrict__ Y) {
-  const int lane = threadIdx.x, q = lane & 15, g = lane >> 4;
-  const int e = blockIdx.y;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 128, n = n0 + 8 * q;
-  const bool n_ok = n < N;
-  const Rsrc rb = make_rsrc(B, r * N * 2);
-  const Rsrc rzp = make_rsrc(zpart, static_cast<int64_t>(splits) * M * r * 4);
-  const Rsrc rp = make_rsrc(part, static_cast<int64_t>(splits) * M * N * 4);
-  f32x4 accl[8];
+// Y = sum_s part[s] + c Z B for M <= 16.  Workgroup (4 waves) = 512
+// columns and row phase e (blockIdx.y); lane (q, g) of wave w owns columns
+// n0 + 128w + 8q .. +7 and row 4g + e.  A workgroup requests at its start
+// the first 8 split partials of its outputs, the first 64 rows of B and the
+// first 8 split partials of Z, so that the common case (splits <= 8,
+// M r <= 1024, r <= 64) waits for memory once.  The workgroup forms
+// Z = RNE_T(sum_s zpart[s]) in LDS, and workgroup (0, 0) writes it out; the
+// LoRA product runs on MFMA with Z from LDS and B transposed in registers
+// (every phase computes all 16 rows; only row 4g + e is kept).  Partials past
+// the last split read as +0 and are added all the same: the running sums
+// start at +0 and can never be -0, so adding +0 leaves them unchanged.
+constexpr int kFinCols = 512;
+__device__ __forceinline__ void fin_add4(float (&s)[4], const uint4 (&v)[8]) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) accl[i] = f32x4{0, 0, 0, 0};
-  for (int64_t j0 = 0; j0 < r; j0 += 32) {
+  for (int k = 0; k < 8; ++k) {
+    s[0] += __builtin_bit_cast(float, v[k].x); s[1] += __builtin_bit_cast(float, v[k].y);
+    s[2] += __builtin_bit_cast(float, v[k].z); s[3] += __builtin_bit_cast(float, v[k].w);
+  }
+}
+__device__ __forceinline__ void fin_add8(float (&s)[8], const uint4 (&a)[8], const uint4 (&b)[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    s[0] += __builtin_bit_cast(float, a[k].x); s[1] += __builtin_bit_cast(float, a[k].y);
+    s[2] += __builtin_bit_cast(float, a[k].z); s[3] += __builtin_bit_cast(float, a[k].w);
+    s[4] += __builtin_bit_cast(float, b[k].x); s[5] += __builtin_bit_cast(float, b[k].y);
+    s[6] += __builtin_bit_cast(float, b[k].z); s[7] += __builtin_bit_cast(float, b[k].w);
+  }
+}
+template <class T>
+__global__ __launch_bounds__(256) void gemv_finish_kernel(const float* __restrict__ part, int splits, int64_t M,
+                                                          int64_t N, const float* __restrict__ zpart,
+                                                          uint16_t* __restrict__ Z, const uint16_t* __restrict__ B,
+                                                          int64_t r, float c, uint16_t* __restrict__ Y) {
+  __shared__ __attribute__((aligned(16))) uint16_t zl[16 * 256];   // Z, M x r (M <= 16, r <= 256)
+  const int t = threadIdx.x, lane = t & 63, q = lane & 15, g = lane >> 4, wave = t >> 6;
+  const int e = blockIdx.y;
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * kFinCols + 128 * wave + 8 * q;
+  const bool n_ok = n < N;
+  const int64_t m = 4 * g + e;
+  const bool out_ok = m < M && n_ok;
+  const int64_t MR = M * r;
+  const Rsrc rb = make_rsrc(B, r * N * 2);
+  const Rsrc rzp = make_rsrc(zpart, static_cast<int64_t>(splits) * MR * 4);
+  const Rsrc rp = make_rsrc(part, static_cast<int64_t>(splits) * M * N * 4);
+  auto load_b = [&](int64_t j0, uint4 (&rows8)[8]) {
     const int64_t jb = j0 + 8 * g;
-    const bool zok = q < M && jb < r;
-    uint4 rows8[8], cols8[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       rows8[i] = ld_b128(rb, (jb + i < r && n_ok) ? static_cast<uint32_t>(((jb + i) * N + n) * 2) : kMasked);
-    float zs[8];
+  };
+  auto load_part = [&](int s0, uint4 (&pa)[8], uint4 (&pb)[8]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) zs[i] = 0.0f;
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t off = (out_ok && s0 + k < splits) ? static_cast<uint32_t>((((s0 + k) * M + m) * N + n) * 4) : kMasked;
+      pa[k] = ld_b128(rp, off);
+      pb[k] = ld_b128(rp, off == kMasked ? kMasked : off + 16);
+    }
+  };
+  // thread t sums elements idx .. idx+3 of the row-major M x r matrix Z
+  // (r % 8 == 0, so a group of 4 never leaves its row)
+  auto load_z = [&](int s0, int64_t idx, uint4 (&za)[8]) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      za[k] = ld_b128(rzp, (idx < MR && s0 + k < splits) ? static_cast<uint32_t>(((s0 + k) * MR + idx) * 4) : kMasked);
+  };
+  auto store_z = [&](int64_t idx, const float (&zs)[4]) {
+    if (idx >= MR) return;
+    const uint2 zv = make_uint2(T::pack2(zs[0], zs[1]), T::pack2(zs[2], zs[3]));
+    *reinterpret_cast<uint2*>(zl + idx) = zv;
+    if (blockIdx.x == 0 && e == 0) *reinterpret_cast<uint2*>(Z + idx) = zv;
+  };
+  uint4 pa[8], pb[8], b0[8], b1[8], za[8];
+  load_part(0, pa, pb);
+  load_b(0, b0);
+  load_b(32, b1);
+  load_z(0, 4 * t, za);
+  {
+    float zs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    fin_add4(zs, za);
+    for (int s0 = 8; s0 < splits; s0 += 8) {
+      load_z(s0, 4 * t, za);
+      fin_add4(zs, za);
+    }
+    store_z(4 * t, zs);
+  }
+  for (int64_t base = 1024; base < MR; base += 1024) {
+    float zs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int s0 = 0; s0 < splits; s0 += 8) {
-      uint4 za[8], zb[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const uint32_t off = (zok && s0 + k < splits) ? static_cast<uint32_t>((((s0 + k) * M + q) * r + jb) * 4) : kMasked;
-        za[k] = ld_b128(rzp, off);
-        zb[k] = ld_b128(rzp, off == kMasked ? kMasked : off + 16);
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (s0 + k >= splits) break;
-        zs[0] += __builtin_bit_cast(float, za[k].x); zs[1] += __builtin_bit_cast(float, za[k].y);
-        zs[2] += __builtin_bit_cast(float, za[k].z); zs[3] += __builtin_bit_cast(float, za[k].w);
-        zs[4] += __builtin_bit_cast(float, zb[k].x); zs[5] += __builtin_bit_cast(float, zb[k].y);
-        zs[6] += __builtin_bit_cast(float, zb[k].z); zs[7] += __builtin_bit_cast(float, zb[k].w);
-      }
+      load_z(s0, base + 4 * t, za);
+      fin_add4(zs, za);
     }
-    uint4 zv = make_uint4(0, 0, 0, 0);
-    if (zok) {
-      zv = make_uint4(T::pack2(zs[0], zs[1]), T::pack2(zs[2], zs[3]), T::pack2(zs[4], zs[5]),
-                      T::pack2(zs[6], zs[7]));
-      if (blockIdx.x == 0 && e == 0) *reinterpret_cast<uint4*>(Z + q * r + jb) = zv;
-    }
+    store_z(base + 4 * t, zs);
+  }
+  __syncthreads();
+  f32x4 accl[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) accl[i] = f32x4{0, 0, 0, 0};
+  auto lora_step = [&](int64_t j0, const uint4 (&rows8)[8]) {
+    const int64_t jb = j0 + 8 * g;
+    const uint4 zv = (q < M && jb < r) ? *reinterpret_cast<const uint4*>(zl + q * r + jb) : make_uint4(0, 0, 0, 0);
+    uint4 cols8[8];
     transpose8x8_bf16(rows8, cols8);
 #pragma unroll
     for (int tc = 0; tc < 8; ++tc)
       accl[tc] = T::mfma16(__builtin_bit_cast(typename T::v8, zv), __builtin_bit_cast(typename T::v8, cols8[tc]), accl[tc]);
+  };
+  lora_step(0, b0);
+  if (r > 32) lora_step(32, b1);
+  for (int64_t j0 = 64; j0 < r; j0 += 32) {
+    load_b(j0, b0);
+    lora_step(j0, b0);
   }
-  const int64_t m = 4 * g + e;
-  if (m >= M || !n_ok) return;
-  float v[8];
-#pragma unroll
-  for (int tc = 0; tc < 8; ++tc) v[tc] = 0.0f;
-  for (int s0 = 0; s0 < splits; s0 += 8) {
-    uint4 pa[8], pb[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t off = (s0 + k < splits) ? static_cast<uint32_t>((((s0 + k) * M + m) * N + n) * 4) : kMasked;
-      pa[k] = ld_b128(rp, off);
-      pb[k] = ld_b128(rp, off == kMasked ? kMasked : off + 16);
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (s0 + k >= splits) break;
-      v[0] += __builtin_bit_cast(float, pa[k].x); v[1] += __builtin_bit_cast(float, pa[k].y);
-      v[2] += __builtin_bit_cast(float, pa[k].z); v[3] += __builtin_bit_cast(float, pa[k].w);
-      v[4] += __builtin_bit_cast(float, pb[k].x); v[5] += __builtin_bit_cast(float, pb[k].y);
-      v[6] += __builtin_bit_cast(float, pb[k].z); v[7] += __builtin_bit_cast(float, pb[k].w);
-    }
+  if (!out_ok) return;
+  float v[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  fin_add8(v, pa, pb);
+  for (int s0 = 8; s0 < splits; s0 += 8) {
+    load_part(s0, pa, pb);
+    fin_add8(v, pa, pb);
   }
   uint4 o;
   o.x = T::pack2(v[0] + c * accl[0][e], v[1] + c * accl[1][e]);
@@ -439,7 +477,7 @@ hipError_t launch_gemv(int64_t M, int64_t K, int64_t N, int64_t r, const uint16_
   tm.stop();
   Timer te(QK_REDUCE, stream);
   const unsigned phases = static_cast<unsigned>(M < 4 ? M : 4);   // rows 4g + e, e < phases
-  hipLaunchKernelGGL(dtype == kDtypeF16 ? gemv_finish_kernel<F16> : gemv_finish_kernel<Bf16>, dim3(static_cast<unsigned>(cdiv(N, 128)), phases), dim3(64), 0, stream,
+  hipLaunchKernelGGL(dtype == kDtypeF16 ? gemv_finish_kernel<F16> : gemv_finish_kernel<Bf16>, dim3(static_cast<unsigned>(cdiv(N, kFinCols)), phases), dim3(256), 0, stream,
                      static_cast<const float*>(part), static_cast<int>(p.gv_splits), M, N,
                      static_cast<const float*>(zpart), Z, B, r, c, Y);
   te.stop();
