@@ -142,24 +142,29 @@ __global__ __launch_bounds__(256) void rowsum_kernel(RsArgs a) {
 // ------------------------------------------------------------ column sums
 // part[split][c][j] = sum, over this split's tokens, of act[m][c] * v[m][j]
 // (both token-major).  A workgroup owns a 64-column x 64-j block; its tokens
-// are divided among the 4 waves, and each wave streams 16-token steps (16
-// activation rows of 64 columns and 16 rows of v, 128 bytes each) through its
-// own ring of kCsSlots LDS slots, so waves never wait for each other.  Within
-// a slot, 16-byte chunk c of row R sits at c ^ (((R >> 1) & 1) << 2), which
+// are divided among its 4 waves, and each wave streams 16-token steps
+// (16 activation rows of 64 columns and 16 rows of v, 128 bytes each) through
+// its own ring of kCsSlots LDS slots, so waves never wait for each other.
+// Rings of four slots (64 KB per workgroup) let two workgroups share a CU,
+// which streams these 128-byte row pieces faster than deeper rings.  Within a
+// slot, 16-byte chunk c of row R sits at c ^ (((R >> 1) & 1) << 2), which
 // keeps the transposing reads below free of bank conflicts.  The MFMA
 // operands (8 consecutive tokens of one column per lane) come from
 // ds_read_b64_tr_b16: in each 16-lane group, lane L names the 4 values of
 // row L/4, columns 4(L%4) .. +3 of a 4 x 16 block, and receives column L of
-// that block.  The four waves' sums are added in LDS in wave order.
+// that block.  The waves' sums are added in LDS in a fixed order.
 #ifndef QN_CS_SLOTS
-#define QN_CS_SLOTS 8
+#define QN_CS_SLOTS 4
 #endif
 #ifndef QN_CS_WGS
 #define QN_CS_WGS 256
 #endif
 constexpr int kCsSlots = QN_CS_SLOTS;
 constexpr int kCsSlot = 2 * 16 * 128;
-constexpr int kCsLds = 4 * kCsSlots * kCsSlot;   // 128 KB
+constexpr int kCsRing = kCsSlots * kCsSlot;
+constexpr int kCsBlock = 64 * 64 * 4;   // one wave's 64 x 64 fp32 sums, for the epilogue
+static_assert(kCsRing >= kCsBlock, "column sums: each wave's epilogue block lives in its own ring");
+constexpr int kCsLds = 4 * kCsRing;
 
 struct CsJob {
   const uint16_t* act;   // M x cols, leading dimension ld
@@ -193,6 +198,35 @@ struct CsJobs {
   CsJob j[kCsJobs];
 };
 
+// A wave's 64 x 64 fp32 sums in an epilogue block.  Lane (h = lane/32,
+// c = 32 ci + lane%32) holds j = 32 vj + 8 jj + 4 h + e.
+// - Partials, [c][j]: groups of 4 j are stored as 16-byte words, the group
+//   index XORed with c % 16 so that the lanes' words spread over the banks.
+// - Transposed, [j][c]: single floats, bit 5 of c flipped on every other
+//   group of 4 rows, so that the two half-waves' stores fall on different banks.
+__device__ __forceinline__ int cs_pos_part(int c, int j) { return c * 64 + (j ^ (4 * (c & 15))); }
+__device__ __forceinline__ int cs_pos_tr(int j, int c) { return j * 64 + (c ^ (((j >> 2) & 1) << 5)); }
+
+// this lane's sums into a wave's epilogue block
+__device__ __forceinline__ void cs_block(float* blk, bool tr, const f32x16 (&acc)[2][2], int lane) {
+  const int h = lane >> 5, cl = lane & 31;
+#pragma unroll
+  for (int vj = 0; vj < 2; ++vj)
+#pragma unroll
+    for (int ci = 0; ci < 2; ++ci)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int c = 32 * ci + cl, j = 32 * vj + 8 * jj + 4 * h;
+        if (tr) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) blk[cs_pos_tr(j + e, c)] = acc[vj][ci][4 * jj + e];
+        } else {
+          *reinterpret_cast<f32x4*>(blk + cs_pos_part(c, j)) =
+              f32x4{acc[vj][ci][4 * jj], acc[vj][ci][4 * jj + 1], acc[vj][ci][4 * jj + 2], acc[vj][ci][4 * jj + 3]};
+        }
+      }
+}
+
 template <class T>
 __global__ __launch_bounds__(256) void colsum_kernel(CsJobs jobs, int64_t M) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -212,7 +246,7 @@ __global__ __launch_bounds__(256) void colsum_kernel(CsJobs jobs, int64_t M) {
   const int64_t share = (((me - mb) + 63) / 64) * 16;   // tokens per wave, a multiple of 16
   const int64_t wb = mb + wave * share, we = min(me, wb + share);
   const int64_t nsteps = we > wb ? (we - wb + 15) / 16 : 0;
-  char* ring = smem + wave * (kCsSlots * kCsSlot);
+  char* ring = smem + wave * kCsRing;
   const int64_t r = J.r;
   const Rsrc ra = make_rsrc(J.act, ((M - 1) * J.ld + J.cols) * 2), rv = make_rsrc(J.v, ((M - 1) * J.v_ld + r) * 2);
   // copy i (0..1) of each operand fills slot rows 8i .. 8i+7: lane -> row
@@ -282,60 +316,37 @@ __global__ __launch_bounds__(256) void colsum_kernel(CsJobs jobs, int64_t M) {
       for (int ci = 0; ci < 2; ++ci) acc[vj][ci] = T::mfma32(fv[vj], fa[ci], acc[vj][ci]);
   }
   __builtin_amdgcn_s_waitcnt(0);
-  if (J.transposed) {
-    // each wave's block as [j][c] (rows of 72 floats: the two half-waves'
-    // stores fall on different banks), then the fixed-order wave sum, scaled,
-    // stored along the columns
-    constexpr int kLd = 72;
-    float* mine = reinterpret_cast<float*>(ring);
-    const int h = lane >> 5, cl = lane & 31;
-#pragma unroll
-    for (int vj = 0; vj < 2; ++vj)
-#pragma unroll
-      for (int ci = 0; ci < 2; ++ci)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) mine[(32 * vj + 8 * jj + 4 * h + e) * kLd + 32 * ci + cl] = acc[vj][ci][4 * jj + e];
-    __syncthreads();
-    const int j = t >> 2, cq = 16 * (t & 3);
+  // Each wave's 64 x 64 sums go to the start of its own ring (its last reads
+  // of the ring are done); the final sum is block 0 + 1 + 2 + 3.
+  const bool tr = J.transposed != 0;
+  float* blocks = reinterpret_cast<float*>(smem);
+  cs_block(reinterpret_cast<float*>(ring), tr, acc, lane);
+  __syncthreads();
+  // thread t: row t / 4 of the 64 x 64 block, four groups of 4 along it
+  const int row = t >> 2, q0 = 16 * (t & 3);
+  if (tr) {
+    // row = j; the scaled sum is stored along the columns of the r x cols result
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int c = cq + 4 * u;
-      f32x4 s4 = *reinterpret_cast<const f32x4*>(smem + (j * kLd + c) * 4);
+      const int c = q0 + 4 * u, pos = cs_pos_tr(row, c);
+      f32x4 s4 = *reinterpret_cast<const f32x4*>(blocks + pos);
 #pragma unroll
-      for (int w = 1; w < 4; ++w) s4 += *reinterpret_cast<const f32x4*>(smem + w * (kCsSlots * kCsSlot) + (j * kLd + c) * 4);
+      for (int w = 1; w < 4; ++w) s4 += *reinterpret_cast<const f32x4*>(blocks + w * (kCsRing / 4) + pos);
       s4 *= J.scale;
-      if (c0 + c < J.cols && jb + j < r) *reinterpret_cast<f32x4*>(J.part + (jb + j) * J.cols + c0 + c) = s4;
+      if (c0 + c < J.cols && jb + row < r) *reinterpret_cast<f32x4*>(J.part + (jb + row) * J.cols + c0 + c) = s4;
     }
     return;
   }
-  // each wave's 64 x 64 block, [c][j] fp32, into the start of its own ring
   {
-    float* mine = reinterpret_cast<float*>(ring);
-    const int h = lane >> 5, cl = lane & 31;
-#pragma unroll
-    for (int vj = 0; vj < 2; ++vj)
-#pragma unroll
-      for (int ci = 0; ci < 2; ++ci)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int c = 32 * ci + cl, j = 32 * vj + 8 * jj + 4 * h;
-          *reinterpret_cast<f32x4*>(mine + c * 64 + j) =
-              f32x4{acc[vj][ci][4 * jj], acc[vj][ci][4 * jj + 1], acc[vj][ci][4 * jj + 2], acc[vj][ci][4 * jj + 3]};
-        }
-  }
-  __syncthreads();
-  {
-    const int c = t >> 2, jq = 16 * (t & 3);
+    // row = c; the split's partial, [c][j]
     float* out = J.part + split * J.cols * r;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int j = jq + 4 * u;
-      f32x4 s4 = *reinterpret_cast<const f32x4*>(smem + (c * 64 + j) * 4);
+      const int j = q0 + 4 * u, pos = cs_pos_part(row, j);
+      f32x4 s4 = *reinterpret_cast<const f32x4*>(blocks + pos);
 #pragma unroll
-      for (int w = 1; w < 4; ++w) s4 += *reinterpret_cast<const f32x4*>(smem + w * (kCsSlots * kCsSlot) + (c * 64 + j) * 4);
-      if (c0 + c < J.cols && jb + j < r) *reinterpret_cast<f32x4*>(out + (c0 + c) * r + jb + j) = s4;
+      for (int w = 1; w < 4; ++w) s4 += *reinterpret_cast<const f32x4*>(blocks + w * (kCsRing / 4) + pos);
+      if (c0 + row < J.cols && jb + j < r) *reinterpret_cast<f32x4*>(out + (c0 + row) * r + jb + j) = s4;
     }
   }
 }
