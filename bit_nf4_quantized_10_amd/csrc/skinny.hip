@@ -38,19 +38,28 @@ TJob tjob(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t cols, float 
 // ------------------------------------------------------------ row sums
 // part[split][m][j] = sum, over this split's share of the reduction, of
 // act[m][k] * wt[j][k]; both operands contiguous along k.  A workgroup owns a
-// 64-row x 64-column output block (columns j0 .. j0+63): four waves of 16 rows
-// x 4 tiles of v_mfma_f32_16x16x32_bf16.  64-wide stages flow through a ring
-// of kRsSlots LDS slots (64 activation rows, then 64 weight rows, 128 bytes
-// each, 16-byte chunk c of row R at c ^ (R & 7)), filled by buffer loads with
-// the LDS destination three stages ahead; one barrier per stage.  The weight
-// rows are shared by the four waves, so each weight slice is fetched once per
-// 64 activation rows.
+// 128-row x 64-column output block (columns j0 .. j0+63): eight waves of 16
+// rows x 4 tiles of v_mfma_f32_16x16x32_bf16.  64-wide stages flow through a
+// ring of kRsSlots LDS slots (128 activation rows, then 64 weight rows, 128
+// bytes each, 16-byte chunk c of row R at c ^ (R & 7)), filled by buffer loads
+// with the LDS destination three stages ahead; one barrier per stage.  The
+// weight rows are shared by the eight waves, so each weight slice is fetched
+// once per 128 activation rows.  One such workgroup per CU (96 KB of LDS)
+// streams faster than two of half the size.
 #ifndef QN_RS_SLOTS
 #define QN_RS_SLOTS 4
 #endif
+#ifndef QN_RS_WAVES
+#define QN_RS_WAVES 8
+#endif
 constexpr int kRsSlots = QN_RS_SLOTS;
-constexpr int kRsSlot = 2 * 64 * 128;
+constexpr int kRsWaves = QN_RS_WAVES;   // 16 activation rows each
+static_assert(kRsWaves == 4 || kRsWaves == 8, "row sums: 4 or 8 waves");
+constexpr int kRsRows = 16 * kRsWaves;
+constexpr int kRsActBytes = kRsRows * 128;
+constexpr int kRsSlot = kRsActBytes + 64 * 128;
 constexpr int kRsLds = kRsSlots * kRsSlot;
+constexpr int kRsWtCopies = 8 / kRsWaves;   // 8-row weight copies per wave and stage
 
 struct RsArgs {
   const uint16_t* act;
@@ -63,54 +72,61 @@ struct RsArgs {
 __device__ __forceinline__ int rs_off(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
 
 template <class T>
-__global__ __launch_bounds__(256) void rowsum_kernel(RsArgs a) {
+__global__ __launch_bounds__(64 * kRsWaves) void rowsum_kernel(RsArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int t = threadIdx.x, lane = t & 63, q = lane & 15, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t rb = blockIdx.x % a.row_blocks, rest = blockIdx.x / a.row_blocks;
-  const int64_t m0 = rb * 64, j0 = (rest % a.j_chunks) * 64, split = rest / a.j_chunks;
+  const int64_t m0 = rb * kRsRows, j0 = (rest % a.j_chunks) * 64, split = rest / a.j_chunks;
   const int64_t beg = split * a.per_split;
   const int64_t len = min(a.red, beg + a.per_split) - beg;
   const int64_t nst = (len + 63) / 64;
   const Rsrc ra = make_rsrc(a.act, ((a.M - 1) * a.act_ld + a.red) * 2);
   const Rsrc rw = make_rsrc(a.wt, ((a.r - 1) * a.wt_ld + a.red) * 2);
-  // copy i (0..1) of each operand fills slot rows 16*wave + 8i .. +7; lane -> row
-  // 16*wave + 8i + lane/8, slot position lane & 7, global chunk (lane & 7) ^ (row & 7)
-  uint32_t av[2], wv[2];
-  int lim[2];
+  // activation copy i (0..1) fills slot rows 16*wave + 8i .. +7; weight copy
+  // i fills weight rows 8 (kRsWtCopies wave + i) .. +7; lane -> row + lane/8,
+  // slot position lane & 7, global chunk (lane & 7) ^ (row & 7)
+  uint32_t av[2], wv[kRsWtCopies];
+  int alim[2], wlim[kRsWtCopies];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int R = 16 * wave + 8 * i + (lane >> 3), c = (lane & 7) ^ (R & 7);
-    const int64_t m = m0 + R, j = j0 + R;
+    const int64_t m = m0 + R;
     av[i] = m < a.M ? static_cast<uint32_t>((m * a.act_ld + beg + 8 * c) * 2) : kMasked;
+    alim[i] = static_cast<int>(len - 8 * c);
+  }
+#pragma unroll
+  for (int i = 0; i < kRsWtCopies; ++i) {
+    const int R = 8 * (kRsWtCopies * wave + i) + (lane >> 3), c = (lane & 7) ^ (R & 7);
+    const int64_t j = j0 + R;
     wv[i] = j < a.r ? static_cast<uint32_t>((j * a.wt_ld + beg + 8 * c) * 2) : kMasked;
-    lim[i] = static_cast<int>(len - 8 * c);
+    wlim[i] = static_cast<int>(len - 8 * c);
   }
   auto copy = [&](int64_t s, int b) {
     const int64_t k0 = s * 64;
     const uint32_t soff = static_cast<uint32_t>(k0 * 2);
     char* slot = smem + b * kRsSlot;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const bool ok = k0 < lim[i];
+    for (int i = 0; i < 2; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + (16 * wave + 8 * i) * 128), 16,
-                                               ok ? av[i] : kMasked, soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(slot + 8192 + (16 * wave + 8 * i) * 128), 16,
-                                               ok ? wv[i] : kMasked, soff, 0, 0);
-    }
+                                               k0 < alim[i] ? av[i] : kMasked, soff, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kRsWtCopies; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(slot + kRsActBytes + 8 * (kRsWtCopies * wave + i) * 128),
+                                               16, k0 < wlim[i] ? wv[i] : kMasked, soff, 0, 0);
   };
   f32x4 acc[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) acc[u] = f32x4{0, 0, 0, 0};
-  // Stage x goes to slot x % S, S - 1 stages ahead (4 copies per wave per
-  // stage); no copies are issued past the last stage.
-  constexpr int S = kRsSlots;
+  // Stage x goes to slot x % S, S - 1 stages ahead (2 + kRsWtCopies copies
+  // per wave per stage); no copies are issued past the last stage.
+  constexpr int S = kRsSlots, kCopies = 2 + kRsWtCopies;
   for (int x = 0; x < S - 1; ++x)
     if (x < nst) copy(x, x);
   int b = 0;
   for (int64_t s = 0; s < nst; ++s) {
     // own copies of stage s landed (later stages may still be in flight)
-    if (s + S - 2 < nst) __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 * (S - 2), 0));
+    if (s + S - 2 < nst) __builtin_amdgcn_s_waitcnt(waitcnt_imm(kCopies * (S - 2), 0));
     else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     __builtin_amdgcn_s_barrier();   // everyone's; slot of stage s-1 released
     if (s + S - 1 < nst) copy(s + S - 1, b == 0 ? S - 1 : b - 1);
@@ -121,7 +137,7 @@ __global__ __launch_bounds__(256) void rowsum_kernel(RsArgs a) {
       const typename T::v8 af = *reinterpret_cast<const typename T::v8*>(slot + rs_off(16 * wave + q, 4 * st + g));
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const typename T::v8 wf = *reinterpret_cast<const typename T::v8*>(slot + 8192 + rs_off(16 * u + q, 4 * st + g));
+        const typename T::v8 wf = *reinterpret_cast<const typename T::v8*>(slot + kRsActBytes + rs_off(16 * u + q, 4 * st + g));
         acc[u] = T::mfma16(af, wf, acc[u]);
       }
     }
@@ -387,7 +403,7 @@ hipError_t rowsum_launch_t(const RsArgs& a, int64_t splits, hipStream_t stream) 
   static const hipError_t lds_limit = hipFuncSetAttribute(reinterpret_cast<const void*>(&rowsum_kernel<T>),
                                                           hipFuncAttributeMaxDynamicSharedMemorySize, kRsLds);
   if (lds_limit != hipSuccess) return lds_limit;
-  hipLaunchKernelGGL(rowsum_kernel<T>, dim3(static_cast<unsigned>(a.row_blocks * a.j_chunks * splits)), dim3(256),
+  hipLaunchKernelGGL(rowsum_kernel<T>, dim3(static_cast<unsigned>(a.row_blocks * a.j_chunks * splits)), dim3(64 * kRsWaves),
                      kRsLds, stream, a);
   return hipGetLastError();
 }
@@ -395,7 +411,7 @@ hipError_t rowsum_launch_t(const RsArgs& a, int64_t splits, hipStream_t stream) 
 hipError_t launch_rowsum(const uint16_t* act, const uint16_t* wt, int64_t M, int64_t r, int64_t red, int64_t splits,
                          int64_t per, float* part, hipStream_t stream, int64_t act_ld = 0, int64_t wt_ld = 0,
                          int dtype = kDtypeBf16) {
-  const RsArgs a{act, wt, M, r, red, per, cdiv(M, 64), cdiv(r, 64), part, act_ld ? act_ld : red, wt_ld ? wt_ld : red};
+  const RsArgs a{act, wt, M, r, red, per, cdiv(M, kRsRows), cdiv(r, 64), part, act_ld ? act_ld : red, wt_ld ? wt_ld : red};
   return dtype == kDtypeF16 ? rowsum_launch_t<F16>(a, splits, stream) : rowsum_launch_t<Bf16>(a, splits, stream);
 }
 
@@ -423,13 +439,13 @@ hipError_t launch_colsum(const CsJob* jobs, int n, int64_t M, hipStream_t stream
 
 // ------------------------------------------------------------ plans
 #ifndef QN_ROWSUM_WAVES
-#define QN_ROWSUM_WAVES 512   // target number of row-sum workgroups
+#define QN_ROWSUM_WAVES 256   // target number of row-sum workgroups
 #endif
 SkinnyPlan plan_skinny(int64_t M, int64_t K, int64_t N, int64_t r) {
   SkinnyPlan p{};
-  // row sums: 64-row blocks x 64-wide column chunks, split along the
-  // reduction into multiples of 256 until ~512 workgroups (2 per CU)
-  const int64_t rs_tiles = cdiv(M, 64) * cdiv(r, 64);
+  // row sums: 128-row blocks x 64-wide column chunks, split along the
+  // reduction into multiples of 256 until ~256 workgroups (1 per CU)
+  const int64_t rs_tiles = cdiv(M, kRsRows) * cdiv(r, 64);
   split_plan(rs_tiles, K, QN_ROWSUM_WAVES, 256, &p.z_splits, &p.z_per);
   split_plan(rs_tiles, N, QN_ROWSUM_WAVES, 256, &p.dz_splits, &p.dz_per);
   // column sums: 64-column blocks of dA and dB together, split along the
