@@ -241,6 +241,17 @@ def main():
 
     q_ms = part(lambda i: [qn.nf4_quantize(m["W"], m["state"], qws, status) for m in mats])
     l_ms = part(lambda i: [run_linear(qn, m, ws) for m in mats])
+
+    # every dense GEMM launch of the step (7 forwards and 7 dX), timed with
+    # the library timers over 5 layer passes: the GEMM kernel's rate over the
+    # whole step, beside the single dominant launch of `roofline`
+    gemm_flops = sum(kernel_flops(k, m["M"], m["K"], m["N"], m["r"]) for m in mats for k in ("fwd_gemm", "bwd_dx"))
+    for k in ("fwd_gemm", "bwd_dx"):
+        qn.qlora_timer_enable(k, True)
+    part(lambda i: [run_linear(qn, m, ws) for m in mats], n=5)
+    g_ms = sum(qn.qlora_timer_read(k)[0] for k in ("fwd_gemm", "bwd_dx")) / 5
+    for k in ("fwd_gemm", "bwd_dx"):
+        qn.qlora_timer_enable(k, False)
     qbytes = 0
     for m in mats:
         sz = qn.nf4_sizes(m["K"] * m["N"])
@@ -253,7 +264,13 @@ def main():
                                      "layers_TFLOPs": round(flops / (l_ms * 1e-3) / 1e12, 1),
                                      "layers_frac_bf16_peak": round(flops / (l_ms * 1e-3) / 1e12
                                                                     / MFMA_BF16_PEAK_TFLOPS, 4),
-                                     "how": "20 back-to-back passes of each half alone"}}
+                                     "how": "20 back-to-back passes of each half alone"},
+                  "dense_gemms_of_step": {"ms_per_step": round(g_ms, 4), "flops_per_step": gemm_flops,
+                                          "TFLOPs": round(gemm_flops / (g_ms * 1e-3) / 1e12, 1),
+                                          "frac_bf16_peak": round(gemm_flops / (g_ms * 1e-3) / 1e12
+                                                                  / MFMA_BF16_PEAK_TFLOPS, 4),
+                                          "how": "the 14 dense GEMM launches of a layers pass (every forward and "
+                                                 "dX, M >= 192 path), each timed on its dispatch packet, 5 passes"}}
     cpu = None if args.no_cpu else cpu_baseline(host, flops)
     del host
     if not args.no_components:
