@@ -342,6 +342,60 @@ def test_layer_random_shapes_match_oracle(M, K, N, r, c):
         assert v <= TOL, (k, v)
 
 
+# Large-M shapes across the GEMMs' work plans: output tile counts from 6 to
+# 200 (256 x 256 tiles), unsplit and split 2 to 32 ways, ragged M, K and N,
+# on the fused (M < 192) and the two-pass (M >= 192) paths.  Every 256 x 256
+# output tile must meet the tolerance on its own.
+SPLIT_PLAN_SHAPES = [
+    (192, 2048, 4096, 64, 0.25),    # forward 16 tiles in 8 splits; dX 8 tiles in 16
+    (176, 4104, 1600, 16, 0.5),     # fused forward 7 tiles, ragged last stage; fused dX 17 tiles
+    (448, 1032, 8192, 32, 0.5),     # forward 64 tiles in 2 splits; dX 10 tiles in 18
+    (960, 264, 11008, 16, 2.0),     # forward 172 tiles unsplit; dX 8 tiles in 32 (ragged K)
+    (2000, 520, 6400, 24, 0.25),    # forward 200 tiles unsplit; dX 24 tiles in 8
+    (320, 8200, 768, 8, 1.0),       # forward 6 tiles in 32; dX 66 tiles in 3
+    (3000, 1280, 1280, 64, 0.5),    # 60 tiles in 2 splits each way
+]
+
+
+@pytest.mark.parametrize("M,K,N,r,c", SPLIT_PLAN_SHAPES)
+def test_layer_split_plans_match_oracle_per_tile(M, K, N, r, c):
+    say(f"layer work plans M={M} K={K} N={N} r={r}")
+    case = _layer_case(M, K, N, r, c, seed=M * 3 + K + N)
+    state, Y, Z, dX, dA, dB = _run_layer(case, M, K, N, r)
+    W_hat = o.dequantize(o.quantize(case["W"]), "bf16").reshape(K, N)
+    Yr, Zr = o.layer_forward(case["X"], W_hat, case["A"], case["B"], c)
+    dXr, dAr, dBr, _ = o.layer_backward(case["G"], case["X"], W_hat, case["A"], case["B"], c)
+    for got, ref, name in ((Y, Yr, "Y"), (Z, Zr, "Z"), (dX, dXr, "dX"), (dA, dAr, "dA"), (dB, dBr, "dB")):
+        g = host(got).astype(np.float64)
+        assert rel_err(g, ref) <= TOL, (name, rel_err(g, ref))
+        if name in ("Y", "dX"):
+            for i in range(0, ref.shape[0], 256):
+                for j in range(0, ref.shape[1], 256):
+                    e = rel_err(g[i:i + 256, j:j + 256], ref[i:i + 256, j:j + 256])
+                    assert e <= TOL, (name, i, j, e)
+
+
+@pytest.mark.parametrize("M,K,N,r", [(192, 2048, 4096, 64), (960, 264, 11008, 16), (320, 8200, 768, 8)])
+def test_layer_split_plans_exact_integer_case_bit_exact(M, K, N, r):
+    say(f"layer work plans, exact-integer M={M} K={K} N={N} r={r}")
+    case = _integer_case(M, K, N, r, seed=M + 7 * N)
+    # sparser X and G keep the long reductions inside bf16's exact range
+    rng = np.random.default_rng(M + K)
+    for k in ("X", "G"):
+        case[k] = case[k] * (rng.random(case[k].shape) < 0.3).astype(np.float32)
+        case[k + "b"] = si.to_bf16_bits(case[k])
+    state, Y, Z, dX, dA, dB = _run_layer(case, M, K, N, r)
+    W_hat = o.dequantize(o.quantize(case["W"]), "bf16").reshape(K, N)
+    Yr, Zr = o.layer_forward(case["X"], W_hat, case["A"], case["B"], case["c"])
+    dXr, dAr, dBr, _ = o.layer_backward(case["G"], case["X"], W_hat, case["A"], case["B"], case["c"])
+    for got, ref, name in ((Y, Yr, "Y"), (Z, Zr, "Z"), (dX, dXr, "dX")):
+        r32 = o.bf16_round(ref.astype(np.float32))
+        assert np.array_equal(r32, ref.astype(np.float32)), f"{name} not bf16-exact by construction"
+        np.testing.assert_array_equal(host(got), r32, err_msg=name)
+    np.testing.assert_array_equal(host(dA), dAr.astype(np.float32))
+    np.testing.assert_array_equal(host(dB), dBr.astype(np.float32))
+
+
 @pytest.mark.parametrize("M", [64, 256])   # fused path; two-pass path (dZ's sum then runs on its own)
 def test_layer_bwd_without_dx(M):
     K, N, r = 256, 128, 16
